@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs for the multi-row sparse-attention decode core.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark. It only draws random numbers and encodes them as bf16 bit patterns;
+it holds none of the decode method's arithmetic (no score, selection, gather or
+attention step lives here).
+
+Workloads (one "row" is one independent decode request):
+
+  config 0: 1 row, kv_len 1024
+  config 1: 8 rows, ragged kv_len drawn uniformly from [600, 8192]
+  config 2: 8 rows, kv_len 32768 each (the throughput shape)
+  config 3: 8 rows, kv_len {1, 37, 511, 512, 513, 4096, 65536, 131072},
+            indexer q/keys drawn from {-1, 0, 1} (heavy score ties)
+  config 4: 1 row, kv_len 1048576 (long context)
+
+Per row the indexer query is [64 heads, 128] bf16 and the indexer keys are
+[kv_len, 128] bf16, both integer-valued (uniform in [-4, 4], or {-1, 0, 1} for
+config 3); the head weights are integers uniform in [-2, 2] stored as f32.
+The attention query is [64 heads, 512] bf16 ~ N(0, 1), the shared key/value
+cache is [kv_len, 512] bf16 ~ N(0, 1) (keys equal values), and the learned
+per-head sink logits are one f32 [64] vector ~ N(0, 1) shared by all rows.
+
+Generation order is fixed so any consumer can regenerate the same bytes:
+  rng = numpy Generator(PCG64(20260000 + config_id))
+  [config 1 only: kv_len per row] -> indexer q [R,64,128] -> weights [R,64]
+  -> for each row: indexer keys [n_r,128] -> attention q [R,64,512]
+  -> sinks [64] -> for each row: kv [n_r,512]
+Large per-row arrays are drawn in chunks of 65536 rows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HEADS = 64
+INDEXER_DIM = 128
+HEAD_DIM = 512
+TOP_K = 512
+RATIO = 4
+CHUNK_ROWS = 65536
+SEED_BASE = 20260000
+
+CONFIG_NAMES = {
+    0: "1 row x 1024 keys",
+    1: "8 rows x ragged U[600,8192] keys",
+    2: "8 rows x 32768 keys",
+    3: "8 rows x {1,37,511,512,513,4096,65536,131072} keys, ternary indexer entries",
+    4: "1 row x 1048576 keys",
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns as uint16. Inputs here are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def int_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Encode small integers (|x| <= 256, exactly representable) as bf16 bits."""
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+@dataclass
+class RowsInputs:
+    """Host copies of one workload. Arrays of bf16 values are uint16 bit
+    patterns; everything is C-contiguous."""
+
+    config_id: int
+    kv_len: list[int]
+    start_pos: list[int]
+    offset: list[int]
+    idx_q: np.ndarray            # uint16 [R, 64, 128]
+    idx_w: np.ndarray            # float32 [R, 64]
+    idx_keys: list[np.ndarray]   # uint16 [n_r, 128] per row
+    attn_q: np.ndarray           # uint16 [R, 64, 512]
+    sinks: np.ndarray            # float32 [64]
+    kv: list[np.ndarray]         # uint16 [n_r, 512] per row
+    scale: float = float(np.float32(1.0 / np.sqrt(HEAD_DIM)))  # the f32 value both sides use
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return len(self.kv_len)
+
+    @property
+    def width(self) -> list[int]:
+        return [min(n, TOP_K) for n in self.kv_len]
+
+
+def config_kv_lens(config_id: int, rng: np.random.Generator | None = None) -> list[int]:
+    if config_id == 0:
+        return [1024]
+    if config_id == 1:
+        assert rng is not None
+        return [int(v) for v in rng.integers(600, 8192, size=8, endpoint=True)]
+    if config_id == 2:
+        return [32768] * 8
+    if config_id == 3:
+        return [1, 37, 511, 512, 513, 4096, 65536, 131072]
+    if config_id == 4:
+        return [1048576]
+    raise ValueError(f"unknown config {config_id}")
+
+
+def _int_rows(rng, n, cols, lo, hi):
+    out = np.empty((n, cols), dtype=np.uint16)
+    for s in range(0, n, CHUNK_ROWS):
+        e = min(n, s + CHUNK_ROWS)
+        out[s:e] = int_to_bf16_bits(rng.integers(lo, hi, size=(e - s, cols), endpoint=True))
+    return out
+
+
+def _normal_rows(rng, n, cols):
+    out = np.empty((n, cols), dtype=np.uint16)
+    for s in range(0, n, CHUNK_ROWS):
+        e = min(n, s + CHUNK_ROWS)
+        out[s:e] = f32_to_bf16_bits(rng.standard_normal((e - s, cols), dtype=np.float32))
+    return out
+
+
+def make_config(config_id: int, seed: int | None = None) -> RowsInputs:
+    """Generate workload `config_id` with the fixed generation order."""
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + config_id if seed is None else seed))
+    kv_len = config_kv_lens(config_id, rng)
+    return make_rows(rng, kv_len, ternary=(config_id == 3), config_id=config_id)
+
+
+def make_rows(rng: np.random.Generator, kv_len: list[int], ternary: bool = False,
+              config_id: int = -1, start_pos: list[int] | None = None,
+              offset: list[int] | None = None) -> RowsInputs:
+    """Generate rows with the given key counts, in the fixed order.
+
+    start_pos defaults to 4 * kv_len - 1 (every cached compressed key is
+    causally visible) and offset to 0."""
+    R = len(kv_len)
+    lo, hi = (-1, 1) if ternary else (-4, 4)
+    idx_q = _int_rows(rng, R * HEADS, INDEXER_DIM, lo, hi).reshape(R, HEADS, INDEXER_DIM)
+    idx_w = rng.integers(-2, 2, size=(R, HEADS), endpoint=True).astype(np.float32)
+    idx_keys = [_int_rows(rng, n, INDEXER_DIM, lo, hi) for n in kv_len]
+    attn_q = _normal_rows(rng, R * HEADS, HEAD_DIM).reshape(R, HEADS, HEAD_DIM)
+    sinks = rng.standard_normal(HEADS, dtype=np.float32)
+    kv = [_normal_rows(rng, n, HEAD_DIM) for n in kv_len]
+    if start_pos is None:
+        start_pos = [RATIO * n - 1 for n in kv_len]
+    if offset is None:
+        offset = [0] * R
+    return RowsInputs(config_id, list(kv_len), list(start_pos), list(offset),
+                      idx_q, idx_w, idx_keys, attn_q, sinks, kv)
+
+
+def small_rows(seed: int, kv_len: list[int], ternary: bool = False, **kw) -> RowsInputs:
+    """Convenience for tests: the same recipe at arbitrary small sizes."""
+    return make_rows(np.random.Generator(np.random.PCG64(seed)), kv_len, ternary=ternary, **kw)

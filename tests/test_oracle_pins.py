@@ -1,0 +1,359 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks an oracle function against a closed form, an identity, a
+brute-force enumeration with an independent primitive, or a textbook reduction
+computed by a different library, so that a dropped term, a wrong sign or index,
+or a transposed operand in the oracle fails at least one of them.
+
+Sources: docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal" (the
+kernels named in each test) and "mlx-native 0.21.0 src/ops/deepseek_rows.rs".
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ds_oracle as O
+from sparse_attention_decode_04_amd import inputs as I
+
+RNG = np.random.default_rng(1234)
+
+
+def bits(x):
+    return I.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def rand_int_bits(shape, lo=-4, hi=4, rng=RNG):
+    return I.int_to_bf16_bits(rng.integers(lo, hi, size=shape, endpoint=True))
+
+
+# ---------------------------------------------------------------- bf16 decode
+
+def test_bf16_decode_matches_torch():
+    x = RNG.standard_normal(4096).astype(np.float32) * 100
+    b = bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(b), ref)
+    assert O.bf16_bits_to_f64(np.array([0x7F80], np.uint16))[0] == np.inf
+    assert O.bf16_bits_to_f64(np.array([0xFF80], np.uint16))[0] == -np.inf
+    assert np.isnan(O.bf16_bits_to_f64(np.array([0x7FC0], np.uint16))[0])
+    assert O.bf16_bits_to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
+
+
+# ------------------------------------------------------------- indexer score
+# deepseek_indexer_score_mma_rows_bf16
+
+def test_valid_count_closed_form():
+    assert O.valid_count(100, 4 * 100 - 1) == 100
+    assert O.valid_count(100, 4 * 100 + 7) == 100      # clipped to kv_len
+    assert O.valid_count(100, 2) == 0                  # (2+1)//4
+    assert O.valid_count(100, 3) == 1
+    assert O.valid_count(100, 42) == 10                # 43//4
+
+
+def test_scores_zero_keys_are_zero():
+    q = rand_int_bits((64, 128))
+    w = RNG.integers(-2, 2, 64, endpoint=True).astype(np.float32)
+    k = bits(np.zeros((37, 128)))
+    s = O.indexer_scores(q, w, k, 4 * 37 - 1)
+    np.testing.assert_array_equal(s, np.zeros(37, np.float32))
+
+
+def test_scores_one_hot_closed_form():
+    # q[h] = c_h e_{a_h}, k[j] = v_j e_{b_j}: dot = c_h v_j [a_h == b_j],
+    # so s[j] = sum over heads h with a_h == b_j of w_h * max(0, c_h v_j).
+    H, D, n = 64, 128, 50
+    a = RNG.integers(0, 8, H)
+    c = RNG.integers(-4, 4, H, endpoint=True)
+    b = RNG.integers(0, 8, n)
+    v = RNG.integers(-4, 4, n, endpoint=True)
+    w = RNG.integers(-2, 2, H, endpoint=True)
+    q = np.zeros((H, D)); q[np.arange(H), a] = c
+    k = np.zeros((n, D)); k[np.arange(n), b] = v
+    expect = np.zeros(n)
+    for j in range(n):
+        for h in range(H):
+            if a[h] == b[j] and c[h] * v[j] > 0:
+                expect[j] += w[h] * c[h] * v[j]
+    s = O.indexer_scores(bits(q), w.astype(np.float32), bits(k), 4 * n - 1)
+    np.testing.assert_array_equal(s, expect.astype(np.float32))
+
+
+def test_scores_relu_odd_part_identity():
+    # relu(x) - relu(-x) = x, so s(K) - s(-K) = K . (sum_h w_h q_h): a linear
+    # identity that holds only if the ReLU, the weights and the head/dim
+    # roles are all right.
+    q_i = RNG.integers(-4, 4, (64, 128), endpoint=True)
+    k_i = RNG.integers(-4, 4, (300, 128), endpoint=True)
+    w_i = RNG.integers(-2, 2, 64, endpoint=True)
+    s_pos = O.indexer_scores_f64(I.int_to_bf16_bits(q_i), w_i.astype(np.float32), I.int_to_bf16_bits(k_i))
+    s_neg = O.indexer_scores_f64(I.int_to_bf16_bits(q_i), w_i.astype(np.float32), I.int_to_bf16_bits(-k_i))
+    expect = k_i.astype(np.int64) @ (w_i.astype(np.int64) @ q_i.astype(np.int64))
+    np.testing.assert_array_equal(s_pos - s_neg, expect.astype(np.float64))
+
+
+def test_scores_homogeneous_and_permutation_invariant():
+    q_i = RNG.integers(-4, 4, (64, 128), endpoint=True)
+    k_i = RNG.integers(-2, 2, (80, 128), endpoint=True)
+    w = RNG.integers(-2, 2, 64, endpoint=True).astype(np.float32)
+    s = O.indexer_scores_f64(I.int_to_bf16_bits(q_i), w, I.int_to_bf16_bits(k_i))
+    s2 = O.indexer_scores_f64(I.int_to_bf16_bits(q_i), w, I.int_to_bf16_bits(2 * k_i))
+    np.testing.assert_array_equal(s2, 2 * s)
+    ph, pd = RNG.permutation(64), RNG.permutation(128)
+    s3 = O.indexer_scores_f64(I.int_to_bf16_bits(q_i[ph][:, pd]), w[ph], I.int_to_bf16_bits(k_i[:, pd]))
+    np.testing.assert_array_equal(s3, s)
+
+
+def test_scores_causal_mask_and_exactness():
+    n = 200
+    q = rand_int_bits((64, 128))
+    w = RNG.integers(-2, 2, 64, endpoint=True).astype(np.float32)
+    k = rand_int_bits((n, 128))
+    s64 = O.indexer_scores_f64(q, w, k)
+    # integer-valued inputs: integral sums far below 2^24, so fp32 is exact
+    assert np.all(s64 == np.round(s64)) and np.abs(s64).max() < 2 ** 24
+    for start_pos in (4 * n - 1, 4 * 77 + 2, 2, 3):
+        s = O.indexer_scores(q, w, k, start_pos)
+        v = O.valid_count(n, start_pos)
+        np.testing.assert_array_equal(s[:v], s64[:v].astype(np.float32))
+        assert np.all(s[v:] == -np.inf)
+
+
+def test_scores_worst_case_magnitude_fits_fp32():
+    # |dot| <= 128*16 = 2048 and |s| <= 64*2*2048 = 262144 < 2^24.
+    q = I.int_to_bf16_bits(np.full((64, 128), 4))
+    k = I.int_to_bf16_bits(np.full((2, 128), 4))
+    w = np.full(64, 2, np.float32)
+    s = O.indexer_scores(q, w, k, 7)
+    assert s[0] == 262144.0 and s[1] == 262144.0
+
+
+def test_scores_non_finite_keys():
+    q = I.int_to_bf16_bits(np.ones((64, 128)))
+    w = np.ones(64, np.float32)
+    k = np.zeros((3, 128), np.float32)
+    k[0, 5] = np.nan      # every dot NaN -> maxNum gives 0 -> score 0
+    k[1, 5] = np.inf      # every dot +inf -> score +inf -> excluded (-inf)
+    k[2, 5] = -np.inf     # every dot -inf -> ReLU 0 -> score 0
+    kb = I.f32_to_bf16_bits(np.where(np.isfinite(k), k, 0))
+    kb[0, 5], kb[1, 5], kb[2, 5] = 0x7FC0, 0x7F80, 0xFF80
+    s = O.indexer_scores(q, w, kb, 11)
+    assert s[0] == 0.0 and s[1] == -np.inf and s[2] == 0.0
+
+
+# ---------------------------------------------------------------------- top-k
+# index_rows_better, deepseek_indexer_topk_{block,merge,finalize}_rows_i32
+
+def brute_topk(scores, valid, offset, k=512):
+    cand = [j for j in range(min(valid, len(scores))) if math.isfinite(float(scores[j]))]
+    cand = sorted(cand, key=lambda j: (-float(scores[j]), j))[:k]
+    return [j + offset for j in cand] + [-1] * (k - len(cand))
+
+
+@pytest.mark.parametrize("n,levels,valid_frac,offset", [
+    (1, 3, 1.0, 0), (37, 3, 1.0, 0), (511, 5, 1.0, 0), (512, 5, 1.0, 7), (513, 4, 1.0, 0),
+    (1000, 3, 0.5, 0), (2048, 2, 1.0, 100), (4096, 50, 1.0, 0), (3000, 1000, 0.9, 0)])
+def test_topk_brute_force(n, levels, valid_frac, offset):
+    s = RNG.integers(-levels, levels, n).astype(np.float32)
+    s[RNG.random(n) < 0.05] = -np.inf
+    valid = int(n * valid_frac)
+    got = O.topk_select(s, valid, offset)
+    assert got.tolist() == brute_topk(s, valid, offset)
+
+
+def test_topk_all_equal_scores_take_lowest_indices():
+    s = np.zeros(4096, np.float32)
+    np.testing.assert_array_equal(O.topk_select(s, 4096), np.arange(512))
+    np.testing.assert_array_equal(O.topk_select(s[:300], 300),
+                                  np.r_[np.arange(300), -np.ones(212)].astype(np.int32))
+
+
+def test_topk_increasing_scores_descending_indices():
+    s = np.arange(5000, dtype=np.float32)
+    np.testing.assert_array_equal(O.topk_select(s, 5000), np.arange(4999, 4999 - 512, -1))
+    np.testing.assert_array_equal(O.topk_select(s, 700), np.arange(699, 699 - 512, -1))
+
+
+def test_topk_ties_straddling_block_boundaries():
+    # equal scores on both sides of the 1024-key block edges: lower index first
+    s = np.zeros(8192, np.float32)
+    tie = np.r_[1000:1050, 2040:2060, 4090:4100, 5000:5500]
+    s[tie] = 7.0
+    s[[3, 9000 % 8192]] = 9.0
+    got = O.topk_select(s, 8192)
+    expect = [3, 808] + sorted(tie.tolist()) + [j for j in range(8192) if s[j] == 0][: 512 - 2 - len(tie)]
+    assert got.tolist() == expect[:512]
+
+
+def test_topk_signed_zero_ties_by_index():
+    s = np.array([0.0, -0.0, 0.0, -0.0, 1.0], np.float32)
+    assert O.topk_select(s, 5)[:5].tolist() == [4, 0, 1, 2, 3]
+
+
+def test_topk_excludes_non_finite_and_pads():
+    s = np.array([np.nan, 3.0, -np.inf, np.inf, 2.0, 3.0], np.float32)
+    got = O.topk_select(s, 6, offset=10)
+    assert got[:4].tolist() == [11, 15, 14, -1]
+
+
+# --------------------------------------------------------------------- gather
+# deepseek_sparse_attention_gather_rows_bf16
+
+def test_gather_is_bitwise_copy_with_sentinels_and_bad_slots():
+    n = 40
+    kv = I.f32_to_bf16_bits(RNG.standard_normal((n, 512)).astype(np.float32))
+    kv[7, 0] = 0x8000            # -0.0 must survive bitwise
+    kv[9, 100] = 0x7FC0          # NaN element
+    kv[11, 3] = 0xFF80           # -inf element
+    idx = np.array([5, -1, 7, 39, 9, 11, -2, 40, 0], np.int32)
+    g, sent, bad, inv = O.gather_row(kv, idx, n)
+    assert inv
+    assert sent.tolist() == [False, True, False, False, False, False, False, False, False]
+    assert bad.tolist() == [False, False, False, False, True, True, True, True, False]
+    for t, i in enumerate(idx):
+        if i in (5, 7, 39, 0):
+            np.testing.assert_array_equal(g[t], kv[i])
+    assert np.all(g[1] == 0) and np.all(g[6] == 0) and np.all(g[7] == 0)
+    exp9 = kv[9].copy(); exp9[100] = 0
+    exp11 = kv[11].copy(); exp11[3] = 0
+    np.testing.assert_array_equal(g[4], exp9)
+    np.testing.assert_array_equal(g[5], exp11)
+    assert g[2, 0] == 0x8000
+    _, _, _, inv2 = O.gather_row(kv, np.array([5, -1, 0]), n)
+    assert not inv2
+
+
+# ------------------------------------------------------------------ attention
+# deepseek_sparse_attention_{score,reduce,sanitize}_rows_bf16
+
+def sdpa_with_sink_reference(Q, G, sinks, scale):
+    """Textbook reduction: attention with a sink equals plain softmax attention
+    over the w keys plus one extra key whose logit is the sink and whose value
+    is zero. Computed with torch's float64 SDPA (an independent routine)."""
+    H, D = Q.shape
+    w = G.shape[0]
+    q = torch.from_numpy(Q)[None, :, None, :]                       # [1,H,1,D]
+    k = torch.cat([torch.from_numpy(G), torch.zeros(1, D, dtype=torch.float64)])
+    k = k[None, None].expand(1, H, w + 1, D).contiguous()
+    v = k.clone(); v[..., w, :] = 0
+    mask = torch.zeros(1, H, 1, w + 1, dtype=torch.float64)
+    mask[0, :, 0, w] = torch.from_numpy(np.asarray(sinks, np.float64))
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    return out[0, :, 0, :].numpy()
+
+
+def rand_attn(w, rng=RNG):
+    qb = I.f32_to_bf16_bits(rng.standard_normal((64, 512)).astype(np.float32))
+    gb = I.f32_to_bf16_bits(rng.standard_normal((w, 512)).astype(np.float32))
+    sinks = rng.standard_normal(64).astype(np.float32)
+    return qb, gb, sinks
+
+
+SCALE = float(np.float32(1 / np.sqrt(512)))
+
+
+@pytest.mark.parametrize("w", [1, 3, 64, 512])
+def test_attention_matches_sdpa_with_zero_value_sink_key(w):
+    qb, gb, sinks = rand_attn(w)
+    got = O.sparse_attention_row(qb, sinks, gb, np.zeros(w, bool), False, SCALE)
+    ref = sdpa_with_sink_reference(O.bf16_bits_to_f64(qb), O.bf16_bits_to_f64(gb), sinks, SCALE)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_sink_softmax_mass_sums_to_one():
+    for w in (1, 10, 512):
+        l = RNG.standard_normal(w) * 5
+        for s in (-3.0, 0.0, 4.0, 50.0):
+            p, ps, Z, m = O.sink_softmax(l, s)
+            assert abs(p.sum() + ps - 1.0) < 1e-12
+            assert np.all(p > 0) and 0 < ps <= 1
+            assert m == max(s, l.max())
+
+
+def test_attention_single_slot_closed_form():
+    # w = 1: out = v0 * sigmoid(l0 - s)
+    qb, gb, sinks = rand_attn(1)
+    Q, G = O.bf16_bits_to_f64(qb), O.bf16_bits_to_f64(gb)
+    got = O.sparse_attention_row(qb, sinks, gb, np.zeros(1, bool), False, SCALE)
+    l0 = SCALE * (Q @ G[0])
+    expect = G[0][None, :] / (1 + np.exp(sinks.astype(np.float64) - l0))[:, None]
+    np.testing.assert_allclose(got, expect, rtol=1e-6, atol=1e-8)
+
+
+def test_attention_zero_query_closed_form():
+    # q = 0: every logit is 0, so out = sum_t v_t / (w + e^s)
+    w = 37
+    _, gb, sinks = rand_attn(w)
+    qb = np.zeros((64, 512), np.uint16)
+    G = O.bf16_bits_to_f64(gb)
+    got = O.sparse_attention_row(qb, sinks, gb, np.zeros(w, bool), False, SCALE)
+    expect = G.sum(0)[None, :] / (w + np.exp(sinks.astype(np.float64)))[:, None]
+    np.testing.assert_allclose(got, expect, rtol=1e-6, atol=1e-8)
+
+
+def test_attention_very_negative_sink_is_plain_softmax():
+    w = 100
+    qb, gb, _ = rand_attn(w)
+    sinks = np.full(64, -1e4, np.float32)
+    got = O.sparse_attention_row(qb, sinks, gb, np.zeros(w, bool), False, SCALE)
+    Q, G = O.bf16_bits_to_f64(qb), O.bf16_bits_to_f64(gb)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None, :, None, :], torch.from_numpy(G)[None, None].expand(1, 64, w, 512).contiguous(),
+        torch.from_numpy(G)[None, None].expand(1, 64, w, 512).contiguous(), scale=SCALE)[0, :, 0].numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_attention_sentinels_are_dropped():
+    w = 20
+    qb, gb, sinks = rand_attn(w)
+    sent = np.zeros(w, bool); sent[[0, 5, 19]] = True
+    g0 = gb.copy(); g0[sent] = 0
+    got = O.sparse_attention_row(qb, sinks, g0, sent, False, SCALE)
+    keep = ~sent
+    ref = sdpa_with_sink_reference(O.bf16_bits_to_f64(qb), O.bf16_bits_to_f64(gb[keep]), sinks, SCALE)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+    # all slots sentinel: only the sink remains, output zero
+    all_s = O.sparse_attention_row(qb, sinks, np.zeros_like(gb), np.ones(w, bool), False, SCALE)
+    assert np.all(all_s == 0)
+
+
+def test_attention_fail_closed_zeroing():
+    w = 16
+    qb, gb, sinks = rand_attn(w)
+    base = O.sparse_attention_row(qb, sinks, gb, np.zeros(w, bool), False, SCALE)
+    assert np.all(np.abs(base).sum(1) > 0)
+    q2 = qb.copy(); q2[3, 17] = 0x7FC0       # NaN in head 3's query
+    s2 = sinks.copy(); s2[9] = np.inf        # non-finite sink of head 9
+    got = O.sparse_attention_row(q2, s2, gb, np.zeros(w, bool), False, SCALE)
+    zero = {3, 9}
+    for h in range(64):
+        if h in zero:
+            assert np.all(got[h] == 0)
+        else:
+            np.testing.assert_array_equal(got[h], base[h])
+    assert np.all(O.sparse_attention_row(qb, sinks, gb, np.zeros(w, bool), True, SCALE) == 0)
+
+
+# ------------------------------------------------------------------ multi-row
+
+def test_rows_are_independent():
+    inp = I.small_rows(77, [40, 600, 1500])
+    res = O.decode_rows(inp)
+    sub = I.RowsInputs(-1, [inp.kv_len[1]], [inp.start_pos[1]], [0], inp.idx_q[1:2], inp.idx_w[1:2],
+                       [inp.idx_keys[1]], inp.attn_q[1:2], inp.sinks, [inp.kv[1]])
+    one = O.decode_rows(sub)[0]
+    for key in ("scores", "indices", "gathered", "out"):
+        np.testing.assert_array_equal(res[1][key], one[key])
+
+
+def test_decode_row_pipeline_consistency():
+    inp = I.small_rows(5, [700])
+    r = O.decode_rows(inp)[0]
+    assert r["indices"].shape == (512,) and r["gathered"].shape == (512, 512)
+    idx = r["indices"]
+    np.testing.assert_array_equal(r["gathered"], inp.kv[0][idx])
+    # the selected keys are the 512 best: the worst selected is no worse than
+    # the best rejected
+    rejected = np.setdiff1d(np.arange(700), idx)
+    assert r["scores"][idx].min() >= r["scores"][rejected].max()
