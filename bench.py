@@ -1,0 +1,193 @@
+"""Throughput of the multi-row sparse-attention decode core on one MI355X.
+
+One step = the whole path for every row of the workload: indexer score ->
+top-512 -> gather -> sparse attention (the four C-ABI calls on one stream).
+Default workload: 8 rows x 32768 cached keys (64 heads x 128 indexer, top-512,
+64 heads x 512 attention), seeded synthetic inputs resident in HBM.
+
+Cache policy: `--copies` independent device copies of the inputs are used in
+rotation (default 8 x ~330 MB), so each step's 64 MiB of indexer keys was
+last touched 7 steps earlier, after ~2.3 GB of other traffic: the keys come
+from HBM, not from the 256 MB last-level cache. `--copies 1` measures the
+warm-cache case.
+
+Prints one JSON line (rank 0, N=1) with the headline value, per-call
+durations from HIP events on the launch stream, the roofline of the dominant
+kernel (the indexer score) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode rows/s (indexer+top-k+sparse attn), 8 rows×32k KV; % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--copies", type=int, default=8)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def indexer_bytes_flops(inp):
+    """Algorithmic HBM bytes and MFMA flops of one indexer-score launch:
+    per key 256 B of keys read + 4 B of score written and 64*128*2 flops;
+    per row 16 KiB of query and 256 B of weights read."""
+    keys = sum(inp.kv_len)
+    return keys * (256 + 4) + inp.rows * (64 * 128 * 2 + 64 * 4), keys * 64 * 128 * 2
+
+
+def step_bytes(inp):
+    """Algorithmic bytes of one whole step (all four calls)."""
+    w = [min(n, 512) for n in inp.kv_len]
+    idx_b, _ = indexer_bytes_flops(inp)
+    topk_b = sum(4 * n for n in inp.kv_len) + inp.rows * 512 * 4
+    gather_b = sum(wi * (1024 + 1024 + 4 + 2) for wi in w)
+    attn_b = sum(64 * 512 * 2 + wi * (1024 + 2) + 64 * 512 * 4 for wi in w) + 256
+    return idx_b + topk_b + gather_b + attn_b
+
+
+def cpu_baseline(inp, seconds):
+    from threadpoolctl import threadpool_info
+
+    from oracle import ds_oracle as O
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        O.decode_rows(inp)
+        rows += inp.rows
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": rows / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows // inp.rows} full oracle steps ({rows} rows of the same workload) in {el:.1f} s; "
+                      f"numpy float64/int64, BLAS threads={threads}, host cpu_count={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): rows are independent requests and "
+              "this build measures one GPU's share; see the sharding notes in the design document.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_decode_04_amd import ds_rows as ds
+    from sparse_attention_decode_04_amd import inputs as I
+    from sparse_attention_decode_04_amd.runner import DeviceInputs, DeviceRows
+
+    ds.load()
+    inp = I.make_config(args.config)
+    base = DeviceInputs(inp)
+    copies = [base]
+    for _ in range(args.copies - 1):
+        c = DeviceInputs.__new__(DeviceInputs)
+        c.inp, c.device = inp, base.device
+        c.idx_q, c.idx_w, c.attn_q, c.sinks = (base.idx_q.clone(), base.idx_w.clone(),
+                                               base.attn_q.clone(), base.sinks.clone())
+        c.keys = [k.clone() for k in base.keys]
+        c.kv = [k.clone() for k in base.kv]
+        copies.append(c)
+    runs = [DeviceRows(c) for c in copies]
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        runs[i % len(runs)].step()
+    torch.cuda.synchronize()
+
+    # Headline: K whole steps, bracketed by device synchronisation.
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        runs[i % len(runs)].step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    # Per-call durations: events around each call on the launch stream.
+    names = ("indexer_score", "topk", "gather", "sparse_attn")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        r = runs[i % len(runs)]
+        e = evs[i]
+        e[0].record(stream); r.indexer_score()
+        e[1].record(stream); r.topk()
+        e[2].record(stream); r.gather()
+        e[3].record(stream); r.sparse_attn()
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    per_call = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
+                for k, n in enumerate(names)}
+
+    idx_bytes, idx_flops = indexer_bytes_flops(inp)
+    idx_s = per_call["indexer_score"] * 1e-3
+    achieved = idx_bytes / idx_s / 1e9
+    rows_per_s = inp.rows / (ms_per_step * 1e-3)
+    keys_per_s = sum(inp.kv_len) / (ms_per_step * 1e-3)
+
+    out = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{I.CONFIG_NAMES[args.config]} (indexer 64x128 bf16 integer-valued, top-512, "
+                        f"sparse attention 64x512 bf16 with sinks, f32 out)",
+            "rows": inp.rows, "kv_len": inp.kv_len if len(set(inp.kv_len)) > 1 else inp.kv_len[0],
+            "top_k": 512, "cache": f"{args.copies} rotating input copies" if args.copies > 1 else "warm",
+        },
+        "keys_per_s": keys_per_s,
+        "step_algorithmic_gb_per_s": step_bytes(inp) / (ms_per_step * 1e-3) / 1e9,
+        "per_call_ms": per_call,
+        "wall_s_timed_region": wall,
+        "roofline": {
+            "kernel": "indexer_score_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": idx_bytes,
+            "mfma_tflops": idx_flops / idx_s / 1e12,
+            "mfma_frac_of_bf16_peak": idx_flops / idx_s / 1e12 / BF16_PEAK_TFLOPS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * ds_rows.h -- C ABI of the MI355X (gfx950) multi-row sparse-attention
+ * decode core.
+ *
+ * One call of each entry point serves up to DS_ROWS_MAX independent decode
+ * requests ("rows"), each with its own key caches, in a single launch
+ * sequence. Per row the path is
+ *
+ *   ds_rows_indexer_score  lightning-indexer score of every cached key
+ *   ds_rows_topk           deterministic causal top-512 of those scores
+ *   ds_rows_gather         copy of the selected rows of the shared KV
+ *   ds_rows_sparse_attn    attention over the gathered rows with a learned
+ *                          per-head sink
+ *
+ * Source pages (docs.rs source views of the Rust crate mlx-native):
+ *   [shader 0.18] "mlx-native 0.18.0 src/shaders/deepseek_rows.metal"
+ *   [host 0.21]   "mlx-native 0.21.0 src/ops/deepseek_rows.rs"
+ * Each entry point names the kernels and dispatch function whose
+ * computation and argument checks it provides.
+ *
+ * Conventions shared by every call
+ *   - Device pointers are plain HIP device addresses owned by the caller.
+ *     The library allocates nothing and keeps no state between calls.
+ *   - bf16 buffers hold raw bfloat16 bit patterns (uint16).
+ *   - Every `*_elems` / `*_bytes` argument is the capacity of the buffer
+ *     it follows; a call checks that each buffer is large enough.
+ *   - All argument checks run before anything is enqueued. A failed check
+ *     returns DS_ERR_INVALID_ARGUMENT, enqueues nothing and leaves a
+ *     message readable through ds_rows_last_error(). A failed launch returns
+ *     DS_ERR_HIP.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream) of the current HIP device and the call returns without
+ *     waiting for it. Calls on one stream run in order, so the four calls
+ *     chain without extra synchronisation.
+ *   - Bad data is not a call error: it is handled fail-closed (outputs are
+ *     zeroed), as described per call.
+ *   - Row r of a multi-row call produces, bit for bit, what a one-row call
+ *     on row r alone produces.
+ */
+#ifndef DS_ROWS_H
+#define DS_ROWS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS_ROWS_MAX 8          /* rows per call */
+#define DS_HEADS 64            /* indexer and attention heads */
+#define DS_INDEXER_DIM 128     /* indexer query/key width */
+#define DS_HEAD_DIM 512        /* attention query/KV width */
+#define DS_TOP_K 512           /* indices selected per row */
+#define DS_RATIO 4             /* query positions per compressed key */
+
+typedef enum {
+  DS_OK = 0,
+  DS_ERR_INVALID_ARGUMENT = 1,
+  DS_ERR_HIP = 2
+} ds_status;
+
+/* Per-row table of the indexer calls; the fields of the pages'
+ * DeepSeekIndexerRow ([host 0.21] DeepSeekIndexerRow,
+ * dispatch_deepseek_indexer_rows). Entries [rows, DS_ROWS_MAX) are ignored. */
+typedef struct {
+  uint32_t rows;                        /* 1..DS_ROWS_MAX */
+  uint32_t kv_len[DS_ROWS_MAX];         /* cached compressed keys, > 0 */
+  uint32_t start_pos[DS_ROWS_MAX];      /* absolute query position; keys
+                                           j >= min(kv_len, (start_pos+1)/4)
+                                           are causally hidden; requires
+                                           kv_len >= (start_pos+1)/4 */
+  int32_t offset[DS_ROWS_MAX];          /* >= 0, added to every emitted index;
+                                           offset + visible - 1 <= INT32_MAX */
+  uint32_t q_row[DS_ROWS_MAX];          /* row of q [_,64,128] and weights [_,64] */
+  uint32_t output_offset[DS_ROWS_MAX];  /* element offset of the row's 512
+                                           output indices; the ranges of all
+                                           rows must be disjoint */
+  const void *keys[DS_ROWS_MAX];        /* device, bf16 [kv_len, 128] */
+  uint64_t keys_elems[DS_ROWS_MAX];     /* capacity of keys[r] in elements */
+} ds_indexer_rows;
+
+/* Per-row table of the gather and attention calls; the fields of the pages'
+ * DeepSeekSparseAttentionRow ([host 0.21] DeepSeekSparseAttentionRow,
+ * dispatch_deepseek_sparse_attention_flash_rows). */
+typedef struct {
+  uint32_t rows;                        /* 1..DS_ROWS_MAX */
+  uint32_t kv_len[DS_ROWS_MAX];         /* rows of the row's KV, > 0 */
+  uint32_t width[DS_ROWS_MAX];          /* selected slots of the row, > 0 */
+  uint32_t index_offset[DS_ROWS_MAX];   /* element offset of the row's `width`
+                                           indices in the indices buffer */
+  uint32_t q_row[DS_ROWS_MAX];          /* row of q/out [_,64,512]; unique */
+  const void *kv[DS_ROWS_MAX];          /* device, bf16 [kv_len, 512]; keys
+                                           and values are the same tensor */
+  uint64_t kv_elems[DS_ROWS_MAX];       /* capacity of kv[r] in elements */
+} ds_sparse_rows;
+
+/* ---- sizes --------------------------------------------------------------
+ * Each returns 0 if the table itself is invalid (see ds_rows_last_error).
+ * Layouts: row r's scores start at r * max(kv_len); the gathered rows and
+ * mask entries of all rows are concatenated in row order, row r starting at
+ * the sum of the widths of rows 0..r-1 (times 512 for the gathered rows). */
+size_t ds_rows_scores_elems(const ds_indexer_rows *rows);        /* rows * max kv_len */
+size_t ds_rows_topk_workspace_bytes(const ds_indexer_rows *rows);
+size_t ds_rows_gathered_elems(const ds_sparse_rows *rows);       /* sum(width) * 512 */
+size_t ds_rows_mask_elems(const ds_sparse_rows *rows);           /* sum(width) */
+size_t ds_rows_attn_workspace_bytes(const ds_sparse_rows *rows);
+
+/* ---- ds_rows_indexer_score ----------------------------------------------
+ * Lightning-indexer score of one query per row against the row's keys
+ * ([shader 0.18] deepseek_indexer_score_mma_rows_bf16):
+ *   scores[r*S + j] = sum_h w[h] * max(0, sum_d q[h,d] * keys_r[j,d])
+ * for j < kv_len[r], where S = max kv_len, q = q[q_row[r]] (bf16 [64,128]),
+ * w = weights[q_row[r]] (f32 [64]). The products are exact and accumulate in
+ * f32. The score is -inf for j >= min(kv_len, (start_pos+1)/4) and when it is
+ * not finite. Entries j >= kv_len[r] of row r are not written.
+ *   q        device bf16 [q_rows, 64, 128], q_elems >= (max q_row + 1) * 8192
+ *   weights  device f32  [q_rows, 64],      weights_elems >= (max q_row + 1) * 64
+ *   scores   device f32, scores_elems >= ds_rows_scores_elems(rows)
+ * Checks: those of [host 0.21] dispatch_deepseek_indexer_rows on the table,
+ * keys capacity >= kv_len * 128, and non-null pointers. */
+ds_status ds_rows_indexer_score(const ds_indexer_rows *rows,
+                                const void *q, size_t q_elems,
+                                const float *weights, size_t weights_elems,
+                                float *scores, size_t scores_elems,
+                                void *stream);
+
+/* ---- ds_rows_topk -------------------------------------------------------
+ * Deterministic causal top-512 of each row's scores ([shader 0.18]
+ * index_rows_better and deepseek_indexer_topk_{block,merge,finalize}_rows_i32):
+ * among keys j < min(kv_len, (start_pos+1)/4) with a finite score, ranked
+ * by score (higher first; equal scores, including -0 and +0, by lower index
+ * first), writes the first min(512, candidates) as j + offset[r] in rank
+ * order to indices[output_offset[r] + t], and -1 to the remaining slots of
+ * the row's 512.
+ *   scores     device f32 as written by ds_rows_indexer_score
+ *   workspace  device scratch, workspace_bytes >= ds_rows_topk_workspace_bytes
+ *              (contents on entry do not matter; clobbered)
+ *   indices    device i32, indices_elems >= max(output_offset + 512)
+ * Checks: as ds_rows_indexer_score (keys pointers are not used here). */
+ds_status ds_rows_topk(const ds_indexer_rows *rows,
+                       const float *scores, size_t scores_elems,
+                       void *workspace, size_t workspace_bytes,
+                       int32_t *indices, size_t indices_elems,
+                       void *stream);
+
+/* ---- ds_rows_gather -----------------------------------------------------
+ * Gathers, for slot t < width[r] of row r with i = indices[index_offset[r]+t]
+ * ([shader 0.18] deepseek_sparse_attention_gather_rows_bf16):
+ *   i == -1               gathered row = 0, mask = -inf   (sentinel)
+ *   i < -1 or i >= kv_len gathered row = 0, mask = NaN    (bad index)
+ *   otherwise             gathered row = kv_r[i] bit for bit, with every
+ *                         non-finite element replaced by +0; mask = NaN if
+ *                         any element was non-finite, else 0.
+ * A NaN mask entry marks the row invalid: ds_rows_sparse_attn then zeroes
+ * the row's whole output.
+ *   indices   device i32, indices_elems >= max(index_offset + width)
+ *   gathered  device bf16 [sum(width), 512], rows concatenated in row order
+ *   mask      device bf16 [sum(width)]
+ * Checks: those of [host 0.21] sparse_params / sparse_io_checks on the table
+ * (rows, kv_len and width non-zero, unique q_row, kv capacity, index range),
+ * output capacities, and non-null pointers. */
+ds_status ds_rows_gather(const ds_sparse_rows *rows,
+                         const int32_t *indices, size_t indices_elems,
+                         void *gathered, size_t gathered_elems,
+                         void *mask, size_t mask_elems,
+                         void *stream);
+
+/* ---- ds_rows_sparse_attn ------------------------------------------------
+ * Attention of each row's query over its gathered rows, keys = values, with
+ * a learned sink logit per head shared by all rows ([shader 0.18]
+ * deepseek_sparse_attention_score_rows_bf16 / _reduce_rows_bf16 /
+ * _sanitize_rows_bf16; [host 0.21] dispatch_deepseek_sparse_attention_flash_rows):
+ *   l[h,t]  = scale * q[h] . G[t]          for slots t whose mask is not -inf
+ *   m       = max(sink[h], max_t l[h,t])
+ *   Z       = exp(sink[h]-m) + sum_t exp(l[h,t]-m)
+ *   out[h]  = sum_t exp(l[h,t]-m)/Z * G[t]       (f32 [64,512] per row)
+ * out[q_row[r], h, :] is zeroed when the row has a NaN mask entry, when
+ * sink[h] or a live logit l[h,t] is not finite, or when Z is not in (0,inf);
+ * any other non-finite output element is zeroed. Logits accumulate in f32
+ * from exact bf16 products; the softmax weights enter the weighted sum as a
+ * bf16 hi+lo pair (relative error ~2^-16) with f32 accumulation.
+ *   q          device bf16 [q_rows, 64, 512], q_elems >= (max q_row+1)*32768
+ *   sinks      device f32 [64]
+ *   gathered   device bf16, as written by ds_rows_gather
+ *   mask       device bf16, as written by ds_rows_gather
+ *   scale      finite and > 0 (1/sqrt(512) for the decode core)
+ *   workspace  device scratch, workspace_bytes >= ds_rows_attn_workspace_bytes
+ *   out        device f32 [q_rows, 64, 512], out_elems >= (max q_row+1)*32768
+ * Checks: as ds_rows_gather, plus scale, sinks and workspace capacity. */
+ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows,
+                              const void *q, size_t q_elems,
+                              const float *sinks, size_t sinks_elems,
+                              const void *gathered, size_t gathered_elems,
+                              const void *mask, size_t mask_elems,
+                              float scale,
+                              void *workspace, size_t workspace_bytes,
+                              float *out, size_t out_elems,
+                              void *stream);
+
+/* Message of the last failed call on this thread ("ds_rows: ..."), or "". */
+const char *ds_rows_last_error(void);
+
+/* Library version string. */
+const char *ds_rows_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_ROWS_H */

@@ -1,0 +1,357 @@
+// C ABI of the multi-row sparse-attention decode core: argument checks,
+// per-row tables, workspace layout and kernel launches.
+//
+// The checks restate those of the host dispatch code on docs.rs
+// "mlx-native 0.21.0 src/ops/deepseek_rows.rs": check_rows, sparse_params,
+// sparse_io_checks, dispatch_deepseek_indexer_rows (causal length, offset
+// range, disjoint outputs) and its `require` capacity checks. Every check runs
+// before anything is enqueued, so a failed call has no effect on the device.
+#include "ds_rows.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "ds_rows_internal.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+ds_status fail(const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = std::string("ds_rows: ") + buf;
+  return DS_ERR_INVALID_ARGUMENT;
+}
+
+ds_status hip_fail(hipError_t e, const char *what) {
+  g_error = std::string("ds_rows: ") + what + ": " + hipGetErrorString(e);
+  return DS_ERR_HIP;
+}
+
+uint32_t div_up(uint64_t a, uint64_t b) { return static_cast<uint32_t>((a + b - 1) / b); }
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// ------------------------------------------------------------ indexer table
+struct IndexerPlan {
+  uint32_t rows = 0;
+  uint64_t max_kv = 0;
+  uint32_t visible[ds::kRowsMax] = {};
+  uint64_t q_rows = 0;          // max q_row + 1
+  uint64_t indices_end = 0;     // max output_offset + 512
+  uint64_t topk_bank = 0;       // u64 entries per ping-pong bank
+};
+
+ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
+  if (!t) return fail("null indexer row table");
+  if (t->rows == 0 || t->rows > DS_ROWS_MAX) return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, t->rows);
+  p->rows = t->rows;
+  for (uint32_t r = 0; r < t->rows; ++r) {
+    if (t->kv_len[r] == 0) return fail("indexer row %u: kv_len must be nonzero", r);
+    if (t->start_pos[r] == UINT32_MAX) return fail("indexer row %u: indexer position overflows", r);
+    const uint32_t causal = (t->start_pos[r] + 1) / DS_RATIO;
+    if (t->kv_len[r] < causal)
+      return fail("indexer row %u: kv_len %u is shorter than %u causal compressed entries", r, t->kv_len[r], causal);
+    if (t->offset[r] < 0)
+      return fail("indexer row %u: offset must be nonnegative; -1 is reserved for the sentinel", r);
+    if (causal > 0 && int64_t(t->offset[r]) + int64_t(causal) - 1 > int64_t(INT32_MAX))
+      return fail("indexer row %u: offset plus compressed index exceeds i32", r);
+    for (uint32_t o = 0; o < r; ++o) {
+      const uint64_t a0 = t->output_offset[r], a1 = a0 + DS_TOP_K;
+      const uint64_t b0 = t->output_offset[o], b1 = b0 + DS_TOP_K;
+      if (a0 < b1 && b0 < a1) return fail("indexer outputs of two rows overlap (rows %u and %u)", o, r);
+    }
+    p->visible[r] = std::min<uint32_t>(t->kv_len[r], causal);
+    p->max_kv = std::max<uint64_t>(p->max_kv, t->kv_len[r]);
+    p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + 1);
+    p->indices_end = std::max<uint64_t>(p->indices_end, uint64_t(t->output_offset[r]) + DS_TOP_K);
+    const uint32_t chunks = std::max<uint32_t>(1, div_up(p->visible[r], ds::kTopkChunk));
+    if (chunks > 1) p->topk_bank += uint64_t(chunks) * DS_TOP_K;
+  }
+  return DS_OK;
+}
+
+uint64_t topk_workspace_bytes(const IndexerPlan &p) { return 2 * p.topk_bank * sizeof(uint64_t); }
+
+// ------------------------------------------------------------- sparse table
+struct SparsePlan {
+  uint32_t rows = 0;
+  uint64_t q_rows = 0;
+  uint64_t index_end = 0;
+  uint64_t slots = 0;                  // sum of widths
+  uint64_t slot_base[ds::kRowsMax] = {};
+  uint32_t chunks[ds::kRowsMax] = {};
+  uint64_t p_base[ds::kRowsMax] = {};
+  uint64_t stat_base[ds::kRowsMax] = {};
+  uint64_t p_elems = 0, stat_elems = 0;
+};
+
+ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
+  if (!t) return fail("null sparse row table");
+  if (t->rows == 0 || t->rows > DS_ROWS_MAX) return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, t->rows);
+  p->rows = t->rows;
+  for (uint32_t r = 0; r < t->rows; ++r) {
+    if (t->kv_len[r] == 0 || t->width[r] == 0) return fail("row %u: kv_len and width must be nonzero", r);
+    for (uint32_t o = 0; o < r; ++o)
+      if (t->q_row[o] == t->q_row[r]) return fail("row %u: q_row %u is used twice", r, t->q_row[r]);
+    p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + 1);
+    p->index_end = std::max<uint64_t>(p->index_end, uint64_t(t->index_offset[r]) + t->width[r]);
+    p->slot_base[r] = p->slots;
+    p->slots += t->width[r];
+    p->chunks[r] = div_up(t->width[r], ds::kAttnChunk);
+    p->p_base[r] = p->p_elems;
+    p->p_elems += uint64_t(ds::kHeads) * p->chunks[r] * ds::kAttnChunk;
+    p->stat_base[r] = p->stat_elems;
+    p->stat_elems += uint64_t(ds::kHeads) * p->chunks[r];
+  }
+  return DS_OK;
+}
+
+uint64_t attn_p_bytes(const SparsePlan &p) { return align256(p.p_elems * sizeof(float)); }
+uint64_t attn_workspace_bytes(const SparsePlan &p) { return attn_p_bytes(p) + align256(p.stat_elems * 16); }
+
+ds_status need(const void *ptr, const char *name) {
+  return ptr ? DS_OK : fail("%s must not be null", name);
+}
+ds_status cap(uint64_t have, uint64_t want, const char *name, const char *unit) {
+  if (have < want) return fail("%s holds %llu %s, needs %llu", name, (unsigned long long)have, unit,
+                               (unsigned long long)want);
+  return DS_OK;
+}
+
+#define DS_TRY(x)                   \
+  do {                              \
+    const ds_status st_ = (x);      \
+    if (st_ != DS_OK) return st_;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t ds_rows_scores_elems(const ds_indexer_rows *rows) {
+  IndexerPlan p;
+  if (check_indexer(rows, &p) != DS_OK) return 0;
+  return p.rows * p.max_kv;
+}
+
+size_t ds_rows_topk_workspace_bytes(const ds_indexer_rows *rows) {
+  IndexerPlan p;
+  if (check_indexer(rows, &p) != DS_OK) return 0;
+  return topk_workspace_bytes(p);
+}
+
+size_t ds_rows_gathered_elems(const ds_sparse_rows *rows) {
+  SparsePlan p;
+  if (check_sparse(rows, &p) != DS_OK) return 0;
+  return p.slots * DS_HEAD_DIM;
+}
+
+size_t ds_rows_mask_elems(const ds_sparse_rows *rows) {
+  SparsePlan p;
+  if (check_sparse(rows, &p) != DS_OK) return 0;
+  return p.slots;
+}
+
+size_t ds_rows_attn_workspace_bytes(const ds_sparse_rows *rows) {
+  SparsePlan p;
+  if (check_sparse(rows, &p) != DS_OK) return 0;
+  return attn_workspace_bytes(p);
+}
+
+ds_status ds_rows_indexer_score(const ds_indexer_rows *rows, const void *q, size_t q_elems, const float *weights,
+                                size_t weights_elems, float *scores, size_t scores_elems, void *stream) {
+  IndexerPlan p;
+  DS_TRY(check_indexer(rows, &p));
+  DS_TRY(need(q, "indexer q"));
+  DS_TRY(need(weights, "indexer weights"));
+  DS_TRY(need(scores, "indexer scores"));
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    if (!rows->keys[r]) return fail("indexer row %u: keys must not be null", r);
+    DS_TRY(cap(rows->keys_elems[r], uint64_t(rows->kv_len[r]) * DS_INDEXER_DIM, "indexer kv", "elements"));
+  }
+  DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_INDEXER_DIM, "indexer q", "elements"));
+  DS_TRY(cap(weights_elems, p.q_rows * DS_HEADS, "indexer weights", "elements"));
+  DS_TRY(cap(scores_elems, p.rows * p.max_kv, "indexer scores", "elements"));
+
+  ds::IndexerArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.w = weights;
+  a.scores = scores;
+  a.score_stride = p.max_kv;
+  a.rows = p.rows;
+  a.keys_per_block = 1024;
+  uint32_t blocks = 0;
+  for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
+    a.blk_begin[r] = blocks;
+    if (r < p.rows) {
+      a.keys[r] = static_cast<const uint16_t *>(rows->keys[r]);
+      a.kv_len[r] = rows->kv_len[r];
+      a.visible[r] = p.visible[r];
+      a.q_row[r] = rows->q_row[r];
+      blocks += div_up(rows->kv_len[r], a.keys_per_block);
+    }
+  }
+  a.blk_begin[ds::kRowsMax] = blocks;
+  const hipError_t e = ds::launch_indexer_score(a, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
+}
+
+ds_status ds_rows_topk(const ds_indexer_rows *rows, const float *scores, size_t scores_elems, void *workspace,
+                       size_t workspace_bytes, int32_t *indices, size_t indices_elems, void *stream) {
+  IndexerPlan p;
+  DS_TRY(check_indexer(rows, &p));
+  DS_TRY(need(scores, "indexer scores"));
+  DS_TRY(need(indices, "indexer output"));
+  const uint64_t ws = topk_workspace_bytes(p);
+  if (ws) DS_TRY(need(workspace, "indexer top-k scratch"));
+  DS_TRY(cap(scores_elems, p.rows * p.max_kv, "indexer scores", "elements"));
+  DS_TRY(cap(workspace_bytes, ws, "indexer top-k scratch", "bytes"));
+  DS_TRY(cap(indices_elems, p.indices_end, "indexer output", "elements"));
+
+  uint64_t *bank[2] = {static_cast<uint64_t *>(workspace), static_cast<uint64_t *>(workspace) + p.topk_bank};
+  uint32_t count[ds::kRowsMax] = {}, chunks[ds::kRowsMax] = {};
+  uint64_t in_base[ds::kRowsMax] = {};
+  bool done[ds::kRowsMax] = {};
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    count[r] = p.visible[r];
+    chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunk));
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (uint32_t level = 0;; ++level) {
+    ds::TopkLevelArgs a{};
+    a.scores = scores;
+    a.score_stride = p.max_kv;
+    a.in = level == 0 ? nullptr : bank[(level - 1) & 1];
+    a.out = bank[level & 1];
+    a.indices = indices;
+    a.rows = p.rows;
+    a.from_scores = level == 0 ? 1 : 0;
+    uint32_t blocks = 0;
+    uint64_t out_elems = 0;
+    for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
+      a.blk_begin[r] = blocks;
+      if (r >= p.rows || done[r]) continue;
+      a.count[r] = count[r];
+      a.in_base[r] = in_base[r];
+      a.out_base[r] = out_elems;
+      a.offset[r] = rows->offset[r];
+      a.out_offset[r] = rows->output_offset[r];
+      if (chunks[r] == 1) a.final_mask |= 1u << r;
+      else out_elems += uint64_t(chunks[r]) * DS_TOP_K;
+      blocks += chunks[r];
+    }
+    a.blk_begin[ds::kRowsMax] = blocks;
+    const hipError_t e = ds::launch_topk_level(a, blocks, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    bool all = true;
+    for (uint32_t r = 0; r < p.rows; ++r) {
+      if (done[r]) continue;
+      if (chunks[r] == 1) { done[r] = true; continue; }
+      all = false;
+      in_base[r] = a.out_base[r];
+      count[r] = chunks[r] * DS_TOP_K;
+      chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunk));
+    }
+    if (all) break;
+  }
+  return DS_OK;
+}
+
+ds_status ds_rows_gather(const ds_sparse_rows *rows, const int32_t *indices, size_t indices_elems, void *gathered,
+                         size_t gathered_elems, void *mask, size_t mask_elems, void *stream) {
+  SparsePlan p;
+  DS_TRY(check_sparse(rows, &p));
+  DS_TRY(need(indices, "indices"));
+  DS_TRY(need(gathered, "gathered_kv"));
+  DS_TRY(need(mask, "mask"));
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    if (!rows->kv[r]) return fail("row %u: kv must not be null", r);
+    DS_TRY(cap(rows->kv_elems[r], uint64_t(rows->kv_len[r]) * DS_HEAD_DIM, "kv", "elements"));
+  }
+  DS_TRY(cap(indices_elems, p.index_end, "indices", "elements"));
+  DS_TRY(cap(gathered_elems, p.slots * DS_HEAD_DIM, "gathered_kv", "elements"));
+  DS_TRY(cap(mask_elems, p.slots, "mask", "elements"));
+
+  ds::GatherArgs a{};
+  a.indices = indices;
+  a.gathered = static_cast<uint16_t *>(gathered);
+  a.mask = static_cast<uint16_t *>(mask);
+  a.rows = p.rows;
+  uint32_t blocks = 0;
+  for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
+    a.blk_begin[r] = blocks;
+    if (r >= p.rows) continue;
+    a.kv[r] = static_cast<const uint16_t *>(rows->kv[r]);
+    a.kv_len[r] = rows->kv_len[r];
+    a.width[r] = rows->width[r];
+    a.index_offset[r] = rows->index_offset[r];
+    a.slot_base[r] = p.slot_base[r];
+    blocks += div_up(rows->width[r], ds::kGatherSlotsPerBlock);
+  }
+  a.blk_begin[ds::kRowsMax] = blocks;
+  const hipError_t e = ds::launch_gather(a, blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DS_OK : hip_fail(e, "gather launch");
+}
+
+ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows, const void *q, size_t q_elems, const float *sinks,
+                              size_t sinks_elems, const void *gathered, size_t gathered_elems, const void *mask,
+                              size_t mask_elems, float scale, void *workspace, size_t workspace_bytes, float *out,
+                              size_t out_elems, void *stream) {
+  SparsePlan p;
+  DS_TRY(check_sparse(rows, &p));
+  if (!std::isfinite(scale) || scale <= 0.0f) return fail("scale must be finite and positive");
+  DS_TRY(need(q, "q"));
+  DS_TRY(need(sinks, "sinks"));
+  DS_TRY(need(gathered, "gathered_kv"));
+  DS_TRY(need(mask, "mask"));
+  DS_TRY(need(workspace, "attention workspace"));
+  DS_TRY(need(out, "output"));
+  DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_HEAD_DIM, "q", "elements"));
+  DS_TRY(cap(out_elems, p.q_rows * DS_HEADS * DS_HEAD_DIM, "output", "elements"));
+  DS_TRY(cap(sinks_elems, DS_HEADS, "sinks", "elements"));
+  DS_TRY(cap(gathered_elems, p.slots * DS_HEAD_DIM, "gathered_kv", "elements"));
+  DS_TRY(cap(mask_elems, p.slots, "mask", "elements"));
+  DS_TRY(cap(workspace_bytes, attn_workspace_bytes(p), "attention workspace", "bytes"));
+
+  ds::AttnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.sinks = sinks;
+  a.gathered = static_cast<const uint16_t *>(gathered);
+  a.mask = static_cast<const uint16_t *>(mask);
+  a.p = static_cast<float *>(workspace);
+  a.stats = reinterpret_cast<float4 *>(static_cast<char *>(workspace) + attn_p_bytes(p));
+  a.out = out;
+  a.scale = scale;
+  a.rows = p.rows;
+  uint32_t blocks = 0;
+  for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
+    a.blk_begin[r] = blocks;
+    if (r >= p.rows) continue;
+    a.width[r] = rows->width[r];
+    a.chunks[r] = p.chunks[r];
+    a.q_row[r] = rows->q_row[r];
+    a.slot_base[r] = p.slot_base[r];
+    a.p_base[r] = p.p_base[r];
+    a.stat_base[r] = p.stat_base[r];
+    blocks += p.chunks[r];
+  }
+  a.blk_begin[ds::kRowsMax] = blocks;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = ds::launch_attn_logits(a, blocks, s);
+  if (e != hipSuccess) return hip_fail(e, "attention logits launch");
+  e = ds::launch_attn_reduce(a, p.rows * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
+  return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
+}
+
+const char *ds_rows_last_error(void) { return g_error.c_str(); }
+
+const char *ds_rows_version(void) { return "ds_rows 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Internal interface between the C ABI (ds_rows.cpp: argument checks, tables,
+// workspace layout) and the gfx950 kernels (*.hip). Each kernel takes one
+// argument struct by value (it lives in the kernarg segment) and every launch
+// returns the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace ds {
+
+constexpr int kRowsMax = 8;
+constexpr int kHeads = 64;
+constexpr int kIdxDim = 128;
+constexpr int kDim = 512;
+constexpr int kTopK = 512;
+constexpr int kRatio = 4;
+
+// ---------------------------------------------------------------- indexer
+// One workgroup of 4 waves scores `keys_per_block` consecutive keys of one
+// row; waves take 16-key tiles round robin.
+constexpr int kIdxThreads = 256;
+constexpr int kIdxTile = 16;
+
+struct IndexerArgs {
+  const uint16_t *keys[kRowsMax];   // bf16 [kv_len, 128] per row
+  const uint16_t *q;                // bf16 [_, 64, 128]
+  const float *w;                   // f32 [_, 64]
+  float *scores;                    // f32 [rows, score_stride]
+  uint64_t score_stride;
+  uint32_t rows;
+  uint32_t keys_per_block;          // multiple of 4 * kIdxTile
+  uint32_t kv_len[kRowsMax];
+  uint32_t visible[kRowsMax];       // min(kv_len, (start_pos + 1) / 4)
+  uint32_t q_row[kRowsMax];
+  uint32_t blk_begin[kRowsMax + 1]; // first block of each row; [rows..] = total
+};
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, hipStream_t s);
+
+// ------------------------------------------------------------------ top-k
+// One selection level: every workgroup reduces up to kTopkChunk candidates
+// of one row to that chunk's best 512, sorted best first. Candidates are
+// 64-bit keys (order-preserving score bits << 32 | ~index); 0 = no candidate.
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkPerThread = 8;
+constexpr int kTopkChunk = kTopkThreads * kTopkPerThread;   // 8192
+constexpr int kTopkSortCap = 1024;
+
+struct TopkLevelArgs {
+  const float *scores;              // level 0 input: f32 [rows, score_stride]
+  uint64_t score_stride;
+  const uint64_t *in;               // later levels: lists of the previous level
+  uint64_t *out;                    // this level's lists (non-final rows)
+  int32_t *indices;                 // final output
+  uint32_t rows;
+  uint32_t from_scores;             // 1 on the first level
+  uint32_t final_mask;              // bit r: this level emits row r's indices
+  uint32_t count[kRowsMax];         // candidates of row r at this level
+  uint64_t in_base[kRowsMax];       // element offset of row r's input in `in`
+  uint64_t out_base[kRowsMax];      // element offset of row r's lists in `out`
+  int32_t offset[kRowsMax];
+  uint32_t out_offset[kRowsMax];
+  uint32_t blk_begin[kRowsMax + 1];
+};
+hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s);
+
+// ----------------------------------------------------------------- gather
+// One workgroup of 4 waves copies 16 slots; one wave moves one 1 KiB row.
+constexpr int kGatherThreads = 256;
+constexpr int kGatherSlotsPerWave = 4;
+constexpr int kGatherSlotsPerBlock = 4 * kGatherSlotsPerWave;
+
+struct GatherArgs {
+  const uint16_t *kv[kRowsMax];     // bf16 [kv_len, 512] per row
+  const int32_t *indices;
+  uint16_t *gathered;               // bf16 [sum(width), 512]
+  uint16_t *mask;                   // bf16 [sum(width)]
+  uint32_t rows;
+  uint32_t kv_len[kRowsMax];
+  uint32_t width[kRowsMax];
+  uint32_t index_offset[kRowsMax];
+  uint64_t slot_base[kRowsMax];     // sum of widths of the rows before r
+  uint32_t blk_begin[kRowsMax + 1];
+};
+hipError_t launch_gather(const GatherArgs &a, uint32_t blocks, hipStream_t s);
+
+// -------------------------------------------------------------- attention
+// Phase 1 (logits): one workgroup of 2 waves per (row, 32-slot chunk)
+// computes scale * q . G for all 64 heads, and per head and chunk the chunk
+// max m_c, the sum s_c of exp(l - m_c) and a bad flag; it stores
+// p~ = exp(l - m_c) (0 for slots that are masked or past the width).
+// Phase 2 (weighted sum): one workgroup of 2 waves per (row, 32-dim chunk)
+// combines the chunk statistics with the sink and accumulates
+// sum_t p~ * exp(m_c - m) / Z * G[t] on MFMA.
+constexpr int kAttnChunk = 32;      // slots per phase-1 workgroup
+constexpr int kAttnDimChunk = 32;   // output dims per phase-2 workgroup
+constexpr int kAttnSuper = 512;     // slots staged in LDS at a time (phase 2)
+
+struct AttnArgs {
+  const uint16_t *q;                // bf16 [_, 64, 512]
+  const float *sinks;               // f32 [64]
+  const uint16_t *gathered;         // bf16 [sum(width), 512]
+  const uint16_t *mask;             // bf16 [sum(width)]
+  float *p;                         // f32 p~: row r at p_base[r], [64][w32]
+  float4 *stats;                    // (m_c, s_c, bad, 0): row r at stat_base[r], [64][chunks]
+  float *out;                       // f32 [_, 64, 512]
+  float scale;
+  uint32_t rows;
+  uint32_t width[kRowsMax];
+  uint32_t chunks[kRowsMax];        // ceil(width / 32)
+  uint32_t q_row[kRowsMax];
+  uint64_t slot_base[kRowsMax];
+  uint64_t p_base[kRowsMax];
+  uint64_t stat_base[kRowsMax];
+  uint32_t blk_begin[kRowsMax + 1]; // phase 1: prefix of chunks
+};
+hipError_t launch_attn_logits(const AttnArgs &a, uint32_t blocks, hipStream_t s);
+hipError_t launch_attn_reduce(const AttnArgs &a, uint32_t blocks, hipStream_t s);
+
+}  // namespace ds

@@ -1,0 +1,238 @@
+"""ctypes binding of libds_rows.so (include/ds_rows.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library. Device buffers are torch tensors on the current HIP device; the
+binding passes their addresses, capacities and torch's current stream. It
+raises DsRowsError with the library's message on any failed call, and
+load() raises if the library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_size_t, c_uint32, c_uint64, c_void_p
+
+import torch
+
+ROWS_MAX = 8
+HEADS = 64
+INDEXER_DIM = 128
+HEAD_DIM = 512
+TOP_K = 512
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds_rows.so")
+
+FUNCTIONS = (
+    "ds_rows_scores_elems", "ds_rows_topk_workspace_bytes", "ds_rows_gathered_elems",
+    "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes", "ds_rows_indexer_score",
+    "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn", "ds_rows_last_error",
+    "ds_rows_version",
+)
+
+
+class DsRowsError(RuntimeError):
+    pass
+
+
+class IndexerRows(ctypes.Structure):
+    """ds_indexer_rows"""
+    _fields_ = [
+        ("rows", c_uint32),
+        ("kv_len", c_uint32 * ROWS_MAX),
+        ("start_pos", c_uint32 * ROWS_MAX),
+        ("offset", c_int32 * ROWS_MAX),
+        ("q_row", c_uint32 * ROWS_MAX),
+        ("output_offset", c_uint32 * ROWS_MAX),
+        ("keys", c_void_p * ROWS_MAX),
+        ("keys_elems", c_uint64 * ROWS_MAX),
+    ]
+
+
+class SparseRows(ctypes.Structure):
+    """ds_sparse_rows"""
+    _fields_ = [
+        ("rows", c_uint32),
+        ("kv_len", c_uint32 * ROWS_MAX),
+        ("width", c_uint32 * ROWS_MAX),
+        ("index_offset", c_uint32 * ROWS_MAX),
+        ("q_row", c_uint32 * ROWS_MAX),
+        ("kv", c_void_p * ROWS_MAX),
+        ("kv_elems", c_uint64 * ROWS_MAX),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise DsRowsError(f"{path} is not built; run python -m sparse_attention_decode_04_amd.build")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.ds_rows_scores_elems.argtypes = [P(IndexerRows)]
+    lib.ds_rows_topk_workspace_bytes.argtypes = [P(IndexerRows)]
+    lib.ds_rows_gathered_elems.argtypes = [P(SparseRows)]
+    lib.ds_rows_mask_elems.argtypes = [P(SparseRows)]
+    lib.ds_rows_attn_workspace_bytes.argtypes = [P(SparseRows)]
+    for f in ("ds_rows_scores_elems", "ds_rows_topk_workspace_bytes", "ds_rows_gathered_elems",
+              "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes"):
+        getattr(lib, f).restype = c_size_t
+    lib.ds_rows_indexer_score.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
+                                          c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_topk.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
+                                 c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_gather.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
+                                   c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_sparse_attn.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
+                                        c_void_p, c_size_t, c_void_p, c_size_t, c_float,
+                                        c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
+    for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.ds_rows_last_error.restype = ctypes.c_char_p
+    lib.ds_rows_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().ds_rows_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise DsRowsError(f"status {status}: {last_error()}")
+
+
+def _arr(ctype, values, n=ROWS_MAX):
+    a = (ctype * n)()
+    for i, v in enumerate(values):
+        a[i] = v
+    return a
+
+
+def indexer_rows(kv_len, start_pos, offset, q_row, output_offset, keys=None, keys_elems=None) -> IndexerRows:
+    """Build a ds_indexer_rows table. `keys` are device tensors (or raw
+    addresses); capacities default to each tensor's element count."""
+    t = IndexerRows()
+    t.rows = len(kv_len)
+    t.kv_len = _arr(c_uint32, kv_len)
+    t.start_pos = _arr(c_uint32, start_pos)
+    t.offset = _arr(c_int32, offset)
+    t.q_row = _arr(c_uint32, q_row)
+    t.output_offset = _arr(c_uint32, output_offset)
+    keys = keys or []
+    t.keys = _arr(c_void_p, [_addr(k) for k in keys])
+    if keys_elems is None:
+        keys_elems = [k.numel() if isinstance(k, torch.Tensor) else 0 for k in keys]
+    t.keys_elems = _arr(c_uint64, keys_elems)
+    return t
+
+
+def sparse_rows(kv_len, width, index_offset, q_row, kv=None, kv_elems=None) -> SparseRows:
+    """Build a ds_sparse_rows table."""
+    t = SparseRows()
+    t.rows = len(kv_len)
+    t.kv_len = _arr(c_uint32, kv_len)
+    t.width = _arr(c_uint32, width)
+    t.index_offset = _arr(c_uint32, index_offset)
+    t.q_row = _arr(c_uint32, q_row)
+    kv = kv or []
+    t.kv = _arr(c_void_p, [_addr(k) for k in kv])
+    if kv_elems is None:
+        kv_elems = [k.numel() if isinstance(k, torch.Tensor) else 0 for k in kv]
+    t.kv_elems = _arr(c_uint64, kv_elems)
+    return t
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"expected a device tensor, got {type(x)}")
+    if not x.is_cuda:
+        raise ValueError("buffers must be device tensors on the HIP device")
+    if not x.is_contiguous():
+        raise ValueError("buffers must be contiguous")
+    return x.data_ptr()
+
+
+def _dev(x, itemsize=None):
+    """(address, element capacity) of a device tensor."""
+    if x is None:
+        return None, 0
+    a = _addr(x)
+    if itemsize is not None and x.element_size() != itemsize:
+        raise ValueError(f"expected {itemsize}-byte elements, got {x.dtype}")
+    return a, x.numel()
+
+
+def _stream(stream):
+    if stream is None:
+        return c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return c_void_p(stream.cuda_stream)
+    return c_void_p(stream)
+
+
+def scores_elems(t: IndexerRows) -> int:
+    return load().ds_rows_scores_elems(ctypes.byref(t))
+
+
+def topk_workspace_bytes(t: IndexerRows) -> int:
+    return load().ds_rows_topk_workspace_bytes(ctypes.byref(t))
+
+
+def gathered_elems(t: SparseRows) -> int:
+    return load().ds_rows_gathered_elems(ctypes.byref(t))
+
+
+def mask_elems(t: SparseRows) -> int:
+    return load().ds_rows_mask_elems(ctypes.byref(t))
+
+
+def attn_workspace_bytes(t: SparseRows) -> int:
+    return load().ds_rows_attn_workspace_bytes(ctypes.byref(t))
+
+
+def indexer_score(t: IndexerRows, q, weights, scores, stream=None):
+    qa, qn = _dev(q, 2)
+    wa, wn = _dev(weights, 4)
+    sa, sn = _dev(scores, 4)
+    _check(load().ds_rows_indexer_score(ctypes.byref(t), qa, qn, wa, wn, sa, sn, _stream(stream)))
+
+
+def topk(t: IndexerRows, scores, workspace, indices, stream=None):
+    sa, sn = _dev(scores, 4)
+    wa = _addr(workspace) if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ia, inn = _dev(indices, 4)
+    _check(load().ds_rows_topk(ctypes.byref(t), sa, sn, wa, wb, ia, inn, _stream(stream)))
+
+
+def gather(t: SparseRows, indices, gathered, mask, stream=None):
+    ia, inn = _dev(indices, 4)
+    ga, gn = _dev(gathered, 2)
+    ma, mn = _dev(mask, 2)
+    _check(load().ds_rows_gather(ctypes.byref(t), ia, inn, ga, gn, ma, mn, _stream(stream)))
+
+
+def sparse_attn(t: SparseRows, q, sinks, gathered, mask, scale, workspace, out, stream=None):
+    qa, qn = _dev(q, 2)
+    sa, sn = _dev(sinks, 4)
+    ga, gn = _dev(gathered, 2)
+    ma, mn = _dev(mask, 2)
+    wa = _addr(workspace)
+    wb = workspace.numel() * workspace.element_size()
+    oa, on = _dev(out, 4)
+    _check(load().ds_rows_sparse_attn(ctypes.byref(t), qa, qn, sa, sn, ga, gn, ma, mn, float(scale),
+                                      wa, wb, oa, on, _stream(stream)))
+
+
+def version() -> str:
+    return load().ds_rows_version().decode()

@@ -1,0 +1,109 @@
+"""Device plumbing around the four C-ABI calls.
+
+DeviceRows uploads one workload (a RowsInputs from inputs.py) to the current
+HIP device, allocates every output and workspace with torch, builds the two
+row tables and runs the decode path as the four library calls in order on one
+stream. It performs no arithmetic of its own.
+
+Row wiring: indexer row r reads q/weights row r and writes its 512 indices at
+512*r; sparse row r reads indices at 512*r with width min(kv_len, 512) and
+writes q/out row r. A subset of rows can be selected (for one-row launches);
+selected rows keep their original q_row and offsets.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import ds_rows as ds
+from .inputs import HEAD_DIM, HEADS, TOP_K, RowsInputs
+
+
+def to_device(a: np.ndarray, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceInputs:
+    """Device copies of a workload's inputs (shared by any number of runs)."""
+
+    def __init__(self, inp: RowsInputs, device="cuda"):
+        self.inp = inp
+        self.device = device
+        self.idx_q = to_device(inp.idx_q, device)
+        self.idx_w = to_device(inp.idx_w, device)
+        self.keys = [to_device(k, device) for k in inp.idx_keys]
+        self.attn_q = to_device(inp.attn_q, device)
+        self.sinks = to_device(inp.sinks, device)
+        self.kv = [to_device(k, device) for k in inp.kv]
+
+
+class DeviceRows:
+    def __init__(self, dev: DeviceInputs, rows=None, width=None):
+        inp = dev.inp
+        self.dev = dev
+        self.rows = list(range(inp.rows)) if rows is None else list(rows)
+        R_all = inp.rows
+        sel = self.rows
+        kv_len = [inp.kv_len[r] for r in sel]
+        self.width = [min(n, TOP_K) for n in kv_len] if width is None else list(width)
+        self.itab = ds.indexer_rows(
+            kv_len, [inp.start_pos[r] for r in sel], [inp.offset[r] for r in sel], sel,
+            [TOP_K * r for r in sel], keys=[dev.keys[r] for r in sel])
+        self.stab = ds.sparse_rows(
+            kv_len, self.width, [TOP_K * r for r in sel], sel, kv=[dev.kv[r] for r in sel])
+        d = dev.device
+        self.scores = torch.empty(ds.scores_elems(self.itab), dtype=torch.float32, device=d)
+        self.topk_ws = torch.empty(max(1, ds.topk_workspace_bytes(self.itab)), dtype=torch.uint8, device=d)
+        self.indices = torch.full((R_all * TOP_K,), -7, dtype=torch.int32, device=d)
+        self.gathered = torch.empty(ds.gathered_elems(self.stab), dtype=torch.int16, device=d)
+        self.mask = torch.empty(ds.mask_elems(self.stab), dtype=torch.int16, device=d)
+        self.attn_ws = torch.empty(ds.attn_workspace_bytes(self.stab), dtype=torch.uint8, device=d)
+        self.out = torch.zeros(R_all * HEADS * HEAD_DIM, dtype=torch.float32, device=d)
+        self.scale = inp.scale
+
+    # the four calls
+    def indexer_score(self, stream=None):
+        ds.indexer_score(self.itab, self.dev.idx_q, self.dev.idx_w, self.scores, stream)
+
+    def topk(self, stream=None):
+        ds.topk(self.itab, self.scores, self.topk_ws, self.indices, stream)
+
+    def gather(self, stream=None):
+        ds.gather(self.stab, self.indices, self.gathered, self.mask, stream)
+
+    def sparse_attn(self, stream=None):
+        ds.sparse_attn(self.stab, self.dev.attn_q, self.dev.sinks, self.gathered, self.mask,
+                       self.scale, self.attn_ws, self.out, stream)
+
+    def step(self, stream=None):
+        self.indexer_score(stream)
+        self.topk(stream)
+        self.gather(stream)
+        self.sparse_attn(stream)
+
+    # host copies, per selected row
+    def results(self) -> list[dict]:
+        torch.cuda.synchronize()
+        inp = self.dev.inp
+        scores = self.scores.cpu().numpy()
+        stride = scores.size // len(self.rows)
+        idx = self.indices.cpu().numpy()
+        gathered = self.gathered.cpu().numpy().view(np.uint16)
+        mask = self.mask.cpu().numpy().view(np.uint16)
+        out = self.out.cpu().numpy().reshape(inp.rows, HEADS, HEAD_DIM)
+        res, base = [], 0
+        for i, r in enumerate(self.rows):
+            w = self.width[i]
+            res.append(dict(
+                row=r,
+                scores=scores[i * stride: i * stride + inp.kv_len[r]],
+                indices=idx[TOP_K * r: TOP_K * (r + 1)],
+                gathered=gathered[base * HEAD_DIM:(base + w) * HEAD_DIM].reshape(w, HEAD_DIM),
+                mask=mask[base: base + w],
+                out=out[r],
+            ))
+            base += w
+        return res

@@ -1,0 +1,237 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X, gfx950).
+
+Every test runs the library through its C ABI (via the ctypes binding) on
+seeded synthetic inputs and compares each step's output with the oracle:
+  indexer scores   exact (integer-valued inputs make every f32 score exact)
+  top-k indices    exact, in rank order
+  gathered rows    bit for bit; mask state (0 / -inf sentinel / NaN bad) exact
+  attention out    max-abs <= 1e-2 and mean-abs <= 1e-3 against the oracle's
+                   float64 result rounded to f32
+and checks that each row of a multi-row launch equals a one-row launch on
+that row bit for bit (docs.rs "mlx-native 0.21.0 src/ops/deepseek_rows.rs",
+module documentation of the rows dispatches).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ds_oracle as O
+from sparse_attention_decode_04_amd import ds_rows as ds
+from sparse_attention_decode_04_amd import inputs as I
+from sparse_attention_decode_04_amd.runner import DeviceInputs, DeviceRows
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+
+_cache = {}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "no HIP device"
+    ds.load()
+    say("library:", ds.version(), "device:", torch.cuda.get_device_name(0))
+    yield
+    _cache.clear()
+
+
+def config(cid):
+    if cid not in _cache:
+        say(f"generating config {cid}: {I.CONFIG_NAMES[cid]}")
+        inp = I.make_config(cid)
+        say(f"oracle for config {cid}")
+        _cache.clear()
+        _cache[cid] = (inp, O.decode_rows(inp), DeviceInputs(inp))
+    return _cache[cid]
+
+
+def mask_expected(orc):
+    m = np.zeros(orc["sentinel"].shape[0], np.uint16)
+    m[orc["sentinel"]] = 0xFF80
+    m[orc["slot_bad"]] = 0x7FC0
+    return m
+
+
+def check_row(got, orc, label, scores=True):
+    if scores:
+        np.testing.assert_array_equal(got["scores"], orc["scores"], err_msg=f"{label} scores")
+    np.testing.assert_array_equal(got["indices"], orc["indices"], err_msg=f"{label} indices")
+    np.testing.assert_array_equal(got["gathered"], orc["gathered"], err_msg=f"{label} gathered")
+    np.testing.assert_array_equal(got["mask"], mask_expected(orc), err_msg=f"{label} mask")
+    err = np.abs(got["out"].astype(np.float64) - orc["out"].astype(np.float64))
+    say(f"  {label}: out max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, label
+
+
+def bitwise_equal(a, b, label):
+    for k in ("scores", "indices", "gathered", "mask"):
+        assert np.array_equal(np.ascontiguousarray(a[k]).view(np.uint8),
+                              np.ascontiguousarray(b[k]).view(np.uint8)), f"{label} {k}"
+    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32)), f"{label} out"
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
+def test_config_parity(cid):
+    inp, orc, dev = config(cid)
+    say(f"config {cid}: multi-row launch, rows={inp.rows}")
+    run = DeviceRows(dev)
+    run.step()
+    got = run.results()
+    for r in range(inp.rows):
+        check_row(got[r], orc[r], f"config {cid} row {r} (kv_len {inp.kv_len[r]})")
+
+
+@pytest.mark.parametrize("cid", [1, 3])
+def test_multi_row_equals_single_row_bitwise(cid):
+    inp, _, dev = config(cid)
+    say(f"config {cid}: multi-row vs single-row launches")
+    multi = DeviceRows(dev)
+    multi.step()
+    m = multi.results()
+    for r in range(inp.rows):
+        one = DeviceRows(dev, rows=[r])
+        one.step()
+        bitwise_equal(m[r], one.results()[0], f"config {cid} row {r}")
+
+
+def test_repeated_steps_are_deterministic():
+    inp, _, dev = config(1)
+    say("config 1: two steps on the same buffers")
+    run = DeviceRows(dev)
+    run.step()
+    a = run.results()
+    run.step()
+    b = run.results()
+    for r in range(inp.rows):
+        bitwise_equal(a[r], b[r], f"repeat row {r}")
+
+
+def test_causal_limit_and_offset():
+    # visible < kv_len, nothing visible, and a nonzero offset across chunks
+    kv_len = [5000, 300, 20000, 9000]
+    start_pos = [4 * 1000 + 2, 2, 4 * 20000 - 1, 4 * 8192 + 1]
+    offset = [0, 0, 12345, 3]
+    inp = I.small_rows(31, kv_len, start_pos=start_pos, offset=offset)
+    say("causal/offset case", kv_len, start_pos, offset)
+    dev = DeviceInputs(inp)
+    run = DeviceRows(dev)
+    run.step()
+    got = run.results()
+    orc = O.decode_rows(inp)
+    for r in range(len(kv_len)):
+        # rows with a nonzero offset emit indices past kv_len: the gather
+        # flags them bad and the row's attention output is zero
+        check_row(got[r], orc[r], f"causal row {r}")
+    assert np.all(got[1]["indices"] == -1)
+    assert np.all(got[2]["out"] == 0)
+
+
+def test_all_equal_scores_take_lowest_indices():
+    kv_len = [600, 20000, 131072]
+    inp = I.small_rows(7, kv_len)
+    for k in inp.idx_keys:
+        k[:] = 0
+    say("all-zero keys", kv_len)
+    run = DeviceRows(DeviceInputs(inp))
+    run.step()
+    got = run.results()
+    for r, n in enumerate(kv_len):
+        assert np.all(got[r]["scores"] == 0)
+        np.testing.assert_array_equal(got[r]["indices"], np.arange(512))
+    orc = O.decode_rows(inp)
+    for r in range(len(kv_len)):
+        check_row(got[r], orc[r], f"tie row {r}")
+
+
+def test_non_finite_indexer_keys():
+    inp = I.small_rows(9, [64])
+    q = inp.idx_q[0]
+    keys = inp.idx_keys[0]
+    keys[3, 5] = 0x7FC0    # NaN
+    keys[4, 9] = 0x7F80    # +inf
+    keys[5, 2] = 0xFF80    # -inf
+    keys[6, :] = 0x7F80
+    say("non-finite indexer keys")
+    run = DeviceRows(DeviceInputs(inp))
+    run.indexer_score()
+    run.topk()
+    got = run.results()[0]
+    exp = O.indexer_scores(q, inp.idx_w[0], keys, inp.start_pos[0])
+    np.testing.assert_array_equal(got["scores"], exp)
+    np.testing.assert_array_equal(got["indices"], O.topk_select(exp, 64))
+
+
+def test_fail_closed_injections():
+    kv_len = [900, 1000, 700, 800]
+    inp = I.small_rows(17, kv_len)
+    inp.attn_q[3, 7, 100] = 0x7FC0          # NaN in row 3, head 7 query
+    inp.sinks[11] = np.inf                  # sink of head 11 (shared by every row)
+    dev = DeviceInputs(inp)
+    run = DeviceRows(dev)
+    run.indexer_score()
+    run.topk()
+    torch.cuda.synchronize()
+    idx = run.indices.cpu().numpy().reshape(-1, 512)[: len(kv_len)].copy()
+    idx[0, [5, 100]] = -1                   # sentinels: excluded
+    idx[1, 7] = kv_len[1]                   # bad index: row 1 zeroed
+    nan_row = int(idx[2, 3])
+    inp.kv[2][nan_row, 17] = 0x7FC0         # non-finite KV element: row 2 zeroed
+    dev.kv[2][nan_row, 17] = torch.tensor(0x7FC0, dtype=torch.int16)
+    run.indices[: idx.size] = torch.from_numpy(idx.reshape(-1)).cuda()
+    say("fail-closed injections")
+    run.gather()
+    run.sparse_attn()
+    got = run.results()
+    for r in range(len(kv_len)):
+        g, sent, bad, inv = O.gather_row(inp.kv[r], idx[r], kv_len[r])
+        out = O.sparse_attention_row(inp.attn_q[r], inp.sinks, g, sent, inv, inp.scale)
+        orc = dict(indices=idx[r], gathered=g, sentinel=sent, slot_bad=bad, out=out)
+        got[r]["indices"] = idx[r]
+        check_row(got[r], orc, f"inject row {r}", scores=False)
+    assert np.all(got[1]["out"] == 0) and np.all(got[2]["out"] == 0)
+    assert np.all(got[3]["out"][7] == 0) and np.all(got[0]["out"][11] == 0)
+    assert np.all(np.abs(got[0]["out"][10]) > 0)
+
+
+def test_widths_other_than_512():
+    rng = np.random.default_rng(5)
+    kv_len = [3000, 5000, 40]
+    width = [100, 700, 40]
+    inp = I.small_rows(23, kv_len)
+    idx = np.full(3 * 1024, -7, np.int32)
+    offs = [0, 1024, 2048]
+    rows_idx = []
+    for r in range(3):
+        sel = rng.choice(kv_len[r], size=width[r], replace=False).astype(np.int32)
+        sel[rng.random(width[r]) < 0.05] = -1
+        idx[offs[r]: offs[r] + width[r]] = sel
+        rows_idx.append(sel)
+    dev = DeviceInputs(inp)
+    t = ds.sparse_rows(kv_len, width, offs, [0, 1, 2], kv=dev.kv)
+    d_idx = torch.from_numpy(idx).cuda()
+    gathered = torch.empty(ds.gathered_elems(t), dtype=torch.int16, device="cuda")
+    mask = torch.empty(ds.mask_elems(t), dtype=torch.int16, device="cuda")
+    ws = torch.empty(ds.attn_workspace_bytes(t), dtype=torch.uint8, device="cuda")
+    out = torch.zeros(3 * 64 * 512, dtype=torch.float32, device="cuda")
+    say("widths", width)
+    ds.gather(t, d_idx, gathered, mask)
+    ds.sparse_attn(t, dev.attn_q, dev.sinks, gathered, mask, inp.scale, ws, out)
+    torch.cuda.synchronize()
+    g_all = gathered.cpu().numpy().view(np.uint16).reshape(-1, 512)
+    m_all = mask.cpu().numpy().view(np.uint16)
+    o_all = out.cpu().numpy().reshape(3, 64, 512)
+    base = 0
+    for r in range(3):
+        g, sent, bad, inv = O.gather_row(inp.kv[r], rows_idx[r], kv_len[r])
+        o = O.sparse_attention_row(inp.attn_q[r], inp.sinks, g, sent, inv, inp.scale)
+        got = dict(indices=rows_idx[r], gathered=g_all[base: base + width[r]],
+                   mask=m_all[base: base + width[r]], out=o_all[r])
+        check_row(got, dict(indices=rows_idx[r], gathered=g, sentinel=sent, slot_bad=bad, out=o),
+                  f"width {width[r]}", scores=False)
+        base += width[r]
