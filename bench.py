@@ -1,7 +1,10 @@
 """Throughput of the multi-row sparse-attention decode core on one MI355X.
 
 One step = the whole path for every row of the workload: indexer score ->
-top-512 -> gather -> sparse attention (the four C-ABI calls on one stream).
+top-512 -> gather of the selected KV rows -> sparse attention with sinks.
+The headline runs it as three C-ABI calls on one stream, the gather fused into
+the attention call (ds_rows_sparse_attn_direct); the four-call form
+(ds_rows_gather, then ds_rows_sparse_attn) is timed beside it.
 Default workload: 8 rows x 32768 cached keys (64 heads x 128 indexer, top-512,
 64 heads x 512 attention), seeded synthetic inputs resident in HBM.
 
@@ -110,37 +113,43 @@ def main():
     runs = [DeviceRows(c) for c in copies]
     stream = torch.cuda.current_stream()
 
-    for i in range(args.warmup):
-        runs[i % len(runs)].step()
-    torch.cuda.synchronize()
 
-    # Headline: K whole steps, bracketed by device synchronisation.
-    t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        runs[i % len(runs)].step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
+    def timed(step_name):
+        """K whole steps bracketed by device synchronisation; ms per step."""
+        for i in range(args.warmup):
+            getattr(runs[i % len(runs)], step_name)()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            getattr(runs[i % len(runs)], step_name)()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0
 
-    # Per-call durations: events around each call on the launch stream.
-    names = ("indexer_score", "topk", "gather", "sparse_attn")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        r = runs[i % len(runs)]
-        e = evs[i]
-        e[0].record(stream); r.indexer_score()
-        e[1].record(stream); r.topk()
-        e[2].record(stream); r.gather()
-        e[3].record(stream); r.sparse_attn()
-        e[4].record(stream)
-    torch.cuda.synchronize()
-    per_call = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
-                for k, n in enumerate(names)}
+    # Headline: the path with the gather fused into the attention call.
+    ms_per_step, wall = timed("step_direct")
+    # The four-call path (gather, then attention on the gathered rows).
+    ms_four, _ = timed("step")
+
+    def per_call_ms(calls):
+        """Mean duration of each call, from HIP events recorded around it on
+        the launch stream, over K steps."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            r = runs[i % len(runs)]
+            for k, c in enumerate(calls):
+                evs[i][k].record(stream)
+                getattr(r, c)()
+            evs[i][len(calls)].record(stream)
+        torch.cuda.synchronize()
+        return {c: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
+                for k, c in enumerate(calls)}
+
+    per_call = per_call_ms(("indexer_score", "topk", "sparse_attn_direct"))
+    per_call_four = per_call_ms(("indexer_score", "topk", "gather", "sparse_attn"))
 
     idx_bytes, idx_flops = indexer_bytes_flops(inp)
     idx_s = per_call["indexer_score"] * 1e-3
@@ -169,7 +178,11 @@ def main():
         },
         "keys_per_s": keys_per_s,
         "step_algorithmic_gb_per_s": step_bytes(inp) / (ms_per_step * 1e-3) / 1e9,
+        "pipeline": "ds_rows_indexer_score -> ds_rows_topk -> ds_rows_sparse_attn_direct (gather fused)",
         "per_call_ms": per_call,
+        "four_call_pipeline": {
+            "calls": "ds_rows_indexer_score -> ds_rows_topk -> ds_rows_gather -> ds_rows_sparse_attn",
+            "ms_per_step": ms_four, "rows_per_s": inp.rows / (ms_four * 1e-3), "per_call_ms": per_call_four},
         "wall_s_timed_region": wall,
         "roofline": {
             "kernel": "indexer_score_kernel",

@@ -186,8 +186,11 @@ ds_status ds_rows_gather(const ds_sparse_rows *rows,
  *   mask       device bf16, as written by ds_rows_gather
  *   scale      finite and > 0 (1/sqrt(512) for the decode core)
  *   workspace  device scratch, workspace_bytes >= ds_rows_attn_workspace_bytes
+ *              (contents on entry do not matter; clobbered)
  *   out        device f32 [q_rows, 64, 512], out_elems >= (max q_row+1)*32768
- * Checks: as ds_rows_gather, plus scale, sinks and workspace capacity. */
+ * Checks: those of [host 0.21] sparse_params / sparse_io_checks on the table,
+ * gathered/mask capacities, scale, sinks and workspace capacity (the KV
+ * pointers of the table are not used by this call). */
 ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows,
                               const void *q, size_t q_elems,
                               const float *sinks, size_t sinks_elems,
@@ -197,6 +200,28 @@ ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows,
                               void *workspace, size_t workspace_bytes,
                               float *out, size_t out_elems,
                               void *stream);
+
+/* ---- ds_rows_sparse_attn_direct -----------------------------------------
+ * ds_rows_gather followed by ds_rows_sparse_attn in one pass: the selected
+ * rows are read straight from kv[r] through the indices (slot t of row r uses
+ * indices[index_offset[r] + t]), with the gather's rules (-1 sentinel slots
+ * are dropped; a bad index or a non-finite KV element zeroes the row's whole
+ * output) and the same attention and output. Nothing is written to a
+ * gathered operand. Output bit-identical to ds_rows_gather +
+ * ds_rows_sparse_attn on the same inputs, except on rows that the fail-closed
+ * rule zeroes in both.
+ *   indices    device i32, indices_elems >= max(index_offset + width)
+ *   workspace  as ds_rows_sparse_attn (same size query)
+ * Checks: those of ds_rows_gather on the table and indices, plus those of
+ * ds_rows_sparse_attn on q, sinks, scale, workspace and out. */
+ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows,
+                                     const void *q, size_t q_elems,
+                                     const float *sinks, size_t sinks_elems,
+                                     const int32_t *indices, size_t indices_elems,
+                                     float scale,
+                                     void *workspace, size_t workspace_bytes,
+                                     float *out, size_t out_elems,
+                                     void *stream);
 
 /* Message of the last failed call on this thread ("ds_rows: ..."), or "". */
 const char *ds_rows_last_error(void);

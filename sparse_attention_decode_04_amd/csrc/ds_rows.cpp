@@ -71,7 +71,7 @@ ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
     p->max_kv = std::max<uint64_t>(p->max_kv, t->kv_len[r]);
     p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + 1);
     p->indices_end = std::max<uint64_t>(p->indices_end, uint64_t(t->output_offset[r]) + DS_TOP_K);
-    const uint32_t chunks = std::max<uint32_t>(1, div_up(p->visible[r], ds::kTopkChunk));
+    const uint32_t chunks = std::max<uint32_t>(1, div_up(p->visible[r], ds::kTopkChunkFirst));
     if (chunks > 1) p->topk_bank += uint64_t(chunks) * DS_TOP_K;
   }
   return DS_OK;
@@ -89,7 +89,8 @@ struct SparsePlan {
   uint32_t chunks[ds::kRowsMax] = {};
   uint64_t p_base[ds::kRowsMax] = {};
   uint64_t stat_base[ds::kRowsMax] = {};
-  uint64_t p_elems = 0, stat_elems = 0;
+  uint64_t gt_base[ds::kRowsMax] = {};
+  uint64_t p_elems = 0, stat_elems = 0, gt_elems = 0;
 };
 
 ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
@@ -109,12 +110,19 @@ ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
     p->p_elems += uint64_t(ds::kHeads) * p->chunks[r] * ds::kAttnChunk;
     p->stat_base[r] = p->stat_elems;
     p->stat_elems += uint64_t(ds::kHeads) * p->chunks[r];
+    p->gt_base[r] = p->gt_elems;
+    p->gt_elems += uint64_t(ds::kDim) * p->chunks[r] * ds::kAttnChunk;
   }
   return DS_OK;
 }
 
-uint64_t attn_p_bytes(const SparsePlan &p) { return align256(p.p_elems * sizeof(float)); }
-uint64_t attn_workspace_bytes(const SparsePlan &p) { return attn_p_bytes(p) + align256(p.stat_elems * 16); }
+// Attention workspace: bf16 p~ hi plane, bf16 p~ lo plane, f32x4 chunk
+// statistics, bf16 feature-major copy of the selected rows.
+uint64_t attn_plane_bytes(const SparsePlan &p) { return align256(p.p_elems * sizeof(uint16_t)); }
+uint64_t attn_stat_bytes(const SparsePlan &p) { return align256(p.stat_elems * 16); }
+uint64_t attn_workspace_bytes(const SparsePlan &p) {
+  return 2 * attn_plane_bytes(p) + attn_stat_bytes(p) + align256(p.gt_elems * sizeof(uint16_t));
+}
 
 ds_status need(const void *ptr, const char *name) {
   return ptr ? DS_OK : fail("%s must not be null", name);
@@ -221,7 +229,7 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows, const float *scores, size_t 
   bool done[ds::kRowsMax] = {};
   for (uint32_t r = 0; r < p.rows; ++r) {
     count[r] = p.visible[r];
-    chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunk));
+    chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunkFirst));
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   for (uint32_t level = 0;; ++level) {
@@ -257,7 +265,7 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows, const float *scores, size_t 
       all = false;
       in_base[r] = a.out_base[r];
       count[r] = chunks[r] * DS_TOP_K;
-      chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunk));
+      chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunkLater));
     }
     if (all) break;
   }
@@ -300,33 +308,25 @@ ds_status ds_rows_gather(const ds_sparse_rows *rows, const int32_t *indices, siz
   return e == hipSuccess ? DS_OK : hip_fail(e, "gather launch");
 }
 
-ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows, const void *q, size_t q_elems, const float *sinks,
-                              size_t sinks_elems, const void *gathered, size_t gathered_elems, const void *mask,
-                              size_t mask_elems, float scale, void *workspace, size_t workspace_bytes, float *out,
-                              size_t out_elems, void *stream) {
-  SparsePlan p;
-  DS_TRY(check_sparse(rows, &p));
-  if (!std::isfinite(scale) || scale <= 0.0f) return fail("scale must be finite and positive");
-  DS_TRY(need(q, "q"));
-  DS_TRY(need(sinks, "sinks"));
-  DS_TRY(need(gathered, "gathered_kv"));
-  DS_TRY(need(mask, "mask"));
-  DS_TRY(need(workspace, "attention workspace"));
-  DS_TRY(need(out, "output"));
-  DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_HEAD_DIM, "q", "elements"));
-  DS_TRY(cap(out_elems, p.q_rows * DS_HEADS * DS_HEAD_DIM, "output", "elements"));
-  DS_TRY(cap(sinks_elems, DS_HEADS, "sinks", "elements"));
-  DS_TRY(cap(gathered_elems, p.slots * DS_HEAD_DIM, "gathered_kv", "elements"));
-  DS_TRY(cap(mask_elems, p.slots, "mask", "elements"));
-  DS_TRY(cap(workspace_bytes, attn_workspace_bytes(p), "attention workspace", "bytes"));
+}  // extern "C"
 
+namespace {
+
+// Both attention entry points after their own operand checks.
+ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool direct, const void *q,
+                           const float *sinks, const void *gathered, const void *mask, const int32_t *indices,
+                           float scale, void *workspace, float *out, void *stream) {
   ds::AttnArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.sinks = sinks;
   a.gathered = static_cast<const uint16_t *>(gathered);
   a.mask = static_cast<const uint16_t *>(mask);
-  a.p = static_cast<float *>(workspace);
-  a.stats = reinterpret_cast<float4 *>(static_cast<char *>(workspace) + attn_p_bytes(p));
+  a.indices = indices;
+  char *ws = static_cast<char *>(workspace);
+  a.p_hi = reinterpret_cast<uint16_t *>(ws);
+  a.p_lo = reinterpret_cast<uint16_t *>(ws + attn_plane_bytes(p));
+  a.stats = reinterpret_cast<float4 *>(ws + 2 * attn_plane_bytes(p));
+  a.gt = reinterpret_cast<uint16_t *>(ws + 2 * attn_plane_bytes(p) + attn_stat_bytes(p));
   a.out = out;
   a.scale = scale;
   a.rows = p.rows;
@@ -334,20 +334,75 @@ ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows, const void *q, size_t 
   for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
     a.blk_begin[r] = blocks;
     if (r >= p.rows) continue;
+    a.kv[r] = static_cast<const uint16_t *>(rows->kv[r]);
+    a.kv_len[r] = rows->kv_len[r];
+    a.index_offset[r] = rows->index_offset[r];
     a.width[r] = rows->width[r];
     a.chunks[r] = p.chunks[r];
     a.q_row[r] = rows->q_row[r];
     a.slot_base[r] = p.slot_base[r];
     a.p_base[r] = p.p_base[r];
     a.stat_base[r] = p.stat_base[r];
+    a.gt_base[r] = p.gt_base[r];
     blocks += p.chunks[r];
   }
   a.blk_begin[ds::kRowsMax] = blocks;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = ds::launch_attn_logits(a, blocks, s);
+  hipError_t e = ds::launch_attn_logits(a, direct, blocks, s);
   if (e != hipSuccess) return hip_fail(e, "attention logits launch");
   e = ds::launch_attn_reduce(a, p.rows * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
   return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
+}
+
+ds_status check_attention_common(const SparsePlan &p, const void *q, size_t q_elems, const float *sinks,
+                                 size_t sinks_elems, float scale, void *workspace, size_t workspace_bytes,
+                                 float *out, size_t out_elems) {
+  if (!std::isfinite(scale) || scale <= 0.0f) return fail("scale must be finite and positive");
+  DS_TRY(need(q, "q"));
+  DS_TRY(need(sinks, "sinks"));
+  DS_TRY(need(workspace, "attention workspace"));
+  DS_TRY(need(out, "output"));
+  DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_HEAD_DIM, "q", "elements"));
+  DS_TRY(cap(out_elems, p.q_rows * DS_HEADS * DS_HEAD_DIM, "output", "elements"));
+  DS_TRY(cap(sinks_elems, DS_HEADS, "sinks", "elements"));
+  DS_TRY(cap(workspace_bytes, attn_workspace_bytes(p), "attention workspace", "bytes"));
+  return DS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows, const void *q, size_t q_elems, const float *sinks,
+                              size_t sinks_elems, const void *gathered, size_t gathered_elems, const void *mask,
+                              size_t mask_elems, float scale, void *workspace, size_t workspace_bytes, float *out,
+                              size_t out_elems, void *stream) {
+  SparsePlan p;
+  DS_TRY(check_sparse(rows, &p));
+  DS_TRY(check_attention_common(p, q, q_elems, sinks, sinks_elems, scale, workspace, workspace_bytes, out,
+                                out_elems));
+  DS_TRY(need(gathered, "gathered_kv"));
+  DS_TRY(need(mask, "mask"));
+  DS_TRY(cap(gathered_elems, p.slots * DS_HEAD_DIM, "gathered_kv", "elements"));
+  DS_TRY(cap(mask_elems, p.slots, "mask", "elements"));
+  return launch_attention(rows, p, false, q, sinks, gathered, mask, nullptr, scale, workspace, out, stream);
+}
+
+ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows, const void *q, size_t q_elems, const float *sinks,
+                                     size_t sinks_elems, const int32_t *indices, size_t indices_elems, float scale,
+                                     void *workspace, size_t workspace_bytes, float *out, size_t out_elems,
+                                     void *stream) {
+  SparsePlan p;
+  DS_TRY(check_sparse(rows, &p));
+  DS_TRY(check_attention_common(p, q, q_elems, sinks, sinks_elems, scale, workspace, workspace_bytes, out,
+                                out_elems));
+  DS_TRY(need(indices, "indices"));
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    if (!rows->kv[r]) return fail("row %u: kv must not be null", r);
+    DS_TRY(cap(rows->kv_elems[r], uint64_t(rows->kv_len[r]) * DS_HEAD_DIM, "kv", "elements"));
+  }
+  DS_TRY(cap(indices_elems, p.index_end, "indices", "elements"));
+  return launch_attention(rows, p, true, q, sinks, nullptr, nullptr, indices, scale, workspace, out, stream);
 }
 
 const char *ds_rows_last_error(void) { return g_error.c_str(); }

@@ -39,12 +39,16 @@ struct IndexerArgs {
 hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, hipStream_t s);
 
 // ------------------------------------------------------------------ top-k
-// One selection level: every workgroup reduces up to kTopkChunk candidates
-// of one row to that chunk's best 512, sorted best first. Candidates are
+// One selection level: every workgroup reduces a chunk of one row's
+// candidates to that chunk's best 512, sorted best first. Candidates are
 // 64-bit keys (order-preserving score bits << 32 | ~index); 0 = no candidate.
+// The first level reads scores (chunks of 32768); later levels read the
+// previous level's 512-key lists (chunks of 16384 keys = 32 lists).
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkPerThread = 8;
-constexpr int kTopkChunk = kTopkThreads * kTopkPerThread;   // 8192
+constexpr int kTopkPerThreadFirst = 32;
+constexpr int kTopkPerThreadLater = 16;
+constexpr uint32_t kTopkChunkFirst = kTopkThreads * kTopkPerThreadFirst;   // 32768
+constexpr uint32_t kTopkChunkLater = kTopkThreads * kTopkPerThreadLater;   // 16384
 constexpr int kTopkSortCap = 1024;
 
 struct TopkLevelArgs {
@@ -66,10 +70,11 @@ struct TopkLevelArgs {
 hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s);
 
 // ----------------------------------------------------------------- gather
-// One workgroup of 4 waves copies 16 slots; one wave moves one 1 KiB row.
-constexpr int kGatherThreads = 256;
-constexpr int kGatherSlotsPerWave = 4;
-constexpr int kGatherSlotsPerBlock = 4 * kGatherSlotsPerWave;
+// One workgroup of 2 waves copies 16 slots; one wave moves one 1 KiB row per
+// slot, eight slots in flight.
+constexpr int kGatherThreads = 128;
+constexpr int kGatherSlotsPerWave = 8;
+constexpr int kGatherSlotsPerBlock = (kGatherThreads / 64) * kGatherSlotsPerWave;
 
 struct GatherArgs {
   const uint16_t *kv[kRowsMax];     // bf16 [kv_len, 512] per row
@@ -86,36 +91,45 @@ struct GatherArgs {
 hipError_t launch_gather(const GatherArgs &a, uint32_t blocks, hipStream_t s);
 
 // -------------------------------------------------------------- attention
-// Phase 1 (logits): one workgroup of 2 waves per (row, 32-slot chunk)
+// Phase 1 (logits): one workgroup of 8 waves per (row, 32-slot chunk)
 // computes scale * q . G for all 64 heads, and per head and chunk the chunk
 // max m_c, the sum s_c of exp(l - m_c) and a bad flag; it stores
-// p~ = exp(l - m_c) (0 for slots that are masked or past the width).
-// Phase 2 (weighted sum): one workgroup of 2 waves per (row, 32-dim chunk)
+// p~ = exp(l - m_c) as a bf16 hi/lo pair (0 for slots that are masked or
+// past the width) and the chunk's rows feature-major (G^T). G comes from the
+// gathered operand, or (direct) from each row's KV through the indices.
+// Phase 2 (weighted sum): one workgroup of 8 waves per (row, 32-dim chunk)
 // combines the chunk statistics with the sink and accumulates
-// sum_t p~ * exp(m_c - m) / Z * G[t] on MFMA.
+// sum_c exp(m_c - m) / Z * (p~ . G)_c on MFMA.
 constexpr int kAttnChunk = 32;      // slots per phase-1 workgroup
 constexpr int kAttnDimChunk = 32;   // output dims per phase-2 workgroup
-constexpr int kAttnSuper = 512;     // slots staged in LDS at a time (phase 2)
+constexpr int kAttnSuper = 512;     // slots per phase-2 operand batch
 
 struct AttnArgs {
   const uint16_t *q;                // bf16 [_, 64, 512]
   const float *sinks;               // f32 [64]
-  const uint16_t *gathered;         // bf16 [sum(width), 512]
-  const uint16_t *mask;             // bf16 [sum(width)]
-  float *p;                         // f32 p~: row r at p_base[r], [64][w32]
-  float4 *stats;                    // (m_c, s_c, bad, 0): row r at stat_base[r], [64][chunks]
+  const uint16_t *gathered;         // bf16 [sum(width), 512] (gathered variant)
+  const uint16_t *mask;             // bf16 [sum(width)] (gathered variant)
+  const int32_t *indices;           // i32 (direct variant)
+  const uint16_t *kv[kRowsMax];     // bf16 [kv_len, 512] per row (direct variant)
+  uint16_t *p_hi;                   // bf16 hi part of p~: row r at p_base[r], [64][w32]
+  uint16_t *p_lo;                   // bf16 lo part of p~, same layout
+  float4 *stats;                    // (m_c, s_c, bad, 0): row r at stat_base[r], [chunks][64]
+  uint16_t *gt;                     // bf16 G^T: row r at gt_base[r], [512][w32]
   float *out;                       // f32 [_, 64, 512]
   float scale;
   uint32_t rows;
   uint32_t width[kRowsMax];
-  uint32_t chunks[kRowsMax];        // ceil(width / 32)
+  uint32_t chunks[kRowsMax];        // ceil(width / 32); w32 = 32 * chunks
   uint32_t q_row[kRowsMax];
+  uint32_t kv_len[kRowsMax];
+  uint32_t index_offset[kRowsMax];
   uint64_t slot_base[kRowsMax];
   uint64_t p_base[kRowsMax];
   uint64_t stat_base[kRowsMax];
+  uint64_t gt_base[kRowsMax];
   uint32_t blk_begin[kRowsMax + 1]; // phase 1: prefix of chunks
 };
-hipError_t launch_attn_logits(const AttnArgs &a, uint32_t blocks, hipStream_t s);
+hipError_t launch_attn_logits(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s);
 hipError_t launch_attn_reduce(const AttnArgs &a, uint32_t blocks, hipStream_t s);
 
 }  // namespace ds

@@ -8,11 +8,12 @@
 //
 // Differences from the pages' kernel (one thread per element, a relaxed
 // atomic store into a caller-zeroed per-row flag): one wave moves one
-// 1 KiB row as 64 lanes x 16 bytes, four rows in flight per wave, and the
-// "row invalid" state is carried per slot in the mask as NaN, written with a
-// plain store by the wave that saw it. The mask therefore needs no zeroed
-// workspace and no atomics; the attention call treats any NaN mask entry of a
-// row as the row's invalid flag.
+// 1 KiB row as 64 lanes x 16 bytes, eight rows in flight per wave, with the
+// wave's eight indices read by eight lanes and broadcast; and the "row
+// invalid" state is carried per slot in the mask as NaN, written with a plain
+// store by the wave that saw it. The mask therefore needs no zeroed workspace
+// and no atomics; the attention call treats any NaN mask entry of a row as
+// the row's invalid flag.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 
@@ -28,14 +29,23 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   const uint16_t *__restrict__ kv = a.kv[r];
   const int32_t *__restrict__ idx = a.indices + a.index_offset[r];
 
+  // Loads are unconditional (clamped to valid slots / KV row 0) and masked
+  // afterwards, so all eight rows are in flight together.
+  const uint32_t my_slot = min(slot0 + (lane % kGatherSlotsPerWave), width - 1);
+  const int32_t my_raw = idx[my_slot];
+  const int32_t my = (slot0 + (lane % kGatherSlotsPerWave) < width) ? my_raw : -1;
   int32_t sel[kGatherSlotsPerWave];
   u32x4 v[kGatherSlotsPerWave];
 #pragma unroll
   for (int s = 0; s < kGatherSlotsPerWave; ++s) {
-    const uint32_t slot = slot0 + s;
-    sel[s] = slot < width ? idx[slot] : -1;
+    sel[s] = __shfl(my, s);
     const bool ok = sel[s] >= 0 && static_cast<uint32_t>(sel[s]) < n;
-    v[s] = ok ? load16(kv + static_cast<uint64_t>(sel[s]) * kDim + 8 * lane) : u32x4{0, 0, 0, 0};
+    v[s] = load16(kv + static_cast<uint64_t>(ok ? sel[s] : 0) * kDim + 8 * lane);
+  }
+#pragma unroll
+  for (int s = 0; s < kGatherSlotsPerWave; ++s) {
+    const bool ok = sel[s] >= 0 && static_cast<uint32_t>(sel[s]) < n;
+    if (!ok) v[s] = u32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int s = 0; s < kGatherSlotsPerWave; ++s) {

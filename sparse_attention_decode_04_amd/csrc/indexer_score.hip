@@ -7,20 +7,21 @@
 // kernel deepseek_indexer_score_mma_rows_bf16 (score, ReLU, head-weight
 // epilogue, causal mask, finite check).
 //
-// Mapping (differs from the pages' Metal design: no threadgroup staging, no
-// fp16 conversion; bf16 products are exact in the f32 accumulator):
+// Mapping (differs from the pages' Metal design: no staging of keys, no fp16
+// conversion; bf16 products are exact in the f32 accumulator):
 //   * MFMA 16x16x32 with M = 16 heads, N = 16 keys, K = 32 features; four
 //     head tiles x four feature steps per 16-key tile.
 //   * Lane l of a wave serves key l%16 and the 64 contiguous bytes
 //     [64*(l/16), +64) of that key's 256-byte row: feature step c uses bytes
-//     16c of that span. The query fragments are loaded with the same feature
-//     assignment, so the contraction is unchanged.
+//     16c of that span. The query fragments use the same feature assignment,
+//     so the contraction is unchanged and no key data is shuffled.
 //   * D lane l holds heads 16m + 4*(l/16) + i of key l%16: the ReLU and head
 //     weights are applied in registers, then two cross-lane adds finish the
 //     head sum.
-//   * The query (64 x 128 bf16) stays in 64 VGPRs for the wave's lifetime;
-//     key tiles are double-buffered in registers so the next tile's four
-//     16-byte loads are in flight while the current tile's 16 MFMAs run.
+//   * The workgroup stages the 16 KiB query in LDS once; each wave keeps its
+//     copy of the query fragments in 64 VGPRs. Key tiles stream through a
+//     ring of four register buffers, so three tiles (12 KiB) of loads are in
+//     flight per wave while a fourth tile's 16 MFMAs run.
 // The arithmetic per key is a fixed instruction sequence independent of the
 // row count or of other rows, so every row is bitwise identical to a
 // one-row launch.
@@ -29,7 +30,11 @@
 
 namespace ds {
 
+constexpr int kIdxRing = 4;   // tile buffers per wave (kIdxRing - 1 in flight)
+
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs a) {
+  __shared__ u32x4 q_lds[kHeads * kIdxDim / 8];   // 16 KiB
+
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
   const uint32_t n = a.kv_len[r];
   const uint32_t visible = a.visible[r];
@@ -40,63 +45,73 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   const float *__restrict__ w = a.w + static_cast<uint64_t>(a.q_row[r]) * kHeads;
   float *__restrict__ scores = a.scores + static_cast<uint64_t>(r) * a.score_stride;
 
-  const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t wave = tid >> 6;
   const uint32_t col = lane & 15;   // key within tile / head within head tile
   const uint32_t grp = lane >> 4;   // 64-byte span of the 256-byte row
 
-  // Query fragments: head 16m + col, features [32*grp + 8c, +8).
-  bf16x8 qa[4][4];
+  // The query and weights go out first (they gate every MFMA), then the
+  // first tiles of keys; the query reaches LDS once its loads have landed.
+  __shared__ float w_lds[kHeads];
+  u32x4 qv[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint16_t *qrow = q + (16 * m + col) * kIdxDim + 32 * grp;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qa[m][c] = as_bf16x8(load16(qrow + 8 * c));
-  }
-  // Head weights of the D rows this lane holds.
-  float wt[4][4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wt[m][i] = w[16 * m + 4 * grp + i];
+  for (int i = 0; i < 4; ++i) qv[i] = load16(q + 8 * (tid + kIdxThreads * i));
+  const float wv = w[tid & (kHeads - 1)];
 
   const uint32_t tiles = (k_end - k0 + kIdxTile - 1) / kIdxTile;
-  uint32_t t = wave;
-  if (t >= tiles) return;
-
-  auto load_tile = [&](uint32_t tile, u32x4 (&kb)[4]) {
-    const uint32_t key = min(k0 + tile * kIdxTile + col, n - 1);   // tail: clamp, not stored
+  const uint32_t mine = tiles > wave ? (tiles - wave + 3) / 4 : 0;   // tiles wave, wave+4, ...
+  auto load_tile = [&](uint32_t i, u32x4 (&kb)[4]) {
+    const uint32_t key = min(k0 + (wave + 4 * i) * kIdxTile + col, n - 1);   // tail: clamp, not stored
     const uint16_t *krow = keys + static_cast<uint64_t>(key) * kIdxDim + 32 * grp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) kb[c] = load16(krow + 8 * c);
   };
+  // Loads are never conditional: a tile index past the wave's last tile is
+  // clamped to it (the extra tile is computed and dropped). Conditional loads
+  // would make the compiler wait for every outstanding load before each
+  // tile's MFMAs instead of keeping kIdxRing - 1 tiles in flight.
+  u32x4 buf[kIdxRing][4];
+  const uint32_t last = mine > 0 ? mine - 1 : 0;
+#pragma unroll
+  for (int p = 0; p < kIdxRing - 1; ++p) load_tile(min(static_cast<uint32_t>(p), last), buf[p]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q_lds[tid + kIdxThreads * i] = qv[i];
+  if (tid < kHeads) w_lds[tid] = wv;
+  __syncthreads();
+  // Query fragments (head 16m + col, features [32*grp + 8c, +8)) and the head
+  // weights of the D rows this lane holds.
+  bf16x8 qa[4][4];
+  float wt[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qa[m][c] = as_bf16x8(q_lds[((16 * m + col) * kIdxDim + 32 * grp + 8 * c) / 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wt[m][i] = w_lds[16 * m + 4 * grp + i];
+  }
+  if (mine == 0) return;
 
-  u32x4 cur[4], nxt[4];
-  load_tile(t, cur);
-  for (; t < tiles; t += 4) {
-    const bool more = t + 4 < tiles;
-    if (more) load_tile(t + 4, nxt);
-
-    float part = 0.0f;
+  for (uint32_t i0 = 0; i0 < mine; i0 += kIdxRing) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < kIdxRing; ++u) {
+      const uint32_t i = i0 + u;
+      load_tile(min(i + kIdxRing - 1, last), buf[(u + kIdxRing - 1) % kIdxRing]);
+      float part = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc = mfma16(qa[m][c], as_bf16x8(cur[c]), acc);
+      for (int m = 0; m < 4; ++m) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part = fmaf(fmaxf(acc[i], 0.0f), wt[m][i], part);
-    }
-    // Sum the four 16-head groups held by lanes col, col+16, col+32, col+48.
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-
-    const uint32_t key = k0 + t * kIdxTile + col;
-    if (grp == 0 && key < k_end) {
-      scores[key] = (key < visible && __builtin_isfinite(part)) ? part : -__builtin_inff();
-    }
-    if (more) {
+        for (int c = 0; c < 4; ++c) acc = mfma16(qa[m][c], as_bf16x8(buf[u][c]), acc);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cur[c] = nxt[c];
+        for (int j = 0; j < 4; ++j) part = fmaf(fmaxf(acc[j], 0.0f), wt[m][j], part);
+      }
+      // Sum the four 16-head groups held by lanes col, col+16, col+32, col+48.
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      const uint32_t key = k0 + (wave + 4 * i) * kIdxTile + col;
+      if (i < mine && grp == 0 && key < k_end)
+        scores[key] = (key < visible && __builtin_isfinite(part)) ? part : -__builtin_inff();
     }
   }
 }

@@ -7,27 +7,48 @@
 // (deepseek_indexer_topk_block_rows_i32), a pairwise merge-path tree with one
 // launch per round (deepseek_indexer_topk_merge_rows_i32) and a finalize pass
 // (deepseek_indexer_topk_finalize_rows_i32). The result is unique (the order
-// is strict and total), so this build reaches it differently:
+// is strict and total), so this build reaches it differently.
 //
-//   * Every candidate becomes one 64-bit key
-//       (order-preserving bits of (score + 0.0f)) << 32 | ~index
-//     so that unsigned key order is exactly the pages' order (+0.0f folds -0
-//     into +0, which the pages' float comparison treats as equal) and 0 means
-//     "no candidate".
-//   * One level: each 1024-thread workgroup takes up to 8192 candidates of one
-//     row, finds a threshold by MSB-first 8-bit radix select on the keys (an
-//     LDS histogram per digit, wave-aggregated when a wave's digits agree),
-//     stops as soon as at most 1024 keys lie at or above the candidate prefix,
-//     compacts those into LDS, sorts them with a bitonic network and keeps the
-//     best 512 in order.
-//   * Levels repeat on the 512-key lists until each row has one list; the
-//     last level writes index + offset, or -1 for empty slots. A row of n
-//     visible keys needs ceil(log_16(n/512)) levels: one up to 8192 keys, two
-//     up to 131072, three up to 2M.
+// Keys. Every candidate is one 64-bit key
+//     (order-preserving bits of (score + 0.0f)) << 32 | ~index
+// so that unsigned key order is exactly the pages' order (+0.0f folds -0 into
+// +0, which the pages' float comparison treats as equal) and 0 means "none".
+//
+// One level. A 1024-thread workgroup takes a chunk of one row's candidates,
+// held in registers (first level: 32768 scores, 32 per thread, kept as their
+// 32 score bits; later levels: 16384 list keys, 16 per thread), and writes that
+// chunk's best min(512, n) keys in rank order.
+//   Counting select (fast path): with smin/smax the chunk's extreme scores,
+//   bin(s) = min(1023, floor((s - smin) * 1024 / (smax - smin))) is monotone
+//   in the score and equal scores share a bin, so every key in a higher bin
+//   outranks every key in a lower one.
+//     1. A sample (each thread's first key) is binned; the bin lo at which 64
+//        samples (or all of them) lie at or above is a likely lower bound for
+//        the 512th key. If at least 512 keys lie in bins >= lo the top 512
+//        certainly do; otherwise lo = 0.
+//     2. Only keys in bins >= lo enter the LDS histogram (a few thousand
+//        atomics instead of 32768); one scan gives the bin d holding the 512th
+//        key and every bin's exclusive suffix count.
+//     3. Keys of bins >= d are scattered into LDS grouped by bin, and a key's
+//        rank is its bin's suffix count plus the number of larger keys in its
+//        own bin.
+//   Taken when at most 1024 keys lie in bins >= d and no such bin holds more
+//   than 64 keys (spread-out score distributions).
+//   Fallback (heavy ties, extreme outliers): MSB-first 8-bit radix select on
+//   the 64-bit keys until at most 1024 remain at or above the prefix, then a
+//   bitonic sort of those in LDS.
+// Levels repeat on the lists until each row has one; the last level writes
+// index + offset, or -1 for empty slots. A row of n visible keys needs one
+// level up to 32768 keys and two up to 1M.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 
 namespace ds {
+
+constexpr int kBins = 1024;
+constexpr uint32_t kFastBinMax = 64;
+constexpr uint32_t kSampleMin = 64;
+constexpr int kWaves = kTopkThreads / 64;
 
 __device__ __forceinline__ uint64_t topk_key(float s, uint32_t index) {
   if (!__builtin_isfinite(s)) return 0;
@@ -37,72 +58,266 @@ __device__ __forceinline__ uint64_t topk_key(float s, uint32_t index) {
   return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~index);
 }
 
+__device__ __forceinline__ float ord_score(uint32_t ord) {
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+// LDS histogram increment; one atomic per wave when every lane has the same
+// bin (heavy ties), one per lane otherwise. `b` >= nbins means "no key".
+__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t b, uint32_t nbins, uint32_t lane) {
+  const uint32_t first = __builtin_amdgcn_readfirstlane(b);
+  const uint64_t same = __ballot(b == first);
+  if (same == __ballot(true)) {
+    if (first < nbins && lane == 0) atomicAdd(&hist[first], static_cast<uint32_t>(__popcll(same)));
+  } else if (b < nbins) {
+    atomicAdd(&hist[b], 1u);
+  }
+}
+
+// Block-wide scan of the 1024-bin histogram from the top bin down: thread t
+// owns bin 1023 - t. Gives that bin's count h, the number of keys in higher
+// bins (`above`), the largest count among bins >= it (`maxge`) and the total
+// count. Contains one barrier; callers separate successive uses of wsum/wmax.
+__device__ __forceinline__ void scan_bins(const uint32_t *hist, uint32_t *wsum, uint32_t *wmax, uint32_t tid,
+                                          uint32_t &h, uint32_t &above, uint32_t &maxge, uint32_t &total) {
+  const uint32_t lane = tid & 63, wave = tid >> 6;
+  h = hist[kBins - 1 - tid];
+  uint32_t incl = h, imax = h;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t up = __shfl_up(incl, o);
+    const uint32_t upm = __shfl_up(imax, o);
+    if (lane >= static_cast<uint32_t>(o)) { incl += up; imax = max(imax, upm); }
+  }
+  if (lane == 63) { wsum[wave] = incl; wmax[wave] = imax; }
+  __syncthreads();
+  uint32_t pre = 0, premax = 0, all = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves / 4; ++v) {
+    const u32x4 s4 = reinterpret_cast<const u32x4 *>(wsum)[v];
+    const u32x4 m4 = reinterpret_cast<const u32x4 *>(wmax)[v];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool before_me = static_cast<uint32_t>(4 * v + k) < wave;
+      pre += before_me ? s4[k] : 0u;
+      premax = before_me ? max(premax, m4[k]) : premax;
+      all += s4[k];
+    }
+  }
+  above = pre + incl - h;
+  maxge = max(premax, imax);
+  total = all;
+}
+
+// kFromScores: the first level, reading f32 scores; a candidate's key is its
+// order-preserving score bits (kept per candidate) and its position (implied).
+// Otherwise: a later level, reading the previous level's 64-bit key lists.
+template <bool kFromScores>
 __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs a) {
-  __shared__ uint32_t hist[256];
+  constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kTopkPerThreadLater;
+  constexpr uint32_t kChunk = kTopkThreads * kPer;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sfx[kBins];
+  __shared__ uint32_t cursor[kBins];
   __shared__ uint64_t cand[kTopkSortCap];
-  __shared__ uint32_t s_valid, s_count, s_digit, s_above, s_bin;
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t wmax[kWaves];
+  __shared__ uint32_t s_valid, s_min, s_max, s_count, s_filt, s_lo, s_digit, s_above, s_bin, s_kept, s_maxbin;
 
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
   const uint32_t chunk = blockIdx.x - a.blk_begin[r];
-  const uint32_t begin = chunk * kTopkChunk;
-  const uint32_t end = min(a.count[r], begin + kTopkChunk);
+  const uint32_t begin = chunk * kChunk;
+  const uint32_t end = min(a.count[r], begin + kChunk);
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
+  const bool final_level = (a.final_mask >> r) & 1u;
 
-  if (tid == 0) { s_valid = 0; s_count = 0; }
+  hist[tid] = 0;
+  cursor[tid] = 0;
+  if (tid == 0) { s_valid = 0; s_min = 0xFFFFFFFFu; s_max = 0; s_count = 0; s_filt = 0; s_lo = 0; }
 
   // Candidate e of this thread sits at position begin + tid + 1024 * e.
-  uint64_t key[kTopkPerThread];
-  if (a.from_scores) {
+  // Loads are unconditional, from positions clamped into the row (every row
+  // holds at least one score or list entry), and masked afterwards: loads
+  // under a branch would make the compiler wait for each one in turn.
+  const uint32_t lastp = end > 0 ? end - 1 : 0;
+  uint32_t ordv[kFromScores ? kPer : 1];     // score bits, 0 = no candidate
+  uint64_t keyv[kFromScores ? 1 : kPer];
+  if constexpr (kFromScores) {
     const float *sc = a.scores + static_cast<uint64_t>(r) * a.score_stride;
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) {
+    for (int e = 0; e < kPer; ++e)
+      ordv[e] = __float_as_uint(sc[min(begin + tid + kTopkThreads * e, lastp)]);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
       const uint32_t p = begin + tid + kTopkThreads * e;
-      key[e] = p < end ? topk_key(sc[p], p) : 0;
+      ordv[e] = p < end ? static_cast<uint32_t>(topk_key(__uint_as_float(ordv[e]), p) >> 32) : 0u;
     }
   } else {
     const uint64_t *in = a.in + a.in_base[r];
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) {
+    for (int e = 0; e < kPer; ++e) keyv[e] = in[min(begin + tid + kTopkThreads * e, lastp)];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (begin + tid + kTopkThreads * e >= end) keyv[e] = 0;
+  }
+  // Opaque register barrier between passes: values derived from the keys
+  // (validity masks, bins) are recomputed in each pass rather than kept live
+  // across the whole kernel, which would exceed the register budget.
+  auto fence_keys = [&]() {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if constexpr (kFromScores) asm volatile("" : "+v"(ordv[e]));
+      else asm volatile("" : "+v"(keyv[e]));
+    }
+  };
+  auto key_at = [&](int e) -> uint64_t {
+    if constexpr (kFromScores) {
       const uint32_t p = begin + tid + kTopkThreads * e;
-      key[e] = p < end ? in[p] : 0;
+      return ordv[e] ? (static_cast<uint64_t>(ordv[e]) << 32) | static_cast<uint32_t>(~p) : 0ull;
+    } else {
+      return keyv[e];
+    }
+  };
+
+  // Count, and the extreme score bits, of the valid keys.
+  uint32_t nvalid = 0, omin = 0xFFFFFFFFu, omax = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    nvalid += __popcll(__ballot(key_at(e) != 0));
+    if (key_at(e) != 0) {
+      const uint32_t o = static_cast<uint32_t>(key_at(e) >> 32);
+      omin = min(omin, o);
+      omax = max(omax, o);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    omin = min(omin, static_cast<uint32_t>(__shfl_xor(omin, o)));
+    omax = max(omax, static_cast<uint32_t>(__shfl_xor(omax, o)));
+  }
+  __syncthreads();   // LDS initialisation above is complete
+  if (lane == 0) {
+    atomicAdd(&s_valid, nvalid);
+    atomicMin(&s_min, omin);
+    atomicMax(&s_max, omax);
+  }
+  __syncthreads();
+  const uint32_t total = s_valid;
+  const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
+
+  auto emit = [&](uint32_t pos, uint64_t kk) {
+    if (final_level) {
+      a.indices[a.out_offset[r] + pos] =
+          kk != 0 ? static_cast<int32_t>(~static_cast<uint32_t>(kk)) + a.offset[r] : -1;
+    } else {
+      a.out[a.out_base[r] + static_cast<uint64_t>(chunk) * kTopK + pos] = kk;
+    }
+  };
+  // Slots past the selected count are empty.
+  for (uint32_t t = need + tid; t < kTopK; t += kTopkThreads) emit(t, 0);
+  if (total == 0) return;
+
+  // ---- fast path: counting select on linear score bins -----------------
+  const float smin = ord_score(s_min), smax = ord_score(s_max);
+  const float range = smax - smin;
+  const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
+  // Branch-free; kBins means "no key". A zero range gives scale 0, so every
+  // (finite) key lands in bin 0.
+  auto bin_of = [&](uint64_t kk) -> uint32_t {
+    const float x = (ord_score(static_cast<uint32_t>(kk >> 32)) - smin) * scale;
+    const uint32_t b = static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)));
+    return kk != 0 ? b : static_cast<uint32_t>(kBins);
+  };
+
+  // 1. Sample (each thread's first key) -> lower bin lo.
+  fence_keys();
+  hist_add(hist, bin_of(key_at(0)), kBins, lane);
+  __syncthreads();
+  {
+    uint32_t h, above, maxge, nsamp;
+    scan_bins(hist, wsum, wmax, tid, h, above, maxge, nsamp);
+    const uint32_t target = min(nsamp, kSampleMin);
+    if (target > 0 && above < target && target <= above + h) s_lo = kBins - 1 - tid;
+  }
+  __syncthreads();
+  uint32_t lo = s_lo;
+  // Keys at or above the sampled bin; every key if they are too few.
+  fence_keys();
+  {
+    uint32_t nf = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const uint32_t b = bin_of(key_at(e));
+      nf += __popcll(__ballot(b < kBins && b >= lo));
+    }
+    hist[tid] = 0;                        // reused for the real histogram
+    if (lane == 0) atomicAdd(&s_filt, nf);
+  }
+  __syncthreads();
+  if (s_filt < need) lo = 0;
+
+  // 2. Histogram of the keys in bins >= lo, scan.
+  fence_keys();
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const uint32_t b = bin_of(key_at(e));
+    hist_add(hist, (b < kBins && b >= lo) ? b : kBins, kBins, lane);
+  }
+  __syncthreads();
+  {
+    uint32_t h, above, maxge, all;
+    scan_bins(hist, wsum, wmax, tid, h, above, maxge, all);
+    const uint32_t b = kBins - 1 - tid;
+    sfx[b] = above;
+    if (above < need && need <= above + h) {
+      s_digit = b;
+      s_kept = above + h;
+      s_maxbin = maxge;
     }
   }
   __syncthreads();
-
-  uint32_t nvalid = 0;
+  const uint32_t d = s_digit;
+  const uint32_t kept = s_kept;
+  if (kept <= kTopkSortCap && s_maxbin <= kFastBinMax) {
+    // 3. Scatter the keys of bins >= d grouped by bin, then rank within bins.
+    fence_keys();
 #pragma unroll
-  for (int e = 0; e < kTopkPerThread; ++e) nvalid += __popcll(__ballot(key[e] != 0));
-  if (lane == 0) atomicAdd(&s_valid, nvalid);
-  __syncthreads();
-  const uint32_t total = s_valid;
+    for (int e = 0; e < kPer; ++e) {
+      const uint32_t b = bin_of(key_at(e));
+      if (b < kBins && b >= d) cand[sfx[b] + atomicAdd(&cursor[b], 1u)] = key_at(e);
+    }
+    __syncthreads();
+    if (tid < kept) {
+      const uint64_t kk = cand[tid];
+      const uint32_t b = bin_of(kk);
+      const uint32_t base = sfx[b], n = hist[b];
+      uint32_t rank = 0;
+      for (uint32_t q = 0; q < n; ++q) rank += cand[base + q] > kk ? 1u : 0u;
+      const uint32_t pos = base + rank;
+      if (pos < need) emit(pos, kk);
+    }
+    return;
+  }
 
-  // Threshold: keep keys >= thr. With at most kTopkSortCap candidates keep
-  // them all; otherwise radix-select digits until the kept set is small.
+  // ---- fallback: radix select on the 64-bit keys, then bitonic sort ------
   uint64_t thr = 1;
   if (total > kTopkSortCap) {
-    uint32_t need = kTopK;          // ranks still to fill below the prefix
+    uint32_t left = kTopK;          // ranks still to fill below the prefix
     uint64_t prefix = 0;
     for (int shift = 56; shift >= 0; shift -= 8) {
+      __syncthreads();
       if (tid < 256) hist[tid] = 0;
       __syncthreads();
+      fence_keys();
 #pragma unroll
-      for (int e = 0; e < kTopkPerThread; ++e) {
-        const bool match = key[e] != 0 &&
-                           (shift == 56 || (key[e] >> (shift + 8)) == (prefix >> (shift + 8)));
-        const uint32_t dig = match ? static_cast<uint32_t>(key[e] >> shift) & 255u : 256u;
-        const uint32_t first = __builtin_amdgcn_readfirstlane(dig);
-        const uint64_t same = __ballot(dig == first);
-        if (same == __ballot(true)) {
-          if (first != 256u && lane == 0) atomicAdd(&hist[first], static_cast<uint32_t>(__popcll(same)));
-        } else if (dig != 256u) {
-          atomicAdd(&hist[dig], 1u);
-        }
+      for (int e = 0; e < kPer; ++e) {
+        const bool match = key_at(e) != 0 &&
+                           (shift == 56 || (key_at(e) >> (shift + 8)) == (prefix >> (shift + 8)));
+        hist_add(hist, match ? static_cast<uint32_t>(key_at(e) >> shift) & 255u : 256u, 256, lane);
       }
       __syncthreads();
       if (tid < 64) {
-        // Lane l holds bins 255-4l .. 252-4l (descending). Find the bin where
-        // the count of keys ranked above it first reaches `need`.
         uint32_t v[4], sum = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) { v[k] = hist[255 - 4 * tid - k]; sum += v[k]; }
@@ -115,7 +330,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
         uint32_t before = incl - sum;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          if (before < need && need <= before + v[k]) {
+          if (before < left && left <= before + v[k]) {
             s_digit = 255 - 4 * tid - k;
             s_above = before;
             s_bin = v[k];
@@ -124,32 +339,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
         }
       }
       __syncthreads();
-      const uint32_t digit = s_digit;
-      need -= s_above;
-      prefix |= static_cast<uint64_t>(digit) << shift;
-      const uint32_t kept = (kTopK - need) + s_bin;
-      __syncthreads();   // s_* and hist are rewritten by the next pass
-      if (kept <= kTopkSortCap) { thr = prefix; break; }
+      left -= s_above;
+      prefix |= static_cast<uint64_t>(s_digit) << shift;
+      if ((kTopK - left) + s_bin <= kTopkSortCap) { thr = prefix; break; }
     }
   }
-
-  // Compact the kept keys (order arbitrary; sorted next).
+  fence_keys();
 #pragma unroll
-  for (int e = 0; e < kTopkPerThread; ++e) {
-    if (key[e] != 0 && key[e] >= thr) {
+  for (int e = 0; e < kPer; ++e) {
+    if (key_at(e) != 0 && key_at(e) >= thr) {
       const uint32_t pos = atomicAdd(&s_count, 1u);
-      if (pos < kTopkSortCap) cand[pos] = key[e];   // at most 1024 by construction
+      if (pos < kTopkSortCap) cand[pos] = key_at(e);   // at most 1024 by construction
     }
   }
   __syncthreads();
-  const uint32_t kept = min(s_count, static_cast<uint32_t>(kTopkSortCap));
-  for (uint32_t i = tid; i < kTopkSortCap; i += kTopkThreads)
-    if (i >= kept) cand[i] = 0;
+  const uint32_t nk = min(s_count, static_cast<uint32_t>(kTopkSortCap));
+  if (tid >= nk) cand[tid] = 0;
   __syncthreads();
-
-  // Bitonic sort, descending, over the smallest power of two >= 512 covering
-  // the kept keys.
-  const uint32_t size = kept <= kTopK ? kTopK : kTopkSortCap;
+  const uint32_t size = nk <= kTopK ? kTopK : kTopkSortCap;
   for (uint32_t k = 2; k <= size; k <<= 1) {
     for (uint32_t j = k >> 1; j > 0; j >>= 1) {
       const uint32_t ixj = tid ^ j;
@@ -161,20 +368,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
       __syncthreads();
     }
   }
-
-  if (tid < kTopK) {
-    const uint64_t kk = cand[tid];
-    if ((a.final_mask >> r) & 1u) {
-      const int32_t idx = kk != 0 ? static_cast<int32_t>(~static_cast<uint32_t>(kk)) + a.offset[r] : -1;
-      a.indices[a.out_offset[r] + tid] = idx;
-    } else {
-      a.out[a.out_base[r] + static_cast<uint64_t>(chunk) * kTopK + tid] = kk;
-    }
-  }
+  if (tid < need) emit(tid, cand[tid]);
 }
 
 hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL(topk_level_kernel, dim3(blocks), dim3(kTopkThreads), 0, s, a);
+  if (a.from_scores)
+    hipLaunchKernelGGL(topk_level_kernel<true>, dim3(blocks), dim3(kTopkThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_level_kernel<false>, dim3(blocks), dim3(kTopkThreads), 0, s, a);
   return hipGetLastError();
 }
 

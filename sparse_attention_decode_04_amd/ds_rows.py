@@ -25,8 +25,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds_rows.
 FUNCTIONS = (
     "ds_rows_scores_elems", "ds_rows_topk_workspace_bytes", "ds_rows_gathered_elems",
     "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes", "ds_rows_indexer_score",
-    "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn", "ds_rows_last_error",
-    "ds_rows_version",
+    "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn", "ds_rows_sparse_attn_direct",
+    "ds_rows_last_error", "ds_rows_version",
 )
 
 
@@ -90,7 +90,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ds_rows_sparse_attn.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                         c_void_p, c_size_t, c_void_p, c_size_t, c_float,
                                         c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
-    for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn"):
+    lib.ds_rows_sparse_attn_direct.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
+                                               c_void_p, c_size_t, c_float, c_void_p, c_size_t,
+                                               c_void_p, c_size_t, c_void_p]
+    for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn",
+              "ds_rows_sparse_attn_direct"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
@@ -232,6 +236,17 @@ def sparse_attn(t: SparseRows, q, sinks, gathered, mask, scale, workspace, out, 
     oa, on = _dev(out, 4)
     _check(load().ds_rows_sparse_attn(ctypes.byref(t), qa, qn, sa, sn, ga, gn, ma, mn, float(scale),
                                       wa, wb, oa, on, _stream(stream)))
+
+
+def sparse_attn_direct(t: SparseRows, q, sinks, indices, scale, workspace, out, stream=None):
+    qa, qn = _dev(q, 2)
+    sa, sn = _dev(sinks, 4)
+    ia, inn = _dev(indices, 4)
+    wa = _addr(workspace)
+    wb = workspace.numel() * workspace.element_size()
+    oa, on = _dev(out, 4)
+    _check(load().ds_rows_sparse_attn_direct(ctypes.byref(t), qa, qn, sa, sn, ia, inn, float(scale),
+                                             wa, wb, oa, on, _stream(stream)))
 
 
 def version() -> str:

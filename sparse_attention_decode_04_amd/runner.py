@@ -78,11 +78,23 @@ class DeviceRows:
         ds.sparse_attn(self.stab, self.dev.attn_q, self.dev.sinks, self.gathered, self.mask,
                        self.scale, self.attn_ws, self.out, stream)
 
+    def sparse_attn_direct(self, stream=None):
+        ds.sparse_attn_direct(self.stab, self.dev.attn_q, self.dev.sinks, self.indices, self.scale,
+                              self.attn_ws, self.out, stream)
+
     def step(self, stream=None):
+        """The four calls: indexer, top-k, gather, attention on the gathered rows."""
         self.indexer_score(stream)
         self.topk(stream)
         self.gather(stream)
         self.sparse_attn(stream)
+
+    def step_direct(self, stream=None):
+        """Indexer, top-k, then attention reading the selected KV rows directly
+        (gather fused into the attention call; no gathered operand written)."""
+        self.indexer_score(stream)
+        self.topk(stream)
+        self.sparse_attn_direct(stream)
 
     # host copies, per selected row
     def results(self) -> list[dict]:

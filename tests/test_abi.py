@@ -44,7 +44,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert set(names) == set(ds.FUNCTIONS)
     out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (ds_rows_\w+)", out))
@@ -123,6 +123,11 @@ def call_attn(lib, t, scale=0.0441941738, q=BIG, sinks=64, g=BIG, m=BIG, ws=BIG,
                                    ctypes.c_float(scale), FAKE, ws, FAKE, out, None)
 
 
+def call_direct(lib, t, scale=0.0441941738, q=BIG, sinks=64, idx=BIG, ws=BIG, out=BIG):
+    return lib.ds_rows_sparse_attn_direct(ctypes.byref(t), FAKE, q, FAKE, sinks, FAKE, idx,
+                                          ctypes.c_float(scale), FAKE, ws, FAKE, out, None)
+
+
 def expect_invalid(status, *fragments):
     assert status == INVALID
     msg = ds.last_error()
@@ -134,19 +139,20 @@ def expect_invalid(status, *fragments):
 # -------------------------------------------------------------------- sizes
 
 def test_size_queries(lib):
-    t = itab((1000, 70000, 8192, 8193))
+    t = itab((1000, 70000, 32768, 32769))
     assert ds.scores_elems(t) == 4 * 70000
-    # top-k lists: only rows longer than one 8192-key chunk need the banks
-    assert ds.topk_workspace_bytes(t) == 2 * 8 * 512 * (9 + 2)
-    assert ds.topk_workspace_bytes(itab((1000, 8192))) == 0
+    # top-k lists: only rows longer than one 32768-key chunk need the banks
+    assert ds.topk_workspace_bytes(t) == 2 * 8 * 512 * (3 + 2)
+    assert ds.topk_workspace_bytes(itab((1000, 32768))) == 0
     s = stab((1000, 37, 1), width=(512, 37, 1))
     assert ds.gathered_elems(s) == (512 + 37 + 1) * 512
     assert ds.mask_elems(s) == 512 + 37 + 1
     chunks = 16 + 2 + 1
-    p_bytes = 64 * chunks * 32 * 4
+    plane_bytes = 64 * chunks * 32 * 2          # bf16 hi plane, then lo plane
     stat_bytes = 64 * chunks * 16
+    gt_bytes = 512 * chunks * 32 * 2            # feature-major copy of the selected rows
     up = lambda x: (x + 255) // 256 * 256
-    assert ds.attn_workspace_bytes(s) == up(p_bytes) + up(stat_bytes)
+    assert ds.attn_workspace_bytes(s) == 2 * up(plane_bytes) + up(stat_bytes) + up(gt_bytes)
     assert ds.scores_elems(itab((0,))) == 0            # invalid table -> 0
 
 
@@ -186,7 +192,7 @@ def test_indexer_capacity_checks(lib):
     expect_invalid(call_score(lib, t, s=2 * 100 - 1), "indexer scores holds")
     expect_invalid(call_score(lib, itab((100,), keys_elems=[100 * 128 - 1])), "indexer kv holds")
     expect_invalid(call_score(lib, t, qp=None), "must not be null")
-    big = itab((20000,))
+    big = itab((40000,))
     expect_invalid(call_topk(lib, big, ws=ds.topk_workspace_bytes(big) - 1), "top-k scratch holds")
     expect_invalid(call_topk(lib, itab((10, 10), out_off=[0, 1024]), idx=1535), "indexer output holds")
 
@@ -200,6 +206,9 @@ def test_sparse_row_checks(lib):
     expect_invalid(call_gather(lib, stab((10,), kv_elems=[10 * 512 - 1])), "kv holds")
     for bad in (float("nan"), float("inf"), 0.0, -1.0):
         expect_invalid(call_attn(lib, stab((10,)), scale=bad), "scale must be finite and positive")
+    s = stab((10,))
+    s.rows = 9
+    expect_invalid(call_direct(lib, s), "rows must be 1..=8")
 
 
 def test_sparse_capacity_checks(lib):
@@ -211,6 +220,12 @@ def test_sparse_capacity_checks(lib):
     expect_invalid(call_attn(lib, t, out=6 * 64 * 512 - 1), "output holds")
     expect_invalid(call_attn(lib, t, sinks=63), "sinks holds")
     expect_invalid(call_attn(lib, t, ws=ds.attn_workspace_bytes(t) - 1), "attention workspace holds")
+    # the direct variant checks the KV capacities and indices like the gather
+    expect_invalid(call_direct(lib, t, idx=4029), "indices holds")
+    expect_invalid(call_direct(lib, stab((10,), kv_elems=[10 * 512 - 1])), "kv holds")
+    expect_invalid(call_direct(lib, t, ws=ds.attn_workspace_bytes(t) - 1), "attention workspace holds")
+    expect_invalid(call_direct(lib, t, scale=float("nan")), "scale must be finite and positive")
+    expect_invalid(call_direct(lib, stab((10, 10), q_row=[1, 1])), "used twice")
 
 
 def test_binding_rejects_host_tensors():

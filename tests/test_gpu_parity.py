@@ -58,12 +58,13 @@ def mask_expected(orc):
     return m
 
 
-def check_row(got, orc, label, scores=True):
+def check_row(got, orc, label, scores=True, gathered=True):
     if scores:
         np.testing.assert_array_equal(got["scores"], orc["scores"], err_msg=f"{label} scores")
     np.testing.assert_array_equal(got["indices"], orc["indices"], err_msg=f"{label} indices")
-    np.testing.assert_array_equal(got["gathered"], orc["gathered"], err_msg=f"{label} gathered")
-    np.testing.assert_array_equal(got["mask"], mask_expected(orc), err_msg=f"{label} mask")
+    if gathered:
+        np.testing.assert_array_equal(got["gathered"], orc["gathered"], err_msg=f"{label} gathered")
+        np.testing.assert_array_equal(got["mask"], mask_expected(orc), err_msg=f"{label} mask")
     err = np.abs(got["out"].astype(np.float64) - orc["out"].astype(np.float64))
     say(f"  {label}: out max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, label
@@ -79,12 +80,20 @@ def bitwise_equal(a, b, label):
 @pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
 def test_config_parity(cid):
     inp, orc, dev = config(cid)
-    say(f"config {cid}: multi-row launch, rows={inp.rows}")
+    say(f"config {cid}: multi-row launch, rows={inp.rows}, gather + attention")
     run = DeviceRows(dev)
     run.step()
     got = run.results()
     for r in range(inp.rows):
         check_row(got[r], orc[r], f"config {cid} row {r} (kv_len {inp.kv_len[r]})")
+    # the direct attention (gather fused in) on the same indices: same output bits
+    say(f"config {cid}: direct attention")
+    direct = DeviceRows(dev)
+    direct.step_direct()
+    got_d = direct.results()
+    for r in range(inp.rows):
+        check_row(got_d[r], orc[r], f"config {cid} row {r} direct", gathered=False)
+        assert np.array_equal(got_d[r]["out"].view(np.uint32), got[r]["out"].view(np.uint32)), r
 
 
 @pytest.mark.parametrize("cid", [1, 3])
@@ -94,10 +103,16 @@ def test_multi_row_equals_single_row_bitwise(cid):
     multi = DeviceRows(dev)
     multi.step()
     m = multi.results()
+    multi_d = DeviceRows(dev)
+    multi_d.step_direct()
+    md = multi_d.results()
     for r in range(inp.rows):
         one = DeviceRows(dev, rows=[r])
         one.step()
         bitwise_equal(m[r], one.results()[0], f"config {cid} row {r}")
+        one_d = DeviceRows(dev, rows=[r])
+        one_d.step_direct()
+        assert np.array_equal(md[r]["out"].view(np.uint32), one_d.results()[0]["out"].view(np.uint32)), r
 
 
 def test_repeated_steps_are_deterministic():
@@ -168,7 +183,7 @@ def test_non_finite_indexer_keys():
 
 
 def test_fail_closed_injections():
-    kv_len = [900, 1000, 700, 800]
+    kv_len = [900, 1000, 700, 800, 950]
     inp = I.small_rows(17, kv_len)
     inp.attn_q[3, 7, 100] = 0x7FC0          # NaN in row 3, head 7 query
     inp.sinks[11] = np.inf                  # sink of head 11 (shared by every row)
@@ -180,21 +195,28 @@ def test_fail_closed_injections():
     idx = run.indices.cpu().numpy().reshape(-1, 512)[: len(kv_len)].copy()
     idx[0, [5, 100]] = -1                   # sentinels: excluded
     idx[1, 7] = kv_len[1]                   # bad index: row 1 zeroed
+    idx[4, 487] = -5                        # bad index deep in the last chunk: row 4 zeroed
     nan_row = int(idx[2, 3])
     inp.kv[2][nan_row, 17] = 0x7FC0         # non-finite KV element: row 2 zeroed
     dev.kv[2][nan_row, 17] = torch.tensor(0x7FC0, dtype=torch.int16)
     run.indices[: idx.size] = torch.from_numpy(idx.reshape(-1)).cuda()
-    say("fail-closed injections")
+    say("fail-closed injections, direct attention")
+    run.sparse_attn_direct()
+    got_d = [g["out"].copy() for g in run.results()]
+    say("fail-closed injections, gather + attention")
+    run.out.zero_()
     run.gather()
     run.sparse_attn()
     got = run.results()
+    for r in range(len(kv_len)):
+        assert np.array_equal(got_d[r].view(np.uint32), got[r]["out"].view(np.uint32)), r
     for r in range(len(kv_len)):
         g, sent, bad, inv = O.gather_row(inp.kv[r], idx[r], kv_len[r])
         out = O.sparse_attention_row(inp.attn_q[r], inp.sinks, g, sent, inv, inp.scale)
         orc = dict(indices=idx[r], gathered=g, sentinel=sent, slot_bad=bad, out=out)
         got[r]["indices"] = idx[r]
         check_row(got[r], orc, f"inject row {r}", scores=False)
-    assert np.all(got[1]["out"] == 0) and np.all(got[2]["out"] == 0)
+    assert np.all(got[1]["out"] == 0) and np.all(got[2]["out"] == 0) and np.all(got[4]["out"] == 0)
     assert np.all(got[3]["out"][7] == 0) and np.all(got[0]["out"][11] == 0)
     assert np.all(np.abs(got[0]["out"][10]) > 0)
 
@@ -219,13 +241,19 @@ def test_widths_other_than_512():
     mask = torch.empty(ds.mask_elems(t), dtype=torch.int16, device="cuda")
     ws = torch.empty(ds.attn_workspace_bytes(t), dtype=torch.uint8, device="cuda")
     out = torch.zeros(3 * 64 * 512, dtype=torch.float32, device="cuda")
-    say("widths", width)
+    say("widths", width, "direct")
+    ds.sparse_attn_direct(t, dev.attn_q, dev.sinks, d_idx, inp.scale, ws, out)
+    torch.cuda.synchronize()
+    o_direct = out.cpu().numpy().reshape(3, 64, 512).copy()
+    out.zero_()
+    say("widths", width, "gather + attention")
     ds.gather(t, d_idx, gathered, mask)
     ds.sparse_attn(t, dev.attn_q, dev.sinks, gathered, mask, inp.scale, ws, out)
     torch.cuda.synchronize()
     g_all = gathered.cpu().numpy().view(np.uint16).reshape(-1, 512)
     m_all = mask.cpu().numpy().view(np.uint16)
     o_all = out.cpu().numpy().reshape(3, 64, 512)
+    assert np.array_equal(o_all.view(np.uint32), o_direct.view(np.uint32))
     base = 0
     for r in range(3):
         g, sent, bad, inv = O.gather_row(inp.kv[r], rows_idx[r], kv_len[r])
