@@ -24,11 +24,11 @@
 //   outranks every key in a lower one.
 //     1. A sample (each thread's first key) is binned; the bin lo at which 64
 //        samples (or all of them) lie at or above is a likely lower bound for
-//        the 512th key. If at least 512 keys lie in bins >= lo the top 512
-//        certainly do; otherwise lo = 0.
+//        the 512th key.
 //     2. Only keys in bins >= lo enter the LDS histogram (a few thousand
 //        atomics instead of 32768); one scan gives the bin d holding the 512th
-//        key and every bin's exclusive suffix count.
+//        key and every bin's exclusive suffix count. If fewer than 512 keys
+//        lie in bins >= lo, the histogram is rebuilt over every key.
 //     3. Keys of bins >= d are scattered into LDS grouped by bin, and a key's
 //        rank is its bin's suffix count plus the number of larger keys in its
 //        own bin.
@@ -62,13 +62,17 @@ __device__ __forceinline__ float ord_score(uint32_t ord) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
-// LDS histogram increment; one atomic per wave when every lane has the same
-// bin (heavy ties), one per lane otherwise. `b` >= nbins means "no key".
+// LDS histogram increment by the active lanes of a wave (callers may call it
+// under a branch); one atomic by the first active lane when every active lane
+// has the same bin (heavy ties), one per lane otherwise. `b` >= nbins means
+// "no key".
 __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t b, uint32_t nbins, uint32_t lane) {
   const uint32_t first = __builtin_amdgcn_readfirstlane(b);
+  const uint64_t active = __ballot(true);
   const uint64_t same = __ballot(b == first);
-  if (same == __ballot(true)) {
-    if (first < nbins && lane == 0) atomicAdd(&hist[first], static_cast<uint32_t>(__popcll(same)));
+  if (same == active) {
+    if (first < nbins && lane == static_cast<uint32_t>(__builtin_ctzll(active)))
+      atomicAdd(&hist[first], static_cast<uint32_t>(__popcll(same)));
   } else if (b < nbins) {
     atomicAdd(&hist[b], 1u);
   }
@@ -112,6 +116,10 @@ __device__ __forceinline__ void scan_bins(const uint32_t *hist, uint32_t *wsum, 
 // kFromScores: the first level, reading f32 scores; a candidate's key is its
 // order-preserving score bits (kept per candidate) and its position (implied).
 // Otherwise: a later level, reading the previous level's 64-bit key lists.
+//
+// The selection is VALU-bound (one workgroup per chunk), so each candidate's
+// bin is computed once and kept in a register; every later pass is a compare
+// or two per candidate.
 template <bool kFromScores>
 __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs a) {
   constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kTopkPerThreadLater;
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   __shared__ uint64_t cand[kTopkSortCap];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[kWaves];
   __shared__ __attribute__((aligned(16))) uint32_t wmax[kWaves];
-  __shared__ uint32_t s_valid, s_min, s_max, s_count, s_filt, s_lo, s_digit, s_above, s_bin, s_kept, s_maxbin;
+  __shared__ uint32_t s_valid, s_min1, s_max, s_count, s_lo, s_digit, s_above, s_bin, s_kept, s_maxbin, s_hist_total;
 
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
   const uint32_t chunk = blockIdx.x - a.blk_begin[r];
@@ -134,7 +142,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
 
   hist[tid] = 0;
   cursor[tid] = 0;
-  if (tid == 0) { s_valid = 0; s_min = 0xFFFFFFFFu; s_max = 0; s_count = 0; s_filt = 0; s_lo = 0; }
+  if (tid == 0) { s_valid = 0; s_min1 = 0xFFFFFFFFu; s_max = 0; s_count = 0; s_lo = 0; }
 
   // Candidate e of this thread sits at position begin + tid + 1024 * e.
   // Loads are unconditional, from positions clamped into the row (every row
@@ -144,26 +152,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   uint32_t ordv[kFromScores ? kPer : 1];     // score bits, 0 = no candidate
   uint64_t keyv[kFromScores ? 1 : kPer];
   if constexpr (kFromScores) {
-    const float *sc = a.scores + static_cast<uint64_t>(r) * a.score_stride;
+    // Uniform base + 32-bit byte offset (rows hold < 2^30 scores), so each
+    // load needs one offset register rather than a 64-bit address.
+    const char *sc = reinterpret_cast<const char *>(a.scores + static_cast<uint64_t>(r) * a.score_stride);
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
-      ordv[e] = __float_as_uint(sc[min(begin + tid + kTopkThreads * e, lastp)]);
+      ordv[e] = *reinterpret_cast<const uint32_t *>(sc + 4u * min(begin + tid + kTopkThreads * e, lastp));
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const uint32_t p = begin + tid + kTopkThreads * e;
       ordv[e] = p < end ? static_cast<uint32_t>(topk_key(__uint_as_float(ordv[e]), p) >> 32) : 0u;
     }
   } else {
-    const uint64_t *in = a.in + a.in_base[r];
+    const char *in = reinterpret_cast<const char *>(a.in + a.in_base[r]);
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) keyv[e] = in[min(begin + tid + kTopkThreads * e, lastp)];
+    for (int e = 0; e < kPer; ++e)
+      keyv[e] = *reinterpret_cast<const uint64_t *>(in + 8u * min(begin + tid + kTopkThreads * e, lastp));
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       if (begin + tid + kTopkThreads * e >= end) keyv[e] = 0;
   }
-  // Opaque register barrier between passes: values derived from the keys
-  // (validity masks, bins) are recomputed in each pass rather than kept live
-  // across the whole kernel, which would exceed the register budget.
+  // Opaque register barrier: values derived from the keys (full 64-bit keys,
+  // masks) are recomputed after it rather than hoisted and kept live across a
+  // loop, which would exceed the register budget.
   auto fence_keys = [&]() {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
@@ -171,35 +182,55 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
       else asm volatile("" : "+v"(keyv[e]));
     }
   };
+  // High word of candidate e (its score bits; 0 = none) and its full key.
+  auto hi_at = [&](int e) -> uint32_t {
+    if constexpr (kFromScores) return ordv[e];
+    else return static_cast<uint32_t>(keyv[e] >> 32);
+  };
+  // The low word ~p of position p = begin + tid + 1024 e is rebuilt from one
+  // opaque base, so that 32 positions are not kept live from the loads on.
   auto key_at = [&](int e) -> uint64_t {
     if constexpr (kFromScores) {
-      const uint32_t p = begin + tid + kTopkThreads * e;
-      return ordv[e] ? (static_cast<uint64_t>(ordv[e]) << 32) | static_cast<uint32_t>(~p) : 0ull;
+      uint32_t nbase = ~(begin + tid);
+      asm volatile("" : "+v"(nbase));
+      const uint32_t np = nbase - kTopkThreads * static_cast<uint32_t>(e);   // = ~p
+      return ordv[e] ? (static_cast<uint64_t>(ordv[e]) << 32) | np : 0ull;
+    } else {
+      return keyv[e];
+    }
+  };
+  // The same for a candidate known to be valid.
+  auto valid_key_at = [&](int e) -> uint64_t {
+    if constexpr (kFromScores) {
+      uint32_t nbase = ~(begin + tid);
+      asm volatile("" : "+v"(nbase));
+      return (static_cast<uint64_t>(ordv[e]) << 32) | (nbase - kTopkThreads * static_cast<uint32_t>(e));
     } else {
       return keyv[e];
     }
   };
 
-  // Count, and the extreme score bits, of the valid keys.
-  uint32_t nvalid = 0, omin = 0xFFFFFFFFu, omax = 0;
+  // Count and extreme score bits of the valid keys. A missing key has high
+  // word 0 (every valid key's is nonzero), so it never raises the maximum and,
+  // as 0 - 1 in unsigned arithmetic, never lowers the minimum.
+  uint32_t nvalid = 0, omin1 = 0xFFFFFFFFu, omax = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    nvalid += __popcll(__ballot(key_at(e) != 0));
-    if (key_at(e) != 0) {
-      const uint32_t o = static_cast<uint32_t>(key_at(e) >> 32);
-      omin = min(omin, o);
-      omax = max(omax, o);
-    }
+    const uint32_t o = hi_at(e);
+    nvalid += o != 0 ? 1u : 0u;
+    omin1 = min(omin1, o - 1u);
+    omax = max(omax, o);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    omin = min(omin, static_cast<uint32_t>(__shfl_xor(omin, o)));
-    omax = max(omax, static_cast<uint32_t>(__shfl_xor(omax, o)));
+    nvalid += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nvalid), o));
+    omin1 = min(omin1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omin1), o)));
+    omax = max(omax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omax), o)));
   }
   __syncthreads();   // LDS initialisation above is complete
   if (lane == 0) {
     atomicAdd(&s_valid, nvalid);
-    atomicMin(&s_min, omin);
+    atomicMin(&s_min1, omin1);
     atomicMax(&s_max, omax);
   }
   __syncthreads();
@@ -219,20 +250,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   if (total == 0) return;
 
   // ---- fast path: counting select on linear score bins -----------------
-  const float smin = ord_score(s_min), smax = ord_score(s_max);
+  const float smin = ord_score(s_min1 + 1u), smax = ord_score(s_max);
   const float range = smax - smin;
   const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
-  // Branch-free; kBins means "no key". A zero range gives scale 0, so every
-  // (finite) key lands in bin 0.
-  auto bin_of = [&](uint64_t kk) -> uint32_t {
-    const float x = (ord_score(static_cast<uint32_t>(kk >> 32)) - smin) * scale;
-    const uint32_t b = static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)));
-    return kk != 0 ? b : static_cast<uint32_t>(kBins);
-  };
+  // Bin of every candidate, once; kBins = no key. A zero range gives scale 0
+  // and every (finite) key bin 0.
+  // Two 16-bit bins per register.
+  uint32_t binp[kPer / 2];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const uint32_t o = hi_at(e);
+    const float x = (ord_score(o) - smin) * scale;
+    const uint32_t b = o != 0 ? static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)))
+                              : static_cast<uint32_t>(kBins);
+    if (e & 1) binp[e / 2] |= b << 16;
+    else binp[e / 2] = b;
+  }
+  auto bin_at = [&](int e) -> uint32_t { return (e & 1) ? binp[e / 2] >> 16 : binp[e / 2] & 0xFFFFu; };
+  // A bin b lies in [lo, kBins) iff b - lo < kBins - lo (unsigned).
+  auto in_range = [](uint32_t b, uint32_t lo) { return b - lo < static_cast<uint32_t>(kBins) - lo; };
 
-  // 1. Sample (each thread's first key) -> lower bin lo.
-  fence_keys();
-  hist_add(hist, bin_of(key_at(0)), kBins, lane);
+  // 1. Sample (each thread's first key) -> likely lower bin lo.
+  hist_add(hist, bin_at(0), kBins, lane);
   __syncthreads();
   {
     uint32_t h, above, maxge, nsamp;
@@ -242,30 +281,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   }
   __syncthreads();
   uint32_t lo = s_lo;
-  // Keys at or above the sampled bin; every key if they are too few.
-  fence_keys();
-  {
-    uint32_t nf = 0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const uint32_t b = bin_of(key_at(e));
-      nf += __popcll(__ballot(b < kBins && b >= lo));
-    }
-    hist[tid] = 0;                        // reused for the real histogram
-    if (lane == 0) atomicAdd(&s_filt, nf);
-  }
+  hist[tid] = 0;                          // reused for the real histogram
   __syncthreads();
-  if (s_filt < need) lo = 0;
 
-  // 2. Histogram of the keys in bins >= lo, scan.
-  fence_keys();
+  // 2. Histogram of the keys in bins >= lo, scan; if they are fewer than
+  //    need, once more over every key (lo = 0).
+  uint32_t d = 0, kept = 0, maxbin = 0;
+  for (;;) {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const uint32_t b = bin_of(key_at(e));
-    hist_add(hist, (b < kBins && b >= lo) ? b : kBins, kBins, lane);
-  }
-  __syncthreads();
-  {
+    for (int e = 0; e < kPer; ++e)
+      if (in_range(bin_at(e), lo)) hist_add(hist, bin_at(e), kBins, lane);
+    __syncthreads();
     uint32_t h, above, maxge, all;
     scan_bins(hist, wsum, wmax, tid, h, above, maxge, all);
     const uint32_t b = kBins - 1 - tid;
@@ -275,22 +301,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
       s_kept = above + h;
       s_maxbin = maxge;
     }
+    if (tid == 0) s_hist_total = all;
+    __syncthreads();
+    if (s_hist_total >= need || lo == 0) {
+      d = s_digit;
+      kept = s_kept;
+      maxbin = s_maxbin;
+      break;
+    }
+    lo = 0;
+    hist[tid] = 0;
+    __syncthreads();
   }
-  __syncthreads();
-  const uint32_t d = s_digit;
-  const uint32_t kept = s_kept;
-  if (kept <= kTopkSortCap && s_maxbin <= kFastBinMax) {
+  if (kept <= kTopkSortCap && maxbin <= kFastBinMax) {
     // 3. Scatter the keys of bins >= d grouped by bin, then rank within bins.
     fence_keys();
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const uint32_t b = bin_of(key_at(e));
-      if (b < kBins && b >= d) cand[sfx[b] + atomicAdd(&cursor[b], 1u)] = key_at(e);
-    }
+    for (int e = 0; e < kPer; ++e)
+      if (in_range(bin_at(e), d)) cand[sfx[bin_at(e)] + atomicAdd(&cursor[bin_at(e)], 1u)] = valid_key_at(e);
     __syncthreads();
     if (tid < kept) {
       const uint64_t kk = cand[tid];
-      const uint32_t b = bin_of(kk);
+      const float x = (ord_score(static_cast<uint32_t>(kk >> 32)) - smin) * scale;
+      const uint32_t b = static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)));
       const uint32_t base = sfx[b], n = hist[b];
       uint32_t rank = 0;
       for (uint32_t q = 0; q < n; ++q) rank += cand[base + q] > kk ? 1u : 0u;
@@ -312,26 +345,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
       fence_keys();
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
-        const bool match = key_at(e) != 0 &&
-                           (shift == 56 || (key_at(e) >> (shift + 8)) == (prefix >> (shift + 8)));
-        hist_add(hist, match ? static_cast<uint32_t>(key_at(e) >> shift) & 255u : 256u, 256, lane);
+        const uint64_t kk = key_at(e);
+        const bool match = kk != 0 && (shift == 56 || (kk >> (shift + 8)) == (prefix >> (shift + 8)));
+        hist_add(hist, match ? static_cast<uint32_t>(kk >> shift) & 255u : 256u, 256, lane);
       }
       __syncthreads();
-      if (tid < 64) {
+      uint32_t t = tid;
+      asm volatile("" : "+v"(t));   // keeps the digit arithmetic out of the loop preheader
+      if (t < 64) {
         uint32_t v[4], sum = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) { v[k] = hist[255 - 4 * tid - k]; sum += v[k]; }
+        for (int k = 0; k < 4; ++k) { v[k] = hist[255 - 4 * t - k]; sum += v[k]; }
         uint32_t incl = sum;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const uint32_t up = __shfl_up(incl, o);
-          if (tid >= static_cast<uint32_t>(o)) incl += up;
+          if (t >= static_cast<uint32_t>(o)) incl += up;
         }
         uint32_t before = incl - sum;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           if (before < left && left <= before + v[k]) {
-            s_digit = 255 - 4 * tid - k;
+            s_digit = 255 - 4 * t - k;
             s_above = before;
             s_bin = v[k];
           }
@@ -347,9 +382,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   fence_keys();
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    if (key_at(e) != 0 && key_at(e) >= thr) {
+    const uint64_t kk = key_at(e);
+    if (kk != 0 && kk >= thr) {
       const uint32_t pos = atomicAdd(&s_count, 1u);
-      if (pos < kTopkSortCap) cand[pos] = key_at(e);   // at most 1024 by construction
+      if (pos < kTopkSortCap) cand[pos] = kk;   // at most 1024 by construction
     }
   }
   __syncthreads();
