@@ -45,7 +45,41 @@ def parse():
     p.add_argument("--copies", type=int, default=8)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 64 MiB device-to-device copy 5 times (reference for the "
+                        "FETCH_SIZE / WRITE_SIZE counter scale) and exit")
     return p.parse_args()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_score_traffic_8x32768.md")
+INDEXER_SOURCES = [os.path.join(ROOT, "sparse_attention_decode_04_amd", "csrc", f)
+                   for f in ("indexer_score.hip", "device_common.hpp", "ds_rows_internal.hpp")]
+
+
+def indexer_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in INDEXER_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per indexer launch from the committed counter summary, or
+    None when there is none or the kernel's sources changed since it was taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE) as fh:
+            for line in fh:
+                if line.startswith("- `") and "`: " in line:
+                    k, v = line[3:].split("`: ", 1)
+                    fields[k] = v.strip()
+        if fields.get("kernel_source_sha256") != indexer_source_hash():
+            return None
+        return {"fetch": float(fields["fetch_bytes_per_launch"]), "write": float(fields["write_bytes_per_launch"])}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def indexer_bytes_flops(inp):
@@ -93,6 +127,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = 64 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
 
     from sparse_attention_decode_04_amd import ds_rows as ds
     from sparse_attention_decode_04_amd import inputs as I
@@ -152,6 +196,7 @@ def main():
     per_call_four = per_call_ms(("indexer_score", "topk", "gather", "sparse_attn"))
 
     idx_bytes, idx_flops = indexer_bytes_flops(inp)
+    traffic = measured_traffic() if args.config == 2 else None
     idx_s = per_call["indexer_score"] * 1e-3
     achieved = idx_bytes / idx_s / 1e9
     rows_per_s = inp.rows / (ms_per_step * 1e-3)
@@ -191,7 +236,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": (traffic["fetch"] + traffic["write"]) if traffic else None,
+            "traffic_fetch_write": [traffic["fetch"], traffic["write"]] if traffic else None,
             "bytes_per_launch": idx_bytes,
             "mfma_tflops": idx_flops / idx_s / 1e12,
             "mfma_frac_of_bf16_peak": idx_flops / idx_s / 1e12 / BF16_PEAK_TFLOPS,
