@@ -209,7 +209,12 @@ ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows,
  * output) and the same attention and output. Nothing is written to a
  * gathered operand. Output bit-identical to ds_rows_gather +
  * ds_rows_sparse_attn on the same inputs, except on rows that the fail-closed
- * rule zeroes in both.
+ * rule zeroes in both. Source: the index-reading form of the pages' sparse
+ * attention, docs.rs "mlx-native 0.21.0 src/ops/deepseek_rows.rs", function
+ * dispatch_deepseek_sparse_attention_rows (its score and reduce kernels in
+ * "mlx-native 0.18.0 src/shaders/deepseek_rows.metal" read the KV through
+ * the indices), with the gather rules of
+ * deepseek_sparse_attention_gather_rows_bf16.
  *   indices    device i32, indices_elems >= max(index_offset + width)
  *   workspace  as ds_rows_sparse_attn (same size query)
  * Checks: those of ds_rows_gather on the table and indices, plus those of
