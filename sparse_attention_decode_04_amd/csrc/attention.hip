@@ -78,8 +78,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
   __shared__ uint32_t state[kAttnChunk];
   __shared__ uint32_t vbad[4][2][kAttnChunk];
 
-  const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
-  const uint32_t c = blockIdx.x - a.blk_begin[r];
+  // Row r runs on XCD r: consecutive workgroups go to consecutive XCDs, so
+  // block b = 8 c + r puts all of a row's chunks in one L2 (its query is
+  // fetched from memory once per row, not once per XCD).
+  const uint32_t r = blockIdx.x % kXcds;
+  const uint32_t c = blockIdx.x / kXcds;
+  if (r >= a.rows || c >= a.chunks[r]) return;
   const uint32_t width = a.width[r];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -222,9 +226,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_reduce_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float fac[kChunksPerSuper * kHeads];
   __shared__ uint32_t s_bad[kHeads];
 
-  constexpr uint32_t kDimChunks = kDim / kAttnDimChunk;
-  const uint32_t r = blockIdx.x / kDimChunks;
-  const uint32_t dc = blockIdx.x % kDimChunks;
+  // Row r on XCD r (block b = 8 dc + r): the row's probability planes,
+  // statistics and G^T are read by all 16 feature chunks through one L2.
+  const uint32_t r = blockIdx.x % kXcds;
+  const uint32_t dc = blockIdx.x / kXcds;
+  if (r >= a.rows) return;
   const uint32_t width = a.width[r];
   const uint32_t nch = a.chunks[r];
   const uint32_t w32 = nch * kAttnChunk;

@@ -330,10 +330,7 @@ ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool
   a.out = out;
   a.scale = scale;
   a.rows = p.rows;
-  uint32_t blocks = 0;
-  for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
-    a.blk_begin[r] = blocks;
-    if (r >= p.rows) continue;
+  for (uint32_t r = 0; r < p.rows; ++r) {
     a.kv[r] = static_cast<const uint16_t *>(rows->kv[r]);
     a.kv_len[r] = rows->kv_len[r];
     a.index_offset[r] = rows->index_offset[r];
@@ -344,13 +341,14 @@ ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool
     a.p_base[r] = p.p_base[r];
     a.stat_base[r] = p.stat_base[r];
     a.gt_base[r] = p.gt_base[r];
-    blocks += p.chunks[r];
   }
-  a.blk_begin[ds::kRowsMax] = blocks;
+  // Block b of either phase serves row b % 8 (one XCD per row).
+  uint32_t max_chunks = 0;
+  for (uint32_t r = 0; r < p.rows; ++r) max_chunks = std::max(max_chunks, p.chunks[r]);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = ds::launch_attn_logits(a, direct, blocks, s);
+  hipError_t e = ds::launch_attn_logits(a, direct, ds::kXcds * max_chunks, s);
   if (e != hipSuccess) return hip_fail(e, "attention logits launch");
-  e = ds::launch_attn_reduce(a, p.rows * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
+  e = ds::launch_attn_reduce(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
   return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
 }
 

@@ -16,6 +16,10 @@ constexpr int kIdxDim = 128;
 constexpr int kDim = 512;
 constexpr int kTopK = 512;
 constexpr int kRatio = 4;
+// MI355X has 8 XCDs, each with its own L2; the dispatcher hands consecutive
+// workgroups of a grid to consecutive XCDs (block b -> XCD b % 8).
+constexpr uint32_t kXcds = 8;
+static_assert(kRowsMax <= static_cast<int>(kXcds), "one XCD per row");
 
 // ---------------------------------------------------------------- indexer
 // One workgroup of 4 waves scores `keys_per_block` consecutive keys of one
@@ -127,7 +131,6 @@ struct AttnArgs {
   uint64_t p_base[kRowsMax];
   uint64_t stat_base[kRowsMax];
   uint64_t gt_base[kRowsMax];
-  uint32_t blk_begin[kRowsMax + 1]; // phase 1: prefix of chunks
 };
 hipError_t launch_attn_logits(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s);
 hipError_t launch_attn_reduce(const AttnArgs &a, uint32_t blocks, hipStream_t s);

@@ -18,28 +18,33 @@
 // held in registers (first level: 32768 scores, 32 per thread, kept as their
 // 32 score bits; later levels: 16384 list keys, 16 per thread), and writes that
 // chunk's best min(512, n) keys in rank order.
-//   Counting select (fast path): with smin/smax the chunk's extreme scores,
+//   Threshold and compaction (common case). A sample (each thread's first key)
+//   gives a threshold T: the smallest sampled score in the top bins holding 64
+//   of the 1024 samples. Every key >= T is appended, by one compare and a
+//   ballot per key, to its wave's LDS region (512 keys per wave). When no
+//   region overflows and at least min(512, n) keys were kept, the chunk's best
+//   keys are exactly the best keys of that set of a few thousand, which the
+//   counting select below then orders with 8 keys per thread. Chunks of at
+//   most 4096 candidates keep every key.
+//   Counting select: with smin/smax the extreme scores of the candidates,
 //   bin(s) = min(1023, floor((s - smin) * 1024 / (smax - smin))) is monotone
 //   in the score and equal scores share a bin, so every key in a higher bin
-//   outranks every key in a lower one.
-//     1. A sample (each thread's first key) is binned; the bin lo at which 64
-//        samples (or all of them) lie at or above is a likely lower bound for
-//        the 512th key.
-//     2. Only keys in bins >= lo enter the LDS histogram (a few thousand
-//        atomics instead of 32768); one scan gives the bin d holding the 512th
-//        key and every bin's exclusive suffix count. If fewer than 512 keys
-//        lie in bins >= lo, the histogram is rebuilt over every key.
-//     3. Keys of bins >= d are scattered into LDS grouped by bin, and a key's
-//        rank is its bin's suffix count plus the number of larger keys in its
-//        own bin.
-//   Taken when at most 1024 keys lie in bins >= d and no such bin holds more
-//   than 64 keys (spread-out score distributions).
+//   outranks every key in a lower one. One LDS histogram (keys of bins >= a
+//   sampled lower bin when the candidates are many) and one block scan give
+//   the bin d holding the 512th key and every bin's suffix count; keys of bins
+//   >= d are scattered into LDS grouped by bin, and a key's rank is its bin's
+//   suffix count plus the number of larger keys in its own bin. Taken when at
+//   most 1024 keys lie in bins >= d and no such bin holds more than 64 keys.
 //   Fallback (heavy ties, extreme outliers): MSB-first 8-bit radix select on
 //   the 64-bit keys until at most 1024 remain at or above the prefix, then a
 //   bitonic sort of those in LDS.
+//   When the compaction does not hold (heavy ties), the counting select runs
+//   on all of the chunk's candidates instead.
+// The code that runs in the common case is kept short: on this GPU a kernel
+// pays for every cold instruction-cache line it executes.
 // Levels repeat on the lists until each row has one; the last level writes
 // index + offset, or -1 for empty slots. A row of n visible keys needs one
-// level up to 32768 keys and two up to 1M.
+// level up to 32768 keys and two up to 16M.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 
@@ -49,6 +54,9 @@ constexpr int kBins = 1024;
 constexpr uint32_t kFastBinMax = 64;
 constexpr uint32_t kSampleMin = 64;
 constexpr int kWaves = kTopkThreads / 64;
+constexpr uint32_t kCompactPerWave = 512;                  // compaction capacity of one wave
+constexpr int kCompactPerLane = kCompactPerWave / 64;      // 8 compacted keys per thread
+constexpr uint32_t kSmallChunk = 4096;                     // chunks this small keep every key
 
 __device__ __forceinline__ uint64_t topk_key(float s, uint32_t index) {
   if (!__builtin_isfinite(s)) return 0;
@@ -113,24 +121,255 @@ __device__ __forceinline__ void scan_bins(const uint32_t *hist, uint32_t *wsum, 
   total = all;
 }
 
-// kFromScores: the first level, reading f32 scores; a candidate's key is its
-// order-preserving score bits (kept per candidate) and its position (implied).
-// Otherwise: a later level, reading the previous level's 64-bit key lists.
-//
-// The selection is VALU-bound (one workgroup per chunk), so each candidate's
-// bin is computed once and kept in a register; every later pass is a compare
-// or two per candidate.
+struct TopkShared {
+  uint32_t hist[kBins];
+  uint32_t sfx[kBins];
+  uint32_t cursor[kBins];
+  uint64_t cand[kTopkSortCap];
+  union {
+    uint64_t compact[kWaves * kCompactPerWave];               // wave regions of kept keys
+    uint32_t ordl[kTopkThreads * kTopkPerThreadFirst];        // first-level fallback: all score bits
+  };
+  __attribute__((aligned(16))) uint32_t wsum[kWaves];
+  __attribute__((aligned(16))) uint32_t wmax[kWaves];
+  __attribute__((aligned(16))) uint32_t wcount[kWaves];
+  uint32_t valid, min1, max, count, lo, digit, above, bin, kept, maxbin, hist_total, thr;
+};
+
+// Candidates of the first level: score bits per candidate (0 = none), index
+// implied by the position begin + tid + 1024 e.
+template <int N>
+struct OrdCand {
+  uint32_t (&o)[N];
+  uint32_t pos0;   // begin + tid
+  __device__ __forceinline__ uint32_t hi(int e) const { return o[e]; }
+  // ~position, rebuilt from one opaque base so that N positions are not kept
+  // live from the loads on.
+  __device__ __forceinline__ uint32_t low(int e) const {
+    uint32_t nbase = ~pos0;
+    asm volatile("" : "+v"(nbase));
+    return nbase - kTopkThreads * static_cast<uint32_t>(e);
+  }
+  __device__ __forceinline__ uint64_t key(int e) const {
+    return o[e] ? (static_cast<uint64_t>(o[e]) << 32) | low(e) : 0ull;
+  }
+  __device__ __forceinline__ uint64_t vkey(int e) const { return (static_cast<uint64_t>(o[e]) << 32) | low(e); }
+  // Opaque register barrier: values derived from the keys (full keys, masks)
+  // are recomputed after it rather than kept live across a loop.
+  __device__ __forceinline__ void fence() const {
+#pragma unroll
+    for (int e = 0; e < N; ++e) asm volatile("" : "+v"(o[e]));
+  }
+};
+
+// The same candidates after they were moved to LDS (ordl[tid + 1024 e]).
+struct LdsOrdCand {
+  const uint32_t *ordl;
+  uint32_t tid, pos0;
+  __device__ __forceinline__ uint32_t hi(int e) const { return ordl[tid + kTopkThreads * e]; }
+  __device__ __forceinline__ uint32_t low(int e) const { return ~pos0 - kTopkThreads * static_cast<uint32_t>(e); }
+  __device__ __forceinline__ uint64_t key(int e) const {
+    const uint32_t o = hi(e);
+    return o ? (static_cast<uint64_t>(o) << 32) | low(e) : 0ull;
+  }
+  __device__ __forceinline__ uint64_t vkey(int e) const { return (static_cast<uint64_t>(hi(e)) << 32) | low(e); }
+  __device__ __forceinline__ void fence() const {}
+};
+
+// Candidates held as full 64-bit keys (0 = none).
+template <int N>
+struct KeyCand {
+  uint64_t (&k)[N];
+  __device__ __forceinline__ uint32_t hi(int e) const { return static_cast<uint32_t>(k[e] >> 32); }
+  __device__ __forceinline__ uint64_t key(int e) const { return k[e]; }
+  __device__ __forceinline__ uint64_t vkey(int e) const { return k[e]; }
+  __device__ __forceinline__ void fence() const {
+#pragma unroll
+    for (int e = 0; e < N; ++e) asm volatile("" : "+v"(k[e]));
+  }
+};
+
+// Best `need` of the workgroup's candidates (kPer per thread, read through
+// `c`; their score bits lie in [omin, omax]), emitted in rank order through
+// emit(pos, key). kSample: pre-filter the histogram by a sampled lower bin
+// (worth it only for many candidates per thread).
+template <int kPer, bool kSample, class Cand, class Emit>
+__device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, uint32_t total, uint32_t need,
+                                                uint32_t omin, uint32_t omax, const Emit &emit) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  __syncthreads();   // earlier readers of the shared arrays are done
+  sh.hist[tid] = 0;
+  sh.cursor[tid] = 0;
+  if (tid == 0) { sh.count = 0; sh.lo = 0; }
+  __syncthreads();
+
+  const float smin = ord_score(omin), smax = ord_score(omax);
+  const float range = smax - smin;
+  const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
+  // Bin of every candidate, once, two 16-bit bins per register; kBins = no
+  // key. A zero range gives scale 0 and every (finite) key bin 0.
+  uint32_t binp[kPer / 2];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const uint32_t o = c.hi(e);
+    const float x = (ord_score(o) - smin) * scale;
+    const uint32_t b = o != 0 ? static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)))
+                              : static_cast<uint32_t>(kBins);
+    if (e & 1) binp[e / 2] |= b << 16;
+    else binp[e / 2] = b;
+  }
+  auto bin_at = [&](int e) -> uint32_t { return (e & 1) ? binp[e / 2] >> 16 : binp[e / 2] & 0xFFFFu; };
+  // A bin b lies in [lo, kBins) iff b - lo < kBins - lo (unsigned).
+  auto in_range = [](uint32_t b, uint32_t lo) { return b - lo < static_cast<uint32_t>(kBins) - lo; };
+
+  uint32_t lo = 0;
+  if constexpr (kSample) {
+    // Sample (each thread's first key) -> likely lower bin lo.
+    hist_add(sh.hist, bin_at(0), kBins, lane);
+    __syncthreads();
+    {
+      uint32_t h, above, maxge, nsamp;
+      scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, nsamp);
+      const uint32_t target = min(nsamp, kSampleMin);
+      if (target > 0 && above < target && target <= above + h) sh.lo = kBins - 1 - tid;
+    }
+    __syncthreads();
+    lo = sh.lo;
+    sh.hist[tid] = 0;
+    __syncthreads();
+  }
+
+  // Histogram of the keys in bins >= lo, scan; if they are fewer than need,
+  // once more over every key (lo = 0).
+  uint32_t d = 0, kept = 0, maxbin = 0;
+  for (;;) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (in_range(bin_at(e), lo)) hist_add(sh.hist, bin_at(e), kBins, lane);
+    __syncthreads();
+    uint32_t h, above, maxge, all;
+    scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, all);
+    const uint32_t b = kBins - 1 - tid;
+    sh.sfx[b] = above;
+    if (above < need && need <= above + h) {
+      sh.digit = b;
+      sh.kept = above + h;
+      sh.maxbin = maxge;
+    }
+    if (tid == 0) sh.hist_total = all;
+    __syncthreads();
+    if (sh.hist_total >= need || lo == 0) {
+      d = sh.digit;
+      kept = sh.kept;
+      maxbin = sh.maxbin;
+      break;
+    }
+    lo = 0;
+    sh.hist[tid] = 0;
+    __syncthreads();
+  }
+  if (kept <= kTopkSortCap && maxbin <= kFastBinMax) {
+    // Scatter the keys of bins >= d grouped by bin, then rank within bins.
+    c.fence();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (in_range(bin_at(e), d)) sh.cand[sh.sfx[bin_at(e)] + atomicAdd(&sh.cursor[bin_at(e)], 1u)] = c.vkey(e);
+    __syncthreads();
+    if (tid < kept) {
+      const uint64_t kk = sh.cand[tid];
+      const float x = (ord_score(static_cast<uint32_t>(kk >> 32)) - smin) * scale;
+      const uint32_t b = static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)));
+      const uint32_t base = sh.sfx[b], n = sh.hist[b];
+      uint32_t rank = 0;
+      for (uint32_t q = 0; q < n; ++q) rank += sh.cand[base + q] > kk ? 1u : 0u;
+      const uint32_t pos = base + rank;
+      if (pos < need) emit(pos, kk);
+    }
+    return;
+  }
+
+  // ---- fallback: radix select on the 64-bit keys, then bitonic sort ------
+  uint64_t thr = 1;
+  if (total > kTopkSortCap) {
+    uint32_t left = kTopK;          // ranks still to fill below the prefix
+    uint64_t prefix = 0;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      __syncthreads();
+      if (tid < 256) sh.hist[tid] = 0;
+      __syncthreads();
+      c.fence();
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const uint64_t kk = c.key(e);
+        const bool match = kk != 0 && (shift == 56 || (kk >> (shift + 8)) == (prefix >> (shift + 8)));
+        hist_add(sh.hist, match ? static_cast<uint32_t>(kk >> shift) & 255u : 256u, 256, lane);
+      }
+      __syncthreads();
+      uint32_t t = tid;
+      asm volatile("" : "+v"(t));   // keeps the digit arithmetic out of the loop preheader
+      if (t < 64) {
+        uint32_t v[4], sum = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { v[k] = sh.hist[255 - 4 * t - k]; sum += v[k]; }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t up = __shfl_up(incl, o);
+          if (t >= static_cast<uint32_t>(o)) incl += up;
+        }
+        uint32_t before = incl - sum;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (before < left && left <= before + v[k]) {
+            sh.digit = 255 - 4 * t - k;
+            sh.above = before;
+            sh.bin = v[k];
+          }
+          before += v[k];
+        }
+      }
+      __syncthreads();
+      left -= sh.above;
+      prefix |= static_cast<uint64_t>(sh.digit) << shift;
+      if ((kTopK - left) + sh.bin <= kTopkSortCap) { thr = prefix; break; }
+    }
+  }
+  c.fence();
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const uint64_t kk = c.key(e);
+    if (kk != 0 && kk >= thr) {
+      const uint32_t pos = atomicAdd(&sh.count, 1u);
+      if (pos < kTopkSortCap) sh.cand[pos] = kk;   // at most 1024 by construction
+    }
+  }
+  __syncthreads();
+  const uint32_t nk = min(sh.count, static_cast<uint32_t>(kTopkSortCap));
+  if (tid >= nk) sh.cand[tid] = 0;
+  __syncthreads();
+  const uint32_t size = nk <= kTopK ? kTopK : kTopkSortCap;
+  for (uint32_t k = 2; k <= size; k <<= 1) {
+    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t ixj = tid ^ j;
+      if (tid < size && ixj > tid) {
+        const uint64_t x = sh.cand[tid], y = sh.cand[ixj];
+        const bool desc = (tid & k) == 0;
+        if (desc ? (x < y) : (x > y)) { sh.cand[tid] = y; sh.cand[ixj] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < need) emit(tid, sh.cand[tid]);
+}
+
+// kFromScores: the first level, reading f32 scores. Otherwise a later level,
+// reading the previous level's 64-bit key lists.
 template <bool kFromScores>
 __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs a) {
   constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kTopkPerThreadLater;
   constexpr uint32_t kChunk = kTopkThreads * kPer;
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t sfx[kBins];
-  __shared__ uint32_t cursor[kBins];
-  __shared__ uint64_t cand[kTopkSortCap];
-  __shared__ __attribute__((aligned(16))) uint32_t wsum[kWaves];
-  __shared__ __attribute__((aligned(16))) uint32_t wmax[kWaves];
-  __shared__ uint32_t s_valid, s_min1, s_max, s_count, s_lo, s_digit, s_above, s_bin, s_kept, s_maxbin, s_hist_total;
+  __shared__ TopkShared sh;
 
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
   const uint32_t chunk = blockIdx.x - a.blk_begin[r];
@@ -138,22 +377,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   const uint32_t end = min(a.count[r], begin + kChunk);
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
+  const uint32_t wave = tid >> 6;
   const bool final_level = (a.final_mask >> r) & 1u;
 
-  hist[tid] = 0;
-  cursor[tid] = 0;
-  if (tid == 0) { s_valid = 0; s_min1 = 0xFFFFFFFFu; s_max = 0; s_count = 0; s_lo = 0; }
+  sh.hist[tid] = 0;
+  if (tid == 0) { sh.valid = 0; sh.min1 = 0xFFFFFFFFu; sh.max = 0; sh.thr = 0xFFFFFFFFu; }
 
   // Candidate e of this thread sits at position begin + tid + 1024 * e.
   // Loads are unconditional, from positions clamped into the row (every row
   // holds at least one score or list entry), and masked afterwards: loads
-  // under a branch would make the compiler wait for each one in turn.
+  // under a branch would make the compiler wait for each one in turn. Each
+  // load takes a uniform base and a 32-bit byte offset (rows hold < 2^30
+  // entries), so it needs one offset register rather than a 64-bit address.
   const uint32_t lastp = end > 0 ? end - 1 : 0;
   uint32_t ordv[kFromScores ? kPer : 1];     // score bits, 0 = no candidate
   uint64_t keyv[kFromScores ? 1 : kPer];
   if constexpr (kFromScores) {
-    // Uniform base + 32-bit byte offset (rows hold < 2^30 scores), so each
-    // load needs one offset register rather than a 64-bit address.
     const char *sc = reinterpret_cast<const char *>(a.scores + static_cast<uint64_t>(r) * a.score_stride);
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
@@ -172,239 +411,119 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     for (int e = 0; e < kPer; ++e)
       if (begin + tid + kTopkThreads * e >= end) keyv[e] = 0;
   }
-  // Opaque register barrier: values derived from the keys (full 64-bit keys,
-  // masks) are recomputed after it rather than hoisted and kept live across a
-  // loop, which would exceed the register budget.
-  auto fence_keys = [&]() {
+  auto run = [&](const auto &c) {
+    // Count and extreme score bits of the valid keys. A missing key has high
+    // word 0 (every valid key's is nonzero), so it never raises the maximum
+    // and, as 0 - 1 in unsigned arithmetic, never lowers the minimum.
+    uint32_t nvalid = 0, omin1 = 0xFFFFFFFFu, omax = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      if constexpr (kFromScores) asm volatile("" : "+v"(ordv[e]));
-      else asm volatile("" : "+v"(keyv[e]));
+      const uint32_t o = c.hi(e);
+      nvalid += o != 0 ? 1u : 0u;
+      omin1 = min(omin1, o - 1u);
+      omax = max(omax, o);
     }
-  };
-  // High word of candidate e (its score bits; 0 = none) and its full key.
-  auto hi_at = [&](int e) -> uint32_t {
-    if constexpr (kFromScores) return ordv[e];
-    else return static_cast<uint32_t>(keyv[e] >> 32);
-  };
-  // The low word ~p of position p = begin + tid + 1024 e is rebuilt from one
-  // opaque base, so that 32 positions are not kept live from the loads on.
-  auto key_at = [&](int e) -> uint64_t {
-    if constexpr (kFromScores) {
-      uint32_t nbase = ~(begin + tid);
-      asm volatile("" : "+v"(nbase));
-      const uint32_t np = nbase - kTopkThreads * static_cast<uint32_t>(e);   // = ~p
-      return ordv[e] ? (static_cast<uint64_t>(ordv[e]) << 32) | np : 0ull;
-    } else {
-      return keyv[e];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      nvalid += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nvalid), o));
+      omin1 = min(omin1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omin1), o)));
+      omax = max(omax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omax), o)));
     }
-  };
-  // The same for a candidate known to be valid.
-  auto valid_key_at = [&](int e) -> uint64_t {
-    if constexpr (kFromScores) {
-      uint32_t nbase = ~(begin + tid);
-      asm volatile("" : "+v"(nbase));
-      return (static_cast<uint64_t>(ordv[e]) << 32) | (nbase - kTopkThreads * static_cast<uint32_t>(e));
-    } else {
-      return keyv[e];
+    __syncthreads();   // LDS initialisation above is complete
+    if (lane == 0) {
+      atomicAdd(&sh.valid, nvalid);
+      atomicMin(&sh.min1, omin1);
+      atomicMax(&sh.max, omax);
     }
-  };
-
-  // Count and extreme score bits of the valid keys. A missing key has high
-  // word 0 (every valid key's is nonzero), so it never raises the maximum and,
-  // as 0 - 1 in unsigned arithmetic, never lowers the minimum.
-  uint32_t nvalid = 0, omin1 = 0xFFFFFFFFu, omax = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const uint32_t o = hi_at(e);
-    nvalid += o != 0 ? 1u : 0u;
-    omin1 = min(omin1, o - 1u);
-    omax = max(omax, o);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    nvalid += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nvalid), o));
-    omin1 = min(omin1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omin1), o)));
-    omax = max(omax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omax), o)));
-  }
-  __syncthreads();   // LDS initialisation above is complete
-  if (lane == 0) {
-    atomicAdd(&s_valid, nvalid);
-    atomicMin(&s_min1, omin1);
-    atomicMax(&s_max, omax);
-  }
-  __syncthreads();
-  const uint32_t total = s_valid;
-  const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
-
-  auto emit = [&](uint32_t pos, uint64_t kk) {
-    if (final_level) {
-      a.indices[a.out_offset[r] + pos] =
-          kk != 0 ? static_cast<int32_t>(~static_cast<uint32_t>(kk)) + a.offset[r] : -1;
-    } else {
-      a.out[a.out_base[r] + static_cast<uint64_t>(chunk) * kTopK + pos] = kk;
-    }
-  };
-  // Slots past the selected count are empty.
-  for (uint32_t t = need + tid; t < kTopK; t += kTopkThreads) emit(t, 0);
-  if (total == 0) return;
-
-  // ---- fast path: counting select on linear score bins -----------------
-  const float smin = ord_score(s_min1 + 1u), smax = ord_score(s_max);
-  const float range = smax - smin;
-  const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
-  // Bin of every candidate, once; kBins = no key. A zero range gives scale 0
-  // and every (finite) key bin 0.
-  // Two 16-bit bins per register.
-  uint32_t binp[kPer / 2];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const uint32_t o = hi_at(e);
-    const float x = (ord_score(o) - smin) * scale;
-    const uint32_t b = o != 0 ? static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)))
-                              : static_cast<uint32_t>(kBins);
-    if (e & 1) binp[e / 2] |= b << 16;
-    else binp[e / 2] = b;
-  }
-  auto bin_at = [&](int e) -> uint32_t { return (e & 1) ? binp[e / 2] >> 16 : binp[e / 2] & 0xFFFFu; };
-  // A bin b lies in [lo, kBins) iff b - lo < kBins - lo (unsigned).
-  auto in_range = [](uint32_t b, uint32_t lo) { return b - lo < static_cast<uint32_t>(kBins) - lo; };
-
-  // 1. Sample (each thread's first key) -> likely lower bin lo.
-  hist_add(hist, bin_at(0), kBins, lane);
-  __syncthreads();
-  {
-    uint32_t h, above, maxge, nsamp;
-    scan_bins(hist, wsum, wmax, tid, h, above, maxge, nsamp);
-    const uint32_t target = min(nsamp, kSampleMin);
-    if (target > 0 && above < target && target <= above + h) s_lo = kBins - 1 - tid;
-  }
-  __syncthreads();
-  uint32_t lo = s_lo;
-  hist[tid] = 0;                          // reused for the real histogram
-  __syncthreads();
-
-  // 2. Histogram of the keys in bins >= lo, scan; if they are fewer than
-  //    need, once more over every key (lo = 0).
-  uint32_t d = 0, kept = 0, maxbin = 0;
-  for (;;) {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (in_range(bin_at(e), lo)) hist_add(hist, bin_at(e), kBins, lane);
     __syncthreads();
-    uint32_t h, above, maxge, all;
-    scan_bins(hist, wsum, wmax, tid, h, above, maxge, all);
-    const uint32_t b = kBins - 1 - tid;
-    sfx[b] = above;
-    if (above < need && need <= above + h) {
-      s_digit = b;
-      s_kept = above + h;
-      s_maxbin = maxge;
-    }
-    if (tid == 0) s_hist_total = all;
-    __syncthreads();
-    if (s_hist_total >= need || lo == 0) {
-      d = s_digit;
-      kept = s_kept;
-      maxbin = s_maxbin;
-      break;
-    }
-    lo = 0;
-    hist[tid] = 0;
-    __syncthreads();
-  }
-  if (kept <= kTopkSortCap && maxbin <= kFastBinMax) {
-    // 3. Scatter the keys of bins >= d grouped by bin, then rank within bins.
-    fence_keys();
-#pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (in_range(bin_at(e), d)) cand[sfx[bin_at(e)] + atomicAdd(&cursor[bin_at(e)], 1u)] = valid_key_at(e);
-    __syncthreads();
-    if (tid < kept) {
-      const uint64_t kk = cand[tid];
-      const float x = (ord_score(static_cast<uint32_t>(kk >> 32)) - smin) * scale;
-      const uint32_t b = static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)));
-      const uint32_t base = sfx[b], n = hist[b];
-      uint32_t rank = 0;
-      for (uint32_t q = 0; q < n; ++q) rank += cand[base + q] > kk ? 1u : 0u;
-      const uint32_t pos = base + rank;
-      if (pos < need) emit(pos, kk);
-    }
-    return;
-  }
+    const uint32_t total = sh.valid;
+    const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
+    const uint32_t gmin = sh.min1 + 1u, gmax = sh.max;
 
-  // ---- fallback: radix select on the 64-bit keys, then bitonic sort ------
-  uint64_t thr = 1;
-  if (total > kTopkSortCap) {
-    uint32_t left = kTopK;          // ranks still to fill below the prefix
-    uint64_t prefix = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      __syncthreads();
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      fence_keys();
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const uint64_t kk = key_at(e);
-        const bool match = kk != 0 && (shift == 56 || (kk >> (shift + 8)) == (prefix >> (shift + 8)));
-        hist_add(hist, match ? static_cast<uint32_t>(kk >> shift) & 255u : 256u, 256, lane);
+    auto emit = [&](uint32_t pos, uint64_t kk) {
+      if (final_level) {
+        a.indices[a.out_offset[r] + pos] =
+            kk != 0 ? static_cast<int32_t>(~static_cast<uint32_t>(kk)) + a.offset[r] : -1;
+      } else {
+        a.out[a.out_base[r] + static_cast<uint64_t>(chunk) * kTopK + pos] = kk;
       }
+    };
+    // Slots past the selected count are empty.
+    for (uint32_t t = need + tid; t < kTopK; t += kTopkThreads) emit(t, 0);
+    if (total == 0) return;
+
+    // Threshold T from the sample (every key when the chunk is small).
+    uint32_t thr = 1;
+    if (end - begin > kSmallChunk) {
+      const float smin = ord_score(gmin), smax = ord_score(gmax);
+      const float range = smax - smin;
+      const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
+      const uint32_t o0 = c.hi(0);
+      const uint32_t b0 = o0 != 0 ? static_cast<uint32_t>(fminf((ord_score(o0) - smin) * scale,
+                                                                 static_cast<float>(kBins - 1)))
+                                  : static_cast<uint32_t>(kBins);
+      hist_add(sh.hist, b0, kBins, lane);
       __syncthreads();
-      uint32_t t = tid;
-      asm volatile("" : "+v"(t));   // keeps the digit arithmetic out of the loop preheader
-      if (t < 64) {
-        uint32_t v[4], sum = 0;
+      uint32_t h, above, maxge, nsamp;
+      scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, nsamp);
+      const uint32_t target = min(nsamp, kSampleMin);
+      if (target > 0 && above < target && target <= above + h) sh.lo = kBins - 1 - tid;
+      if (nsamp == 0 && tid == 0) sh.lo = 0;
+      __syncthreads();
+      const uint32_t lo = sh.lo;
+      uint32_t t = (b0 < kBins && b0 >= lo) ? o0 : 0xFFFFFFFFu;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) { v[k] = hist[255 - 4 * t - k]; sum += v[k]; }
-        uint32_t incl = sum;
+      for (int o = 32; o > 0; o >>= 1) t = min(t, static_cast<uint32_t>(__shfl_xor(static_cast<int>(t), o)));
+      if (lane == 0) atomicMin(&sh.thr, t);
+      __syncthreads();
+      thr = sh.thr;
+    }
+    // Compaction: keys with score bits >= T go to the wave's region, in
+    // candidate order; the running count is wave-uniform.
+    uint64_t *region = sh.compact + wave * kCompactPerWave;
+    uint32_t wcount = 0;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t up = __shfl_up(incl, o);
-          if (t >= static_cast<uint32_t>(o)) incl += up;
-        }
-        uint32_t before = incl - sum;
+    for (int e = 0; e < kPer; ++e) {
+      const bool in = c.hi(e) >= thr;            // a missing key (0) is below any T >= 1
+      const uint64_t mask = __ballot(in);
+      const uint32_t pos = wcount + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+      if (in && pos < kCompactPerWave) region[pos] = c.vkey(e);
+      wcount += static_cast<uint32_t>(__popcll(mask));
+    }
+    if (lane == 0) sh.wcount[wave] = wcount;
+    __syncthreads();
+    uint32_t kept = 0, overflow = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (before < left && left <= before + v[k]) {
-            s_digit = 255 - 4 * t - k;
-            s_above = before;
-            s_bin = v[k];
-          }
-          before += v[k];
-        }
+    for (int v = 0; v < kWaves / 4; ++v) {
+      const u32x4 w4 = reinterpret_cast<const u32x4 *>(sh.wcount)[v];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        kept += w4[k];
+        overflow |= w4[k] > kCompactPerWave ? 1u : 0u;
       }
-      __syncthreads();
-      left -= s_above;
-      prefix |= static_cast<uint64_t>(s_digit) << shift;
-      if ((kTopK - left) + s_bin <= kTopkSortCap) { thr = prefix; break; }
     }
-  }
-  fence_keys();
+    if (!overflow && kept >= need) {
+      // The chunk's best keys are the best of the kept ones.
+      uint64_t kc[kCompactPerLane];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const uint64_t kk = key_at(e);
-    if (kk != 0 && kk >= thr) {
-      const uint32_t pos = atomicAdd(&s_count, 1u);
-      if (pos < kTopkSortCap) cand[pos] = kk;   // at most 1024 by construction
-    }
-  }
-  __syncthreads();
-  const uint32_t nk = min(s_count, static_cast<uint32_t>(kTopkSortCap));
-  if (tid >= nk) cand[tid] = 0;
-  __syncthreads();
-  const uint32_t size = nk <= kTopK ? kTopK : kTopkSortCap;
-  for (uint32_t k = 2; k <= size; k <<= 1) {
-    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-      const uint32_t ixj = tid ^ j;
-      if (tid < size && ixj > tid) {
-        const uint64_t x = cand[tid], y = cand[ixj];
-        const bool desc = (tid & k) == 0;
-        if (desc ? (x < y) : (x > y)) { cand[tid] = y; cand[ixj] = x; }
-      }
+      for (int j = 0; j < kCompactPerLane; ++j)
+        kc[j] = lane + 64u * j < wcount ? region[lane + 64 * j] : 0ull;
+      counting_select<kCompactPerLane, false>(sh, KeyCand<kCompactPerLane>{kc}, kept, need, max(thr, gmin), gmax,
+                                              emit);
+    } else if constexpr (kFromScores) {
+      // Heavy ties: select over every candidate. The score bits move to LDS
+      // (over the compaction regions), which frees their registers.
       __syncthreads();
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) sh.ordl[tid + kTopkThreads * e] = c.hi(e);
+      counting_select<kPer, true>(sh, LdsOrdCand{sh.ordl, tid, begin + tid}, total, need, gmin, gmax, emit);
+    } else {
+      counting_select<kPer, true>(sh, c, total, need, gmin, gmax, emit);
     }
-  }
-  if (tid < need) emit(tid, cand[tid]);
+  };
+  if constexpr (kFromScores) run(OrdCand<kPer>{ordv, begin + tid});
+  else run(KeyCand<kPer>{keyv});
 }
 
 hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s) {
