@@ -94,31 +94,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
   const uint32_t g = lane >> 5;
   const uint32_t f0 = 128 * kq + 64 * g;   // this lane group's 64 features
 
-  // Query fragments first: they do not depend on the slot indices.
+  // The lane's slot: its state and its source row. Loads are unconditional
+  // (a slot past the width reads the row's last slot, a sentinel or bad index
+  // reads KV row 0) and masked afterwards, so they are all in flight at once.
+  // The slot's index (or mask entry) is loaded first: the KV row load depends
+  // on it, and loads complete in issue order.
+  const uint32_t slot = c * kAttnChunk + col;
+  const uint32_t cslot = min(slot, width - 1);
+  int32_t raw_index = 0;
+  uint16_t raw_mask = 0;
+  if (kDirect) raw_index = a.indices[a.index_offset[r] + cslot];
+  else raw_mask = a.mask[a.slot_base[r] + cslot];
+
+  // Query fragments: they do not depend on the slot.
   const uint16_t *qrow = a.q + (static_cast<uint64_t>(a.q_row[r]) * kHeads + 32 * hh + col) * kDim + f0;
   u32x4 qa[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) qa[s] = load16(qrow + 8 * s);
 
-  // The lane's slot: its state and its source row. Loads are unconditional
-  // (a slot past the width reads the row's last slot, a sentinel or bad index
-  // reads KV row 0) and masked afterwards, so they are all in flight at once.
-  const uint32_t slot = c * kAttnChunk + col;
-  const uint32_t cslot = min(slot, width - 1);
   uint32_t st;
   const uint16_t *src;
   if (kDirect) {
-    const int32_t raw = a.indices[a.index_offset[r] + cslot];
-    const int32_t i = slot < width ? raw : -1;
+    const int32_t i = slot < width ? raw_index : -1;
     const bool ok = i >= 0 && static_cast<uint32_t>(i) < a.kv_len[r];
     st = ok ? kLive : ((slot < width && i != -1) ? kBad : kSkip);
     src = a.kv[r] + static_cast<uint64_t>(ok ? i : 0) * kDim;
   } else {
-    const uint16_t mraw = a.mask[a.slot_base[r] + cslot];
-    st = slot < width ? mask_state(mraw) : kSkip;
+    st = slot < width ? mask_state(raw_mask) : kSkip;
     src = a.gathered + (a.slot_base[r] + cslot) * kDim;
   }
   const bool use = kDirect ? st == kLive : slot < width;
+  // This thread's head (epilogue: head tid / 8) sink, stored with the chunk
+  // statistics so that phase 2 gets it in the same load.
+  const float sink_h = a.sinks[tid >> 3];
   u32x4 gb[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) gb[s] = load16(src + f0 + 8 * s);
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
   *reinterpret_cast<u16x4 *>(a.p_lo + pidx) = lo;
   if (part == 0)
     a.stats[a.stat_base[r] + static_cast<uint64_t>(c) * kHeads + head] =
-        make_float4(mx, ssum, bad ? 1.0f : 0.0f, 0.0f);
+        make_float4(mx, ssum, bad ? 1.0f : 0.0f, sink_h);
 }
 
 // ---------------------------------------------------------------- phase 2
@@ -249,7 +257,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_reduce_kernel(AttnArgs a) {
   const uint16_t *plo = a.p_lo + a.p_base[r] + static_cast<uint64_t>(ahead) * w32;
   const uint16_t *gtr = a.gt + a.gt_base[r] + static_cast<uint64_t>(dc * kAttnDimChunk + col) * w32;
 
-  const float sink = a.sinks[head];
   f32x16 out = {};
   float m = 0.0f, invz = 0.0f;
   for (uint32_t s0 = 0; s0 < width; s0 += kAttnSuper) {
@@ -281,6 +288,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_reduce_kernel(AttnArgs a) {
     if (s0 == 0) {
       // m, Z and the bad flag of each head need every chunk: those of the
       // first span are in registers; rows wider than one span read the rest.
+      const float sink = x0.w;   // phase 1 stores each head's sink with its statistics
       bool bad = !__builtin_isfinite(sink);
       float mm = bad ? 0.0f : sink;
       auto take_max = [&](const float4 &x) {

@@ -117,7 +117,7 @@ struct AttnArgs {
   const uint16_t *kv[kRowsMax];     // bf16 [kv_len, 512] per row (direct variant)
   uint16_t *p_hi;                   // bf16 hi part of p~: row r at p_base[r], [64][w32]
   uint16_t *p_lo;                   // bf16 lo part of p~, same layout
-  float4 *stats;                    // (m_c, s_c, bad, 0): row r at stat_base[r], [chunks][64]
+  float4 *stats;                    // (m_c, s_c, bad, sink): row r at stat_base[r], [chunks][64]
   uint16_t *gt;                     // bf16 G^T: row r at gt_base[r], [512][w32]
   float *out;                       // f32 [_, 64, 512]
   float scale;
