@@ -53,7 +53,7 @@ def parse():
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_score_traffic_8x32768.md")
 INDEXER_SOURCES = [os.path.join(ROOT, "sparse_attention_decode_04_amd", "csrc", f)
-                   for f in ("indexer_score.hip", "device_common.hpp", "ds_rows_internal.hpp")]
+                   for f in ("indexer_score.hip", "device_common.hpp", "select_common.hpp", "ds_rows_internal.hpp")]
 
 
 def indexer_source_hash():
@@ -184,6 +184,8 @@ def main():
     ms_per_step, wall = timed("step_direct")
     # The four-call path (gather, then attention on the gathered rows).
     ms_four, _ = timed("step")
+    # Score and top-k in one call (first selection stage in the indexer).
+    ms_fused, _ = timed("step_fused")
 
     def per_call_ms(calls):
         """Mean duration of each call, from HIP events recorded around it on
@@ -216,6 +218,7 @@ def main():
     per_call = per_call_ms(("indexer_score", "topk", "sparse_attn_direct"))
     indexer_ms = back_to_back_ms("indexer_score", max(args.steps, 50))
     per_call_four = per_call_ms(("indexer_score", "topk", "gather", "sparse_attn"))
+    per_call_fused = per_call_ms(("indexer_topk", "sparse_attn_direct"))
 
     idx_bytes, idx_flops = indexer_bytes_flops(inp)
     traffic = measured_traffic() if args.config == 2 else None
@@ -250,6 +253,9 @@ def main():
         "four_call_pipeline": {
             "calls": "ds_rows_indexer_score -> ds_rows_topk -> ds_rows_gather -> ds_rows_sparse_attn",
             "ms_per_step": ms_four, "rows_per_s": inp.rows / (ms_four * 1e-3), "per_call_ms": per_call_four},
+        "fused_pipeline": {
+            "calls": "ds_rows_indexer_topk -> ds_rows_sparse_attn_direct",
+            "ms_per_step": ms_fused, "rows_per_s": inp.rows / (ms_fused * 1e-3), "per_call_ms": per_call_fused},
         "wall_s_timed_region": wall,
         "roofline": {
             "kernel": "indexer_score_kernel",

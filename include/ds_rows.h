@@ -12,6 +12,10 @@
  *   ds_rows_sparse_attn    attention over the gathered rows with a learned
  *                          per-head sink
  *
+ * and two fused forms of it: ds_rows_indexer_topk (score and top-512 in one
+ * call, the first selection stage in the indexer's epilogue) and
+ * ds_rows_sparse_attn_direct (gather and attention in one call).
+ *
  * Source pages (docs.rs source views of the Rust crate mlx-native):
  *   [shader 0.18] "mlx-native 0.18.0 src/shaders/deepseek_rows.metal"
  *   [host 0.21]   "mlx-native 0.21.0 src/ops/deepseek_rows.rs"
@@ -102,6 +106,7 @@ typedef struct {
  * the sum of the widths of rows 0..r-1 (times 512 for the gathered rows). */
 size_t ds_rows_scores_elems(const ds_indexer_rows *rows);        /* rows * max kv_len */
 size_t ds_rows_topk_workspace_bytes(const ds_indexer_rows *rows);
+size_t ds_rows_indexer_topk_workspace_bytes(const ds_indexer_rows *rows);
 size_t ds_rows_gathered_elems(const ds_sparse_rows *rows);       /* sum(width) * 512 */
 size_t ds_rows_mask_elems(const ds_sparse_rows *rows);           /* sum(width) */
 size_t ds_rows_attn_workspace_bytes(const ds_sparse_rows *rows);
@@ -143,6 +148,33 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows,
                        void *workspace, size_t workspace_bytes,
                        int32_t *indices, size_t indices_elems,
                        void *stream);
+
+/* ---- ds_rows_indexer_topk -----------------------------------------------
+ * ds_rows_indexer_score followed by ds_rows_topk, with the first selection
+ * stage moved into the indexer ([shader 0.18] deepseek_indexer_score_mma_
+ * rows_bf16 and deepseek_indexer_topk_{block,merge,finalize}_rows_i32; the
+ * pages' block stage keeps each 1024-key block's best 512). Writes the same
+ * scores and the same indices as the two calls, bit for bit.
+ * Each 1024-key block of the indexer keeps the keys of its top score bins
+ * (at least 64, at most 128, or every valid key when it has at most 128)
+ * and a floor below which lie all of its other keys; the top-k levels then
+ * select from those candidates, and a row's result stands only if no block
+ * floor lies above its 512th key. Otherwise (heavy ties, scores sorted by
+ * position) the row is selected again from its scores in the same call,
+ * which is exact but slower.
+ *   q, weights, scores  as ds_rows_indexer_score
+ *   workspace  device scratch, workspace_bytes >=
+ *              ds_rows_indexer_topk_workspace_bytes (contents on entry do
+ *              not matter; clobbered)
+ *   indices    device i32, indices_elems >= max(output_offset + 512)
+ * Checks: those of ds_rows_indexer_score and of ds_rows_topk. */
+ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows,
+                               const void *q, size_t q_elems,
+                               const float *weights, size_t weights_elems,
+                               float *scores, size_t scores_elems,
+                               void *workspace, size_t workspace_bytes,
+                               int32_t *indices, size_t indices_elems,
+                               void *stream);
 
 /* ---- ds_rows_gather -----------------------------------------------------
  * Gathers, for slot t < width[r] of row r with i = indices[index_offset[r]+t]

@@ -46,7 +46,13 @@ struct IndexerPlan {
   uint64_t q_rows = 0;          // max q_row + 1
   uint64_t indices_end = 0;     // max output_offset + 512
   uint64_t topk_bank = 0;       // u64 entries per ping-pong bank
+  // Indexer grid: blocks of kIndexerKeysPerBlock keys, rows in order.
+  uint32_t blk_begin[ds::kRowsMax + 1] = {};
+  // Fused indexer + top-k: candidate lists, block floors, list banks.
+  uint64_t fused_bank = 0;
 };
+
+constexpr uint32_t kIndexerKeysPerBlock = 1024;
 
 ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
   if (!t) return fail("null indexer row table");
@@ -73,11 +79,28 @@ ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
     p->indices_end = std::max<uint64_t>(p->indices_end, uint64_t(t->output_offset[r]) + DS_TOP_K);
     const uint32_t chunks = std::max<uint32_t>(1, div_up(p->visible[r], ds::kTopkChunkFirst));
     if (chunks > 1) p->topk_bank += uint64_t(chunks) * DS_TOP_K;
+    const uint32_t blocks = div_up(t->kv_len[r], kIndexerKeysPerBlock);
+    p->blk_begin[r + 1] = p->blk_begin[r] + blocks;
+    const uint32_t fchunks = div_up(uint64_t(blocks) * ds::kIdxCand, ds::kTopkChunkLater);
+    if (fchunks > 1) p->fused_bank += uint64_t(fchunks) * DS_TOP_K;
   }
+  for (uint32_t r = t->rows; r < ds::kRowsMax; ++r) p->blk_begin[r + 1] = p->blk_begin[r];
   return DS_OK;
 }
 
 uint64_t topk_workspace_bytes(const IndexerPlan &p) { return 2 * p.topk_bank * sizeof(uint64_t); }
+
+// Fused workspace: candidate lists (kIdxCand keys per indexer block), block
+// floors, then two ping-pong banks of list keys.
+uint64_t fused_cand_bytes(const IndexerPlan &p) {
+  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxCand * sizeof(uint64_t));
+}
+uint64_t fused_floor_bytes(const IndexerPlan &p) {
+  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * sizeof(uint64_t));
+}
+uint64_t fused_workspace_bytes(const IndexerPlan &p) {
+  return fused_cand_bytes(p) + fused_floor_bytes(p) + 2 * p.fused_bank * sizeof(uint64_t);
+}
 
 // ------------------------------------------------------------- sparse table
 struct SparsePlan {
@@ -139,9 +162,126 @@ ds_status cap(uint64_t have, uint64_t want, const char *name, const char *unit) 
     if (st_ != DS_OK) return st_;   \
   } while (0)
 
+// Operand checks shared by the indexer entry points.
+ds_status check_indexer_operands(const ds_indexer_rows *rows, const IndexerPlan &p, const void *q, size_t q_elems,
+                                 const float *weights, size_t weights_elems, const float *scores,
+                                 size_t scores_elems) {
+  DS_TRY(need(q, "indexer q"));
+  DS_TRY(need(weights, "indexer weights"));
+  DS_TRY(need(scores, "indexer scores"));
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    if (!rows->keys[r]) return fail("indexer row %u: keys must not be null", r);
+    DS_TRY(cap(rows->keys_elems[r], uint64_t(rows->kv_len[r]) * DS_INDEXER_DIM, "indexer kv", "elements"));
+  }
+  DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_INDEXER_DIM, "indexer q", "elements"));
+  DS_TRY(cap(weights_elems, p.q_rows * DS_HEADS, "indexer weights", "elements"));
+  DS_TRY(cap(scores_elems, p.rows * p.max_kv, "indexer scores", "elements"));
+  return DS_OK;
+}
+
+// Indexer launch; with cand/floors set, also the fused top-k stage.
+ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, const void *q, const float *weights,
+                         float *scores, uint64_t *cand, uint64_t *floors, void *stream) {
+  ds::IndexerArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.w = weights;
+  a.scores = scores;
+  a.score_stride = p.max_kv;
+  a.rows = p.rows;
+  a.keys_per_block = kIndexerKeysPerBlock;
+  a.cand = cand;
+  a.floors = floors;
+  for (uint32_t r = 0; r <= ds::kRowsMax; ++r) a.blk_begin[r] = p.blk_begin[r];
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    a.keys[r] = static_cast<const uint16_t *>(rows->keys[r]);
+    a.kv_len[r] = rows->kv_len[r];
+    a.visible[r] = p.visible[r];
+    a.q_row[r] = rows->q_row[r];
+  }
+  const hipError_t e = ds::launch_indexer_score(a, p.blk_begin[ds::kRowsMax], cand != nullptr,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
+}
+
+// First-level input of the top-k levels: the scores (lists == nullptr;
+// count = visible keys) or the fused indexer's candidate lists (count and
+// base per row, with the block floors to check on the final level).
+struct TopkInput {
+  const uint64_t *lists = nullptr;
+  const uint64_t *floors = nullptr;
+  uint32_t count[ds::kRowsMax] = {};
+  uint64_t base[ds::kRowsMax] = {};
+};
+
+// Selection levels until every row has one list; the last writes indices.
+ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, const float *scores,
+                          const TopkInput &in, uint64_t *bank0, uint64_t *bank1, int32_t *indices, void *stream) {
+  uint64_t *bank[2] = {bank0, bank1};
+  const bool from_lists = in.lists != nullptr;
+  const uint32_t first_chunk = from_lists ? ds::kTopkChunkLater : ds::kTopkChunkFirst;
+  uint32_t count[ds::kRowsMax] = {}, chunks[ds::kRowsMax] = {};
+  uint64_t in_base[ds::kRowsMax] = {};
+  bool done[ds::kRowsMax] = {};
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    count[r] = in.count[r];
+    in_base[r] = in.base[r];
+    chunks[r] = std::max<uint32_t>(1, div_up(count[r], first_chunk));
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (uint32_t level = 0;; ++level) {
+    ds::TopkLevelArgs a{};
+    a.scores = scores;
+    a.score_stride = p.max_kv;
+    a.in = level == 0 ? in.lists : bank[(level - 1) & 1];
+    a.out = bank[level & 1];
+    a.indices = indices;
+    a.rows = p.rows;
+    a.from_scores = (level == 0 && !from_lists) ? 1 : 0;
+    a.floors = in.floors;
+    uint32_t blocks = 0;
+    uint64_t out_elems = 0;
+    for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
+      a.blk_begin[r] = blocks;
+      if (r >= p.rows || done[r]) continue;
+      a.count[r] = count[r];
+      a.in_base[r] = in_base[r];
+      a.out_base[r] = out_elems;
+      a.offset[r] = rows->offset[r];
+      a.out_offset[r] = rows->output_offset[r];
+      if (chunks[r] == 1) {
+        a.final_mask |= 1u << r;
+        if (from_lists) {
+          a.check_mask |= 1u << r;
+          a.floor_begin[r] = p.blk_begin[r];
+          a.floor_count[r] = p.blk_begin[r + 1] - p.blk_begin[r];
+          a.fallback_count[r] = p.visible[r];
+        }
+      } else {
+        out_elems += uint64_t(chunks[r]) * DS_TOP_K;
+      }
+      blocks += chunks[r];
+    }
+    a.blk_begin[ds::kRowsMax] = blocks;
+    const hipError_t e = ds::launch_topk_level(a, blocks, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    bool all = true;
+    for (uint32_t r = 0; r < p.rows; ++r) {
+      if (done[r]) continue;
+      if (chunks[r] == 1) { done[r] = true; continue; }
+      all = false;
+      in_base[r] = a.out_base[r];
+      count[r] = chunks[r] * DS_TOP_K;
+      chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunkLater));
+    }
+    if (all) break;
+  }
+  return DS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
 
 size_t ds_rows_scores_elems(const ds_indexer_rows *rows) {
   IndexerPlan p;
@@ -177,38 +317,8 @@ ds_status ds_rows_indexer_score(const ds_indexer_rows *rows, const void *q, size
                                 size_t weights_elems, float *scores, size_t scores_elems, void *stream) {
   IndexerPlan p;
   DS_TRY(check_indexer(rows, &p));
-  DS_TRY(need(q, "indexer q"));
-  DS_TRY(need(weights, "indexer weights"));
-  DS_TRY(need(scores, "indexer scores"));
-  for (uint32_t r = 0; r < p.rows; ++r) {
-    if (!rows->keys[r]) return fail("indexer row %u: keys must not be null", r);
-    DS_TRY(cap(rows->keys_elems[r], uint64_t(rows->kv_len[r]) * DS_INDEXER_DIM, "indexer kv", "elements"));
-  }
-  DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_INDEXER_DIM, "indexer q", "elements"));
-  DS_TRY(cap(weights_elems, p.q_rows * DS_HEADS, "indexer weights", "elements"));
-  DS_TRY(cap(scores_elems, p.rows * p.max_kv, "indexer scores", "elements"));
-
-  ds::IndexerArgs a{};
-  a.q = static_cast<const uint16_t *>(q);
-  a.w = weights;
-  a.scores = scores;
-  a.score_stride = p.max_kv;
-  a.rows = p.rows;
-  a.keys_per_block = 1024;
-  uint32_t blocks = 0;
-  for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
-    a.blk_begin[r] = blocks;
-    if (r < p.rows) {
-      a.keys[r] = static_cast<const uint16_t *>(rows->keys[r]);
-      a.kv_len[r] = rows->kv_len[r];
-      a.visible[r] = p.visible[r];
-      a.q_row[r] = rows->q_row[r];
-      blocks += div_up(rows->kv_len[r], a.keys_per_block);
-    }
-  }
-  a.blk_begin[ds::kRowsMax] = blocks;
-  const hipError_t e = ds::launch_indexer_score(a, blocks, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
+  DS_TRY(check_indexer_operands(rows, p, q, q_elems, weights, weights_elems, scores, scores_elems));
+  return launch_indexer(rows, p, q, weights, scores, nullptr, nullptr, stream);
 }
 
 ds_status ds_rows_topk(const ds_indexer_rows *rows, const float *scores, size_t scores_elems, void *workspace,
@@ -223,53 +333,43 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows, const float *scores, size_t 
   DS_TRY(cap(workspace_bytes, ws, "indexer top-k scratch", "bytes"));
   DS_TRY(cap(indices_elems, p.indices_end, "indexer output", "elements"));
 
-  uint64_t *bank[2] = {static_cast<uint64_t *>(workspace), static_cast<uint64_t *>(workspace) + p.topk_bank};
-  uint32_t count[ds::kRowsMax] = {}, chunks[ds::kRowsMax] = {};
-  uint64_t in_base[ds::kRowsMax] = {};
-  bool done[ds::kRowsMax] = {};
+  TopkInput in{};
+  for (uint32_t r = 0; r < p.rows; ++r) in.count[r] = p.visible[r];
+  uint64_t *bank = static_cast<uint64_t *>(workspace);
+  return run_topk_levels(rows, p, scores, in, bank, bank + p.topk_bank, indices, stream);
+}
+
+size_t ds_rows_indexer_topk_workspace_bytes(const ds_indexer_rows *rows) {
+  IndexerPlan p;
+  if (check_indexer(rows, &p) != DS_OK) return 0;
+  return fused_workspace_bytes(p);
+}
+
+ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_t q_elems, const float *weights,
+                               size_t weights_elems, float *scores, size_t scores_elems, void *workspace,
+                               size_t workspace_bytes, int32_t *indices, size_t indices_elems, void *stream) {
+  IndexerPlan p;
+  DS_TRY(check_indexer(rows, &p));
+  DS_TRY(check_indexer_operands(rows, p, q, q_elems, weights, weights_elems, scores, scores_elems));
+  DS_TRY(need(workspace, "indexer top-k workspace"));
+  DS_TRY(need(indices, "indexer output"));
+  DS_TRY(cap(workspace_bytes, fused_workspace_bytes(p), "indexer top-k workspace", "bytes"));
+  DS_TRY(cap(indices_elems, p.indices_end, "indexer output", "elements"));
+
+  char *ws = static_cast<char *>(workspace);
+  uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
+  uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
+  uint64_t *bank = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
+  DS_TRY(launch_indexer(rows, p, q, weights, scores, cand, floors, stream));
+
+  TopkInput in{};
+  in.lists = cand;
+  in.floors = floors;
   for (uint32_t r = 0; r < p.rows; ++r) {
-    count[r] = p.visible[r];
-    chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunkFirst));
+    in.count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand;
+    in.base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
   }
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  for (uint32_t level = 0;; ++level) {
-    ds::TopkLevelArgs a{};
-    a.scores = scores;
-    a.score_stride = p.max_kv;
-    a.in = level == 0 ? nullptr : bank[(level - 1) & 1];
-    a.out = bank[level & 1];
-    a.indices = indices;
-    a.rows = p.rows;
-    a.from_scores = level == 0 ? 1 : 0;
-    uint32_t blocks = 0;
-    uint64_t out_elems = 0;
-    for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
-      a.blk_begin[r] = blocks;
-      if (r >= p.rows || done[r]) continue;
-      a.count[r] = count[r];
-      a.in_base[r] = in_base[r];
-      a.out_base[r] = out_elems;
-      a.offset[r] = rows->offset[r];
-      a.out_offset[r] = rows->output_offset[r];
-      if (chunks[r] == 1) a.final_mask |= 1u << r;
-      else out_elems += uint64_t(chunks[r]) * DS_TOP_K;
-      blocks += chunks[r];
-    }
-    a.blk_begin[ds::kRowsMax] = blocks;
-    const hipError_t e = ds::launch_topk_level(a, blocks, s);
-    if (e != hipSuccess) return hip_fail(e, "top-k launch");
-    bool all = true;
-    for (uint32_t r = 0; r < p.rows; ++r) {
-      if (done[r]) continue;
-      if (chunks[r] == 1) { done[r] = true; continue; }
-      all = false;
-      in_base[r] = a.out_base[r];
-      count[r] = chunks[r] * DS_TOP_K;
-      chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunkLater));
-    }
-    if (all) break;
-  }
-  return DS_OK;
+  return run_topk_levels(rows, p, scores, in, bank, bank + p.fused_bank, indices, stream);
 }
 
 ds_status ds_rows_gather(const ds_sparse_rows *rows, const int32_t *indices, size_t indices_elems, void *gathered,

@@ -26,6 +26,16 @@ static_assert(kRowsMax <= static_cast<int>(kXcds), "one XCD per row");
 // row; waves take 16-key tiles round robin.
 constexpr int kIdxThreads = 256;
 constexpr int kIdxTile = 16;
+constexpr uint32_t kIdxMaxKeysPerBlock = 1024;
+// Fused top-k stage (ds_rows_indexer_topk): every workgroup also writes up to
+// kIdxCand candidate keys of its own block (the keys of its top score bins,
+// at least kIdxCandMin of them, or every valid key when there are at most
+// kIdxCand) and a floor: 0 when it wrote every valid key of the block,
+// otherwise its smallest written key, below which lie all of its unwritten
+// keys (~0 when its top bins held more than kIdxCand keys).
+constexpr uint32_t kIdxCand = 128;
+constexpr uint32_t kIdxCandMin = 64;
+constexpr int kIdxCandBins = 256;
 
 struct IndexerArgs {
   const uint16_t *keys[kRowsMax];   // bf16 [kv_len, 128] per row
@@ -39,8 +49,10 @@ struct IndexerArgs {
   uint32_t visible[kRowsMax];       // min(kv_len, (start_pos + 1) / 4)
   uint32_t q_row[kRowsMax];
   uint32_t blk_begin[kRowsMax + 1]; // first block of each row; [rows..] = total
+  uint64_t *cand;                   // fused: kIdxCand keys per block (0 = none)
+  uint64_t *floors;                 // fused: one floor per block
 };
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, hipStream_t s);
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, bool fused, hipStream_t s);
 
 // ------------------------------------------------------------------ top-k
 // One selection level: every workgroup reduces a chunk of one row's
@@ -70,6 +82,15 @@ struct TopkLevelArgs {
   int32_t offset[kRowsMax];
   uint32_t out_offset[kRowsMax];
   uint32_t blk_begin[kRowsMax + 1];
+  // Candidates from the fused indexer: on the final level of a row with bit r
+  // of check_mask, the result stands only if no block floor of the row says
+  // that an unwritten key could rank; otherwise the row is selected again from
+  // its `fallback_count` scores.
+  uint32_t check_mask;
+  const uint64_t *floors;
+  uint32_t floor_begin[kRowsMax];
+  uint32_t floor_count[kRowsMax];
+  uint32_t fallback_count[kRowsMax];
 };
 hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s);
 

@@ -47,6 +47,7 @@
 // level up to 32768 keys and two up to 16M.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
+#include "select_common.hpp"
 
 namespace ds {
 
@@ -57,34 +58,6 @@ constexpr int kWaves = kTopkThreads / 64;
 constexpr uint32_t kCompactPerWave = 512;                  // compaction capacity of one wave
 constexpr int kCompactPerLane = kCompactPerWave / 64;      // 8 compacted keys per thread
 constexpr uint32_t kSmallChunk = 4096;                     // chunks this small keep every key
-
-__device__ __forceinline__ uint64_t topk_key(float s, uint32_t index) {
-  if (!__builtin_isfinite(s)) return 0;
-  s += 0.0f;                                   // -0 -> +0
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~index);
-}
-
-__device__ __forceinline__ float ord_score(uint32_t ord) {
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
-
-// LDS histogram increment by the active lanes of a wave (callers may call it
-// under a branch); one atomic by the first active lane when every active lane
-// has the same bin (heavy ties), one per lane otherwise. `b` >= nbins means
-// "no key".
-__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t b, uint32_t nbins, uint32_t lane) {
-  const uint32_t first = __builtin_amdgcn_readfirstlane(b);
-  const uint64_t active = __ballot(true);
-  const uint64_t same = __ballot(b == first);
-  if (same == active) {
-    if (first < nbins && lane == static_cast<uint32_t>(__builtin_ctzll(active)))
-      atomicAdd(&hist[first], static_cast<uint32_t>(__popcll(same)));
-  } else if (b < nbins) {
-    atomicAdd(&hist[b], 1u);
-  }
-}
 
 // Block-wide scan of the 1024-bin histogram from the top bin down: thread t
 // owns bin 1023 - t. Gives that bin's count h, the number of keys in higher
@@ -133,7 +106,8 @@ struct TopkShared {
   __attribute__((aligned(16))) uint32_t wsum[kWaves];
   __attribute__((aligned(16))) uint32_t wmax[kWaves];
   __attribute__((aligned(16))) uint32_t wcount[kWaves];
-  uint32_t valid, min1, max, count, lo, digit, above, bin, kept, maxbin, hist_total, thr;
+  uint64_t fin[kTopK];                                          // checked final level: result before the check
+  uint32_t valid, min1, max, count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
 };
 
 // Candidates of the first level: score bits per candidate (0 = none), index
@@ -363,6 +337,114 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
   if (tid < need) emit(tid, sh.cand[tid]);
 }
 
+// Exact top-min(512, n) of n scores, streamed from memory by one workgroup:
+// MSB-first 8-bit radix select on the 64-bit keys until at most 1024 keys lie
+// at or above the prefix, then a bitonic sort of those in LDS. Used when the
+// fused indexer's candidates cannot be shown to contain a row's top 512
+// (heavy ties, sorted scores); slow but independent of the score
+// distribution. Emits every slot (0 past the selected count).
+template <class Emit>
+__device__ __forceinline__ void select_from_scores(TopkShared &sh, const float *sc, uint32_t n, const Emit &emit) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  constexpr int kU = 8;   // loads in flight per thread
+  const uint32_t last = n > 0 ? n - 1 : 0;
+  auto keys = [&](uint32_t p0, uint64_t (&kk)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t p = p0 + u * kTopkThreads + tid;
+      kk[u] = topk_key(sc[min(p, last)], p);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (p0 + u * kTopkThreads + tid >= n) kk[u] = 0;
+  };
+  uint64_t prefix = 0, thr = 1;
+  uint32_t left = kTopK, total = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    __syncthreads();
+    if (tid < 256) sh.hist[tid] = 0;
+    if (tid == 0) sh.count = 0;
+    __syncthreads();
+    uint32_t nv = 0;
+    for (uint32_t p0 = 0; p0 < n; p0 += kU * kTopkThreads) {
+      uint64_t kk[kU];
+      keys(p0, kk);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        nv += kk[u] != 0 ? 1u : 0u;
+        const bool match = kk[u] != 0 && (shift == 56 || (kk[u] >> (shift + 8)) == (prefix >> (shift + 8)));
+        hist_add(sh.hist, match ? static_cast<uint32_t>(kk[u] >> shift) & 255u : 256u, 256, lane);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nv += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nv), off));
+    if (lane == 0) atomicAdd(&sh.count, nv);
+    __syncthreads();
+    total = sh.count;
+    if (total <= kTopkSortCap) { thr = 1; break; }   // (the same on every pass)
+    uint32_t t = tid;
+    asm volatile("" : "+v"(t));
+    if (t < 64) {
+      uint32_t v[4], sum = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { v[k] = sh.hist[255 - 4 * t - k]; sum += v[k]; }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t up = __shfl_up(incl, o);
+        if (t >= static_cast<uint32_t>(o)) incl += up;
+      }
+      uint32_t before = incl - sum;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (before < left && left <= before + v[k]) {
+          sh.digit = 255 - 4 * t - k;
+          sh.above = before;
+          sh.bin = v[k];
+        }
+        before += v[k];
+      }
+    }
+    __syncthreads();
+    left -= sh.above;
+    prefix |= static_cast<uint64_t>(sh.digit) << shift;
+    if ((kTopK - left) + sh.bin <= kTopkSortCap) { thr = prefix; break; }
+  }
+  const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
+  __syncthreads();
+  if (tid == 0) sh.count = 0;
+  __syncthreads();
+  for (uint32_t p0 = 0; p0 < n; p0 += kU * kTopkThreads) {
+    uint64_t kk[kU];
+    keys(p0, kk);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (kk[u] != 0 && kk[u] >= thr) {
+        const uint32_t pos = atomicAdd(&sh.count, 1u);
+        if (pos < kTopkSortCap) sh.cand[pos] = kk[u];   // at most 1024 by construction
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nk = min(sh.count, static_cast<uint32_t>(kTopkSortCap));
+  if (tid >= nk) sh.cand[tid] = 0;
+  __syncthreads();
+  const uint32_t size = nk <= kTopK ? kTopK : kTopkSortCap;
+  for (uint32_t k = 2; k <= size; k <<= 1) {
+    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t ixj = tid ^ j;
+      if (tid < size && ixj > tid) {
+        const uint64_t x = sh.cand[tid], y = sh.cand[ixj];
+        const bool desc = (tid & k) == 0;
+        if (desc ? (x < y) : (x > y)) { sh.cand[tid] = y; sh.cand[ixj] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < kTopK) emit(tid, tid < need ? sh.cand[tid] : 0ull);
+}
+
 // kFromScores: the first level, reading f32 scores. Otherwise a later level,
 // reading the previous level's 64-bit key lists.
 template <bool kFromScores>
@@ -440,7 +522,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
     const uint32_t gmin = sh.min1 + 1u, gmax = sh.max;
 
-    auto emit = [&](uint32_t pos, uint64_t kk) {
+    // A checked final level keeps its result in LDS until the floors allow it.
+    // (Fused-indexer candidates are lists, so only later levels check.)
+    const bool check = !kFromScores && final_level && ((a.check_mask >> r) & 1u);
+    auto emit_out = [&](uint32_t pos, uint64_t kk) {
       if (final_level) {
         a.indices[a.out_offset[r] + pos] =
             kk != 0 ? static_cast<int32_t>(~static_cast<uint32_t>(kk)) + a.offset[r] : -1;
@@ -448,78 +533,107 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
         a.out[a.out_base[r] + static_cast<uint64_t>(chunk) * kTopK + pos] = kk;
       }
     };
+    auto emit = [&](uint32_t pos, uint64_t kk) {
+      if (check) sh.fin[pos] = kk;
+      else emit_out(pos, kk);
+    };
+    // Best `need` of this chunk's candidates (total valid, score bits in
+    // [gmin, gmax]), in rank order through emit(pos, key).
+    auto select_chunk = [&](uint32_t total, uint32_t need, uint32_t gmin, uint32_t gmax, const auto &emit) {
+      // Threshold T from the sample (every key when the chunk is small).
+      uint32_t thr = 1;
+      if (end - begin > kSmallChunk) {
+        const float smin = ord_score(gmin), smax = ord_score(gmax);
+        const float range = smax - smin;
+        const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
+        const uint32_t o0 = c.hi(0);
+        const uint32_t b0 = o0 != 0 ? static_cast<uint32_t>(fminf((ord_score(o0) - smin) * scale,
+                                                                   static_cast<float>(kBins - 1)))
+                                    : static_cast<uint32_t>(kBins);
+        hist_add(sh.hist, b0, kBins, lane);
+        __syncthreads();
+        uint32_t h, above, maxge, nsamp;
+        scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, nsamp);
+        const uint32_t target = min(nsamp, kSampleMin);
+        if (target > 0 && above < target && target <= above + h) sh.lo = kBins - 1 - tid;
+        if (nsamp == 0 && tid == 0) sh.lo = 0;
+        __syncthreads();
+        const uint32_t lo = sh.lo;
+        uint32_t t = (b0 < kBins && b0 >= lo) ? o0 : 0xFFFFFFFFu;
+  #pragma unroll
+        for (int o = 32; o > 0; o >>= 1) t = min(t, static_cast<uint32_t>(__shfl_xor(static_cast<int>(t), o)));
+        if (lane == 0) atomicMin(&sh.thr, t);
+        __syncthreads();
+        thr = sh.thr;
+      }
+      // Compaction: keys with score bits >= T go to the wave's region, in
+      // candidate order; the running count is wave-uniform.
+      uint64_t *region = sh.compact + wave * kCompactPerWave;
+      uint32_t wcount = 0;
+  #pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const bool in = c.hi(e) >= thr;            // a missing key (0) is below any T >= 1
+        const uint64_t mask = __ballot(in);
+        const uint32_t pos = wcount + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+        if (in && pos < kCompactPerWave) region[pos] = c.vkey(e);
+        wcount += static_cast<uint32_t>(__popcll(mask));
+      }
+      if (lane == 0) sh.wcount[wave] = wcount;
+      __syncthreads();
+      uint32_t kept = 0, overflow = 0;
+  #pragma unroll
+      for (int v = 0; v < kWaves / 4; ++v) {
+        const u32x4 w4 = reinterpret_cast<const u32x4 *>(sh.wcount)[v];
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          kept += w4[k];
+          overflow |= w4[k] > kCompactPerWave ? 1u : 0u;
+        }
+      }
+      if (!overflow && kept >= need) {
+        // The chunk's best keys are the best of the kept ones.
+        uint64_t kc[kCompactPerLane];
+  #pragma unroll
+        for (int j = 0; j < kCompactPerLane; ++j)
+          kc[j] = lane + 64u * j < wcount ? region[lane + 64 * j] : 0ull;
+        counting_select<kCompactPerLane, false>(sh, KeyCand<kCompactPerLane>{kc}, kept, need, max(thr, gmin), gmax,
+                                                emit);
+      } else if constexpr (kFromScores) {
+        // Heavy ties: select over every candidate. The score bits move to LDS
+        // (over the compaction regions), which frees their registers.
+        __syncthreads();
+  #pragma unroll
+        for (int e = 0; e < kPer; ++e) sh.ordl[tid + kTopkThreads * e] = c.hi(e);
+        counting_select<kPer, true>(sh, LdsOrdCand{sh.ordl, tid, begin + tid}, total, need, gmin, gmax, emit);
+      } else {
+        counting_select<kPer, true>(sh, c, total, need, gmin, gmax, emit);
+      }
+    };
     // Slots past the selected count are empty.
     for (uint32_t t = need + tid; t < kTopK; t += kTopkThreads) emit(t, 0);
-    if (total == 0) return;
-
-    // Threshold T from the sample (every key when the chunk is small).
-    uint32_t thr = 1;
-    if (end - begin > kSmallChunk) {
-      const float smin = ord_score(gmin), smax = ord_score(gmax);
-      const float range = smax - smin;
-      const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
-      const uint32_t o0 = c.hi(0);
-      const uint32_t b0 = o0 != 0 ? static_cast<uint32_t>(fminf((ord_score(o0) - smin) * scale,
-                                                                 static_cast<float>(kBins - 1)))
-                                  : static_cast<uint32_t>(kBins);
-      hist_add(sh.hist, b0, kBins, lane);
-      __syncthreads();
-      uint32_t h, above, maxge, nsamp;
-      scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, nsamp);
-      const uint32_t target = min(nsamp, kSampleMin);
-      if (target > 0 && above < target && target <= above + h) sh.lo = kBins - 1 - tid;
-      if (nsamp == 0 && tid == 0) sh.lo = 0;
-      __syncthreads();
-      const uint32_t lo = sh.lo;
-      uint32_t t = (b0 < kBins && b0 >= lo) ? o0 : 0xFFFFFFFFu;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) t = min(t, static_cast<uint32_t>(__shfl_xor(static_cast<int>(t), o)));
-      if (lane == 0) atomicMin(&sh.thr, t);
-      __syncthreads();
-      thr = sh.thr;
-    }
-    // Compaction: keys with score bits >= T go to the wave's region, in
-    // candidate order; the running count is wave-uniform.
-    uint64_t *region = sh.compact + wave * kCompactPerWave;
-    uint32_t wcount = 0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const bool in = c.hi(e) >= thr;            // a missing key (0) is below any T >= 1
-      const uint64_t mask = __ballot(in);
-      const uint32_t pos = wcount + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-      if (in && pos < kCompactPerWave) region[pos] = c.vkey(e);
-      wcount += static_cast<uint32_t>(__popcll(mask));
-    }
-    if (lane == 0) sh.wcount[wave] = wcount;
+    if (total > 0) select_chunk(total, need, gmin, gmax, emit);
+    if constexpr (kFromScores) return;
+    if (!check) return;
+    // A key that a block of the fused indexer did not write ranks below that
+    // block's floor; the result stands unless some floor lies above the last
+    // selected key (or the row has fewer than 512 candidates and a block left
+    // keys out).
     __syncthreads();
-    uint32_t kept = 0, overflow = 0;
-#pragma unroll
-    for (int v = 0; v < kWaves / 4; ++v) {
-      const u32x4 w4 = reinterpret_cast<const u32x4 *>(sh.wcount)[v];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        kept += w4[k];
-        overflow |= w4[k] > kCompactPerWave ? 1u : 0u;
-      }
+    if (tid == 0) sh.viol = 0;
+    __syncthreads();
+    const uint64_t klast = need > 0 ? sh.fin[need - 1] : 0ull;
+    uint32_t viol = 0;
+    for (uint32_t b = tid; b < a.floor_count[r]; b += kTopkThreads) {
+      const uint64_t f = a.floors[a.floor_begin[r] + b];
+      viol |= (f != 0 && (need < static_cast<uint32_t>(kTopK) || f > klast)) ? 1u : 0u;
     }
-    if (!overflow && kept >= need) {
-      // The chunk's best keys are the best of the kept ones.
-      uint64_t kc[kCompactPerLane];
-#pragma unroll
-      for (int j = 0; j < kCompactPerLane; ++j)
-        kc[j] = lane + 64u * j < wcount ? region[lane + 64 * j] : 0ull;
-      counting_select<kCompactPerLane, false>(sh, KeyCand<kCompactPerLane>{kc}, kept, need, max(thr, gmin), gmax,
-                                              emit);
-    } else if constexpr (kFromScores) {
-      // Heavy ties: select over every candidate. The score bits move to LDS
-      // (over the compaction regions), which frees their registers.
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) sh.ordl[tid + kTopkThreads * e] = c.hi(e);
-      counting_select<kPer, true>(sh, LdsOrdCand{sh.ordl, tid, begin + tid}, total, need, gmin, gmax, emit);
+    if (__ballot(viol != 0) != 0 && lane == 0) atomicOr(&sh.viol, 1u);
+    __syncthreads();
+    if (sh.viol == 0) {
+      for (uint32_t t = tid; t < kTopK; t += kTopkThreads) emit_out(t, sh.fin[t]);
     } else {
-      counting_select<kPer, true>(sh, c, total, need, gmin, gmax, emit);
+      select_from_scores(sh, a.scores + static_cast<uint64_t>(r) * a.score_stride, a.fallback_count[r], emit_out);
     }
   };
   if constexpr (kFromScores) run(OrdCand<kPer>{ordv, begin + tid});

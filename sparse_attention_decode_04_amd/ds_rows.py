@@ -26,7 +26,7 @@ FUNCTIONS = (
     "ds_rows_scores_elems", "ds_rows_topk_workspace_bytes", "ds_rows_gathered_elems",
     "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes", "ds_rows_indexer_score",
     "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn", "ds_rows_sparse_attn_direct",
-    "ds_rows_last_error", "ds_rows_version",
+    "ds_rows_last_error", "ds_rows_version", "ds_rows_indexer_topk_workspace_bytes", "ds_rows_indexer_topk",
 )
 
 
@@ -78,8 +78,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ds_rows_gathered_elems.argtypes = [P(SparseRows)]
     lib.ds_rows_mask_elems.argtypes = [P(SparseRows)]
     lib.ds_rows_attn_workspace_bytes.argtypes = [P(SparseRows)]
+    lib.ds_rows_indexer_topk_workspace_bytes.argtypes = [P(IndexerRows)]
     for f in ("ds_rows_scores_elems", "ds_rows_topk_workspace_bytes", "ds_rows_gathered_elems",
-              "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes"):
+              "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes", "ds_rows_indexer_topk_workspace_bytes"):
         getattr(lib, f).restype = c_size_t
     lib.ds_rows_indexer_score.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                           c_void_p, c_size_t, c_void_p]
@@ -93,8 +94,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ds_rows_sparse_attn_direct.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                                c_void_p, c_size_t, c_float, c_void_p, c_size_t,
                                                c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_indexer_topk.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
+                                         c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn",
-              "ds_rows_sparse_attn_direct"):
+              "ds_rows_sparse_attn_direct", "ds_rows_indexer_topk"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
@@ -192,6 +195,10 @@ def topk_workspace_bytes(t: IndexerRows) -> int:
     return load().ds_rows_topk_workspace_bytes(ctypes.byref(t))
 
 
+def indexer_topk_workspace_bytes(t: IndexerRows) -> int:
+    return load().ds_rows_indexer_topk_workspace_bytes(ctypes.byref(t))
+
+
 def gathered_elems(t: SparseRows) -> int:
     return load().ds_rows_gathered_elems(ctypes.byref(t))
 
@@ -217,6 +224,16 @@ def topk(t: IndexerRows, scores, workspace, indices, stream=None):
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ia, inn = _dev(indices, 4)
     _check(load().ds_rows_topk(ctypes.byref(t), sa, sn, wa, wb, ia, inn, _stream(stream)))
+
+
+def indexer_topk(t: IndexerRows, q, weights, scores, workspace, indices, stream=None):
+    qa, qn = _dev(q, 2)
+    wa, wn = _dev(weights, 4)
+    sa, sn = _dev(scores, 4)
+    ka = _addr(workspace)
+    kb = workspace.numel() * workspace.element_size()
+    ia, inn = _dev(indices, 4)
+    _check(load().ds_rows_indexer_topk(ctypes.byref(t), qa, qn, wa, wn, sa, sn, ka, kb, ia, inn, _stream(stream)))
 
 
 def gather(t: SparseRows, indices, gathered, mask, stream=None):

@@ -57,6 +57,7 @@ class DeviceRows:
         d = dev.device
         self.scores = torch.empty(ds.scores_elems(self.itab), dtype=torch.float32, device=d)
         self.topk_ws = torch.empty(max(1, ds.topk_workspace_bytes(self.itab)), dtype=torch.uint8, device=d)
+        self.fused_ws = torch.empty(ds.indexer_topk_workspace_bytes(self.itab), dtype=torch.uint8, device=d)
         self.indices = torch.full((R_all * TOP_K,), -7, dtype=torch.int32, device=d)
         self.gathered = torch.empty(ds.gathered_elems(self.stab), dtype=torch.int16, device=d)
         self.mask = torch.empty(ds.mask_elems(self.stab), dtype=torch.int16, device=d)
@@ -70,6 +71,9 @@ class DeviceRows:
 
     def topk(self, stream=None):
         ds.topk(self.itab, self.scores, self.topk_ws, self.indices, stream)
+
+    def indexer_topk(self, stream=None):
+        ds.indexer_topk(self.itab, self.dev.idx_q, self.dev.idx_w, self.scores, self.fused_ws, self.indices, stream)
 
     def gather(self, stream=None):
         ds.gather(self.stab, self.indices, self.gathered, self.mask, stream)
@@ -94,6 +98,12 @@ class DeviceRows:
         (gather fused into the attention call; no gathered operand written)."""
         self.indexer_score(stream)
         self.topk(stream)
+        self.sparse_attn_direct(stream)
+
+    def step_fused(self, stream=None):
+        """Indexer with the first top-k stage fused in (one call for score and
+        top-512), then attention reading the selected KV rows directly."""
+        self.indexer_topk(stream)
         self.sparse_attn_direct(stream)
 
     # host copies, per selected row

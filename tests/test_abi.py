@@ -44,7 +44,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     assert set(names) == set(ds.FUNCTIONS)
     out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (ds_rows_\w+)", out))
@@ -114,6 +114,10 @@ def call_topk(lib, t, s=BIG, ws=BIG, idx=BIG):
     return lib.ds_rows_topk(ctypes.byref(t), FAKE, s, FAKE, ws, FAKE, idx, None)
 
 
+def call_fused(lib, t, q=BIG, w=BIG, s=BIG, ws=BIG, idx=BIG, wsp=FAKE):
+    return lib.ds_rows_indexer_topk(ctypes.byref(t), FAKE, q, FAKE, w, FAKE, s, wsp, ws, FAKE, idx, None)
+
+
 def call_gather(lib, t, idx=BIG, g=BIG, m=BIG):
     return lib.ds_rows_gather(ctypes.byref(t), FAKE, idx, FAKE, g, FAKE, m, None)
 
@@ -144,6 +148,17 @@ def test_size_queries(lib):
     # top-k lists: only rows longer than one 32768-key chunk need the banks
     assert ds.topk_workspace_bytes(t) == 2 * 8 * 512 * (3 + 2)
     assert ds.topk_workspace_bytes(itab((1000, 32768))) == 0
+    # fused: 128 candidate keys and one floor per 1024-key block (each region
+    # 256-byte aligned), plus list banks for rows whose candidates exceed one
+    # 16384-key chunk (rows over 131072 keys)
+    blocks = 1 + 69 + 32 + 33
+    assert ds.indexer_topk_workspace_bytes(t) == blocks * 128 * 8 + 1280   # 1080 B of floors -> 1280
+    big = itab((200000,))
+    nb = 196
+    cand = -(-nb * 128 * 8 // 256) * 256
+    floors = -(-nb * 8 // 256) * 256
+    chunks = -(-nb * 128 // 16384)
+    assert ds.indexer_topk_workspace_bytes(big) == cand + floors + 2 * chunks * 512 * 8
     s = stab((1000, 37, 1), width=(512, 37, 1))
     assert ds.gathered_elems(s) == (512 + 37 + 1) * 512
     assert ds.mask_elems(s) == 512 + 37 + 1
@@ -183,6 +198,19 @@ def test_indexer_row_checks(lib):
     assert ds.scores_elems(itab((10,), start_pos=[2], offset=[2 ** 31 - 1])) == 10
     expect_invalid(call_topk(lib, itab((10, 10), out_off=[0, 511])), "overlap")
     assert ds.scores_elems(itab((10, 10), out_off=[512, 0])) == 20
+
+
+def test_fused_indexer_topk_checks(lib):
+    t = itab((100, 50), q_row=[3, 0])
+    need = ds.indexer_topk_workspace_bytes(t)
+    expect_invalid(call_fused(lib, t, q=4 * 64 * 128 - 1), "indexer q holds")
+    expect_invalid(call_fused(lib, t, w=4 * 64 - 1), "indexer weights holds")
+    expect_invalid(call_fused(lib, t, s=2 * 100 - 1), "indexer scores holds")
+    expect_invalid(call_fused(lib, t, ws=need - 1), "indexer top-k workspace holds")
+    expect_invalid(call_fused(lib, t, wsp=None), "indexer top-k workspace must not be null")
+    expect_invalid(call_fused(lib, itab((10, 10), out_off=[0, 1024]), idx=1535), "indexer output holds")
+    expect_invalid(call_fused(lib, itab((10, 0))), "row 1: kv_len must be nonzero")
+    expect_invalid(call_fused(lib, itab((10,), keys_elems=[10 * 128 - 1])), "indexer kv holds")
 
 
 def test_indexer_capacity_checks(lib):
