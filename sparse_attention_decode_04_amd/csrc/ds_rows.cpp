@@ -90,13 +90,13 @@ ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
 
 uint64_t topk_workspace_bytes(const IndexerPlan &p) { return 2 * p.topk_bank * sizeof(uint64_t); }
 
-// Fused workspace: candidate lists (kIdxCand keys per indexer block), block
-// floors, then two ping-pong banks of list keys.
+// Fused workspace: candidate lists (kIdxCand keys per indexer block), wave
+// floors (kIdxFloors per block), then two ping-pong banks of list keys.
 uint64_t fused_cand_bytes(const IndexerPlan &p) {
   return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxCand * sizeof(uint64_t));
 }
 uint64_t fused_floor_bytes(const IndexerPlan &p) {
-  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * sizeof(uint64_t));
+  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxFloors * sizeof(uint32_t));
 }
 uint64_t fused_workspace_bytes(const IndexerPlan &p) {
   return fused_cand_bytes(p) + fused_floor_bytes(p) + 2 * p.fused_bank * sizeof(uint64_t);
@@ -181,7 +181,7 @@ ds_status check_indexer_operands(const ds_indexer_rows *rows, const IndexerPlan 
 
 // Indexer launch; with cand/floors set, also the fused top-k stage.
 ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, const void *q, const float *weights,
-                         float *scores, uint64_t *cand, uint64_t *floors, void *stream) {
+                         float *scores, uint64_t *cand, uint32_t *floors, void *stream) {
   ds::IndexerArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.w = weights;
@@ -208,7 +208,7 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
 // base per row, with the block floors to check on the final level).
 struct TopkInput {
   const uint64_t *lists = nullptr;
-  const uint64_t *floors = nullptr;
+  const uint32_t *floors = nullptr;
   uint32_t count[ds::kRowsMax] = {};
   uint64_t base[ds::kRowsMax] = {};
 };
@@ -252,8 +252,8 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
         a.final_mask |= 1u << r;
         if (from_lists) {
           a.check_mask |= 1u << r;
-          a.floor_begin[r] = p.blk_begin[r];
-          a.floor_count[r] = p.blk_begin[r + 1] - p.blk_begin[r];
+          a.floor_begin[r] = p.blk_begin[r] * ds::kIdxFloors;
+          a.floor_count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxFloors;
           a.fallback_count[r] = p.visible[r];
         }
       } else {
@@ -358,7 +358,7 @@ ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_
 
   char *ws = static_cast<char *>(workspace);
   uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
-  uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
+  uint32_t *floors = reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p));
   uint64_t *bank = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
   DS_TRY(launch_indexer(rows, p, q, weights, scores, cand, floors, stream));
 

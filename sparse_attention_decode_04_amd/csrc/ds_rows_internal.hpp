@@ -27,15 +27,17 @@ static_assert(kRowsMax <= static_cast<int>(kXcds), "one XCD per row");
 constexpr int kIdxThreads = 256;
 constexpr int kIdxTile = 16;
 constexpr uint32_t kIdxMaxKeysPerBlock = 1024;
-// Fused top-k stage (ds_rows_indexer_topk): every workgroup also writes up to
-// kIdxCand candidate keys of its own block (the keys of its top score bins,
-// at least kIdxCandMin of them, or every valid key when there are at most
-// kIdxCand) and a floor: 0 when it wrote every valid key of the block,
-// otherwise its smallest written key, below which lie all of its unwritten
-// keys (~0 when its top bins held more than kIdxCand keys).
-constexpr uint32_t kIdxCand = 128;
-constexpr uint32_t kIdxCandMin = 64;
-constexpr int kIdxCandBins = 256;
+// Fused top-k stage (ds_rows_indexer_topk): every wave of the indexer also
+// writes up to kIdxWaveCand candidate keys of its own 256 keys (those at or
+// above its kIdxWaveKeep-th best score, or every valid key when it has at
+// most kIdxWaveCand) and a 32-bit floor: 0 when it wrote every valid key,
+// otherwise score bits T such that all of its unwritten keys lie below the
+// key T << 32 (0xFFFFFFFF, above every valid key, when ties at its threshold
+// exceed the room).
+constexpr uint32_t kIdxWaveKeep = 24;
+constexpr uint32_t kIdxWaveCand = 32;
+constexpr uint32_t kIdxCand = (kIdxThreads / 64) * kIdxWaveCand;   // 128 per block
+constexpr uint32_t kIdxFloors = kIdxThreads / 64;                   // 4 per block
 
 struct IndexerArgs {
   const uint16_t *keys[kRowsMax];   // bf16 [kv_len, 128] per row
@@ -50,7 +52,7 @@ struct IndexerArgs {
   uint32_t q_row[kRowsMax];
   uint32_t blk_begin[kRowsMax + 1]; // first block of each row; [rows..] = total
   uint64_t *cand;                   // fused: kIdxCand keys per block (0 = none)
-  uint64_t *floors;                 // fused: one floor per block
+  uint32_t *floors;                 // fused: kIdxFloors floors per block (one per wave)
 };
 hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, bool fused, hipStream_t s);
 
@@ -59,12 +61,13 @@ hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, bool fuse
 // candidates to that chunk's best 512, sorted best first. Candidates are
 // 64-bit keys (order-preserving score bits << 32 | ~index); 0 = no candidate.
 // The first level reads scores (chunks of 32768); later levels read the
-// previous level's 512-key lists (chunks of 16384 keys = 32 lists).
+// previous level's 512-key lists or the fused indexer's candidates (chunks of
+// 8192 keys).
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkPerThreadFirst = 32;
-constexpr int kTopkPerThreadLater = 16;
+constexpr int kTopkPerThreadLater = 8;
 constexpr uint32_t kTopkChunkFirst = kTopkThreads * kTopkPerThreadFirst;   // 32768
-constexpr uint32_t kTopkChunkLater = kTopkThreads * kTopkPerThreadLater;   // 16384
+constexpr uint32_t kTopkChunkLater = kTopkThreads * kTopkPerThreadLater;   // 8192
 constexpr int kTopkSortCap = 1024;
 
 struct TopkLevelArgs {
@@ -87,7 +90,7 @@ struct TopkLevelArgs {
   // that an unwritten key could rank; otherwise the row is selected again from
   // its `fallback_count` scores.
   uint32_t check_mask;
-  const uint64_t *floors;
+  const uint32_t *floors;
   uint32_t floor_begin[kRowsMax];
   uint32_t floor_count[kRowsMax];
   uint32_t fallback_count[kRowsMax];

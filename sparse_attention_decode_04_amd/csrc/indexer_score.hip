@@ -28,13 +28,15 @@
 //
 // Fused top-k stage (kFused, for ds_rows_indexer_topk). The pages' first
 // top-k stage sorts every 1024-key block and keeps its best 512
-// (deepseek_indexer_topk_block_rows_i32); here the workgroup, with its
-// block's scores still in LDS, keeps only the keys of its top score bins: at
-// least 64 of them (or all valid keys when there are at most 128), at most
-// 128. Linear bins over the block's own score range are monotone in the score,
-// so every key it does not keep ranks below every key it keeps; it writes the
-// smallest kept key as the block's floor. The final top-k level uses the
-// floors to prove that no unkept key can reach the row's top 512.
+// (deepseek_indexer_topk_block_rows_i32). Here every wave keeps, from the 256
+// scores it just computed (still in its registers: after the head sum each
+// group of 16 lanes holds the tile's 16 scores, and the group whose number
+// matches the tile's position keeps them), only the keys at or above its
+// 24th best score bits: a bitwise search with ballot counts finds that
+// threshold T without LDS or barriers. It writes those keys (at most 32) and
+// the floor T: all of its other keys lie below the key T << 32; the final top-k
+// level uses the floors to prove that no unkept key can reach the row's top
+// 512, and selects from the scores again when one could.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 #include "select_common.hpp"
@@ -42,117 +44,58 @@
 namespace ds {
 
 constexpr int kIdxRing = 4;   // tile buffers per wave (kIdxRing - 1 in flight)
+// The fused stage keeps one tile in kIdxRing per lane, in a 4-deep queue.
+static_assert(kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile <= 4 * kIdxRing, "tiles per wave");
 
-// The block's candidates (fused stage, see above): scores of its keys as
-// order-preserving bits (0 = not valid) in LDS, 4 per thread.
-__device__ __forceinline__ void block_candidates(const IndexerArgs &a, const uint32_t *s_ord, uint32_t *s_hist,
-                                                 uint32_t *s_misc, unsigned long long *s_floor, uint32_t k0) {
-  const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid & 63;
-  constexpr int kPer = kIdxMaxKeysPerBlock / kIdxThreads;   // 4
-  uint32_t o[kPer];
-  uint32_t nvalid = 0, omin1 = 0xFFFFFFFFu, omax = 0;
+// One wave's candidates (fused stage, see above): o[e] are the score bits
+// (0 = not valid) of keys key0 + 64 * (wave + 4 * (4 * (n - 1 - e) + grp)) / 4
+// ..., passed in as their key indices kidx[e].
+__device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint32_t (&o)[4],
+                                                const uint32_t (&kidx)[4], uint32_t wave, uint32_t lane) {
+  const uint64_t slot0 = static_cast<uint64_t>(blockIdx.x) * kIdxCand + wave * kIdxWaveCand;
+  const uint64_t floor_at = static_cast<uint64_t>(blockIdx.x) * kIdxFloors + wave;
+  auto count_ge = [&](uint32_t t) -> uint32_t {   // keys of the wave with score bits >= t
+    uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    o[j] = s_ord[tid + kIdxThreads * j];
-    nvalid += o[j] != 0 ? 1u : 0u;
-    omin1 = min(omin1, o[j] - 1u);   // a missing key (0) wraps to the maximum
-    omax = max(omax, o[j]);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    nvalid += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nvalid), off));
-    omin1 = min(omin1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omin1), off)));
-    omax = max(omax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omax), off)));
-  }
-  if (lane == 0) {
-    atomicAdd(&s_misc[0], nvalid);
-    atomicMin(&s_misc[1], omin1);
-    atomicMax(&s_misc[2], omax);
-  }
-  __syncthreads();
-  const uint32_t total = s_misc[0];
-  const float smin = ord_score(s_misc[1] + 1u), smax = ord_score(s_misc[2]);
-  const float range = smax - smin;
-  const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kIdxCandBins) / range : 0.0f;
-  uint32_t bin[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const float x = (ord_score(o[j]) - smin) * scale;
-    bin[j] = o[j] != 0 ? static_cast<uint32_t>(fminf(x, static_cast<float>(kIdxCandBins - 1)))
-                       : static_cast<uint32_t>(kIdxCandBins);
-  }
-  // Lowest kept bin: every bin when the block has at most kIdxCand valid
-  // keys, otherwise the highest bin at which kIdxCandMin keys lie at or above.
-  uint32_t lo = 0, kept = total;
-  if (total > kIdxCand) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) hist_add(s_hist, bin[j], kIdxCandBins, lane);
-    __syncthreads();
-    if (tid < 64) {   // wave 0: lane l scans bins 255 - 4l .. 252 - 4l
-      uint32_t v[4], sum = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) { v[k] = s_hist[kIdxCandBins - 1 - 4 * tid - k]; sum += v[k]; }
-      uint32_t incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t up = __shfl_up(incl, off);
-        if (tid >= static_cast<uint32_t>(off)) incl += up;
-      }
-      uint32_t before = incl - sum;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (before < kIdxCandMin && kIdxCandMin <= before + v[k]) {
-          s_misc[3] = kIdxCandBins - 1 - 4 * tid - k;
-          s_misc[4] = before + v[k];
-        }
-        before += v[k];
-      }
+    for (int e = 0; e < 4; ++e) c += static_cast<uint32_t>(__popcll(__ballot(o[e] >= t)));
+    return c;
+  };
+  const uint32_t nvalid = count_ge(1u);
+  uint32_t thr = 1;   // keep every valid key
+  if (nvalid > kIdxWaveCand) {
+    // Largest T with at least kIdxWaveKeep keys at or above it: the
+    // kIdxWaveKeep-th best score bits.
+    thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = thr | (1u << bit);
+      if (count_ge(c) >= kIdxWaveKeep) thr = c;
     }
-    __syncthreads();
-    lo = s_misc[3];
-    kept = s_misc[4];
   }
-  const uint64_t blk = blockIdx.x;
-  uint64_t *cand = a.cand + blk * kIdxCand;
-  if (kept > kIdxCand) {
-    // Heavy ties in the boundary bin: write nothing; the floor ~0 makes the
-    // row fall back to a selection over its scores.
-    if (tid < kIdxCand) cand[tid] = 0;
-    if (tid == 0) a.floors[blk] = ~0ull;
+  const uint32_t kept = count_ge(thr);
+  if (kept > kIdxWaveCand) {
+    // Ties at the threshold overflow the room: write nothing; the floor ~0
+    // makes the row fall back to a selection over its scores.
+    if (lane < kIdxWaveCand) a.cand[slot0 + lane] = 0;
+    if (lane == 0) a.floors[floor_at] = 0xFFFFFFFFu;
     return;
   }
-  uint64_t mine = ~0ull;
+  uint32_t base = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if (bin[j] < static_cast<uint32_t>(kIdxCandBins) && bin[j] >= lo) {
-      const uint32_t key_index = k0 + tid + kIdxThreads * j;
-      const uint64_t kk = (static_cast<uint64_t>(o[j]) << 32) | static_cast<uint32_t>(~key_index);
-      cand[atomicAdd(&s_misc[5], 1u)] = kk;
-      mine = min(mine, kk);
-    }
+  for (int e = 0; e < 4; ++e) {
+    const bool in = o[e] >= thr;
+    const uint64_t mask = __ballot(in);
+    const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+    if (in) a.cand[slot0 + pos] = (static_cast<uint64_t>(o[e]) << 32) | static_cast<uint32_t>(~kidx[e]);
+    base += static_cast<uint32_t>(__popcll(mask));
   }
-  if (tid >= kept && tid < kIdxCand) cand[tid] = 0;   // unused slots
-  // The floor: the smallest kept key, or 0 when every valid key was kept.
-  uint64_t m = mine;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t ohi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(m >> 32)), off));
-    const uint32_t olo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(m)), off));
-    m = min(m, (static_cast<uint64_t>(ohi) << 32) | olo);
-  }
-  if (lane == 0) atomicMin(s_floor, static_cast<unsigned long long>(m));
-  __syncthreads();
-  if (tid == 0) a.floors[blk] = kept == total ? 0ull : static_cast<uint64_t>(*s_floor);
+  if (lane >= kept && lane < kIdxWaveCand) a.cand[slot0 + lane] = 0;   // unused slots
+  if (lane == 0) a.floors[floor_at] = kept == nvalid ? 0u : thr;
 }
 
 template <bool kFused>
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs a) {
   __shared__ u32x4 q_lds[kHeads * kIdxDim / 8];   // 16 KiB
-  __shared__ uint32_t s_ord[kFused ? kIdxMaxKeysPerBlock : 1];
-  __shared__ uint32_t s_hist[kFused ? kIdxCandBins : 1];
-  __shared__ uint32_t s_misc[8];
-  __shared__ unsigned long long s_floor;
 
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
   const uint32_t n = a.kv_len[r];
@@ -197,15 +140,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
 #pragma unroll
   for (int i = 0; i < 4; ++i) q_lds[tid + kIdxThreads * i] = qv[i];
   if (tid < kHeads) w_lds[tid] = wv;
-  if constexpr (kFused) {
-#pragma unroll
-    for (int j = 0; j < static_cast<int>(kIdxMaxKeysPerBlock / kIdxThreads); ++j) s_ord[tid + kIdxThreads * j] = 0;
-    s_hist[tid] = 0;
-    if (tid == 0) {
-      s_misc[0] = 0; s_misc[1] = 0xFFFFFFFFu; s_misc[2] = 0; s_misc[3] = 0; s_misc[4] = 0; s_misc[5] = 0;
-      s_floor = ~0ull;
-    }
-  }
   __syncthreads();
   // Query fragments (head 16m + col, features [32*grp + 8c, +8)) and the head
   // weights of the D rows this lane holds.
@@ -218,9 +152,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
 #pragma unroll
     for (int i = 0; i < 4; ++i) wt[m][i] = w_lds[16 * m + 4 * grp + i];
   }
-  if (!kFused && mine == 0) return;   // (the fused stage below needs every wave)
+  if (!kFused && mine == 0) return;   // (in the fused stage every wave writes its floor)
 
+  // Fused stage: the score bits this lane keeps, one per group of kIdxRing
+  // tiles (newest first); tile i0 + u goes to the lanes of group u.
+  uint32_t fifo[4] = {0, 0, 0, 0};
   for (uint32_t i0 = 0; i0 < mine; i0 += kIdxRing) {
+    uint32_t captured = 0;
 #pragma unroll
     for (int u = 0; u < kIdxRing; ++u) {
       const uint32_t i = i0 + u;
@@ -238,16 +176,30 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
       const uint32_t key = k0 + (wave + 4 * i) * kIdxTile + col;
-      if (i < mine && grp == 0 && key < k_end) {
-        const float v = (key < visible && __builtin_isfinite(part)) ? part : -__builtin_inff();
-        scores[key] = v;
-        if constexpr (kFused) s_ord[key - k0] = static_cast<uint32_t>(topk_key(v, key) >> 32);
+      const float v = (key < visible && __builtin_isfinite(part)) ? part : -__builtin_inff();
+      if (i < mine && grp == 0 && key < k_end) scores[key] = v;
+      if constexpr (kFused) {
+        const uint32_t ord = (i < mine && key < k_end) ? static_cast<uint32_t>(topk_key(v, key) >> 32) : 0u;
+        captured = grp == static_cast<uint32_t>(u) ? ord : captured;
       }
+    }
+    if constexpr (kFused) {
+      fifo[3] = fifo[2];
+      fifo[2] = fifo[1];
+      fifo[1] = fifo[0];
+      fifo[0] = captured;
     }
   }
   if constexpr (kFused) {
-    __syncthreads();
-    block_candidates(a, s_ord, s_hist, s_misc, &s_floor, k0);
+    // fifo[e] holds tile i = kIdxRing * (groups - 1 - e) + grp.
+    const uint32_t groups = (mine + kIdxRing - 1) / kIdxRing;
+    uint32_t kidx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t i = kIdxRing * (groups - 1 - e) + grp;   // (unused when groups <= e: fifo[e] is 0)
+      kidx[e] = k0 + (wave + 4 * i) * kIdxTile + col;
+    }
+    wave_candidates(a, fifo, kidx, wave, lane);
   }
 }
 

@@ -16,7 +16,7 @@
 //
 // One level. A 1024-thread workgroup takes a chunk of one row's candidates,
 // held in registers (first level: 32768 scores, 32 per thread, kept as their
-// 32 score bits; later levels: 16384 list keys, 16 per thread), and writes that
+// 32 score bits; later levels: 8192 list keys, 8 per thread), and writes that
 // chunk's best min(512, n) keys in rank order.
 //   Threshold and compaction (common case). A sample (each thread's first key)
 //   gives a threshold T: the smallest sampled score in the top bins holding 64
@@ -44,7 +44,7 @@
 // pays for every cold instruction-cache line it executes.
 // Levels repeat on the lists until each row has one; the last level writes
 // index + offset, or -1 for empty slots. A row of n visible keys needs one
-// level up to 32768 keys and two up to 16M.
+// level up to 32768 keys, two up to 512K and three up to 8M.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 #include "select_common.hpp"
@@ -493,6 +493,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     for (int e = 0; e < kPer; ++e)
       if (begin + tid + kTopkThreads * e >= end) keyv[e] = 0;
   }
+  // A checked final level needs the row's floors at the end; their first
+  // 1024 are loaded now, with the candidates.
+  uint32_t floor0 = 0;
+  if constexpr (!kFromScores) {
+    if (final_level && ((a.check_mask >> r) & 1u) && a.floor_count[r] > 0)
+      floor0 = a.floors[a.floor_begin[r] + min(tid, a.floor_count[r] - 1)];
+  }
   auto run = [&](const auto &c) {
     // Count and extreme score bits of the valid keys. A missing key has high
     // word 0 (every valid key's is nonzero), so it never raises the maximum
@@ -615,19 +622,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     if (total > 0) select_chunk(total, need, gmin, gmax, emit);
     if constexpr (kFromScores) return;
     if (!check) return;
-    // A key that a block of the fused indexer did not write ranks below that
-    // block's floor; the result stands unless some floor lies above the last
-    // selected key (or the row has fewer than 512 candidates and a block left
-    // keys out).
+    // A key that a wave of the fused indexer did not write ranks below that
+    // wave's floor key; the result stands unless some floor lies above the
+    // last selected key (or the row has fewer than 512 candidates and a wave
+    // left keys out).
     __syncthreads();
     if (tid == 0) sh.viol = 0;
     __syncthreads();
     const uint64_t klast = need > 0 ? sh.fin[need - 1] : 0ull;
-    uint32_t viol = 0;
-    for (uint32_t b = tid; b < a.floor_count[r]; b += kTopkThreads) {
-      const uint64_t f = a.floors[a.floor_begin[r] + b];
-      viol |= (f != 0 && (need < static_cast<uint32_t>(kTopK) || f > klast)) ? 1u : 0u;
-    }
+    auto violates = [&](uint32_t f) {
+      return f != 0 && (need < static_cast<uint32_t>(kTopK) || (static_cast<uint64_t>(f) << 32) > klast);
+    };
+    uint32_t viol = (tid < a.floor_count[r] && violates(floor0)) ? 1u : 0u;
+    for (uint32_t b = tid + kTopkThreads; b < a.floor_count[r]; b += kTopkThreads)
+      viol |= violates(a.floors[a.floor_begin[r] + b]) ? 1u : 0u;
     if (__ballot(viol != 0) != 0 && lane == 0) atomicOr(&sh.viol, 1u);
     __syncthreads();
     if (sh.viol == 0) {

@@ -148,16 +148,17 @@ def test_size_queries(lib):
     # top-k lists: only rows longer than one 32768-key chunk need the banks
     assert ds.topk_workspace_bytes(t) == 2 * 8 * 512 * (3 + 2)
     assert ds.topk_workspace_bytes(itab((1000, 32768))) == 0
-    # fused: 128 candidate keys and one floor per 1024-key block (each region
-    # 256-byte aligned), plus list banks for rows whose candidates exceed one
-    # 16384-key chunk (rows over 131072 keys)
+    # fused: 128 candidate keys and four u32 floors per 1024-key block (each
+    # region 256-byte aligned), plus two list banks for rows whose candidates
+    # exceed one 8192-key chunk (rows over 65536 keys): here the 70000-key
+    # row, 69 blocks -> 8832 candidates -> 2 chunks of 512
     blocks = 1 + 69 + 32 + 33
-    assert ds.indexer_topk_workspace_bytes(t) == blocks * 128 * 8 + 1280   # 1080 B of floors -> 1280
+    assert ds.indexer_topk_workspace_bytes(t) == blocks * 128 * 8 + 2304 + 2 * 2 * 512 * 8
     big = itab((200000,))
     nb = 196
     cand = -(-nb * 128 * 8 // 256) * 256
-    floors = -(-nb * 8 // 256) * 256
-    chunks = -(-nb * 128 // 16384)
+    floors = -(-nb * 4 * 4 // 256) * 256
+    chunks = -(-nb * 128 // 8192)
     assert ds.indexer_topk_workspace_bytes(big) == cand + floors + 2 * chunks * 512 * 8
     s = stab((1000, 37, 1), width=(512, 37, 1))
     assert ds.gathered_elems(s) == (512 + 37 + 1) * 512
