@@ -2,9 +2,12 @@
 
 One step = the whole path for every row of the workload: indexer score ->
 top-512 -> gather of the selected KV rows -> sparse attention with sinks.
-The headline runs it as three C-ABI calls on one stream, the gather fused into
-the attention call (ds_rows_sparse_attn_direct); the four-call form
-(ds_rows_gather, then ds_rows_sparse_attn) is timed beside it.
+The headline runs it as two C-ABI calls on one stream:
+ds_rows_indexer_topk (scores and top-512, the first selection stage in the
+indexer's epilogue) and ds_rows_sparse_attn_direct (gather fused into the
+attention). The three-call form (separate ds_rows_indexer_score and
+ds_rows_topk) and the four-call form (ds_rows_gather, then
+ds_rows_sparse_attn) compute the same outputs and are timed beside it.
 Default workload: 8 rows x 32768 cached keys (64 heads x 128 indexer, top-512,
 64 heads x 512 attention), seeded synthetic inputs resident in HBM.
 
@@ -16,7 +19,8 @@ warm-cache case.
 
 Prints one JSON line (rank 0, N=1) with the headline value, per-call
 durations from HIP events on the launch stream, the roofline of the dominant
-kernel (the indexer score) and the CPU oracle timed on a bounded sample.
+kernel (the indexer, in its fused form) and the CPU oracle timed on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -51,7 +55,7 @@ def parse():
     return p.parse_args()
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_score_traffic_8x32768.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_fused_traffic_8x32768.md")
 INDEXER_SOURCES = [os.path.join(ROOT, "sparse_attention_decode_04_amd", "csrc", f)
                    for f in ("indexer_score.hip", "device_common.hpp", "select_common.hpp", "ds_rows_internal.hpp")]
 
@@ -89,22 +93,28 @@ def measured_traffic():
         return None
 
 
-def indexer_bytes_flops(inp):
-    """Algorithmic HBM bytes and MFMA flops of one indexer-score launch:
-    per key 256 B of keys read + 4 B of score written and 64*128*2 flops;
-    per row 16 KiB of query and 256 B of weights read."""
+def indexer_bytes_flops(inp, fused=False):
+    """Algorithmic HBM bytes and MFMA flops of one indexer launch: per key
+    256 B of keys read + 4 B of score written and 64*128*2 flops; per row
+    16 KiB of query and 256 B of weights read; in the fused form also, per
+    1024-key block, 128 candidate keys of 8 B and four 4 B floors written."""
     keys = sum(inp.kv_len)
-    return keys * (256 + 4) + inp.rows * (64 * 128 * 2 + 64 * 4), keys * 64 * 128 * 2
+    b = keys * (256 + 4) + inp.rows * (64 * 128 * 2 + 64 * 4)
+    if fused:
+        b += sum(-(-n // 1024) for n in inp.kv_len) * (128 * 8 + 4 * 4)
+    return b, keys * 64 * 128 * 2
 
 
 def step_bytes(inp):
-    """Algorithmic bytes of one whole step (all four calls)."""
+    """Algorithmic bytes of one headline step: the fused indexer, the top-k
+    levels over its candidates (read, plus the indices written), and the
+    attention reading its selected KV rows through the indices."""
     w = [min(n, 512) for n in inp.kv_len]
-    idx_b, _ = indexer_bytes_flops(inp)
-    topk_b = sum(4 * n for n in inp.kv_len) + inp.rows * 512 * 4
-    gather_b = sum(wi * (1024 + 1024 + 4 + 2) for wi in w)
-    attn_b = sum(64 * 512 * 2 + wi * (1024 + 2) + 64 * 512 * 4 for wi in w) + 256
-    return idx_b + topk_b + gather_b + attn_b
+    blocks = sum(-(-n // 1024) for n in inp.kv_len)
+    idx_b, _ = indexer_bytes_flops(inp, fused=True)
+    topk_b = blocks * (128 * 8 + 4 * 4) + inp.rows * 512 * 4
+    attn_b = sum(64 * 512 * 2 + wi * (1024 + 4) + 64 * 512 * 4 for wi in w) + 256
+    return idx_b + topk_b + attn_b
 
 
 def cpu_baseline(inp, seconds):
@@ -180,12 +190,13 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0
 
-    # Headline: the path with the gather fused into the attention call.
-    ms_per_step, wall = timed("step_direct")
+    # Headline: score + top-k in one call, then attention with the gather
+    # fused in.
+    ms_per_step, wall = timed("step_fused")
+    # Separate score and top-k calls, then the same attention.
+    ms_three, _ = timed("step_direct")
     # The four-call path (gather, then attention on the gathered rows).
     ms_four, _ = timed("step")
-    # Score and top-k in one call (first selection stage in the indexer).
-    ms_fused, _ = timed("step_fused")
 
     def per_call_ms(calls):
         """Mean duration of each call, from HIP events recorded around it on
@@ -215,12 +226,12 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n
 
-    per_call = per_call_ms(("indexer_score", "topk", "sparse_attn_direct"))
-    indexer_ms = back_to_back_ms("indexer_score", max(args.steps, 50))
+    per_call = per_call_ms(("indexer_topk", "sparse_attn_direct"))
+    indexer_ms = back_to_back_ms("indexer_candidates", max(args.steps, 50))
+    per_call_three = per_call_ms(("indexer_score", "topk", "sparse_attn_direct"))
     per_call_four = per_call_ms(("indexer_score", "topk", "gather", "sparse_attn"))
-    per_call_fused = per_call_ms(("indexer_topk", "sparse_attn_direct"))
 
-    idx_bytes, idx_flops = indexer_bytes_flops(inp)
+    idx_bytes, idx_flops = indexer_bytes_flops(inp, fused=True)
     traffic = measured_traffic() if args.config == 2 else None
     idx_s = indexer_ms * 1e-3
     achieved = idx_bytes / idx_s / 1e9
@@ -248,17 +259,18 @@ def main():
         },
         "keys_per_s": keys_per_s,
         "step_algorithmic_gb_per_s": step_bytes(inp) / (ms_per_step * 1e-3) / 1e9,
-        "pipeline": "ds_rows_indexer_score -> ds_rows_topk -> ds_rows_sparse_attn_direct (gather fused)",
+        "pipeline": "ds_rows_indexer_topk (first top-k stage in the indexer) -> ds_rows_sparse_attn_direct "
+                    "(gather fused)",
         "per_call_ms": per_call,
+        "three_call_pipeline": {
+            "calls": "ds_rows_indexer_score -> ds_rows_topk -> ds_rows_sparse_attn_direct",
+            "ms_per_step": ms_three, "rows_per_s": inp.rows / (ms_three * 1e-3), "per_call_ms": per_call_three},
         "four_call_pipeline": {
             "calls": "ds_rows_indexer_score -> ds_rows_topk -> ds_rows_gather -> ds_rows_sparse_attn",
             "ms_per_step": ms_four, "rows_per_s": inp.rows / (ms_four * 1e-3), "per_call_ms": per_call_four},
-        "fused_pipeline": {
-            "calls": "ds_rows_indexer_topk -> ds_rows_sparse_attn_direct",
-            "ms_per_step": ms_fused, "rows_per_s": inp.rows / (ms_fused * 1e-3), "per_call_ms": per_call_fused},
         "wall_s_timed_region": wall,
         "roofline": {
-            "kernel": "indexer_score_kernel",
+            "kernel": "indexer_score_kernel<true> (indexer with the fused top-k candidate stage)",
             "kernel_ms": indexer_ms,
             "timing": "HIP events on the launch stream around back-to-back launches over the rotating input copies",
             "bound": "hbm",

@@ -176,6 +176,19 @@ ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows,
                                int32_t *indices, size_t indices_elems,
                                void *stream);
 
+/* ---- ds_rows_indexer_candidates -----------------------------------------
+ * The first kernel of ds_rows_indexer_topk alone: writes the scores (as
+ * ds_rows_indexer_score) and leaves the waves' candidates and floors in the
+ * workspace, where nothing else reads them. For timing the fused indexer
+ * kernel on its own; arguments and checks as ds_rows_indexer_topk, without
+ * the indices. */
+ds_status ds_rows_indexer_candidates(const ds_indexer_rows *rows,
+                                     const void *q, size_t q_elems,
+                                     const float *weights, size_t weights_elems,
+                                     float *scores, size_t scores_elems,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /* ---- ds_rows_gather -----------------------------------------------------
  * Gathers, for slot t < width[r] of row r with i = indices[index_offset[r]+t]
  * ([shader 0.18] deepseek_sparse_attention_gather_rows_bf16):

@@ -345,6 +345,19 @@ size_t ds_rows_indexer_topk_workspace_bytes(const ds_indexer_rows *rows) {
   return fused_workspace_bytes(p);
 }
 
+ds_status ds_rows_indexer_candidates(const ds_indexer_rows *rows, const void *q, size_t q_elems, const float *weights,
+                                     size_t weights_elems, float *scores, size_t scores_elems, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  IndexerPlan p;
+  DS_TRY(check_indexer(rows, &p));
+  DS_TRY(check_indexer_operands(rows, p, q, q_elems, weights, weights_elems, scores, scores_elems));
+  DS_TRY(need(workspace, "indexer top-k workspace"));
+  DS_TRY(cap(workspace_bytes, fused_workspace_bytes(p), "indexer top-k workspace", "bytes"));
+  char *ws = static_cast<char *>(workspace);
+  return launch_indexer(rows, p, q, weights, scores, reinterpret_cast<uint64_t *>(ws),
+                        reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p)), stream);
+}
+
 ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_t q_elems, const float *weights,
                                size_t weights_elems, float *scores, size_t scores_elems, void *workspace,
                                size_t workspace_bytes, int32_t *indices, size_t indices_elems, void *stream) {

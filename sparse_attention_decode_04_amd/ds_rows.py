@@ -27,6 +27,7 @@ FUNCTIONS = (
     "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes", "ds_rows_indexer_score",
     "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn", "ds_rows_sparse_attn_direct",
     "ds_rows_last_error", "ds_rows_version", "ds_rows_indexer_topk_workspace_bytes", "ds_rows_indexer_topk",
+    "ds_rows_indexer_candidates",
 )
 
 
@@ -96,8 +97,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                c_void_p, c_size_t, c_void_p]
     lib.ds_rows_indexer_topk.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                          c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_indexer_candidates.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
+                                               c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn",
-              "ds_rows_sparse_attn_direct", "ds_rows_indexer_topk"):
+              "ds_rows_sparse_attn_direct", "ds_rows_indexer_topk", "ds_rows_indexer_candidates"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
@@ -234,6 +237,15 @@ def indexer_topk(t: IndexerRows, q, weights, scores, workspace, indices, stream=
     kb = workspace.numel() * workspace.element_size()
     ia, inn = _dev(indices, 4)
     _check(load().ds_rows_indexer_topk(ctypes.byref(t), qa, qn, wa, wn, sa, sn, ka, kb, ia, inn, _stream(stream)))
+
+
+def indexer_candidates(t: IndexerRows, q, weights, scores, workspace, stream=None):
+    qa, qn = _dev(q, 2)
+    wa, wn = _dev(weights, 4)
+    sa, sn = _dev(scores, 4)
+    ka = _addr(workspace)
+    kb = workspace.numel() * workspace.element_size()
+    _check(load().ds_rows_indexer_candidates(ctypes.byref(t), qa, qn, wa, wn, sa, sn, ka, kb, _stream(stream)))
 
 
 def gather(t: SparseRows, indices, gathered, mask, stream=None):

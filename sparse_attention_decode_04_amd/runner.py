@@ -75,6 +75,9 @@ class DeviceRows:
     def indexer_topk(self, stream=None):
         ds.indexer_topk(self.itab, self.dev.idx_q, self.dev.idx_w, self.scores, self.fused_ws, self.indices, stream)
 
+    def indexer_candidates(self, stream=None):
+        ds.indexer_candidates(self.itab, self.dev.idx_q, self.dev.idx_w, self.scores, self.fused_ws, stream)
+
     def gather(self, stream=None):
         ds.gather(self.stab, self.indices, self.gathered, self.mask, stream)
 

@@ -44,7 +44,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert set(names) == set(ds.FUNCTIONS)
     out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (ds_rows_\w+)", out))
@@ -212,6 +212,8 @@ def test_fused_indexer_topk_checks(lib):
     expect_invalid(call_fused(lib, itab((10, 10), out_off=[0, 1024]), idx=1535), "indexer output holds")
     expect_invalid(call_fused(lib, itab((10, 0))), "row 1: kv_len must be nonzero")
     expect_invalid(call_fused(lib, itab((10,), keys_elems=[10 * 128 - 1])), "indexer kv holds")
+    expect_invalid(lib.ds_rows_indexer_candidates(ctypes.byref(t), FAKE, BIG, FAKE, BIG, FAKE, BIG, FAKE, need - 1,
+                                                  None), "indexer top-k workspace holds")
 
 
 def test_indexer_capacity_checks(lib):
