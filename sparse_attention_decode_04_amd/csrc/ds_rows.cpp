@@ -110,10 +110,9 @@ struct SparsePlan {
   uint64_t slots = 0;                  // sum of widths
   uint64_t slot_base[ds::kRowsMax] = {};
   uint32_t chunks[ds::kRowsMax] = {};
-  uint64_t p_base[ds::kRowsMax] = {};
   uint64_t stat_base[ds::kRowsMax] = {};
-  uint64_t gt_base[ds::kRowsMax] = {};
-  uint64_t p_elems = 0, stat_elems = 0, gt_elems = 0;
+  uint64_t part_base[ds::kRowsMax] = {};
+  uint64_t stat_elems = 0, part_elems = 0;
 };
 
 ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
@@ -129,22 +128,18 @@ ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
     p->slot_base[r] = p->slots;
     p->slots += t->width[r];
     p->chunks[r] = div_up(t->width[r], ds::kAttnChunk);
-    p->p_base[r] = p->p_elems;
-    p->p_elems += uint64_t(ds::kHeads) * p->chunks[r] * ds::kAttnChunk;
     p->stat_base[r] = p->stat_elems;
     p->stat_elems += uint64_t(ds::kHeads) * p->chunks[r];
-    p->gt_base[r] = p->gt_elems;
-    p->gt_elems += uint64_t(ds::kDim) * p->chunks[r] * ds::kAttnChunk;
+    p->part_base[r] = p->part_elems;
+    p->part_elems += uint64_t(ds::kHeads) * ds::kDim * p->chunks[r];
   }
   return DS_OK;
 }
 
-// Attention workspace: bf16 p~ hi plane, bf16 p~ lo plane, f32x4 chunk
-// statistics, bf16 feature-major copy of the selected rows.
-uint64_t attn_plane_bytes(const SparsePlan &p) { return align256(p.p_elems * sizeof(uint16_t)); }
+// Attention workspace: f32x4 chunk statistics, then the f32 chunk outputs.
 uint64_t attn_stat_bytes(const SparsePlan &p) { return align256(p.stat_elems * 16); }
 uint64_t attn_workspace_bytes(const SparsePlan &p) {
-  return 2 * attn_plane_bytes(p) + attn_stat_bytes(p) + align256(p.gt_elems * sizeof(uint16_t));
+  return attn_stat_bytes(p) + align256(p.part_elems * sizeof(float));
 }
 
 ds_status need(const void *ptr, const char *name) {
@@ -436,10 +431,8 @@ ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool
   a.mask = static_cast<const uint16_t *>(mask);
   a.indices = indices;
   char *ws = static_cast<char *>(workspace);
-  a.p_hi = reinterpret_cast<uint16_t *>(ws);
-  a.p_lo = reinterpret_cast<uint16_t *>(ws + attn_plane_bytes(p));
-  a.stats = reinterpret_cast<float4 *>(ws + 2 * attn_plane_bytes(p));
-  a.gt = reinterpret_cast<uint16_t *>(ws + 2 * attn_plane_bytes(p) + attn_stat_bytes(p));
+  a.stats = reinterpret_cast<float4 *>(ws);
+  a.opart = reinterpret_cast<float *>(ws + attn_stat_bytes(p));
   a.out = out;
   a.scale = scale;
   a.rows = p.rows;
@@ -451,17 +444,16 @@ ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool
     a.chunks[r] = p.chunks[r];
     a.q_row[r] = rows->q_row[r];
     a.slot_base[r] = p.slot_base[r];
-    a.p_base[r] = p.p_base[r];
     a.stat_base[r] = p.stat_base[r];
-    a.gt_base[r] = p.gt_base[r];
+    a.part_base[r] = p.part_base[r];
   }
   // Block b of either phase serves row b % 8 (one XCD per row).
   uint32_t max_chunks = 0;
   for (uint32_t r = 0; r < p.rows; ++r) max_chunks = std::max(max_chunks, p.chunks[r]);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = ds::launch_attn_logits(a, direct, ds::kXcds * max_chunks, s);
-  if (e != hipSuccess) return hip_fail(e, "attention logits launch");
-  e = ds::launch_attn_reduce(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
+  hipError_t e = ds::launch_attn_chunks(a, direct, ds::kXcds * max_chunks, s);
+  if (e != hipSuccess) return hip_fail(e, "attention chunk launch");
+  e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
   return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
 }
 

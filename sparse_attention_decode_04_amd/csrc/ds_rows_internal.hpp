@@ -119,18 +119,15 @@ struct GatherArgs {
 hipError_t launch_gather(const GatherArgs &a, uint32_t blocks, hipStream_t s);
 
 // -------------------------------------------------------------- attention
-// Phase 1 (logits): one workgroup of 8 waves per (row, 32-slot chunk)
-// computes scale * q . G for all 64 heads, and per head and chunk the chunk
-// max m_c, the sum s_c of exp(l - m_c) and a bad flag; it stores
-// p~ = exp(l - m_c) as a bf16 hi/lo pair (0 for slots that are masked or
-// past the width) and the chunk's rows feature-major (G^T). G comes from the
-// gathered operand, or (direct) from each row's KV through the indices.
-// Phase 2 (weighted sum): one workgroup of 8 waves per (row, 32-dim chunk)
-// combines the chunk statistics with the sink and accumulates
-// sum_c exp(m_c - m) / Z * (p~ . G)_c on MFMA.
-constexpr int kAttnChunk = 32;      // slots per phase-1 workgroup
+// Phase 1 (chunk): one workgroup of 8 waves per (row, 64-slot chunk)
+// computes the logits scale * q . G for all 64 heads, per head the chunk max
+// m_c, p~ = exp(l - m_c), s_c = sum p~ and a bad flag, and the chunk's part
+// of the output, O_c = p~ . G (64 heads x 512 dims, f32), on MFMA. G comes
+// from the gathered operand, or (direct) from each row's KV through the
+// indices. Phase 2 (combine): one workgroup per (row, 32-dim chunk) weighs
+// the chunks with the sink: out = sum_c exp(m_c - m) O_c / Z.
+constexpr int kAttnChunk = 64;      // slots per phase-1 workgroup
 constexpr int kAttnDimChunk = 32;   // output dims per phase-2 workgroup
-constexpr int kAttnSuper = 512;     // slots per phase-2 operand batch
 
 struct AttnArgs {
   const uint16_t *q;                // bf16 [_, 64, 512]
@@ -139,24 +136,21 @@ struct AttnArgs {
   const uint16_t *mask;             // bf16 [sum(width)] (gathered variant)
   const int32_t *indices;           // i32 (direct variant)
   const uint16_t *kv[kRowsMax];     // bf16 [kv_len, 512] per row (direct variant)
-  uint16_t *p_hi;                   // bf16 hi part of p~: row r at p_base[r], [64][w32]
-  uint16_t *p_lo;                   // bf16 lo part of p~, same layout
   float4 *stats;                    // (m_c, s_c, bad, sink): row r at stat_base[r], [chunks][64]
-  uint16_t *gt;                     // bf16 G^T: row r at gt_base[r], [512][w32]
+  float *opart;                     // f32 O_c: row r at part_base[r], [chunks][64][512]
   float *out;                       // f32 [_, 64, 512]
   float scale;
   uint32_t rows;
   uint32_t width[kRowsMax];
-  uint32_t chunks[kRowsMax];        // ceil(width / 32); w32 = 32 * chunks
+  uint32_t chunks[kRowsMax];        // ceil(width / 64)
   uint32_t q_row[kRowsMax];
   uint32_t kv_len[kRowsMax];
   uint32_t index_offset[kRowsMax];
   uint64_t slot_base[kRowsMax];
-  uint64_t p_base[kRowsMax];
   uint64_t stat_base[kRowsMax];
-  uint64_t gt_base[kRowsMax];
+  uint64_t part_base[kRowsMax];
 };
-hipError_t launch_attn_logits(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s);
-hipError_t launch_attn_reduce(const AttnArgs &a, uint32_t blocks, hipStream_t s);
+hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs &a, uint32_t blocks, hipStream_t s);
 
 }  // namespace ds

@@ -163,12 +163,11 @@ def test_size_queries(lib):
     s = stab((1000, 37, 1), width=(512, 37, 1))
     assert ds.gathered_elems(s) == (512 + 37 + 1) * 512
     assert ds.mask_elems(s) == 512 + 37 + 1
-    chunks = 16 + 2 + 1
-    plane_bytes = 64 * chunks * 32 * 2          # bf16 hi plane, then lo plane
-    stat_bytes = 64 * chunks * 16
-    gt_bytes = 512 * chunks * 32 * 2            # feature-major copy of the selected rows
+    chunks = 8 + 1 + 1                          # 64-slot chunks of widths 512, 37, 1
+    stat_bytes = 64 * chunks * 16               # f32x4 statistics per (chunk, head)
+    part_bytes = chunks * 64 * 512 * 4          # f32 output of each chunk
     up = lambda x: (x + 255) // 256 * 256
-    assert ds.attn_workspace_bytes(s) == 2 * up(plane_bytes) + up(stat_bytes) + up(gt_bytes)
+    assert ds.attn_workspace_bytes(s) == up(stat_bytes) + up(part_bytes)
     assert ds.scores_elems(itab((0,))) == 0            # invalid table -> 0
 
 
