@@ -44,12 +44,13 @@
 namespace ds {
 
 constexpr int kIdxRing = 4;   // tile buffers per wave (kIdxRing - 1 in flight)
+constexpr uint32_t kIdxWaves = kIdxThreads / 64;
+constexpr int kQVec = kHeads * kIdxDim / 8 / kIdxThreads;   // 16-byte query pieces per thread
 // The fused stage keeps one tile in kIdxRing per lane, in a 4-deep queue.
 static_assert(kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile <= 4 * kIdxRing, "tiles per wave");
 
 // One wave's candidates (fused stage, see above): o[e] are the score bits
-// (0 = not valid) of keys key0 + 64 * (wave + 4 * (4 * (n - 1 - e) + grp)) / 4
-// ..., passed in as their key indices kidx[e].
+// (0 = not valid) of the lane's kept keys, kidx[e] their key indices.
 __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint32_t (&o)[4],
                                                 const uint32_t (&kidx)[4], uint32_t wave, uint32_t lane) {
   const uint64_t slot0 = static_cast<uint64_t>(blockIdx.x) * kIdxCand + wave * kIdxWaveCand;
@@ -116,15 +117,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   // The query and weights go out first (they gate every MFMA), then the
   // first tiles of keys; the query reaches LDS once its loads have landed.
   __shared__ float w_lds[kHeads];
-  u32x4 qv[4];
+  u32x4 qv[kQVec];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) qv[i] = load16(q + 8 * (tid + kIdxThreads * i));
+  for (int i = 0; i < kQVec; ++i) qv[i] = load16(q + 8 * (tid + kIdxThreads * i));
   const float wv = w[tid & (kHeads - 1)];
 
   const uint32_t tiles = (k_end - k0 + kIdxTile - 1) / kIdxTile;
-  const uint32_t mine = tiles > wave ? (tiles - wave + 3) / 4 : 0;   // tiles wave, wave+4, ...
+  const uint32_t mine = tiles > wave ? (tiles - wave + kIdxWaves - 1) / kIdxWaves : 0;   // tiles wave, wave+W, ...
   auto load_tile = [&](uint32_t i, u32x4 (&kb)[4]) {
-    const uint32_t key = min(k0 + (wave + 4 * i) * kIdxTile + col, n - 1);   // tail: clamp, not stored
+    const uint32_t key = min(k0 + (wave + kIdxWaves * i) * kIdxTile + col, n - 1);   // tail: clamp, not stored
     const uint16_t *krow = keys + static_cast<uint64_t>(key) * kIdxDim + 32 * grp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) kb[c] = load16(krow + 8 * c);
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
 #pragma unroll
   for (int p = 0; p < kIdxRing - 1; ++p) load_tile(min(static_cast<uint32_t>(p), last), buf[p]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q_lds[tid + kIdxThreads * i] = qv[i];
+  for (int i = 0; i < kQVec; ++i) q_lds[tid + kIdxThreads * i] = qv[i];
   if (tid < kHeads) w_lds[tid] = wv;
   __syncthreads();
   // Query fragments (head 16m + col, features [32*grp + 8c, +8)) and the head
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
       // Sum the four 16-head groups held by lanes col, col+16, col+32, col+48.
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
-      const uint32_t key = k0 + (wave + 4 * i) * kIdxTile + col;
+      const uint32_t key = k0 + (wave + kIdxWaves * i) * kIdxTile + col;
       const float v = (key < visible && __builtin_isfinite(part)) ? part : -__builtin_inff();
       if (i < mine && grp == 0 && key < k_end) scores[key] = v;
       if constexpr (kFused) {
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t i = kIdxRing * (groups - 1 - e) + grp;   // (unused when groups <= e: fifo[e] is 0)
-      kidx[e] = k0 + (wave + 4 * i) * kIdxTile + col;
+      kidx[e] = k0 + (wave + kIdxWaves * i) * kIdxTile + col;
     }
     wave_candidates(a, fifo, kidx, wave, lane);
   }
