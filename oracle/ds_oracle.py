@@ -209,3 +209,154 @@ def decode_rows(inp) -> list[dict]:
                               inp.offset[r], inp.attn_q[r], inp.sinks, inp.kv[r],
                               inp.kv_len[r], min(inp.kv_len[r], TOP_K), inp.scale))
     return res
+
+
+# ---------------------------------------------------------------------------
+# Learned KV compressor, one decode token per row
+# ---------------------------------------------------------------------------
+#
+# [shader 0.18] deepseek_compressor_rows_bf16 and [host 0.21]
+# dispatch_deepseek_compressor_rows. Each row owns a recurrent state of two
+# f32 tensors (values and scores) of coff * ratio rows by coff * head_dim
+# features, coff = 2 for ratio 4 (windows overlap by one block) and 1
+# otherwise. The decode token is written into the state; when it completes a
+# block of `ratio` positions the row emits one compressed vector: per feature,
+# a softmax over the window's scores weights the window's values, the result
+# is rounded to bf16, RMS-normalised with a learned scale and stored as bf16.
+#
+# Readings (also in the design notes):
+#   * The state is f32 on the pages, so the state update is done in f32: the
+#     value is copied (non-finite -> 0) and the score is the f32 sum of the
+#     input score and the position embedding (NaN when either the sum or the
+#     value is not finite).
+#   * Pooling and normalisation are computed in float64. The pooled value is
+#     rounded to bf16 (round to nearest even) straight from float64; the
+#     normalised value likewise.
+#   * The sum of squares is invalid when it exceeds the f32 range (the pages
+#     keep it in f32); outputs beyond the bf16 range are not special-cased.
+#   * A row that emits nothing writes zeros.
+
+COMPRESSOR_SHAPES = ((4, 128), (4, 512), (128, 512))
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of float64 values, rounded to nearest with ties
+    to even directly from the float64 value (one rounding). bf16 keeps f32's
+    exponent range and 8 significant bits; values beyond its largest finite
+    value after rounding become +-inf; NaN becomes the canonical quiet NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.uint16)
+    flat = x.reshape(-1)
+    res = out.reshape(-1)
+    bf16_max = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    for i, v in enumerate(flat):
+        if np.isnan(v):
+            res[i] = 0x7FC0
+            continue
+        if np.isinf(v):
+            res[i] = 0xFF80 if v < 0 else 0x7F80
+            continue
+        if v == 0.0:
+            res[i] = 0x8000 if np.signbit(v) else 0
+            continue
+        _, e = np.frexp(v)                      # |v| = m * 2^e, 0.5 <= m < 1
+        ulp = 2.0 ** max(int(e) - 8, -133)      # 8 significant bits; subnormal spacing 2^-133
+        r = float(np.round(v / ulp)) * ulp      # np.round rounds half to even
+        if abs(r) > bf16_max:
+            res[i] = 0xFF80 if r < 0 else 0x7F80
+            continue
+        res[i] = np.uint16(np.array(r, dtype=np.float32).view(np.uint32) >> np.uint32(16))
+    return out
+
+
+def compressor_dims(ratio: int, head_dim: int):
+    """(coff, projected features, state rows) of a supported (ratio, head_dim);
+    [host 0.21] dispatch_deepseek_compressor_rows accepts (4,128), (4,512) and
+    (128,512)."""
+    if (int(ratio), int(head_dim)) not in COMPRESSOR_SHAPES:
+        raise ValueError(f"unsupported compressor shape ({ratio},{head_dim})")
+    coff = 2 if ratio == 4 else 1
+    return coff, coff * head_dim, coff * ratio
+
+
+def compressor_row(kv, score, ape, norm, kv_state, score_state, start_pos: int,
+                   ratio: int, head_dim: int, eps: float):
+    """One decode token at absolute position `start_pos` (> 0) of one row.
+
+    kv, score: f32 [coff*head_dim]; ape: f32 [ratio, coff*head_dim];
+    norm: f32 [head_dim]; kv_state, score_state: f32 [coff*ratio,
+    coff*head_dim] (not modified). Returns (new kv_state, new score_state,
+    output bf16 bits [head_dim]).
+    [shader 0.18] deepseek_compressor_rows_bf16 (token write, window pooling,
+    RMS normalisation, fail-closed zeroing, overlap shift)."""
+    coff, proj, _ = compressor_dims(ratio, head_dim)
+    overlap = ratio == 4
+    kv = np.asarray(kv, dtype=np.float32)
+    score = np.asarray(score, dtype=np.float32)
+    ape = np.asarray(ape, dtype=np.float32)
+    norm64 = np.asarray(norm, dtype=np.float32).astype(np.float64)
+    kvs = np.array(kv_state, dtype=np.float32, copy=True)
+    scs = np.array(score_state, dtype=np.float32, copy=True)
+
+    # Write the token into its slot of the current block.
+    token = int(start_pos) % ratio
+    slot = (ratio if overlap else 0) + token
+    with np.errstate(over="ignore", invalid="ignore"):
+        s = score + ape[token]                  # f32 addition
+    kvs[slot] = np.where(np.isfinite(kv), kv, np.float32(0.0))
+    scs[slot] = np.where(np.isfinite(s) & np.isfinite(kv), s, np.float32(np.nan))
+
+    out = np.zeros(head_dim, dtype=np.uint16)
+    if (int(start_pos) + 1) % ratio != 0:
+        return kvs, scs, out
+
+    # The window of feature f: the previous block's rows at feature f and the
+    # current block's rows at feature head_dim + f (overlap), or the current
+    # block's rows at feature f.
+    window = 2 * ratio if overlap else ratio
+    f = np.arange(head_dim)
+    S = np.empty((window, head_dim), dtype=np.float64)
+    V = np.empty((window, head_dim), dtype=np.float64)
+    for item in range(window):
+        feat = f + head_dim if (overlap and item >= ratio) else f
+        S[item] = scs[item, feat]
+        V[item] = kvs[item, feat]
+    bad = (np.isnan(S) | (S == np.inf) | ~np.isfinite(V)).any(axis=0)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        m = S.max(axis=0)
+        wts = np.exp(S - m[None, :])
+        pooled = (wts * V).sum(axis=0) / wts.sum(axis=0)
+    finite = np.isfinite(pooled)
+    c = bf16_bits_to_f64(bf16_round_bits(np.where(finite, pooled, 0.0)))
+    bad |= ~finite | ~np.isfinite(norm64)
+    total = float((c * c).sum())
+    invalid = bool(bad.any()) or not (total <= FLT_MAX)
+    if not invalid:
+        rms = 1.0 / np.sqrt(total / head_dim + float(eps))
+        invalid = not np.isfinite(rms)
+    if not invalid:
+        normalized = c * rms * norm64
+        invalid = not np.isfinite(normalized).all()
+    if not invalid:
+        out = bf16_round_bits(normalized)
+
+    if overlap:
+        # The current block becomes the previous one.
+        kvs[:ratio] = kvs[ratio:2 * ratio]
+        scs[:ratio] = scs[ratio:2 * ratio]
+    return kvs, scs, out
+
+
+def compressor_rows(inp):
+    """Every row of a compressor workload (an object with the fields of the
+    seeded generator's CompressorInputs), row by row. Returns (kv_states,
+    score_states, outputs) as lists."""
+    kvs, scs, outs = [], [], []
+    for r in range(len(inp.start_pos)):
+        a, b, o = compressor_row(inp.kv[r], inp.score[r], inp.ape, inp.norm, inp.kv_state[r],
+                                 inp.score_state[r], inp.start_pos[r], inp.ratio, inp.head_dim, inp.eps)
+        kvs.append(a)
+        scs.append(b)
+        outs.append(o)
+    return kvs, scs, outs

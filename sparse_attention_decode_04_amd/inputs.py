@@ -155,3 +155,64 @@ def make_rows(rng: np.random.Generator, kv_len: list[int], ternary: bool = False
 def small_rows(seed: int, kv_len: list[int], ternary: bool = False, **kw) -> RowsInputs:
     """Convenience for tests: the same recipe at arbitrary small sizes."""
     return make_rows(np.random.Generator(np.random.PCG64(seed)), kv_len, ternary=ternary, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Learned KV compressor, one decode token per row
+# ---------------------------------------------------------------------------
+# Shapes: coff = 2 for ratio 4 (overlapping windows) and 1 otherwise; the
+# token's projected value and score are [coff * head_dim] f32, the position
+# embedding [ratio, coff * head_dim] f32, the RMS scale [head_dim] f32 and
+# each row's two recurrent states [coff * ratio, coff * head_dim] f32.
+# Values, scores, embeddings and states ~ N(0, 1); the RMS scale ~ U[0.5, 1.5];
+# epsilon 1e-6. The pages give no weights, so all are synthetic.
+# Generation order: rng = Generator(PCG64(seed)) -> kv [R,P] -> score [R,P]
+# -> ape [ratio,P] -> norm [head_dim] -> kv_state [R,S,P] -> score_state [R,S,P]
+# -> [default positions].
+
+COMPRESSOR_SEED_BASE = 20261000
+COMPRESSOR_SHAPES = ((4, 128), (4, 512), (128, 512))
+
+
+@dataclass
+class CompressorInputs:
+    ratio: int
+    head_dim: int
+    start_pos: list[int]
+    kv: np.ndarray             # float32 [R, P]
+    score: np.ndarray          # float32 [R, P]
+    ape: np.ndarray            # float32 [ratio, P]
+    norm: np.ndarray           # float32 [head_dim]
+    kv_state: np.ndarray       # float32 [R, S, P]
+    score_state: np.ndarray    # float32 [R, S, P]
+    eps: float = 1e-6
+
+    @property
+    def rows(self) -> int:
+        return len(self.start_pos)
+
+
+def make_compressor(seed: int, rows: int, ratio: int, head_dim: int,
+                    start_pos: list[int] | None = None) -> CompressorInputs:
+    """Seeded compressor inputs. start_pos defaults to positions that end a
+    block for every row (ratio * k - 1, k uniform in [1, 4096])."""
+    if (ratio, head_dim) not in COMPRESSOR_SHAPES:
+        raise ValueError(f"unsupported compressor shape ({ratio},{head_dim})")
+    coff = 2 if ratio == 4 else 1
+    P, S = coff * head_dim, coff * ratio
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kv = rng.standard_normal((rows, P), dtype=np.float32)
+    score = rng.standard_normal((rows, P), dtype=np.float32)
+    ape = rng.standard_normal((ratio, P), dtype=np.float32)
+    norm = rng.uniform(0.5, 1.5, size=head_dim).astype(np.float32)
+    kv_state = rng.standard_normal((rows, S, P), dtype=np.float32)
+    score_state = rng.standard_normal((rows, S, P), dtype=np.float32)
+    if start_pos is None:
+        start_pos = [ratio * int(k) - 1 for k in rng.integers(1, 4096, size=rows, endpoint=True)]
+    return CompressorInputs(ratio, head_dim, list(start_pos), kv, score, ape, norm, kv_state, score_state)
+
+
+def compressor_workload(ratio: int, head_dim: int) -> CompressorInputs:
+    """The measured compressor workload of a shape: 8 rows, every row's token
+    ends a block (the step that pools and normalises)."""
+    return make_compressor(COMPRESSOR_SEED_BASE + ratio * 1000 + head_dim, 8, ratio, head_dim)
