@@ -117,6 +117,69 @@ def step_bytes(inp):
     return idx_b + topk_b + attn_b
 
 
+def compressor_bytes(inp):
+    """Algorithmic HBM bytes of one ds_rows_compressor call: per row, the
+    token's value and score and its position-embedding row (f32, P each),
+    the state row the token lands in (written, both states), the output
+    (bf16) and, for a token that ends a block, the window (head_dim features
+    of each window row, both states) plus, with overlap, the shift (the
+    current block's other half read, ratio rows of both states written);
+    the RMS scale once per call."""
+    coff = 2 if inp.ratio == 4 else 1
+    P, hd, ratio = coff * inp.head_dim, inp.head_dim, inp.ratio
+    total = 4 * hd
+    for pos in inp.start_pos:
+        b = 3 * 4 * P + 2 * 4 * P + 2 * hd
+        if (pos + 1) % ratio == 0:
+            window = 2 * ratio if coff == 2 else ratio
+            b += window * hd * 4 * 2
+            if coff == 2:
+                b += ratio * hd * 4 * 2 + ratio * P * 4 * 2
+        total += b
+    return total
+
+
+def compressor_bench(torch, n_calls):
+    """Each compressor shape at 8 rows (every token ends a block): mean call
+    duration, algorithmic bytes and their rate against HBM peak. A call is a
+    few microseconds of GPU work, less than the Python binding needs to
+    enqueue one, so 16 calls (one per state set) are captured once in a HIP
+    graph and the graph is replayed; the duration is HIP-event time over the
+    replays divided by the calls."""
+    from sparse_attention_decode_04_amd import inputs as I
+    from sparse_attention_decode_04_amd.runner import DeviceCompressor
+    res = {}
+    stream = torch.cuda.current_stream()
+    for ratio, hd in I.COMPRESSOR_SHAPES:
+        inp = I.compressor_workload(ratio, hd)
+        dev = DeviceCompressor(inp, copies=16)
+        for c in range(16):
+            dev.run(c)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in range(16):
+                dev.run(c)
+        reps = max(1, n_calls // 16)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / (16 * reps)
+        nbytes = compressor_bytes(inp)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[f"ratio{ratio}_dim{hd}"] = {
+            "rows": inp.rows, "us_per_call": ms * 1e3, "rows_per_s": inp.rows / (ms * 1e-3),
+            "bytes_per_call": nbytes, "achieved_gb_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "bound": "latency (< 5 MB per call)"}
+    return res
+
+
 def cpu_baseline(inp, seconds):
     from threadpoolctl import threadpool_info
 
@@ -284,6 +347,11 @@ def main():
             "mfma_tflops": idx_flops / idx_s / 1e12,
             "mfma_frac_of_bf16_peak": idx_flops / idx_s / 1e12 / BF16_PEAK_TFLOPS,
         },
+    }
+    out["compressor"] = {
+        "call": "ds_rows_compressor (one decode token per row: state write, window pooling, RMS norm)",
+        "timing": "HIP events around replays of a HIP graph holding 16 calls (16 state sets)",
+        "shapes": compressor_bench(torch, max(args.steps, 50)),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

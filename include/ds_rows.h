@@ -14,7 +14,9 @@
  *
  * and two fused forms of it: ds_rows_indexer_topk (score and top-512 in one
  * call, the first selection stage in the indexer's epilogue) and
- * ds_rows_sparse_attn_direct (gather and attention in one call).
+ * ds_rows_sparse_attn_direct (gather and attention in one call). The step
+ * before them, ds_rows_compressor, turns each row's decode token into its
+ * next compressed cache row.
  *
  * Source pages (docs.rs source views of the Rust crate mlx-native):
  *   [shader 0.18] "mlx-native 0.18.0 src/shaders/deepseek_rows.metal"
@@ -272,6 +274,64 @@ ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows,
                                      void *workspace, size_t workspace_bytes,
                                      float *out, size_t out_elems,
                                      void *stream);
+
+/* ---- ds_rows_compressor -------------------------------------------------
+ * One decode token of the learned KV compressor per row, each row with its
+ * own recurrent state ([shader 0.18] deepseek_compressor_rows_bf16;
+ * [host 0.21] dispatch_deepseek_compressor_rows). The step that produces the
+ * compressed KV rows and indexer keys the calls above read.
+ * Shapes: (ratio, head_dim) in {(4,128), (4,512), (128,512)}; coff = 2 for
+ * ratio 4 (each window reaches one block back) and 1 for ratio 128;
+ * P = coff * head_dim; every state is f32 [coff * ratio, P] row-major
+ * (ds_rows_compressor_state_elems).
+ * For row r with token position pos = start_pos[r], t = pos % ratio:
+ *   - state row slot = (ratio if ratio == 4 else 0) + t takes
+ *       kv_state  = kv[r, :]                 (0 where not finite)
+ *       score_state = score[r, :] + ape[t, :] (f32 sum; NaN where the sum or
+ *                                              the value is not finite)
+ *   - if (pos + 1) % ratio == 0, output feature f < head_dim pools the window
+ *     (ratio 4: state rows 0..3 at feature f and rows 4..7 at feature
+ *     head_dim + f; ratio 128: rows 0..127 at feature f):
+ *       c[f] = bf16( sum_i e^(s_i - m) v_i / sum_i e^(s_i - m) ),  m = max s_i
+ *       out[r, f] = bf16( c[f] * rsqrt(mean_f c^2 + epsilon) * norm[f] )
+ *     and the whole output row is zero if a window score is NaN or +inf, a
+ *     window value is not finite, a pooled value, norm element, the RMS
+ *     scale or an output value is not finite. With ratio 4 the state rows
+ *     0..3 then take rows 4..7 (this block becomes the previous one).
+ *   - otherwise out[r, :] = 0.
+ * Pooling and normalisation accumulate in f32 (exp via the hardware
+ * exponential), so outputs agree with an exact evaluation to within two bf16
+ * units in the last place; the state update is exact.
+ *   rows       table: start_pos[r] in 1..UINT32_MAX-1; kv_state[r] and
+ *              score_state[r] device f32 (read and written), capacities in
+ *              elements; all 2 * rows state buffers must be disjoint
+ *   kv, score  device f32 [rows, P] (row r of the call is entry r)
+ *   ape        device f32 [ratio, P] (position-in-block embedding)
+ *   norm       device f32 [head_dim] (RMS scale)
+ *   epsilon    finite and > 0
+ *   output     device bf16 [rows, head_dim]
+ * Checks: those of [host 0.21] dispatch_deepseek_compressor_rows (rows,
+ * shape, epsilon, positions, state capacities, disjoint states, operand
+ * capacities) and non-null pointers. */
+typedef struct {
+  uint32_t rows;                        /* 1..DS_ROWS_MAX */
+  uint32_t start_pos[DS_ROWS_MAX];      /* the token's absolute position, > 0 */
+  float *kv_state[DS_ROWS_MAX];         /* device f32 [coff*ratio, P] */
+  float *score_state[DS_ROWS_MAX];      /* device f32 [coff*ratio, P] */
+  uint64_t kv_state_elems[DS_ROWS_MAX];
+  uint64_t score_state_elems[DS_ROWS_MAX];
+} ds_compressor_rows;
+
+size_t ds_rows_compressor_state_elems(uint32_t ratio, uint32_t head_dim);  /* 0 if unsupported */
+
+ds_status ds_rows_compressor(const ds_compressor_rows *rows,
+                             uint32_t ratio, uint32_t head_dim, float epsilon,
+                             const float *kv, size_t kv_elems,
+                             const float *score, size_t score_elems,
+                             const float *ape, size_t ape_elems,
+                             const float *norm, size_t norm_elems,
+                             void *output, size_t output_elems,
+                             void *stream);
 
 /* Message of the last failed call on this thread ("ds_rows: ..."), or "". */
 const char *ds_rows_last_error(void);

@@ -513,3 +513,91 @@ const char *ds_rows_last_error(void) { return g_error.c_str(); }
 const char *ds_rows_version(void) { return "ds_rows 0.1.0 (gfx950)"; }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- compressor
+namespace {
+
+bool compressor_shape_ok(uint32_t ratio, uint32_t head_dim) {
+  return (ratio == 4 && (head_dim == 128 || head_dim == 512)) || (ratio == 128 && head_dim == 512);
+}
+
+bool ranges_overlap(const void *a, uint64_t an, const void *b, uint64_t bn) {
+  const auto a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ds_rows_compressor_state_elems(uint32_t ratio, uint32_t head_dim) {
+  if (!compressor_shape_ok(ratio, head_dim)) {
+    fail("compressor (ratio, head_dim) must be (4,128), (4,512) or (128,512), got (%u,%u)", ratio, head_dim);
+    return 0;
+  }
+  const uint64_t coff = ratio == 4 ? 2 : 1;
+  return static_cast<size_t>(coff * ratio * coff * head_dim);
+}
+
+ds_status ds_rows_compressor(const ds_compressor_rows *rows, uint32_t ratio, uint32_t head_dim, float epsilon,
+                             const float *kv, size_t kv_elems, const float *score, size_t score_elems,
+                             const float *ape, size_t ape_elems, const float *norm, size_t norm_elems, void *output,
+                             size_t output_elems, void *stream) {
+  if (!rows) return fail("null compressor row table");
+  if (rows->rows == 0 || rows->rows > DS_ROWS_MAX)
+    return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, rows->rows);
+  if (!compressor_shape_ok(ratio, head_dim))
+    return fail("compressor (ratio, head_dim) must be (4,128), (4,512) or (128,512), got (%u,%u)", ratio, head_dim);
+  if (!std::isfinite(epsilon) || epsilon <= 0.0f) return fail("compressor epsilon must be finite and positive");
+  const uint64_t coff = ratio == 4 ? 2 : 1;
+  const uint64_t proj = coff * head_dim;
+  const uint64_t state = coff * ratio * proj;
+  const uint32_t n = rows->rows;
+  for (uint32_t r = 0; r < n; ++r) {
+    if (rows->start_pos[r] == 0 || rows->start_pos[r] == UINT32_MAX)
+      return fail("compressor row %u: position must be in 1..u32::MAX, got %u", r, rows->start_pos[r]);
+    if (!rows->kv_state[r]) return fail("compressor row %u: kv_state must not be null", r);
+    if (!rows->score_state[r]) return fail("compressor row %u: score_state must not be null", r);
+    DS_TRY(cap(rows->kv_state_elems[r], state, "kv_state", "elements"));
+    DS_TRY(cap(rows->score_state_elems[r], state, "score_state", "elements"));
+  }
+  // Every state buffer of every row is written: all must be disjoint.
+  for (uint32_t r = 0; r < 2 * n; ++r) {
+    const void *pr = r < n ? rows->kv_state[r] : rows->score_state[r - n];
+    for (uint32_t o = 0; o < r; ++o) {
+      const void *po = o < n ? rows->kv_state[o] : rows->score_state[o - n];
+      if (ranges_overlap(pr, state * sizeof(float), po, state * sizeof(float)))
+        return fail("compressor states overlap (state buffers %u and %u)", o, r);
+    }
+  }
+  DS_TRY(need(kv, "kv"));
+  DS_TRY(need(score, "score"));
+  DS_TRY(need(ape, "ape"));
+  DS_TRY(need(norm, "norm"));
+  DS_TRY(need(output, "output"));
+  DS_TRY(cap(kv_elems, n * proj, "kv", "elements"));
+  DS_TRY(cap(score_elems, n * proj, "score", "elements"));
+  DS_TRY(cap(ape_elems, ratio * proj, "ape", "elements"));
+  DS_TRY(cap(norm_elems, head_dim, "norm", "elements"));
+  DS_TRY(cap(output_elems, uint64_t(n) * head_dim, "output", "elements"));
+
+  ds::CompressorArgs a{};
+  a.kv = kv;
+  a.score = score;
+  a.ape = ape;
+  a.norm = norm;
+  a.out = static_cast<uint16_t *>(output);
+  for (uint32_t r = 0; r < n; ++r) {
+    a.kv_state[r] = rows->kv_state[r];
+    a.score_state[r] = rows->score_state[r];
+    a.start_pos[r] = rows->start_pos[r];
+  }
+  a.rows = n;
+  a.ratio = ratio;
+  a.head_dim = head_dim;
+  a.eps = epsilon;
+  const hipError_t e = ds::launch_compressor(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DS_OK : hip_fail(e, "compressor launch");
+}
+
+}  // extern "C"

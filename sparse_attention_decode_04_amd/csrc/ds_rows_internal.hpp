@@ -153,4 +153,22 @@ struct AttnArgs {
 hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs &a, uint32_t blocks, hipStream_t s);
 
+
+// -------------------------------------------------------------- compressor
+// One decode token of the learned KV compressor per row; one workgroup per
+// row (256 threads for ratio 4, 1024 for ratio 128).
+struct CompressorArgs {
+  const float *kv;                  // f32 [rows, P] (P = coff * head_dim)
+  const float *score;               // f32 [rows, P]
+  const float *ape;                 // f32 [ratio, P]
+  const float *norm;                // f32 [head_dim]
+  uint16_t *out;                    // bf16 [rows, head_dim]
+  float *kv_state[kRowsMax];        // f32 [coff * ratio, P] per row
+  float *score_state[kRowsMax];
+  uint32_t rows, ratio, head_dim;
+  uint32_t start_pos[kRowsMax];
+  float eps;
+};
+hipError_t launch_compressor(const CompressorArgs &a, hipStream_t s);
+
 }  // namespace ds

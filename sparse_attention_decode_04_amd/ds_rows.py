@@ -27,7 +27,7 @@ FUNCTIONS = (
     "ds_rows_mask_elems", "ds_rows_attn_workspace_bytes", "ds_rows_indexer_score",
     "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn", "ds_rows_sparse_attn_direct",
     "ds_rows_last_error", "ds_rows_version", "ds_rows_indexer_topk_workspace_bytes", "ds_rows_indexer_topk",
-    "ds_rows_indexer_candidates",
+    "ds_rows_indexer_candidates", "ds_rows_compressor_state_elems", "ds_rows_compressor",
 )
 
 
@@ -59,6 +59,18 @@ class SparseRows(ctypes.Structure):
         ("q_row", c_uint32 * ROWS_MAX),
         ("kv", c_void_p * ROWS_MAX),
         ("kv_elems", c_uint64 * ROWS_MAX),
+    ]
+
+
+class CompressorRows(ctypes.Structure):
+    """ds_compressor_rows"""
+    _fields_ = [
+        ("rows", c_uint32),
+        ("start_pos", c_uint32 * ROWS_MAX),
+        ("kv_state", c_void_p * ROWS_MAX),
+        ("score_state", c_void_p * ROWS_MAX),
+        ("kv_state_elems", c_uint64 * ROWS_MAX),
+        ("score_state_elems", c_uint64 * ROWS_MAX),
     ]
 
 
@@ -99,8 +111,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     lib.ds_rows_indexer_candidates.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                                c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_compressor_state_elems.argtypes = [c_uint32, c_uint32]
+    lib.ds_rows_compressor_state_elems.restype = c_size_t
+    lib.ds_rows_compressor.argtypes = [P(CompressorRows), c_uint32, c_uint32, c_float,
+                                       c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t,
+                                       c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn",
-              "ds_rows_sparse_attn_direct", "ds_rows_indexer_topk", "ds_rows_indexer_candidates"):
+              "ds_rows_sparse_attn_direct", "ds_rows_indexer_topk", "ds_rows_indexer_candidates",
+              "ds_rows_compressor"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
@@ -155,6 +173,25 @@ def sparse_rows(kv_len, width, index_offset, q_row, kv=None, kv_elems=None) -> S
     if kv_elems is None:
         kv_elems = [k.numel() if isinstance(k, torch.Tensor) else 0 for k in kv]
     t.kv_elems = _arr(c_uint64, kv_elems)
+    return t
+
+
+def compressor_rows(start_pos, kv_state=None, score_state=None, kv_state_elems=None,
+                    score_state_elems=None) -> CompressorRows:
+    """Build a ds_compressor_rows table from per-row device state tensors."""
+    t = CompressorRows()
+    t.rows = len(start_pos)
+    t.start_pos = _arr(c_uint32, start_pos)
+    kv_state = kv_state or []
+    score_state = score_state or []
+    t.kv_state = _arr(c_void_p, [_addr(k) for k in kv_state])
+    t.score_state = _arr(c_void_p, [_addr(k) for k in score_state])
+    if kv_state_elems is None:
+        kv_state_elems = [k.numel() if isinstance(k, torch.Tensor) else 0 for k in kv_state]
+    if score_state_elems is None:
+        score_state_elems = [k.numel() if isinstance(k, torch.Tensor) else 0 for k in score_state]
+    t.kv_state_elems = _arr(c_uint64, kv_state_elems)
+    t.score_state_elems = _arr(c_uint64, score_state_elems)
     return t
 
 
@@ -276,6 +313,20 @@ def sparse_attn_direct(t: SparseRows, q, sinks, indices, scale, workspace, out, 
     oa, on = _dev(out, 4)
     _check(load().ds_rows_sparse_attn_direct(ctypes.byref(t), qa, qn, sa, sn, ia, inn, float(scale),
                                              wa, wb, oa, on, _stream(stream)))
+
+
+def compressor_state_elems(ratio: int, head_dim: int) -> int:
+    return load().ds_rows_compressor_state_elems(ratio, head_dim)
+
+
+def compressor(t: CompressorRows, ratio, head_dim, eps, kv, score, ape, norm, out, stream=None):
+    ka, kn = _dev(kv, 4)
+    sa, sn = _dev(score, 4)
+    aa, an = _dev(ape, 4)
+    na, nn = _dev(norm, 4)
+    oa, on = _dev(out, 2)
+    _check(load().ds_rows_compressor(ctypes.byref(t), int(ratio), int(head_dim), float(eps), ka, kn, sa, sn,
+                                     aa, an, na, nn, oa, on, _stream(stream)))
 
 
 def version() -> str:

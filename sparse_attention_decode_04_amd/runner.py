@@ -132,3 +132,38 @@ class DeviceRows:
             ))
             base += w
         return res
+
+
+class DeviceCompressor:
+    """One compressor workload (a CompressorInputs from inputs.py) on the
+    current HIP device: inputs, per-row states (fresh copies of the
+    workload's states) and a bf16 output. `copies` > 1
+    keeps several independent state sets, for timing without reusing one
+    row's state between calls."""
+
+    def __init__(self, inp, device="cuda", rows=None, copies=1):
+        self.inp = inp
+        self.rows = list(range(inp.rows)) if rows is None else list(rows)
+        self.kv = to_device(inp.kv[self.rows], device)
+        self.score = to_device(inp.score[self.rows], device)
+        self.ape = to_device(inp.ape, device)
+        self.norm = to_device(inp.norm, device)
+        self.out = torch.zeros(len(self.rows), inp.head_dim, dtype=torch.int16, device=device)
+        self.states = []
+        for _ in range(copies):
+            kvs = [to_device(inp.kv_state[r], device) for r in self.rows]
+            scs = [to_device(inp.score_state[r], device) for r in self.rows]
+            self.states.append((kvs, scs))
+        self.tables = [ds.compressor_rows([inp.start_pos[r] for r in self.rows], kvs, scs)
+                       for kvs, scs in self.states]
+
+    def run(self, copy=0, stream=None):
+        inp = self.inp
+        ds.compressor(self.tables[copy], inp.ratio, inp.head_dim, inp.eps, self.kv, self.score, self.ape,
+                      self.norm, self.out, stream)
+
+    def results(self, copy=0):
+        torch.cuda.synchronize()
+        kvs, scs = self.states[copy]
+        out = self.out.cpu().numpy().view(np.uint16)
+        return ([k.cpu().numpy() for k in kvs], [s.cpu().numpy() for s in scs], [out[i] for i in range(len(self.rows))])

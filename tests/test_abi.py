@@ -44,7 +44,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     assert set(names) == set(ds.FUNCTIONS)
     out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (ds_rows_\w+)", out))
@@ -68,6 +68,9 @@ int main(void) {
   printf("ds_sparse_rows %zu\n", sizeof(ds_sparse_rows));
   F(ds_sparse_rows, kv_len); F(ds_sparse_rows, width); F(ds_sparse_rows, index_offset);
   F(ds_sparse_rows, q_row); F(ds_sparse_rows, kv); F(ds_sparse_rows, kv_elems);
+  printf("ds_compressor_rows %zu\n", sizeof(ds_compressor_rows));
+  F(ds_compressor_rows, start_pos); F(ds_compressor_rows, kv_state); F(ds_compressor_rows, score_state);
+  F(ds_compressor_rows, kv_state_elems); F(ds_compressor_rows, score_state_elems);
   return 0;
 }
 """
@@ -80,7 +83,9 @@ int main(void) {
     got = dict(l.rsplit(" ", 1) for l in lines if l)
     assert int(got["ds_indexer_rows"]) == ctypes.sizeof(ds.IndexerRows)
     assert int(got["ds_sparse_rows"]) == ctypes.sizeof(ds.SparseRows)
-    for (T, C) in (("ds_indexer_rows", ds.IndexerRows), ("ds_sparse_rows", ds.SparseRows)):
+    assert int(got["ds_compressor_rows"]) == ctypes.sizeof(ds.CompressorRows)
+    for (T, C) in (("ds_indexer_rows", ds.IndexerRows), ("ds_sparse_rows", ds.SparseRows),
+                   ("ds_compressor_rows", ds.CompressorRows)):
         for name, _ in C._fields_[1:]:
             assert int(got[f"{T}.{name}"]) == getattr(C, name).offset, (T, name)
 
@@ -264,3 +269,64 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         ds.indexer_score(t, torch.zeros(64 * 128, dtype=torch.int16), torch.zeros(64),
                          torch.zeros(10))
+
+
+# ---------------------------------------------------------------- compressor
+# Checks restated from dispatch_deepseek_compressor_rows ("mlx-native 0.21.0
+# src/ops/deepseek_rows.rs"): rows, supported shapes, epsilon, positions,
+# state capacities, disjoint states, operand capacities.
+
+def ctab(start_pos=(7,), ratio=4, head_dim=128, state_elems=None, kv_addr=None, sc_addr=None):
+    R = len(start_pos)
+    n = ds.compressor_state_elems(ratio, head_dim)
+    stride = 0x1000000
+    kv_addr = [FAKE + 2 * r * stride for r in range(R)] if kv_addr is None else kv_addr
+    sc_addr = [FAKE + (2 * r + 1) * stride for r in range(R)] if sc_addr is None else sc_addr
+    se = [n] * R if state_elems is None else state_elems
+    return ds.compressor_rows(list(start_pos), kv_addr, sc_addr, se, se)
+
+
+def call_comp(lib, t, ratio=4, head_dim=128, eps=1e-6, kv=BIG, score=BIG, ape=BIG, norm=BIG, out=BIG, outp=FAKE):
+    return lib.ds_rows_compressor(ctypes.byref(t), ratio, head_dim, ctypes.c_float(eps), FAKE, kv, FAKE, score,
+                                  FAKE, ape, FAKE, norm, outp, out, None)
+
+
+def test_compressor_sizes(lib):
+    assert ds.compressor_state_elems(4, 128) == 8 * 256
+    assert ds.compressor_state_elems(4, 512) == 8 * 1024
+    assert ds.compressor_state_elems(128, 512) == 128 * 512
+    assert ds.compressor_state_elems(128, 128) == 0
+    assert "must be (4,128), (4,512) or (128,512)" in ds.last_error()
+
+
+def test_compressor_checks(lib):
+    expect_invalid(call_comp(lib, ctab(), ratio=4, head_dim=256), "must be (4,128), (4,512) or (128,512)")
+    expect_invalid(call_comp(lib, ctab(), ratio=128, head_dim=128), "got (128,128)")
+    for bad in (0.0, -1e-6, float("nan"), float("inf")):
+        expect_invalid(call_comp(lib, ctab(), eps=bad), "epsilon must be finite and positive")
+    expect_invalid(call_comp(lib, ctab((7, 0))), "row 1: position must be in 1..u32::MAX, got 0")
+    expect_invalid(call_comp(lib, ctab((0xFFFFFFFF,))), "position must be in 1..u32::MAX")
+    t = ctab()
+    t.rows = 9
+    expect_invalid(call_comp(lib, t), "rows must be 1..=8")
+    t.rows = 0
+    expect_invalid(call_comp(lib, t), "rows must be 1..=8")
+    expect_invalid(call_comp(lib, ctab(state_elems=[2047])), "kv_state holds 2047 elements, needs 2048")
+    t = ctab()
+    t.score_state_elems[0] = 100
+    expect_invalid(call_comp(lib, t), "score_state holds")
+    # states of different rows, or a row's two states, must not overlap
+    expect_invalid(call_comp(lib, ctab((7, 11), kv_addr=[FAKE, FAKE + 4096],
+                                       sc_addr=[FAKE + 0x1000000, FAKE + 0x2000000])), "compressor states overlap")
+    expect_invalid(call_comp(lib, ctab((7,), kv_addr=[FAKE], sc_addr=[FAKE + 2048 * 4 - 4])), "states overlap")
+    call_comp(lib, ctab((7,), kv_addr=[FAKE], sc_addr=[FAKE + 2048 * 4]), kv=0)   # adjacent is fine...
+    assert "states overlap" not in ds.last_error()                                 # ...it fails on kv
+    t2 = ctab((7, 11))
+    expect_invalid(call_comp(lib, t2, kv=2 * 256 - 1), "kv holds 511")
+    expect_invalid(call_comp(lib, t2, score=2 * 256 - 1), "score holds")
+    expect_invalid(call_comp(lib, t2, ape=4 * 256 - 1), "ape holds")
+    expect_invalid(call_comp(lib, t2, norm=127), "norm holds")
+    expect_invalid(call_comp(lib, t2, out=2 * 128 - 1), "output holds")
+    expect_invalid(call_comp(lib, t2, outp=None), "output must not be null")
+    t3 = ctab((127,), ratio=128, head_dim=512)
+    expect_invalid(call_comp(lib, t3, ratio=128, head_dim=512, ape=128 * 512 - 1), "ape holds")
