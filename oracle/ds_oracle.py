@@ -360,3 +360,18 @@ def compressor_rows(inp):
         scs.append(b)
         outs.append(o)
     return kvs, scs, outs
+
+
+# ---------------------------------------------------------------------------
+# Multi-query indexer
+# ---------------------------------------------------------------------------
+
+def indexer_scores_mq(q_bits: np.ndarray, w: np.ndarray, key_bits: np.ndarray,
+                      start_pos: int, ratio: int = RATIO) -> np.ndarray:
+    """float32 scores [Q, n] of Q consecutive queries of one row against the
+    row's keys: query t is at absolute position start_pos + t, so its causal
+    limit is min(n, (start_pos + t + 1) // ratio); otherwise as
+    indexer_scores. [shader 0.18] deepseek_indexer_score_mma_rows_bf16 (its
+    query loop over a group's rows, each with its own causal count)."""
+    Q = q_bits.shape[0]
+    return np.stack([indexer_scores(q_bits[t], w[t], key_bits, int(start_pos) + t, ratio) for t in range(Q)])

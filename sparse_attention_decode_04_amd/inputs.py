@@ -216,3 +216,48 @@ def compressor_workload(ratio: int, head_dim: int) -> CompressorInputs:
     """The measured compressor workload of a shape: 8 rows, every row's token
     ends a block (the step that pools and normalises)."""
     return make_compressor(COMPRESSOR_SEED_BASE + ratio * 1000 + head_dim, 8, ratio, head_dim)
+
+
+# ---------------------------------------------------------------------------
+# Multi-query indexer (several consecutive queries per row)
+# ---------------------------------------------------------------------------
+# Row r's Q queries are q/weights rows r*Q .. r*Q + Q - 1 ([R*Q, 64, 128]
+# bf16 and [R*Q, 64] f32), integer-valued as in the single-query workloads;
+# keys [n_r, 128] per row. Query t of row r sits at position start_pos + t;
+# start_pos defaults to 4 * n_r - Q, so the last query sees every key.
+# Generation order: rng = Generator(PCG64(seed)) -> q -> weights -> keys per row.
+
+MQ_SEED_BASE = 20262000
+
+
+@dataclass
+class MultiQueryInputs:
+    query_len: int
+    kv_len: list[int]
+    start_pos: list[int]
+    idx_q: np.ndarray            # uint16 [R*Q, 64, 128]
+    idx_w: np.ndarray            # float32 [R*Q, 64]
+    idx_keys: list[np.ndarray]   # uint16 [n_r, 128] per row
+
+    @property
+    def rows(self) -> int:
+        return len(self.kv_len)
+
+
+def make_mq(seed: int, kv_len: list[int], query_len: int, ternary: bool = False,
+            start_pos: list[int] | None = None) -> MultiQueryInputs:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    R, Q = len(kv_len), query_len
+    lo, hi = (-1, 1) if ternary else (-4, 4)
+    idx_q = _int_rows(rng, R * Q * HEADS, INDEXER_DIM, lo, hi).reshape(R * Q, HEADS, INDEXER_DIM)
+    idx_w = rng.integers(-2, 2, size=(R * Q, HEADS), endpoint=True).astype(np.float32)
+    idx_keys = [_int_rows(rng, n, INDEXER_DIM, lo, hi) for n in kv_len]
+    if start_pos is None:
+        start_pos = [RATIO * n - Q for n in kv_len]
+    return MultiQueryInputs(Q, list(kv_len), list(start_pos), idx_q, idx_w, idx_keys)
+
+
+def mq_workload(query_len: int = 8) -> MultiQueryInputs:
+    """The measured multi-query workload: 8 rows x 32768 keys, query_len
+    queries per row."""
+    return make_mq(MQ_SEED_BASE + query_len, [32768] * 8, query_len)

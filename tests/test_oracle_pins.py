@@ -357,3 +357,41 @@ def test_decode_row_pipeline_consistency():
     # the best rejected
     rejected = np.setdiff1d(np.arange(700), idx)
     assert r["scores"][idx].min() >= r["scores"][rejected].max()
+
+
+# ------------------------------------------------------- multi-query indexer
+
+def test_mq_scores_per_query_causal_limits():
+    # Query t of a row sits at start_pos + t: with start_pos = 10 and four
+    # queries the visible counts are floor(11/4), floor(12/4), floor(13/4),
+    # floor(14/4) = 2, 3, 3, 3 (of 6 keys).
+    inp = I.make_mq(71, [6], 4, start_pos=[10])
+    s = O.indexer_scores_mq(inp.idx_q[:4], inp.idx_w[:4], inp.idx_keys[0], 10)
+    assert s.shape == (4, 6)
+    for t, vis in enumerate([2, 3, 3, 3]):
+        assert np.all(np.isneginf(s[t, vis:]))
+    # positive weights and a one-hot query make every visible score exactly
+    # max(0, key feature) for that query's feature
+    q = np.zeros((4, 64, 128), np.uint16)
+    for t in range(4):
+        q[t, :, 5 + t] = I.int_to_bf16_bits(np.array(1))
+    w = np.ones((4, 64), np.float32)
+    keys = I.int_to_bf16_bits(np.arange(6 * 128).reshape(6, 128) % 9 - 4)
+    s = O.indexer_scores_mq(q, w, keys, 10)
+    kv = (np.arange(6 * 128).reshape(6, 128) % 9 - 4).astype(np.float64)
+    for t, vis in enumerate([2, 3, 3, 3]):
+        np.testing.assert_array_equal(s[t, :vis], 64 * np.maximum(kv[:vis, 5 + t], 0))
+
+
+def test_mq_defaults_make_every_key_visible_to_the_last_query():
+    # start_pos defaults to 4n - Q: the last query (position 4n - 1) sees all
+    # n keys, the first (position 4n - Q) sees floor((4n - Q + 1) / 4).
+    inp = I.make_mq(72, [9, 2], 3)
+    for r, n in enumerate(inp.kv_len):
+        q, w = inp.idx_q[3 * r:3 * r + 3], inp.idx_w[3 * r:3 * r + 3]
+        assert inp.start_pos[r] == 4 * n - 3
+        assert O.valid_count(n, inp.start_pos[r] + 2) == n
+        assert O.valid_count(n, inp.start_pos[r]) == (4 * n - 2) // 4
+        s = O.indexer_scores_mq(q, w, inp.idx_keys[r], inp.start_pos[r])
+        for t in range(3):
+            np.testing.assert_array_equal(s[t], O.indexer_scores(q[t], w[t], inp.idx_keys[r], inp.start_pos[r] + t))
