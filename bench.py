@@ -180,6 +180,45 @@ def compressor_bench(torch, n_calls):
     return res
 
 
+def mq_bytes_flops(inp):
+    """Algorithmic bytes and MFMA flops of one ds_rows_indexer_score_mq call:
+    per key 256 B read and 4 B per query written, 2*64*128 flops per query;
+    per row its queries and weights (16 KiB + 256 B each)."""
+    Q, keys = inp.query_len, sum(inp.kv_len)
+    nbytes = keys * (256 + 4 * Q) + inp.rows * Q * (64 * 128 * 2 + 64 * 4)
+    return nbytes, 2 * 64 * 128 * Q * keys
+
+
+def mq_bench(torch, n_calls, query_len=8, copies=4):
+    """The multi-query indexer on 8 rows x 32768 keys x `query_len` queries:
+    mean call duration from HIP events around back-to-back calls over
+    `copies` rotating key copies, against the bf16 MFMA and HBM peaks."""
+    from sparse_attention_decode_04_amd import inputs as I
+    from sparse_attention_decode_04_amd.runner import DeviceMultiQuery
+    inp = I.mq_workload(query_len)
+    devs = [DeviceMultiQuery(inp) for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+    for d in devs:
+        d.run()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(n_calls):
+        devs[i % copies].run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / n_calls
+    nbytes, flops = mq_bytes_flops(inp)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"call": "ds_rows_indexer_score_mq", "rows": inp.rows, "kv_len": inp.kv_len[0], "query_len": query_len,
+            "timing": f"HIP events around back-to-back calls over {copies} rotating key copies",
+            "ms_per_call": ms, "keys_per_s": sum(inp.kv_len) / (ms * 1e-3),
+            "mfma_tflops": tflops, "mfma_frac_of_bf16_peak": tflops / BF16_PEAK_TFLOPS,
+            "achieved_gb_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "bytes_per_call": nbytes, "flops_per_call": flops}
+
+
 def cpu_baseline(inp, seconds):
     from threadpoolctl import threadpool_info
 
@@ -348,6 +387,7 @@ def main():
             "mfma_frac_of_bf16_peak": idx_flops / idx_s / 1e12 / BF16_PEAK_TFLOPS,
         },
     }
+    out["multi_query_indexer"] = mq_bench(torch, max(args.steps, 50))
     out["compressor"] = {
         "call": "ds_rows_compressor (one decode token per row: state write, window pooling, RMS norm)",
         "timing": "HIP events around replays of a HIP graph holding 16 calls (16 state sets)",

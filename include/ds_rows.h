@@ -191,6 +191,35 @@ ds_status ds_rows_indexer_candidates(const ds_indexer_rows *rows,
                                      void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/* ---- ds_rows_indexer_score_mq -------------------------------------------
+ * Lightning-indexer scores of query_len (1..8) consecutive queries per row,
+ * e.g. speculative or multi-token decode ([shader 0.18]
+ * deepseek_indexer_score_mma_rows_bf16: its loop over the query rows of a
+ * group, each with its own causal count; the pages' rows dispatch runs it
+ * with one query). Query t of row r is q[q_row[r] + t] (bf16 [64,128]) with
+ * weights[q_row[r] + t], at absolute position start_pos[r] + t:
+ *   scores[(r*query_len + t)*S + j] = sum_h w[h] * max(0, q[h] . keys_r[j])
+ * for j < kv_len[r], S = max kv_len, and -inf for
+ * j >= min(kv_len, (start_pos + t + 1)/4) or a non-finite score. Arithmetic
+ * per key as ds_rows_indexer_score (query_len = 1 gives its bits).
+ * The scores of query t of row r sit where ds_rows_topk expects row
+ * e = r*query_len + t of a table with kv_len[r] and start_pos[r] + t, so a
+ * ds_rows_topk call on such a table (rows*query_len <= 8) selects each
+ * query's top 512.
+ *   q        device bf16, q_elems >= (max q_row + query_len) * 8192
+ *   weights  device f32, weights_elems >= (max q_row + query_len) * 64
+ *   scores   device f32, scores_elems >= ds_rows_indexer_mq_scores_elems
+ * Checks: rows 1..8, query_len 1..8, kv_len > 0, start_pos + query_len
+ * <= UINT32_MAX, kv_len >= (start_pos + query_len)/4 (the last query's causal
+ * length), key capacities, operand capacities, non-null pointers. The
+ * table's offset and output_offset are not used. */
+size_t ds_rows_indexer_mq_scores_elems(const ds_indexer_rows *rows, uint32_t query_len);
+ds_status ds_rows_indexer_score_mq(const ds_indexer_rows *rows, uint32_t query_len,
+                                   const void *q, size_t q_elems,
+                                   const float *weights, size_t weights_elems,
+                                   float *scores, size_t scores_elems,
+                                   void *stream);
+
 /* ---- ds_rows_gather -----------------------------------------------------
  * Gathers, for slot t < width[r] of row r with i = indices[index_offset[r]+t]
  * ([shader 0.18] deepseek_sparse_attention_gather_rows_bf16):

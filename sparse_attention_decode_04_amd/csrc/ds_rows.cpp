@@ -601,3 +601,86 @@ ds_status ds_rows_compressor(const ds_compressor_rows *rows, uint32_t ratio, uin
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------- multi-query indexer
+namespace {
+
+constexpr uint32_t kMqKeysPerBlock = 512;
+
+struct MqPlan {
+  uint32_t rows = 0;
+  uint64_t max_kv = 0;
+  uint64_t q_rows = 0;                      // max q_row + query_len
+  uint32_t blk_begin[ds::kRowsMax + 1] = {};
+};
+
+// The row-table checks that concern scoring (rows, kv_len, positions and the
+// causal length of the last query); offsets and output offsets are not used.
+ds_status check_mq(const ds_indexer_rows *t, uint32_t query_len, MqPlan *p) {
+  if (!t) return fail("null indexer row table");
+  if (t->rows == 0 || t->rows > DS_ROWS_MAX) return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, t->rows);
+  if (query_len == 0 || query_len > uint32_t(ds::kMqMaxQueries))
+    return fail("query_len must be 1..=%d, got %u", ds::kMqMaxQueries, query_len);
+  p->rows = t->rows;
+  for (uint32_t r = 0; r < t->rows; ++r) {
+    if (t->kv_len[r] == 0) return fail("indexer row %u: kv_len must be nonzero", r);
+    if (uint64_t(t->start_pos[r]) + query_len > UINT32_MAX)
+      return fail("indexer row %u: indexer position overflows", r);
+    const uint32_t causal = (t->start_pos[r] + query_len) / DS_RATIO;   // the last query's
+    if (t->kv_len[r] < causal)
+      return fail("indexer row %u: kv_len %u is shorter than %u causal compressed entries", r, t->kv_len[r], causal);
+    p->max_kv = std::max<uint64_t>(p->max_kv, t->kv_len[r]);
+    p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + query_len);
+    p->blk_begin[r + 1] = p->blk_begin[r] + div_up(t->kv_len[r], kMqKeysPerBlock);
+  }
+  for (uint32_t r = t->rows; r < ds::kRowsMax; ++r) p->blk_begin[r + 1] = p->blk_begin[r];
+  return DS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ds_rows_indexer_mq_scores_elems(const ds_indexer_rows *rows, uint32_t query_len) {
+  MqPlan p;
+  if (check_mq(rows, query_len, &p) != DS_OK) return 0;
+  return static_cast<size_t>(uint64_t(p.rows) * query_len * p.max_kv);
+}
+
+ds_status ds_rows_indexer_score_mq(const ds_indexer_rows *rows, uint32_t query_len, const void *q, size_t q_elems,
+                                   const float *weights, size_t weights_elems, float *scores, size_t scores_elems,
+                                   void *stream) {
+  MqPlan p;
+  DS_TRY(check_mq(rows, query_len, &p));
+  DS_TRY(need(q, "indexer q"));
+  DS_TRY(need(weights, "indexer weights"));
+  DS_TRY(need(scores, "indexer scores"));
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    if (!rows->keys[r]) return fail("indexer row %u: keys must not be null", r);
+    DS_TRY(cap(rows->keys_elems[r], uint64_t(rows->kv_len[r]) * DS_INDEXER_DIM, "indexer kv", "elements"));
+  }
+  DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_INDEXER_DIM, "indexer q", "elements"));
+  DS_TRY(cap(weights_elems, p.q_rows * DS_HEADS, "indexer weights", "elements"));
+  DS_TRY(cap(scores_elems, uint64_t(p.rows) * query_len * p.max_kv, "indexer scores", "elements"));
+
+  ds::IndexerMqArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.w = weights;
+  a.scores = scores;
+  a.score_stride = p.max_kv;
+  a.rows = p.rows;
+  a.query_len = query_len;
+  a.keys_per_block = kMqKeysPerBlock;
+  for (uint32_t r = 0; r <= ds::kRowsMax; ++r) a.blk_begin[r] = p.blk_begin[r];
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    a.keys[r] = static_cast<const uint16_t *>(rows->keys[r]);
+    a.kv_len[r] = rows->kv_len[r];
+    a.q_row[r] = rows->q_row[r];
+    for (uint32_t t = 0; t < query_len; ++t)
+      a.visible[r * ds::kMqMaxQueries + t] = std::min<uint32_t>(rows->kv_len[r], (rows->start_pos[r] + t + 1) / DS_RATIO);
+  }
+  const hipError_t e = ds::launch_indexer_mq(a, p.blk_begin[ds::kRowsMax], static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DS_OK : hip_fail(e, "multi-query indexer launch");
+}
+
+}  // extern "C"

@@ -154,6 +154,29 @@ hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t blocks, h
 hipError_t launch_attn_combine(const AttnArgs &a, uint32_t blocks, hipStream_t s);
 
 
+// ---------------------------------------------------------- multi-query indexer
+// query_len (1..8) consecutive queries per row; one workgroup of 4 waves per
+// `keys_per_block` keys (a multiple of 64) of one row; wave w owns queries w
+// and w + 4. Scores of query t of row r at (r * query_len + t) * score_stride.
+constexpr int kMqThreads = 256;
+constexpr int kMqMaxQueries = 8;
+
+struct IndexerMqArgs {
+  const uint16_t *keys[kRowsMax];   // bf16 [kv_len, 128] per row
+  const uint16_t *q;                // bf16 [_, 64, 128]; row r's query t at q_row[r] + t
+  const float *w;                   // f32 [_, 64], same rows
+  float *scores;                    // f32 [rows * query_len, score_stride]
+  uint64_t score_stride;
+  uint32_t rows;
+  uint32_t query_len;
+  uint32_t keys_per_block;
+  uint32_t kv_len[kRowsMax];
+  uint32_t q_row[kRowsMax];
+  uint32_t visible[kRowsMax * kMqMaxQueries];   // [r * 8 + t]: min(kv_len, (start_pos + t + 1) / 4)
+  uint32_t blk_begin[kRowsMax + 1];
+};
+hipError_t launch_indexer_mq(const IndexerMqArgs &a, uint32_t blocks, hipStream_t s);
+
 // -------------------------------------------------------------- compressor
 // One decode token of the learned KV compressor per row; one workgroup per
 // row (256 threads for ratio 4, 1024 for ratio 128).

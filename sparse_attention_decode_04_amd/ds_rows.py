@@ -28,6 +28,7 @@ FUNCTIONS = (
     "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn", "ds_rows_sparse_attn_direct",
     "ds_rows_last_error", "ds_rows_version", "ds_rows_indexer_topk_workspace_bytes", "ds_rows_indexer_topk",
     "ds_rows_indexer_candidates", "ds_rows_compressor_state_elems", "ds_rows_compressor",
+    "ds_rows_indexer_mq_scores_elems", "ds_rows_indexer_score_mq",
 )
 
 
@@ -111,6 +112,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     lib.ds_rows_indexer_candidates.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                                c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_indexer_mq_scores_elems.argtypes = [P(IndexerRows), c_uint32]
+    lib.ds_rows_indexer_mq_scores_elems.restype = c_size_t
+    lib.ds_rows_indexer_score_mq.argtypes = [P(IndexerRows), c_uint32, c_void_p, c_size_t, c_void_p, c_size_t,
+                                             c_void_p, c_size_t, c_void_p]
     lib.ds_rows_compressor_state_elems.argtypes = [c_uint32, c_uint32]
     lib.ds_rows_compressor_state_elems.restype = c_size_t
     lib.ds_rows_compressor.argtypes = [P(CompressorRows), c_uint32, c_uint32, c_float,
@@ -118,7 +123,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn",
               "ds_rows_sparse_attn_direct", "ds_rows_indexer_topk", "ds_rows_indexer_candidates",
-              "ds_rows_compressor"):
+              "ds_rows_compressor", "ds_rows_indexer_score_mq"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
@@ -313,6 +318,18 @@ def sparse_attn_direct(t: SparseRows, q, sinks, indices, scale, workspace, out, 
     oa, on = _dev(out, 4)
     _check(load().ds_rows_sparse_attn_direct(ctypes.byref(t), qa, qn, sa, sn, ia, inn, float(scale),
                                              wa, wb, oa, on, _stream(stream)))
+
+
+def indexer_mq_scores_elems(t: IndexerRows, query_len: int) -> int:
+    return load().ds_rows_indexer_mq_scores_elems(ctypes.byref(t), int(query_len))
+
+
+def indexer_score_mq(t: IndexerRows, query_len, q, weights, scores, stream=None):
+    qa, qn = _dev(q, 2)
+    wa, wn = _dev(weights, 4)
+    sa, sn = _dev(scores, 4)
+    _check(load().ds_rows_indexer_score_mq(ctypes.byref(t), int(query_len), qa, qn, wa, wn, sa, sn,
+                                           _stream(stream)))
 
 
 def compressor_state_elems(ratio: int, head_dim: int) -> int:

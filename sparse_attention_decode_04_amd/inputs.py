@@ -224,7 +224,8 @@ def compressor_workload(ratio: int, head_dim: int) -> CompressorInputs:
 # Row r's Q queries are q/weights rows r*Q .. r*Q + Q - 1 ([R*Q, 64, 128]
 # bf16 and [R*Q, 64] f32), integer-valued as in the single-query workloads;
 # keys [n_r, 128] per row. Query t of row r sits at position start_pos + t;
-# start_pos defaults to 4 * n_r - Q, so the last query sees every key.
+# start_pos defaults to max(0, 4 * n_r - Q), so the last query sees every key
+# (rows of fewer than Q / 4 keys need Q <= 4 * n_r).
 # Generation order: rng = Generator(PCG64(seed)) -> q -> weights -> keys per row.
 
 MQ_SEED_BASE = 20262000
@@ -253,7 +254,7 @@ def make_mq(seed: int, kv_len: list[int], query_len: int, ternary: bool = False,
     idx_w = rng.integers(-2, 2, size=(R * Q, HEADS), endpoint=True).astype(np.float32)
     idx_keys = [_int_rows(rng, n, INDEXER_DIM, lo, hi) for n in kv_len]
     if start_pos is None:
-        start_pos = [RATIO * n - Q for n in kv_len]
+        start_pos = [max(0, RATIO * n - Q) for n in kv_len]
     return MultiQueryInputs(Q, list(kv_len), list(start_pos), idx_q, idx_w, idx_keys)
 
 

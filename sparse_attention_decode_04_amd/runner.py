@@ -167,3 +167,33 @@ class DeviceCompressor:
         kvs, scs = self.states[copy]
         out = self.out.cpu().numpy().view(np.uint16)
         return ([k.cpu().numpy() for k in kvs], [s.cpu().numpy() for s in scs], [out[i] for i in range(len(self.rows))])
+
+
+class DeviceMultiQuery:
+    """A multi-query indexer workload (MultiQueryInputs from inputs.py) on the
+    current HIP device: keys, queries, weights and the scores buffer
+    [rows * query_len, max kv_len]. `rows` selects a subset (each keeps its
+    own queries)."""
+
+    def __init__(self, inp, device="cuda", rows=None):
+        self.inp = inp
+        self.rows = list(range(inp.rows)) if rows is None else list(rows)
+        Q = inp.query_len
+        self.q = to_device(inp.idx_q, device)
+        self.w = to_device(inp.idx_w, device)
+        self.keys = [to_device(inp.idx_keys[r], device) for r in self.rows]
+        kv = [inp.kv_len[r] for r in self.rows]
+        self.table = ds.indexer_rows(kv, [inp.start_pos[r] for r in self.rows], [0] * len(self.rows),
+                                     [Q * r for r in self.rows], [TOP_K * i for i in range(len(self.rows))],
+                                     keys=self.keys)
+        self.scores = torch.empty(ds.indexer_mq_scores_elems(self.table, Q), dtype=torch.float32, device=device)
+
+    def run(self, stream=None):
+        ds.indexer_score_mq(self.table, self.inp.query_len, self.q, self.w, self.scores, stream)
+
+    def results(self):
+        """scores[i][t] = float32 [kv_len] of selected row i, query t."""
+        torch.cuda.synchronize()
+        Q = self.inp.query_len
+        s = self.scores.cpu().numpy().reshape(len(self.rows) * Q, -1)
+        return [[s[i * Q + t, : self.inp.kv_len[r]] for t in range(Q)] for i, r in enumerate(self.rows)]

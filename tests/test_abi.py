@@ -44,7 +44,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert set(names) == set(ds.FUNCTIONS)
     out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (ds_rows_\w+)", out))
@@ -330,3 +330,29 @@ def test_compressor_checks(lib):
     expect_invalid(call_comp(lib, t2, outp=None), "output must not be null")
     t3 = ctab((127,), ratio=128, head_dim=512)
     expect_invalid(call_comp(lib, t3, ratio=128, head_dim=512, ape=128 * 512 - 1), "ape holds")
+
+
+# ------------------------------------------------------- multi-query indexer
+
+def call_mq(lib, t, Q, q=BIG, w=BIG, s=BIG):
+    return lib.ds_rows_indexer_score_mq(ctypes.byref(t), Q, FAKE, q, FAKE, w, FAKE, s, None)
+
+
+def test_mq_sizes_and_checks(lib):
+    t = itab((100, 50), start_pos=[4 * 100 - 8, 4 * 50 - 8], q_row=[3, 0])
+    assert ds.indexer_mq_scores_elems(t, 8) == 2 * 8 * 100
+    assert ds.indexer_mq_scores_elems(t, 9) == 0
+    assert "query_len must be 1..=8, got 9" in ds.last_error()
+    expect_invalid(call_mq(lib, t, 0), "query_len must be 1..=8, got 0")
+    # the last query (start_pos + 7) must still fit the cache
+    expect_invalid(call_mq(lib, itab((100,), start_pos=[4 * 100 - 4]), 8),
+                   "kv_len 100 is shorter than 101 causal compressed entries")
+    expect_invalid(call_mq(lib, itab((100,), start_pos=[0xFFFFFFFF - 3]), 4), "indexer position overflows")
+    # queries q_row .. q_row + 7: max q_row 3 -> 11 query rows
+    expect_invalid(call_mq(lib, t, 8, q=11 * 64 * 128 - 1), "indexer q holds")
+    expect_invalid(call_mq(lib, t, 8, w=11 * 64 - 1), "indexer weights holds")
+    expect_invalid(call_mq(lib, t, 8, s=2 * 8 * 100 - 1), "indexer scores holds")
+    expect_invalid(call_mq(lib, itab((100,), start_pos=[392], keys_elems=[100 * 128 - 1]), 8), "indexer kv holds")
+    # overlapping output offsets do not matter to the scores
+    u = itab((10, 10), start_pos=[32, 32], out_off=[0, 0])
+    expect_invalid(call_mq(lib, u, 8, s=2 * 8 * 10 - 1), "indexer scores holds")
