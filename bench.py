@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--copies", type=int, default=8)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--leg", choices=("all", "multi_query", "compressor"), default="all",
+                   help="run only the multi-query indexer or the compressor leg and print its JSON object")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 64 MiB device-to-device copy 5 times (reference for the "
                         "FETCH_SIZE / WRITE_SIZE counter scale) and exit")
@@ -262,6 +264,12 @@ def main():
     from sparse_attention_decode_04_amd.runner import DeviceInputs, DeviceRows
 
     ds.load()
+    if args.leg == "multi_query":
+        print(json.dumps(mq_bench(torch, args.steps)), flush=True)
+        return
+    if args.leg == "compressor":
+        print(json.dumps(compressor_bench(torch, args.steps)), flush=True)
+        return
     inp = I.make_config(args.config)
     base = DeviceInputs(inp)
     copies = [base]

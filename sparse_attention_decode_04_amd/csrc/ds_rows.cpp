@@ -605,7 +605,7 @@ ds_status ds_rows_compressor(const ds_compressor_rows *rows, uint32_t ratio, uin
 // ------------------------------------------------------- multi-query indexer
 namespace {
 
-constexpr uint32_t kMqKeysPerBlock = 512;
+constexpr uint32_t kMqKeysPerBlock = 1024;
 
 struct MqPlan {
   uint32_t rows = 0;

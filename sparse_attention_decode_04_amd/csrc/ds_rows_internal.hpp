@@ -155,10 +155,9 @@ hipError_t launch_attn_combine(const AttnArgs &a, uint32_t blocks, hipStream_t s
 
 
 // ---------------------------------------------------------- multi-query indexer
-// query_len (1..8) consecutive queries per row; one workgroup of 4 waves per
-// `keys_per_block` keys (a multiple of 64) of one row; wave w owns queries w
-// and w + 4. Scores of query t of row r at (r * query_len + t) * score_stride.
-constexpr int kMqThreads = 256;
+// query_len (1..8) consecutive queries per row; one workgroup of 8 waves per
+// `keys_per_block` keys (a multiple of 64) of one row; wave w owns query w. Scores of query t of row r at
+// (r * query_len + t) * score_stride.
 constexpr int kMqMaxQueries = 8;
 
 struct IndexerMqArgs {

@@ -13,37 +13,64 @@
 // With Q queries per row a key is used Q times, so at Q = 8 the contraction
 // does 512 flops per key byte and the MFMA units, not HBM, set the pace.
 // Mapping:
-//   * Workgroup of 4 waves per `keys_per_block` keys of one row. Wave w owns
-//     queries w and w + 4: their 64x128 bf16 query fragments stay in VGPRs
-//     (64 per query), with the head weights of the D rows each lane holds.
-//   * Keys stream through LDS in chunks of 64 (16 KiB), two chunks resident:
-//     every thread loads its 64 bytes of chunk c + 1 into registers while the
-//     waves compute chunk c, then stores them. In LDS the sixteen 16-byte
+//   * Workgroup of 8 waves per `keys_per_block` keys of one row; wave w owns
+//     query w (waves past query_len only help stage the keys): its 64x128
+//     bf16 query fragments stay in 64 VGPRs, with the head weights of the D
+//     rows each lane holds.
+//   * Keys stream through LDS in chunks of 64 (16 KiB), two chunks resident.
+//     Each thread's pieces of chunk c + 1 are loaded into registers while
+//     chunk c is computed and stored to LDS at the end of the iteration
+//     (deeper register prefetch measured no faster: the compiler then drains
+//     the loads while rotating the staging registers).
+//     Within a chunk all 64 MFMAs of the four 16-key tiles are issued before
+//     the epilogues read their results. In LDS the sixteen 16-byte
 //     pieces of key row k are permuted (piece j at slot j ^ (k mod 16)), so
 //     the MFMA operand reads of 16 consecutive keys hit 16 different slots.
 //   * MFMA 16x16x32 with M = 16 heads, N = 16 keys, K = 32 features: lane l
 //     takes key l%16 and the 64-byte span [64*(l/16), +64) of its row, step c
 //     the 16 bytes at 16c of it; the query fragments use the same feature
-//     assignment. ReLU and head weights are applied in registers and two
-//     cross-lane adds finish the head sum: the per-key arithmetic is that of
-//     the single-query indexer, so query_len = 1 gives its bits.
+//     assignment. ReLU and head weights are applied in registers; after the
+//     chunk's four tiles, two lane-row swaps (v_permlane16_swap,
+//     v_permlane32_swap) finish the head sums of all four at once, leaving
+//     lane l with key l of the chunk, so the scores go out as one 256-byte
+//     store per wave. The additions keep the single-query indexer's order,
+//     so query_len = 1 gives its bits.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 
 namespace ds {
 
-constexpr int kMqWaves = kMqThreads / 64;
 constexpr int kMqChunk = 64;                        // keys per LDS chunk
 constexpr int kMqChunkBytes = kMqChunk * kIdxDim * 2;
-constexpr int kMqPieces = kMqChunkBytes / 16 / kMqThreads;   // 16-byte pieces per thread per chunk
+constexpr int kMqDepth = 1;                         // chunks in flight ahead of the one computed
 
 __device__ __forceinline__ uint32_t mq_lds_offset(uint32_t key_local, uint32_t piece) {
   return key_local * (kIdxDim * 2) + ((piece ^ (key_local & 15u)) << 4);
 }
 
-// kQw: queries per wave (1 for query_len <= 4, 2 up to 8).
-template <int kQw>
-__global__ __launch_bounds__(kMqThreads) void indexer_mq_kernel(IndexerMqArgs a) {
+// Lane rows of 16 (rows 0..3 of the wave). With x and y per lane:
+// swap_rows16_sum returns, in even rows, x(row) + x(row + 1) and in odd rows
+// y(row - 1) + y(row) (v_permlane16_swap exchanges the odd rows of its first
+// operand with the even rows of its second).
+__device__ __forceinline__ float swap_rows16_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Halves of 32 lanes: returns, in the low half, x(l) + x(l + 32) and in the
+// high half y(l - 32) + y(l) (v_permlane32_swap exchanges the high half of its
+// first operand with the low half of its second).
+__device__ __forceinline__ float swap_halves_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// kWaves waves per workgroup; wave w owns query w (waves past query_len only
+// stage keys).
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kPieces = kMqChunkBytes / 16 / kThreads;   // 16-byte pieces per thread per chunk
+  constexpr int kTiles = kMqChunk / 16;
   __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][kMqChunkBytes];   // 32 KiB
 
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
@@ -63,94 +90,130 @@ __global__ __launch_bounds__(kMqThreads) void indexer_mq_kernel(IndexerMqArgs a)
   // Staging: piece p = tid + threads * u of a chunk is key p / 16, 16-byte
   // piece p % 16 of its row. Keys past the row's end are clamped (loaded,
   // never stored as scores).
-  u32x4 st[kMqPieces];
-  auto load_chunk = [&](uint32_t c) {
+  // Chunk c's pieces sit in staging set c % kMqDepth from their load, issued
+  // kMqDepth chunks ahead, until they are stored to LDS slot c % 2 at the end
+  // of the iteration before c (kMqDepth = 1: one set, one chunk ahead).
+  u32x4 st[kMqDepth][kPieces];
+  auto load_chunk = [&](uint32_t c, u32x4 (&set)[kPieces]) {
 #pragma unroll
-    for (int u = 0; u < kMqPieces; ++u) {
-      const uint32_t p = tid + kMqThreads * u;
+    for (int u = 0; u < kPieces; ++u) {
+      const uint32_t p = tid + kThreads * u;
       const uint32_t key = min(k0 + kMqChunk * c + (p >> 4), n - 1);
-      st[u] = load16(keys + static_cast<uint64_t>(key) * kIdxDim + 8 * (p & 15u));
+      set[u] = load16(keys + static_cast<uint64_t>(key) * kIdxDim + 8 * (p & 15u));
     }
   };
-  auto store_chunk = [&](int slot) {
+  auto store_chunk = [&](int slot, const u32x4 (&set)[kPieces]) {
 #pragma unroll
-    for (int u = 0; u < kMqPieces; ++u) {
-      const uint32_t p = tid + kMqThreads * u;
-      *reinterpret_cast<u32x4 *>(&kbuf[slot][mq_lds_offset(p >> 4, p & 15u)]) = st[u];
+    for (int u = 0; u < kPieces; ++u) {
+      const uint32_t p = tid + kThreads * u;
+      *reinterpret_cast<u32x4 *>(&kbuf[slot][mq_lds_offset(p >> 4, p & 15u)]) = set[u];
     }
   };
-  load_chunk(0);
+#pragma unroll
+  for (int d = 0; d < kMqDepth; ++d) load_chunk(min(static_cast<uint32_t>(d), chunks - 1), st[d]);
 
-  // This wave's queries, their fragments (head 16m + col, features
-  // [32*grp + 8c, +8)) and the head weights of the D rows of this lane.
-  bf16x8 qa[kQw][4][4];
-  float wt[kQw][4][4];
-  bool live[kQw];
-  uint32_t vis[kQw];
-  float *srow[kQw];
-#pragma unroll
-  for (int k = 0; k < kQw; ++k) {
-    const uint32_t t = wave + kMqWaves * k;
-    live[k] = t < Q;
-    const uint32_t tq = live[k] ? t : 0;
-    const uint64_t qrow = static_cast<uint64_t>(a.q_row[r]) + tq;
+  // This wave's query: its fragments (head 16m + col, features
+  // [32*grp + 8s, +8)) and the head weights of the D rows of this lane.
+  const bool live = wave < Q;   // wave-uniform
+  const uint32_t t = live ? wave : 0;
+  const uint64_t qrow = static_cast<uint64_t>(a.q_row[r]) + t;
+  bf16x8 qa[4][4];
+  float wt[4][4];
+  {
     const uint16_t *q = a.q + qrow * kHeads * kIdxDim;
     const float *w = a.w + qrow * kHeads;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qa[k][m][c] = as_bf16x8(load16(q + (16 * m + col) * kIdxDim + 32 * grp + 8 * c));
+      for (int s = 0; s < 4; ++s) qa[m][s] = as_bf16x8(load16(q + (16 * m + col) * kIdxDim + 32 * grp + 8 * s));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wt[k][m][i] = w[16 * m + 4 * grp + i];
+      for (int i = 0; i < 4; ++i) wt[m][i] = w[16 * m + 4 * grp + i];
     }
-    vis[k] = a.visible[r * kRowsMax + tq];
-    srow[k] = a.scores + (static_cast<uint64_t>(r) * Q + tq) * a.score_stride;
   }
-  store_chunk(0);
+  const uint32_t vis = a.visible[r * kRowsMax + t];
+  float *srow = a.scores + (static_cast<uint64_t>(r) * Q + t) * a.score_stride;
+  // Every load issued so far (the query, weights and first chunks) has
+  // landed: without this wait the compiler, unsure whether the query's
+  // loads are done when the loop starts, would wait for the in-flight
+  // chunks inside every iteration.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  store_chunk(0, st[0]);
   __syncthreads();
 
-  for (uint32_t c = 0; c < chunks; ++c) {
+  for (uint32_t c0 = 0; c0 < chunks; c0 += kMqDepth) {
+#pragma unroll
+   for (int u = 0; u < kMqDepth; ++u) {
+    const uint32_t c = c0 + u;
+    if (c >= chunks) break;   // uniform
     const int slot = c & 1;
-    load_chunk(min(c + 1, chunks - 1));   // next chunk in flight (the last is loaded again, unused)
-    const unsigned char *kb = kbuf[slot];
+    // Set u (chunk c) is in LDS already: refill it with chunk c + depth
+    // (past the end, the last chunk again, unused).
+    load_chunk(min(c + kMqDepth, chunks - 1), st[u]);
+    if (live) {
+      const unsigned char *kb = kbuf[slot];
+      // Tile kt: B operand (key 16kt + col, pieces 4*grp + s), read one tile
+      // ahead of its products; the four head tiles' accumulators are issued
+      // step by step so that their chains interleave.
+      auto read_b = [&](int kt, bf16x8 (&b)[4]) {
+        const uint32_t kl = 16 * kt + col;
 #pragma unroll
-    for (int kt = 0; kt < kMqChunk / 16; ++kt) {
-      // B operand of the tile's 16 keys: key 16kt + col, pieces 4*grp + s.
-      bf16x8 b[4];
-      const uint32_t kl = 16 * kt + col;
+        for (int s = 0; s < 4; ++s) b[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + mq_lds_offset(kl, 4 * grp + s)));
+      };
+      auto products = [&](const bf16x8 (&b)[4], f32x4 (&acc)[4]) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + mq_lds_offset(kl, 4 * grp + s)));
-      const uint32_t key = k0 + kMqChunk * c + kl;
+        for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < kQw; ++k) {
-        if (!live[k]) continue;   // wave-uniform
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[m] = mfma16(qa[m][s], b[s], acc[m]);
+        }
+      };
+      // part[kt]: this lane's head-group sum for key 16kt + col.
+      auto epilogue = [&](const f32x4 (&acc)[4]) {
         float part = 0.0f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mfma16(qa[k][m][s], b[s], acc);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) part = fmaf(fmaxf(acc[j], 0.0f), wt[k][m][j], part);
+          for (int j = 0; j < 4; ++j) part = fmaf(fmaxf(acc[m][j], 0.0f), wt[m][j], part);
         }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        if (grp == 0 && key < k_end)
-          srow[k][key] = (key < vis[k] && __builtin_isfinite(part)) ? part : -__builtin_inff();
-      }
+        return part;
+      };
+      // All four tiles' products first (B read one tile ahead), then the
+      // epilogues: every MFMA result is long complete when it is read.
+      bf16x8 b0[4], b1[4];
+      f32x4 acc[kTiles][4];
+      float part[kTiles];
+      read_b(0, b0);
+      read_b(1, b1);
+      products(b0, acc[0]);
+      read_b(2, b0);
+      products(b1, acc[1]);
+      read_b(3, b1);
+      products(b0, acc[2]);
+      products(b1, acc[3]);
+#pragma unroll
+      for (int kt = 0; kt < kTiles; ++kt) part[kt] = epilogue(acc[kt]);
+      // Head sums of the chunk's four tiles at once: lane row g (16 lanes)
+      // holds the partial of head group g for every tile; two swaps of lane
+      // rows leave lane row g with the full sum of tile g, added in the order
+      // (g0 + g1) + (g2 + g3) of the single-query indexer. Lane l then holds
+      // key 64c + l of the chunk.
+      const float t01 = swap_rows16_sum(part[0], part[1]);   // even rows: tile 0, odd rows: tile 1
+      const float t23 = swap_rows16_sum(part[2], part[3]);   // even rows: tile 2, odd rows: tile 3
+      const float sum = swap_halves_sum(t01, t23);            // lane row g: tile g
+      const uint32_t key = k0 + kMqChunk * c + lane;
+      if (key < k_end) srow[key] = (key < vis && __builtin_isfinite(sum)) ? sum : -__builtin_inff();
     }
     // The other slot was last read in the previous iteration, before its
     // closing barrier; the barrier below publishes the next chunk.
-    store_chunk(slot ^ 1);
+    store_chunk(slot ^ 1, st[(u + 1) % kMqDepth]);
     __syncthreads();
+   }
   }
 }
 
 hipError_t launch_indexer_mq(const IndexerMqArgs &a, uint32_t blocks, hipStream_t s) {
-  if (a.query_len <= kMqWaves)
-    hipLaunchKernelGGL(indexer_mq_kernel<1>, dim3(blocks), dim3(kMqThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(indexer_mq_kernel<2>, dim3(blocks), dim3(kMqThreads), 0, s, a);
+  hipLaunchKernelGGL(indexer_mq_kernel<kMqMaxQueries>, dim3(blocks), dim3(64 * kMqMaxQueries), 0, s, a);
   return hipGetLastError();
 }
 
