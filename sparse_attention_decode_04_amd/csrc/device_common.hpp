@@ -47,6 +47,22 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Lane rows of 16 (rows 0..3 of the wave). With x and y per lane:
+// swap_rows16_sum returns, in even rows, x(row) + x(row + 1) and in odd rows
+// y(row - 1) + y(row) (v_permlane16_swap exchanges the odd rows of its first
+// operand with the even rows of its second).
+__device__ __forceinline__ float swap_rows16_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Halves of 32 lanes: returns, in the low half, x(l) + x(l + 32) and in the
+// high half y(l - 32) + y(l) (v_permlane32_swap exchanges the high half of its
+// first operand with the low half of its second).
+__device__ __forceinline__ float swap_halves_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Row of a multi-row launch owning workgroup `b`: the last r with
 // blk_begin[r] <= b. Entries past the last row hold the total block count.
 __device__ __forceinline__ uint32_t row_of_block(const uint32_t *blk_begin, uint32_t b) {

@@ -48,22 +48,6 @@ __device__ __forceinline__ uint32_t mq_lds_offset(uint32_t key_local, uint32_t p
   return key_local * (kIdxDim * 2) + ((piece ^ (key_local & 15u)) << 4);
 }
 
-// Lane rows of 16 (rows 0..3 of the wave). With x and y per lane:
-// swap_rows16_sum returns, in even rows, x(row) + x(row + 1) and in odd rows
-// y(row - 1) + y(row) (v_permlane16_swap exchanges the odd rows of its first
-// operand with the even rows of its second).
-__device__ __forceinline__ float swap_rows16_sum(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Halves of 32 lanes: returns, in the low half, x(l) + x(l + 32) and in the
-// high half y(l - 32) + y(l) (v_permlane32_swap exchanges the high half of its
-// first operand with the low half of its second).
-__device__ __forceinline__ float swap_halves_sum(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // kWaves waves per workgroup; wave w owns query w (waves past query_len only
 // stage keys).
 template <int kWaves>

@@ -16,12 +16,18 @@
 //     16c of that span. The query fragments use the same feature assignment,
 //     so the contraction is unchanged and no key data is shuffled.
 //   * D lane l holds heads 16m + 4*(l/16) + i of key l%16: the ReLU and head
-//     weights are applied in registers, then two cross-lane adds finish the
-//     head sum.
+//     weights are applied in registers; after every 4 tiles two lane-row
+//     swaps (v_permlane16_swap, v_permlane32_swap) finish the four head sums
+//     at once, leaving lane row g with tile g's 16 scores.
 //   * The workgroup stages the 16 KiB query in LDS once; each wave keeps its
 //     copy of the query fragments in 64 VGPRs. Key tiles stream through a
 //     ring of four register buffers, so three tiles (12 KiB) of loads are in
-//     flight per wave while a fourth tile's 16 MFMAs run.
+//     flight per wave while a fourth tile's 16 MFMAs run. A row's 16-key
+//     tiles are dealt round robin over all of its waves (wave w of the row's
+//     workgroup b takes tiles 4b + w, 4b + w + S, ..., S = 4 x the row's
+//     workgroups), so the row's waves read neighbouring tiles at any time
+//     (measured faster than a contiguous 1024-key range per workgroup; deeper
+//     rings, 512-key workgroups and 8-wave workgroups measured slower).
 // The arithmetic per key is a fixed instruction sequence independent of the
 // row count or of other rows, so every row is bitwise identical to a
 // one-row launch.
@@ -29,10 +35,9 @@
 // Fused top-k stage (kFused, for ds_rows_indexer_topk). The pages' first
 // top-k stage sorts every 1024-key block and keeps its best 512
 // (deepseek_indexer_topk_block_rows_i32). Here every wave keeps, from the 256
-// scores it just computed (still in its registers: after the head sum each
-// group of 16 lanes holds the tile's 16 scores, and the group whose number
-// matches the tile's position keeps them), only the keys at or above its
-// 24th best score bits: a bitwise search with ballot counts finds that
+// scores it just computed (still in its registers: after each group of 4
+// tiles every lane holds one score, lane row g that of tile g), only the
+// keys at or above its 24th best score bits: a bitwise search with ballot counts finds that
 // threshold T without LDS or barriers. It writes those keys (at most 32) and
 // the floor T: all of its other keys lie below the key T << 32; the final top-k
 // level uses the floors to prove that no unkept key can reach the row's top
@@ -46,8 +51,13 @@ namespace ds {
 constexpr int kIdxRing = 4;   // tile buffers per wave (kIdxRing - 1 in flight)
 constexpr uint32_t kIdxWaves = kIdxThreads / 64;
 constexpr int kQVec = kHeads * kIdxDim / 8 / kIdxThreads;   // 16-byte query pieces per thread
-// The fused stage keeps one tile in kIdxRing per lane, in a 4-deep queue.
-static_assert(kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile <= 4 * kIdxRing, "tiles per wave");
+// Every lane ends each group of 4 tiles with one score (lane row g: tile
+// 4j + g); the fused stage queues the last four, so a wave takes at most 16
+// tiles, and ring passes cover whole groups.
+static_assert(kIdxRing % 4 == 0, "ring passes hold whole groups of 4 tiles");
+static_assert(kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile <= 16, "tiles per wave");
+static_assert((kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile + kIdxRing - 1) / kIdxRing * (kIdxRing / 4) <= 4,
+              "groups of 4 tiles per wave fit the queue");
 
 // One wave's candidates (fused stage, see above): o[e] are the score bits
 // (0 = not valid) of the lane's kept keys, kidx[e] their key indices.
@@ -101,8 +111,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
   const uint32_t n = a.kv_len[r];
   const uint32_t visible = a.visible[r];
-  const uint32_t k0 = (blockIdx.x - a.blk_begin[r]) * a.keys_per_block;
-  const uint32_t k_end = min(n, k0 + a.keys_per_block);
+  // Tiles of 16 keys are dealt round robin over the row's waves: wave w of
+  // the row's workgroup b takes tiles t0 = 4b + w, t0 + S, t0 + 2S, ...
+  // (S = 4 x the row's workgroups), so at any time the row's waves read
+  // neighbouring tiles.
+  const uint32_t nblk = a.blk_begin[r + 1] - a.blk_begin[r];
+  const uint32_t tstride = kIdxWaves * nblk;
   const uint16_t *__restrict__ keys = a.keys[r];
   const uint16_t *__restrict__ q = a.q + static_cast<uint64_t>(a.q_row[r]) * kHeads * kIdxDim;
   const float *__restrict__ w = a.w + static_cast<uint64_t>(a.q_row[r]) * kHeads;
@@ -122,10 +136,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   for (int i = 0; i < kQVec; ++i) qv[i] = load16(q + 8 * (tid + kIdxThreads * i));
   const float wv = w[tid & (kHeads - 1)];
 
-  const uint32_t tiles = (k_end - k0 + kIdxTile - 1) / kIdxTile;
-  const uint32_t mine = tiles > wave ? (tiles - wave + kIdxWaves - 1) / kIdxWaves : 0;   // tiles wave, wave+W, ...
+  const uint32_t tiles = (n + kIdxTile - 1) / kIdxTile;
+  const uint32_t t0 = kIdxWaves * (blockIdx.x - a.blk_begin[r]) + wave;
+  const uint32_t mine = tiles > t0 ? (tiles - t0 + tstride - 1) / tstride : 0;
+  auto key_of = [&](uint32_t i) { return (t0 + tstride * i) * kIdxTile + col; };
   auto load_tile = [&](uint32_t i, u32x4 (&kb)[4]) {
-    const uint32_t key = min(k0 + (wave + kIdxWaves * i) * kIdxTile + col, n - 1);   // tail: clamp, not stored
+    const uint32_t key = min(key_of(i), n - 1);   // tail: clamp, not stored
     const uint16_t *krow = keys + static_cast<uint64_t>(key) * kIdxDim + 32 * grp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) kb[c] = load16(krow + 8 * c);
@@ -155,50 +171,54 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   }
   if (!kFused && mine == 0) return;   // (in the fused stage every wave writes its floor)
 
-  // Fused stage: the score bits this lane keeps, one per group of kIdxRing
-  // tiles (newest first); tile i0 + u goes to the lanes of group u.
+  // Tiles go in groups of 4: each lane keeps its head group's partial sum of
+  // the group's tiles, then two lane-row swaps finish all four head sums at
+  // once and leave lane row g with tile 4j + g (lane col: key col of it). The
+  // additions are (g0 + g1) + (g2 + g3), the order of a per-tile two-step
+  // cross-lane sum. Fused stage: that score is the one this lane keeps, in
+  // a queue of the wave's last four groups (newest first).
   uint32_t fifo[4] = {0, 0, 0, 0};
   for (uint32_t i0 = 0; i0 < mine; i0 += kIdxRing) {
-    uint32_t captured = 0;
+    float part[4];
 #pragma unroll
     for (int u = 0; u < kIdxRing; ++u) {
       const uint32_t i = i0 + u;
       load_tile(min(i + kIdxRing - 1, last), buf[(u + kIdxRing - 1) % kIdxRing]);
-      float part = 0.0f;
+      float p = 0.0f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc = mfma16(qa[m][c], as_bf16x8(buf[u][c]), acc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) part = fmaf(fmaxf(acc[j], 0.0f), wt[m][j], part);
+        for (int j = 0; j < 4; ++j) p = fmaf(fmaxf(acc[j], 0.0f), wt[m][j], p);
       }
-      // Sum the four 16-head groups held by lanes col, col+16, col+32, col+48.
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      const uint32_t key = k0 + (wave + kIdxWaves * i) * kIdxTile + col;
-      const float v = (key < visible && __builtin_isfinite(part)) ? part : -__builtin_inff();
-      if (i < mine && grp == 0 && key < k_end) scores[key] = v;
-      if constexpr (kFused) {
-        const uint32_t ord = (i < mine && key < k_end) ? static_cast<uint32_t>(topk_key(v, key) >> 32) : 0u;
-        captured = grp == static_cast<uint32_t>(u) ? ord : captured;
+      part[u & 3] = p;
+      if ((u & 3) == 3) {
+        const float t01 = swap_rows16_sum(part[0], part[1]);   // even rows: tile 0, odd rows: tile 1
+        const float t23 = swap_rows16_sum(part[2], part[3]);   // even rows: tile 2, odd rows: tile 3
+        const float sum = swap_halves_sum(t01, t23);            // lane row g: tile g of the group
+        const uint32_t ti = i0 + (u - 3) + grp;
+        const uint32_t key = key_of(ti);
+        const float v = (key < visible && __builtin_isfinite(sum)) ? sum : -__builtin_inff();
+        if (ti < mine && key < n) scores[key] = v;
+        if constexpr (kFused) {
+          fifo[3] = fifo[2];
+          fifo[2] = fifo[1];
+          fifo[1] = fifo[0];
+          fifo[0] = (ti < mine && key < n) ? static_cast<uint32_t>(topk_key(v, key) >> 32) : 0u;
+        }
       }
-    }
-    if constexpr (kFused) {
-      fifo[3] = fifo[2];
-      fifo[2] = fifo[1];
-      fifo[1] = fifo[0];
-      fifo[0] = captured;
     }
   }
   if constexpr (kFused) {
-    // fifo[e] holds tile i = kIdxRing * (groups - 1 - e) + grp.
-    const uint32_t groups = (mine + kIdxRing - 1) / kIdxRing;
+    // fifo[e] holds tile i = 4 * (groups - 1 - e) + grp.
+    const uint32_t groups = (mine + kIdxRing - 1) / kIdxRing * (kIdxRing / 4);
     uint32_t kidx[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t i = kIdxRing * (groups - 1 - e) + grp;   // (unused when groups <= e: fifo[e] is 0)
-      kidx[e] = k0 + (wave + kIdxWaves * i) * kIdxTile + col;
+      const uint32_t i = 4 * (groups - 1 - e) + grp;   // (unused when groups <= e: fifo[e] is 0)
+      kidx[e] = key_of(i);
     }
     wave_candidates(a, fifo, kidx, wave, lane);
   }
