@@ -19,20 +19,21 @@
 // rows G[t] come either from the gathered operand and its mask (after
 // ds_rows_gather) or, in the direct variant, straight from each row's KV
 // through the indices (the gather fused in).
-//   phase 1, per (row, 64-slot chunk c), 8 waves: the query (64 KiB) and
-//     the chunk's rows (64 KiB) are loaded once each, into LDS; the logits
-//     on MFMA 32x32x16 (M = 32 heads, N = 32 slots, K = 16 features), four
-//     waves each taking one 32x32 tile over all 512 features. Per head: the
-//     chunk max m_c, p~ = exp(l - m_c) as a bf16 pair
-//     (hi = bf16(p~), lo = bf16(p~ - hi): ~16 significant bits) and
-//     s_c = sum p~. Then the chunk's output O_c = p~ . G_c (64 heads x 512
-//     features, f32) on MFMA 16x16x32 (M = 16 heads, N = 16 features,
-//     K = 32 slots), each wave owning 64 features. The chunk's rows stay in
-//     LDS as loaded (slot-major); the B operand, 8 consecutive slots of one
-//     feature per lane, comes from two transposing LDS reads
-//     (ds_read_b64_tr_b16: within each 16-lane group, lane i receives the
-//     i-th 16-bit element of the 8-byte pieces that lanes 4k + i/4 address,
-//     k = 0..3).
+//   phase 1, per (row, 64-slot chunk c, group of 16 heads), 8 waves: the
+//     group's query heads (16 KiB) and the chunk's rows (64 KiB) are loaded
+//     once each, into LDS (the four head groups of a chunk run on one XCD
+//     and share the rows through its L2); the logits on MFMA 16x16x32
+//     (M = 16 heads, N = 16 slots, K = 32 features; eight waves, each one
+//     slot tile and half the features). Per head: the chunk max m_c,
+//     p~ = exp(l - m_c) as a bf16 pair (hi = bf16(p~), lo = bf16(p~ - hi):
+//     ~16 significant bits) and s_c = sum p~. Then the chunk's output
+//     O_c = p~ . G_c (16 heads x 512 features, f32) on MFMA 16x16x32
+//     (M = 16 heads, N = 16 features, K = 32 slots), each wave owning 64
+//     features. The chunk's rows stay in LDS as loaded (slot-major); the B
+//     operand, 8 consecutive slots of one feature per lane, comes from two
+//     transposing LDS reads (ds_read_b64_tr_b16: within each 16-lane group,
+//     lane i receives the i-th 16-bit element of the 8-byte pieces that
+//     lanes 4k + i/4 address, k = 0..3).
 //   phase 2, per (row, 32-feature chunk), 4 waves: m, Z and the bad flag of
 //     each head from the chunk statistics and the sink, then
 //     out = sum_c e^(m_c - m) O_c / Z in a fixed chunk order.
@@ -75,57 +76,54 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
 }
 
 constexpr int kChunkThreads = 512;              // 8 waves
+constexpr int kHg = kHeads / kAttnHeadGroups;   // heads per phase-1 workgroup (16)
 constexpr int kRowStride = kDim + 8;            // bf16 per LDS row of q and of the chunk's rows: 1040 B
 constexpr int kRedStride = kAttnChunk + 1;      // padded f32 row of the logits
 constexpr int kPStride = kAttnChunk + 8;        // bf16 per LDS head row of p~: 144 B
 constexpr int kCombineThreads = 256;
-// LDS of phase 1: the chunk's rows, and one region that holds the query
-// during the logits and then the logits and p~.
-constexpr int kVtBytes = kAttnChunk * kRowStride * 2;                  // 66,560
-constexpr int kQBytes = kHeads * kRowStride * 2;                       // 66,560
-constexpr int kRedBytes = kHeads * kRedStride * 4;                     // 16,640
-constexpr int kPBytes = kHeads * kPStride * 2;                         // 9,216
-static_assert(kRedBytes + 2 * kPBytes <= kQBytes, "logits and p~ fit over the query");
+static_assert(kHg == 16, "one MFMA row tile of heads per workgroup");
 
 // ---------------------------------------------------------------- phase 1
 template <bool kDirect>
 __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kVtBytes / 2];   // the chunk's rows, slot-major
-  __shared__ __attribute__((aligned(16))) unsigned char ureg[kQBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kAttnChunk * kRowStride];   // the chunk's rows, slot-major
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kHg * kRowStride];       // this group's query heads
+  __shared__ float red[2 * kHg * kRedStride];                                      // logits, one plane per K half
+  __shared__ __attribute__((aligned(16))) uint16_t phi[kHg * kPStride];            // p~ hi
+  __shared__ __attribute__((aligned(16))) uint16_t plo[kHg * kPStride];            // p~ lo
   __shared__ uint32_t state[kAttnChunk];
-  uint16_t *q_lds = reinterpret_cast<uint16_t *>(ureg);                  // query [64][kRowStride]
-  float *red = reinterpret_cast<float *>(ureg);                          // logits [64][kRedStride]
-  uint16_t *phi = reinterpret_cast<uint16_t *>(ureg + kRedBytes);        // p~ hi [64][kPStride]
-  uint16_t *plo = reinterpret_cast<uint16_t *>(ureg + kRedBytes + kPBytes);
 
   // Row r runs on XCD r (consecutive workgroups go to consecutive XCDs), so
-  // all chunks of a row share one L2.
+  // the head groups and chunks of a row share one L2: the four head groups
+  // of a chunk read the same selected rows.
   const uint32_t r = blockIdx.x % kXcds;
-  const uint32_t c = blockIdx.x / kXcds;
+  const uint32_t rest = blockIdx.x / kXcds;
+  const uint32_t hg = rest % kAttnHeadGroups;
+  const uint32_t c = rest / kAttnHeadGroups;
   if (r >= a.rows || c >= a.chunks[r]) return;
   const uint32_t width = a.width[r];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const uint32_t wave = tid >> 6;
 
-  // Loads: thread t moves features 64 (t % 8) .. +64 of slot t / 8 and of
-  // head t / 8 of the query, each byte once. They are unconditional (a slot
-  // past the width reads the row's last slot, a sentinel or bad index reads
-  // KV row 0) and masked afterwards, so they are all in flight at once. The
-  // slot's index (or mask entry) goes first: the KV row load depends on it,
-  // and loads complete in issue order.
-  const uint32_t sl = tid >> 3;            // slot within the chunk (and query head)
-  const uint32_t fp = 64 * (tid & 7);      // this thread's 64 features
+  // Loads: thread t moves features 64 (t % 8) .. +64 of slot t / 8, and
+  // features 16 (t % 32) .. +16 of query head t / 32 of the group, each byte
+  // once. They are unconditional (a slot past the width reads the row's last
+  // slot, a sentinel or bad index reads KV row 0) and masked afterwards, so
+  // they are all in flight at once. The slot's index (or mask entry) goes
+  // first: the KV row load depends on it, and loads complete in issue order.
+  const uint32_t sl = tid >> 3;            // slot within the chunk
+  const uint32_t fp = 64 * (tid & 7);      // this thread's 64 features of it
   const uint32_t slot = c * kAttnChunk + sl;
   const uint32_t cslot = min(slot, width - 1);
   int32_t raw_index = 0;
   uint16_t raw_mask = 0;
   if (kDirect) raw_index = a.indices[a.index_offset[r] + cslot];
   else raw_mask = a.mask[a.slot_base[r] + cslot];
-  const uint16_t *qrow = a.q + (static_cast<uint64_t>(a.q_row[r]) * kHeads + sl) * kDim + fp;
-  u32x4 qv[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) qv[s] = load16(qrow + 8 * s);
+  const uint32_t qh = tid >> 5;            // query head within the group (and the softmax head)
+  const uint32_t qf = 16 * (tid & 31);
+  const uint16_t *qrow = a.q + (static_cast<uint64_t>(a.q_row[r]) * kHeads + kHg * hg + qh) * kDim + qf;
+  const u32x4 qv0 = load16(qrow), qv1 = load16(qrow + 8);
   uint32_t st;
   const uint16_t *src;
   if (kDirect) {
@@ -138,20 +136,19 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
     src = a.gathered + (a.slot_base[r] + cslot) * kDim;
   }
   const bool use = kDirect ? st == kLive : slot < width;
-  // The sink of head t / 8 (the epilogue's head), stored with the chunk
-  // statistics so that phase 2 gets it in the same load.
-  const float sink_h = a.sinks[tid >> 3];
+  // The sink of the softmax head, stored with the chunk statistics so that
+  // phase 2 gets it in the same load.
+  const float sink_h = a.sinks[kHg * hg + qh];
   u32x4 gb[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) gb[s] = load16(src + fp + 8 * s);
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     if (!use) gb[s] = u32x4{0, 0, 0, 0};
+  *reinterpret_cast<u32x4 *>(&q_lds[qh * kRowStride + qf]) = qv0;
+  *reinterpret_cast<u32x4 *>(&q_lds[qh * kRowStride + qf + 8]) = qv1;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    *reinterpret_cast<u32x4 *>(&q_lds[sl * kRowStride + fp + 8 * s]) = qv[s];
-    *reinterpret_cast<u32x4 *>(&vt[sl * kRowStride + fp + 8 * s]) = gb[s];
-  }
+  for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(&vt[sl * kRowStride + fp + 8 * s]) = gb[s];
   if (kDirect) {
     // Gather semantics: a non-finite element makes the row invalid. The eight
     // threads of a slot are eight consecutive lanes.
@@ -168,89 +165,84 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
   if ((tid & 7) == 0) state[sl] = st;
   __syncthreads();
 
-  // Logits on MFMA 32x32x16, full K = 512 per tile: waves 0..3 take the tiles
-  // (heads 32 (w % 2) .., slots 32 (w / 2) ..); operands from LDS, lane l
-  // reading row l % 32 at features 16 j + 8 (l / 32) in step j.
-  f32x16 acc = {};
-  const uint32_t col = lane & 31;
-  const uint32_t g = lane >> 5;
-  const uint32_t th = 32 * (wave & 1), ts = 32 * ((wave >> 1) & 1);
-  if (wave < 4) {
-    const uint16_t *qa = &q_lds[(th + col) * kRowStride + 8 * g];
-    const uint16_t *kb = &vt[(ts + col) * kRowStride + 8 * g];
+  // Logits on MFMA 16x16x32 (M = 16 heads, N = 16 slots, K = 32 features):
+  // wave w takes slots 16 (w % 4) .. +16 and features 256 (w / 4) .. +256
+  // (eight steps); lane l reads row l % 16 at features 32 j + 8 (l / 16) of
+  // step j. The two halves of K go to two planes, added in the softmax.
+  {
+    const uint32_t col = lane & 15;
+    const uint32_t grp = lane >> 4;
+    const uint32_t ts = 16 * (wave & 3), kh = wave >> 2;
+    const uint16_t *qa = &q_lds[col * kRowStride + 256 * kh + 8 * grp];
+    const uint16_t *kb = &vt[(ts + col) * kRowStride + 256 * kh + 8 * grp];
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < kDim / 16; ++j)
-      acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(qa + 16 * j)),
-                   as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + 16 * j)), acc);
-  }
-  __syncthreads();   // the query region becomes the logits
-  if (wave < 4) {
+    for (int j = 0; j < 8; ++j)
+      acc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(qa + 32 * j)),
+                   as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + 32 * j)), acc);
+    // D lane l: slot ts + l % 16, heads 4 (l / 16) + i.
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      red[(th + 8 * (i / 4) + 4 * g + (i % 4)) * kRedStride + ts + col] = acc[i];
+    for (int i = 0; i < 4; ++i) red[(kh * kHg + 4 * grp + i) * kRedStride + ts + col] = acc[i];
   }
   __syncthreads();
 
-  // Softmax statistics. Thread t: head t / 8, slots 8 * (t % 8) .. +8.
+  // Softmax statistics. Thread t: head t / 32, slots 2 (t % 32) .. +2.
   {
-    const uint32_t head = tid >> 3;
-    const uint32_t part = tid & 7;
-    float lv[8];
-    uint32_t sj[8];
+    const uint32_t head = qh;
+    const uint32_t part = tid & 31;
+    float lv[2];
+    uint32_t sj[2];
     bool bad = false;
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t s = 8 * part + j;
-      lv[j] = red[head * kRedStride + s] * a.scale;
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t s = 2 * part + j;
+      lv[j] = (red[head * kRedStride + s] + red[(kHg + head) * kRedStride + s]) * a.scale;
       sj[j] = state[s];
       const bool live = sj[j] == kLive;
       bad |= (sj[j] == kBad) || (live && !__builtin_isfinite(lv[j]));
       if (live && __builtin_isfinite(lv[j])) mx = fmaxf(mx, lv[j]);
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
+    for (int o = 1; o < 32; o <<= 1) {
       mx = fmaxf(mx, __shfl_xor(mx, o));
       const int other = __shfl_xor(static_cast<int>(bad), o);   // every lane must take part
       bad = bad || other != 0;
     }
     float ssum = 0.0f;
-    u16x8 hi, lo;
+    uint32_t hi2 = 0, lo2 = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const bool live = sj[j] == kLive && __builtin_isfinite(lv[j]);
       const float p = live ? expf(lv[j] - mx) : 0.0f;
       ssum += p;
-      hi[j] = bf16_rne_bits(p);
-      lo[j] = bf16_rne_bits(p - bf16_bits_to_float(hi[j]));
+      const uint16_t h = bf16_rne_bits(p);
+      const uint16_t l = bf16_rne_bits(p - bf16_bits_to_float(h));
+      hi2 |= static_cast<uint32_t>(h) << (16 * j);
+      lo2 |= static_cast<uint32_t>(l) << (16 * j);
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) ssum += __shfl_xor(ssum, o);
-    *reinterpret_cast<u16x8 *>(&phi[head * kPStride + 8 * part]) = hi;
-    *reinterpret_cast<u16x8 *>(&plo[head * kPStride + 8 * part]) = lo;
+    for (int o = 1; o < 32; o <<= 1) ssum += __shfl_xor(ssum, o);
+    *reinterpret_cast<uint32_t *>(&phi[head * kPStride + 2 * part]) = hi2;
+    *reinterpret_cast<uint32_t *>(&plo[head * kPStride + 2 * part]) = lo2;
     if (part == 0)
-      a.stats[a.stat_base[r] + static_cast<uint64_t>(c) * kHeads + head] =
+      a.stats[a.stat_base[r] + static_cast<uint64_t>(c) * kHeads + kHg * hg + head] =
           make_float4(mx, ssum, bad ? 1.0f : 0.0f, sink_h);
   }
   __syncthreads();
 
-  // O_c = p~ . G_c: this wave's 64 features, all 64 heads, K = 64 slots.
+  // O_c = p~ . G_c for the group's 16 heads: wave w's 64 features, K = 64
+  // slots (MFMA 16x16x32: M = 16 heads, N = 16 features, K = 32 slots).
   const uint32_t li = lane & 15;
   const uint32_t lg = lane >> 4;
-  f32x4 o[4][4];
+  f32x4 o[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 ahi[4], alo[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const uint32_t off = (16 * mt + li) * kPStride + 32 * ks + 8 * lg;   // head 16mt + li, slots ..+8
-      ahi[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&phi[off]));
-      alo[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&plo[off]));
-    }
+    const uint32_t off = li * kPStride + 32 * ks + 8 * lg;   // head li, slots 32 ks + 8 lg ..+8
+    const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&phi[off]));
+    const bf16x8 alo = as_bf16x8(*reinterpret_cast<const u32x4 *>(&plo[off]));
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       // Lane li of group lg receives features n0 + li of slots s0 .. s0+3
@@ -262,23 +254,17 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
       const s16x4 b1 = lds_read_tr16(&vt[(s0 + 4 + li / 4) * kRowStride + n0 + 4 * (li % 4)]);
       const s16x8 b8 = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
       const bf16x8 b = __builtin_bit_cast(bf16x8, b8);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        o[mt][nt] = mfma16(ahi[mt], b, o[mt][nt]);
-        o[mt][nt] = mfma16(alo[mt], b, o[mt][nt]);
-      }
+      o[nt] = mfma16(ahi, b, o[nt]);
+      o[nt] = mfma16(alo, b, o[nt]);
     }
   }
-  // D lane l of tile (mt, nt): feature 64 wave + 16 nt + l % 16, heads
-  // 16 mt + 4 (l / 16) + i.
-  float *dst = a.opart + a.part_base[r] + static_cast<uint64_t>(c) * kHeads * kDim;
+  // D lane l of tile nt: feature 64 wave + 16 nt + l % 16, heads 4 (l / 16) + i.
+  float *dst = a.opart + a.part_base[r] + (static_cast<uint64_t>(c) * kHeads + kHg * hg) * kDim;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[(16 * mt + 4 * lg + i) * kDim + 64 * wave + 16 * nt + li] = o[mt][nt][i];
+    for (int i = 0; i < 4; ++i)
+      dst[(4 * lg + i) * kDim + 64 * wave + 16 * nt + li] = o[nt][i];
 }
 
 // ---------------------------------------------------------------- phase 2

@@ -447,11 +447,12 @@ ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool
     a.stat_base[r] = p.stat_base[r];
     a.part_base[r] = p.part_base[r];
   }
-  // Block b of either phase serves row b % 8 (one XCD per row).
+  // Block b of either phase serves row b % 8 (one XCD per row); phase 1 has
+  // kAttnHeadGroups workgroups per (row, chunk).
   uint32_t max_chunks = 0;
   for (uint32_t r = 0; r < p.rows; ++r) max_chunks = std::max(max_chunks, p.chunks[r]);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = ds::launch_attn_chunks(a, direct, ds::kXcds * max_chunks, s);
+  hipError_t e = ds::launch_attn_chunks(a, direct, ds::kXcds * max_chunks * ds::kAttnHeadGroups, s);
   if (e != hipSuccess) return hip_fail(e, "attention chunk launch");
   e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
   return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
