@@ -269,29 +269,33 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- phase 2
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
-  // Row r on XCD r (block b = 8 dc + r), as in phase 1.
+  // Row r on XCD r (block b = 8 dc + r), as in phase 1. Thread t: head t / 4,
+  // dims d0 .. d0 + 4 kVec of the workgroup's kAttnDimChunk.
+  constexpr int kVec = kAttnDimChunk / 4 / 4;   // f32x4 per thread
   const uint32_t r = blockIdx.x % kXcds;
   const uint32_t dc = blockIdx.x / kXcds;
   if (r >= a.rows) return;
   const uint32_t nch = a.chunks[r];
   const uint32_t tid = threadIdx.x;
   const uint32_t head = tid >> 2;
-  const uint32_t d0 = kAttnDimChunk * dc + 8 * (tid & 3);
+  const uint32_t d0 = kAttnDimChunk * dc + 4 * kVec * (tid & 3);
   const float4 *stats = a.stats + a.stat_base[r] + head;
   const float *op = a.opart + a.part_base[r] + static_cast<uint64_t>(head) * kDim + d0;
   constexpr int kB = 8;   // chunks per batch of loads
   auto stat_at = [&](uint32_t cc) { return stats[static_cast<uint64_t>(min(cc, nch - 1)) * kHeads]; };
-  auto part_at = [&](uint32_t cc, int half) {
-    return *reinterpret_cast<const f32x4 *>(op + static_cast<uint64_t>(min(cc, nch - 1)) * kHeads * kDim + 4 * half);
+  auto part_at = [&](uint32_t cc, int h) {
+    return *reinterpret_cast<const f32x4 *>(op + static_cast<uint64_t>(min(cc, nch - 1)) * kHeads * kDim + 4 * h);
   };
 
   // First batch of statistics and outputs, all loads in flight at once.
   float4 x[kB];
-  f32x4 p0[kB], p1[kB];
+  f32x4 pv[kB][kVec];
 #pragma unroll
   for (int i = 0; i < kB; ++i) x[i] = stat_at(i);
 #pragma unroll
-  for (int i = 0; i < kB; ++i) { p0[i] = part_at(i, 0); p1[i] = part_at(i, 1); }
+  for (int i = 0; i < kB; ++i)
+#pragma unroll
+    for (int h = 0; h < kVec; ++h) pv[i][h] = part_at(i, h);
 
   // m, the bad flag and Z over all chunks, with the sink.
   const float sink = x[0].w;   // phase 1 stores the head's sink with every statistic
@@ -316,36 +320,38 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   }
   bad |= !(z > 0.0f && __builtin_isfinite(z));
 
-  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc[kVec];
+#pragma unroll
+  for (int h = 0; h < kVec; ++h) acc[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < kB; ++i) {
     const float w = static_cast<uint32_t>(i) < nch ? weight(x[i]) : 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc0[k] = fmaf(w, p0[i][k], acc0[k]);
-      acc1[k] = fmaf(w, p1[i][k], acc1[k]);
-    }
+    for (int h = 0; h < kVec; ++h)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(w, pv[i][h][k], acc[h][k]);
   }
   for (uint32_t cc = kB; cc < nch; ++cc) {
     const float w = weight(stat_at(cc));
-    const f32x4 q0 = part_at(cc, 0), q1 = part_at(cc, 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc0[k] = fmaf(w, q0[k], acc0[k]);
-      acc1[k] = fmaf(w, q1[k], acc1[k]);
+    for (int h = 0; h < kVec; ++h) {
+      const f32x4 q = part_at(cc, h);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(w, q[k], acc[h][k]);
     }
   }
   const float invz = bad ? 0.0f : 1.0f / z;
-  f32x4 v0, v1;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float u0 = acc0[k] * invz, u1 = acc1[k] * invz;
-    v0[k] = (!bad && __builtin_isfinite(u0)) ? u0 : 0.0f;
-    v1[k] = (!bad && __builtin_isfinite(u1)) ? u1 : 0.0f;
-  }
   float *dst = a.out + (static_cast<uint64_t>(a.q_row[r]) * kHeads + head) * kDim + d0;
-  *reinterpret_cast<f32x4 *>(dst) = v0;
-  *reinterpret_cast<f32x4 *>(dst + 4) = v1;
+#pragma unroll
+  for (int h = 0; h < kVec; ++h) {
+    f32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float u = acc[h][k] * invz;
+      v[k] = (!bad && __builtin_isfinite(u)) ? u : 0.0f;
+    }
+    *reinterpret_cast<f32x4 *>(dst + 4 * h) = v;
+  }
 }
 
 hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s) {
