@@ -163,11 +163,13 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows,
  * select from those candidates, and a row's result stands only if no floor
  * lies above its 512th key. Otherwise (heavy ties, scores sorted by
  * position) the row is selected again from its scores in the same call,
- * which is exact but slower.
+ * which is exact but slower. A call with a row of fewer than 16384 visible
+ * keys (too few for its waves' candidates to hold its top 512 reliably)
+ * runs the separate score and top-k kernels instead, with the same result.
  *   q, weights, scores  as ds_rows_indexer_score
  *   workspace  device scratch, workspace_bytes >=
- *              ds_rows_indexer_topk_workspace_bytes (contents on entry do
- *              not matter; clobbered)
+ *              ds_rows_indexer_topk_workspace_bytes (enough for either
+ *              path; contents on entry do not matter; clobbered)
  *   indices    device i32, indices_elems >= max(output_offset + 512)
  * Checks: those of ds_rows_indexer_score and of ds_rows_topk. */
 ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows,

@@ -102,6 +102,25 @@ uint64_t fused_workspace_bytes(const IndexerPlan &p) {
   return fused_cand_bytes(p) + fused_floor_bytes(p) + 2 * p.fused_bank * sizeof(uint64_t);
 }
 
+// ds_rows_indexer_topk keeps the first selection stage in the indexer only
+// when every row has at least this many visible keys. Each wave keeps about
+// 24 of its 256 keys, so a row's candidates can hold its top 512 only past
+// ~5.5K keys, and below ~16K a wave often holds more than 24 of them (the
+// row then falls back to a selection over its scores): such calls run the
+// separate score and top-k kernels instead, which give the same result.
+constexpr uint32_t kFusedMinVisible = 16384;
+
+bool fused_rows(const IndexerPlan &p) {
+  for (uint32_t r = 0; r < p.rows; ++r)
+    if (p.visible[r] < kFusedMinVisible) return false;
+  return true;
+}
+
+// Enough for either path (and for ds_rows_indexer_candidates).
+uint64_t indexer_topk_workspace_bytes(const IndexerPlan &p) {
+  return std::max(fused_workspace_bytes(p), topk_workspace_bytes(p));
+}
+
 // ------------------------------------------------------------- sparse table
 struct SparsePlan {
   uint32_t rows = 0;
@@ -337,7 +356,7 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows, const float *scores, size_t 
 size_t ds_rows_indexer_topk_workspace_bytes(const ds_indexer_rows *rows) {
   IndexerPlan p;
   if (check_indexer(rows, &p) != DS_OK) return 0;
-  return fused_workspace_bytes(p);
+  return indexer_topk_workspace_bytes(p);
 }
 
 ds_status ds_rows_indexer_candidates(const ds_indexer_rows *rows, const void *q, size_t q_elems, const float *weights,
@@ -347,7 +366,7 @@ ds_status ds_rows_indexer_candidates(const ds_indexer_rows *rows, const void *q,
   DS_TRY(check_indexer(rows, &p));
   DS_TRY(check_indexer_operands(rows, p, q, q_elems, weights, weights_elems, scores, scores_elems));
   DS_TRY(need(workspace, "indexer top-k workspace"));
-  DS_TRY(cap(workspace_bytes, fused_workspace_bytes(p), "indexer top-k workspace", "bytes"));
+  DS_TRY(cap(workspace_bytes, indexer_topk_workspace_bytes(p), "indexer top-k workspace", "bytes"));
   char *ws = static_cast<char *>(workspace);
   return launch_indexer(rows, p, q, weights, scores, reinterpret_cast<uint64_t *>(ws),
                         reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p)), stream);
@@ -361,9 +380,16 @@ ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_
   DS_TRY(check_indexer_operands(rows, p, q, q_elems, weights, weights_elems, scores, scores_elems));
   DS_TRY(need(workspace, "indexer top-k workspace"));
   DS_TRY(need(indices, "indexer output"));
-  DS_TRY(cap(workspace_bytes, fused_workspace_bytes(p), "indexer top-k workspace", "bytes"));
+  DS_TRY(cap(workspace_bytes, indexer_topk_workspace_bytes(p), "indexer top-k workspace", "bytes"));
   DS_TRY(cap(indices_elems, p.indices_end, "indexer output", "elements"));
 
+  if (!fused_rows(p)) {
+    DS_TRY(launch_indexer(rows, p, q, weights, scores, nullptr, nullptr, stream));
+    TopkInput in{};
+    for (uint32_t r = 0; r < p.rows; ++r) in.count[r] = p.visible[r];
+    uint64_t *bank = static_cast<uint64_t *>(workspace);
+    return run_topk_levels(rows, p, scores, in, bank, bank + p.topk_bank, indices, stream);
+  }
   char *ws = static_cast<char *>(workspace);
   uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
   uint32_t *floors = reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p));

@@ -165,6 +165,10 @@ def test_size_queries(lib):
     floors = -(-nb * 4 * 4 // 256) * 256
     chunks = -(-nb * 128 // 8192)
     assert ds.indexer_topk_workspace_bytes(big) == cand + floors + 2 * chunks * 512 * 8
+    # the size covers both of the call's paths: a lone 1000-key row (which
+    # takes the separate score and top-k kernels) still gets the fused
+    # stage's candidates (one block: 1 KiB) and floors (16 B -> 256)
+    assert ds.indexer_topk_workspace_bytes(itab((1000,))) == 1024 + 256
     s = stab((1000, 37, 1), width=(512, 37, 1))
     assert ds.gathered_elems(s) == (512 + 37 + 1) * 512
     assert ds.mask_elems(s) == 512 + 37 + 1

@@ -100,7 +100,8 @@ def test_fused_multi_row_equals_single_row():
 def test_fused_ties_across_blocks_fall_back():
     # every score 0: each block keeps its lowest indices, the floors of later
     # blocks sit above the 512th key and the row is selected from its scores
-    kv_len = [600, 20000, 131072]
+    # (every row long enough for the fused stage)
+    kv_len = [17000, 20000, 131072]
     inp = I.small_rows(7, kv_len)
     for k in inp.idx_keys:
         k[:] = 0
@@ -132,7 +133,7 @@ def sorted_scores(seed, kv_len, sign):
 def test_fused_sorted_scores_fall_back(sign):
     # ascending: the top 512 are the last keys, all in the last blocks;
     # descending: the first keys. Either way the blocks' candidates miss some.
-    kv_len = [5000, 40000, 65536]
+    kv_len = [16384, 40000, 65536]
     inp = sorted_scores(13, kv_len, sign)
     say("fused: scores sorted by position, sign", sign, kv_len)
     got, sep = fused_and_separate(DeviceInputs(inp))
@@ -155,3 +156,29 @@ def test_fused_causal_offset_and_non_finite():
     got, sep = fused_and_separate(DeviceInputs(inp))
     check_scores_indices(got, sep, inp, "causal")
     assert np.all(got[1]["indices"] == -1)
+
+
+def test_fused_long_rows_causal_offset_and_non_finite():
+    # every row has at least 16384 visible keys, so the call keeps the fused
+    # stage: causal limits inside the cache, offsets, non-finite keys
+    kv_len = [40000, 20000, 70000]
+    start_pos = [4 * 17000 + 2, 4 * 20000 - 1, 4 * 66000 + 3]
+    offset = [7, 0, 100000]
+    inp = I.small_rows(33, kv_len, start_pos=start_pos, offset=offset)
+    keys = inp.idx_keys[1]
+    keys[3, 5] = 0x7FC0
+    keys[4, 9] = 0x7F80
+    keys[6, :] = 0x7F80
+    say("fused: long rows, causal limits, offsets, non-finite keys")
+    got, sep = fused_and_separate(DeviceInputs(inp))
+    check_scores_indices(got, sep, inp, "long causal")
+
+
+def test_short_row_takes_the_separate_kernels():
+    # a row under 16384 visible keys sends the whole call through the
+    # separate score and top-k kernels: same results
+    kv_len = [600, 40000]
+    inp = I.small_rows(34, kv_len)
+    say("fused call with a short row")
+    got, sep = fused_and_separate(DeviceInputs(inp))
+    check_scores_indices(got, sep, inp, "short row")
