@@ -155,11 +155,7 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
     bool nf = false;
 #pragma unroll
     for (int s = 0; s < 8; ++s) nf |= any_nonfinite(gb[s]);
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      const int other = __shfl_xor(static_cast<int>(nf), o);   // every lane must take part
-      nf = nf || other != 0;
-    }
+    nf = ((__ballot(nf) >> (lane & 56u)) & 0xFFull) != 0;
     if (st == kLive && nf) st = kBad;
   }
   if ((tid & 7) == 0) state[sl] = st;
@@ -203,12 +199,8 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
       bad |= (sj[j] == kBad) || (live && !__builtin_isfinite(lv[j]));
       if (live && __builtin_isfinite(lv[j])) mx = fmaxf(mx, lv[j]);
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, o));
-      const int other = __shfl_xor(static_cast<int>(bad), o);   // every lane must take part
-      bad = bad || other != 0;
-    }
+    mx = half_max(mx);
+    bad = half_any(bad);
     float ssum = 0.0f;
     uint32_t hi2 = 0, lo2 = 0;
 #pragma unroll
@@ -221,8 +213,7 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
       hi2 |= static_cast<uint32_t>(h) << (16 * j);
       lo2 |= static_cast<uint32_t>(l) << (16 * j);
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) ssum += __shfl_xor(ssum, o);
+    ssum = half_sum(ssum);
     *reinterpret_cast<uint32_t *>(&phi[head * kPStride + 2 * part]) = hi2;
     *reinterpret_cast<uint32_t *>(&plo[head * kPStride + 2 * part]) = lo2;
     if (part == 0)

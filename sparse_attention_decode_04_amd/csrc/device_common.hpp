@@ -63,6 +63,102 @@ __device__ __forceinline__ float swap_halves_sum(float x, float y) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Cross-lane steps by DPP (row = 16 lanes). update_dpp(old, v, ...) gives
+// each lane the moved value, or `old` where the source lies outside the row
+// or the lane's row is masked off.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 to rows 2 and 3
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), kCtrl, kRowMask, 0xF, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<kCtrl>(0u, __float_as_uint(v)));
+}
+
+// Inclusive prefix over the 64 lanes of a wave in lane order (sum or max of
+// unsigned values): doubling steps inside each row, then the row totals
+// carried into the rows above.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  x += dpp_u32<kDppRowShr1>(0u, x);
+  x += dpp_u32<kDppRowShr2>(0u, x);
+  x += dpp_u32<kDppRowShr4>(0u, x);
+  x += dpp_u32<kDppRowShr8>(0u, x);
+  x += dpp_u32<kDppRowBcast15, 0xA>(0u, x);
+  x += dpp_u32<kDppRowBcast31, 0xC>(0u, x);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_prefix_max(uint32_t x) {
+  x = max(x, dpp_u32<kDppRowShr1>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr2>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr4>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr8>(0u, x));
+  x = max(x, dpp_u32<kDppRowBcast15, 0xA>(0u, x));
+  x = max(x, dpp_u32<kDppRowBcast31, 0xC>(0u, x));
+  return x;
+}
+
+// Whole-wave reductions, the result in every lane: inside each row by
+// rotations and pair swaps, then across row pairs (v_permlane16_swap) and
+// wave halves (v_permlane32_swap). Each step combines a lane with a partner
+// holding the same two operands in the other order, so every lane ends with
+// the same bits (also for floating point).
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
+  x = op(x, dpp_u32<kDppRowRor8>(x, x));
+  x = op(x, dpp_u32<kDppRowRor4>(x, x));
+  x = op(x, dpp_u32<kDppQuadSwap2>(x, x));
+  x = op(x, dpp_u32<kDppQuadSwap1>(x, x));
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(r[0], r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(h[0], h[1]);
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t p, uint32_t q) { return p + q; });
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t p, uint32_t q) { return min(p, q); });
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t p, uint32_t q) { return max(p, q); });
+}
+
+// Reductions over the 32 lanes of a wave half (lanes 0..31 or 32..63), the
+// result in every lane of the half (same scheme, without the last step).
+__device__ __forceinline__ float half_sum(float v) {
+  v += dpp_f32<kDppRowRor8>(v);
+  v += dpp_f32<kDppRowRor4>(v);
+  v += dpp_f32<kDppQuadSwap2>(v);
+  v += dpp_f32<kDppQuadSwap1>(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Whether any lane of this lane's 32-lane half has the flag set.
+__device__ __forceinline__ bool half_any(bool f) {
+  const uint64_t m = __ballot(f);
+  return ((m >> (__lane_id() & 32u)) & 0xFFFFFFFFull) != 0;
+}
+
 // Row of a multi-row launch owning workgroup `b`: the last r with
 // blk_begin[r] <= b. Entries past the last row hold the total block count.
 __device__ __forceinline__ uint32_t row_of_block(const uint32_t *blk_begin, uint32_t b) {

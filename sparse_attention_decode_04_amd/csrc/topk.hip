@@ -67,13 +67,7 @@ __device__ __forceinline__ void scan_bins(const uint32_t *hist, uint32_t *wsum, 
                                           uint32_t &h, uint32_t &above, uint32_t &maxge, uint32_t &total) {
   const uint32_t lane = tid & 63, wave = tid >> 6;
   h = hist[kBins - 1 - tid];
-  uint32_t incl = h, imax = h;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t up = __shfl_up(incl, o);
-    const uint32_t upm = __shfl_up(imax, o);
-    if (lane >= static_cast<uint32_t>(o)) { incl += up; imax = max(imax, upm); }
-  }
+  const uint32_t incl = wave_prefix_sum(h), imax = wave_prefix_max(h);
   if (lane == 63) { wsum[wave] = incl; wmax[wave] = imax; }
   __syncthreads();
   uint32_t pre = 0, premax = 0, all = 0;
@@ -106,8 +100,11 @@ struct TopkShared {
   __attribute__((aligned(16))) uint32_t wsum[kWaves];
   __attribute__((aligned(16))) uint32_t wmax[kWaves];
   __attribute__((aligned(16))) uint32_t wcount[kWaves];
+  __attribute__((aligned(16))) uint32_t wvalid[kWaves];     // per-wave candidate statistics
+  __attribute__((aligned(16))) uint32_t wmin1[kWaves];
+  __attribute__((aligned(16))) uint32_t wmaxo[kWaves];
   uint64_t fin[kTopK];                                          // checked final level: result before the check
-  uint32_t valid, min1, max, count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
+  uint32_t count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
 };
 
 // Candidates of the first level: score bits per candidate (0 = none), index
@@ -463,7 +460,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   const bool final_level = (a.final_mask >> r) & 1u;
 
   sh.hist[tid] = 0;
-  if (tid == 0) { sh.valid = 0; sh.min1 = 0xFFFFFFFFu; sh.max = 0; sh.thr = 0xFFFFFFFFu; }
+  if (tid == 0) sh.thr = 0xFFFFFFFFu;
 
   // Candidate e of this thread sits at position begin + tid + 1024 * e.
   // Loads are unconditional, from positions clamped into the row (every row
@@ -512,22 +509,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
       omin1 = min(omin1, o - 1u);
       omax = max(omax, o);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      nvalid += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nvalid), o));
-      omin1 = min(omin1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omin1), o)));
-      omax = max(omax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(omax), o)));
-    }
-    __syncthreads();   // LDS initialisation above is complete
+    // Per-wave totals in LDS slots, combined by every thread after one
+    // barrier (which also publishes the LDS initialisation above).
+    nvalid = wave_sum(nvalid);
+    omin1 = wave_min(omin1);
+    omax = wave_max(omax);
     if (lane == 0) {
-      atomicAdd(&sh.valid, nvalid);
-      atomicMin(&sh.min1, omin1);
-      atomicMax(&sh.max, omax);
+      sh.wvalid[wave] = nvalid;
+      sh.wmin1[wave] = omin1;
+      sh.wmaxo[wave] = omax;
     }
     __syncthreads();
-    const uint32_t total = sh.valid;
+    uint32_t total = 0, min1 = 0xFFFFFFFFu, gmax = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves / 4; ++v) {
+      const u32x4 n4 = reinterpret_cast<const u32x4 *>(sh.wvalid)[v];
+      const u32x4 l4 = reinterpret_cast<const u32x4 *>(sh.wmin1)[v];
+      const u32x4 h4 = reinterpret_cast<const u32x4 *>(sh.wmaxo)[v];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        total += n4[k];
+        min1 = min(min1, l4[k]);
+        gmax = max(gmax, h4[k]);
+      }
+    }
     const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
-    const uint32_t gmin = sh.min1 + 1u, gmax = sh.max;
+    const uint32_t gmin = min1 + 1u;
 
     // A checked final level keeps its result in LDS until the floors allow it.
     // (Fused-indexer candidates are lists, so only later levels check.)
@@ -567,8 +574,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
         __syncthreads();
         const uint32_t lo = sh.lo;
         uint32_t t = (b0 < kBins && b0 >= lo) ? o0 : 0xFFFFFFFFu;
-  #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) t = min(t, static_cast<uint32_t>(__shfl_xor(static_cast<int>(t), o)));
+        t = wave_min(t);
         if (lane == 0) atomicMin(&sh.thr, t);
         __syncthreads();
         thr = sh.thr;
