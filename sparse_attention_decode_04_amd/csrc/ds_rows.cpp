@@ -276,6 +276,10 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
       blocks += chunks[r];
     }
     a.blk_begin[ds::kRowsMax] = blocks;
+    uint32_t max_count = 0;
+    for (uint32_t r = 0; r < p.rows; ++r)
+      if (!done[r]) max_count = std::max(max_count, count[r]);
+    a.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
     const hipError_t e = ds::launch_topk_level(a, blocks, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     bool all = true;

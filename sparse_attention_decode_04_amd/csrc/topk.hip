@@ -164,16 +164,21 @@ struct KeyCand {
 // `c`; their score bits lie in [omin, omax]), emitted in rank order through
 // emit(pos, key). kSample: pre-filter the histogram by a sampled lower bin
 // (worth it only for many candidates per thread).
-template <int kPer, bool kSample, class Cand, class Emit>
+// kFresh: hist, cursor, count and lo still hold the zeros written at the
+// start of the kernel (published by a barrier since), and no earlier reader
+// of the shared arrays remains, so they are not cleared again.
+template <int kPer, bool kSample, bool kFresh = false, class Cand, class Emit>
 __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, uint32_t total, uint32_t need,
                                                 uint32_t omin, uint32_t omax, const Emit &emit) {
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  __syncthreads();   // earlier readers of the shared arrays are done
-  sh.hist[tid] = 0;
-  sh.cursor[tid] = 0;
-  if (tid == 0) { sh.count = 0; sh.lo = 0; }
-  __syncthreads();
+  if constexpr (!kFresh) {
+    __syncthreads();   // earlier readers of the shared arrays are done
+    sh.hist[tid] = 0;
+    sh.cursor[tid] = 0;
+    if (tid == 0) { sh.count = 0; sh.lo = 0; }
+    __syncthreads();
+  }
 
   const float smin = ord_score(omin), smax = ord_score(omax);
   const float range = smax - smin;
@@ -444,9 +449,11 @@ __device__ __forceinline__ void select_from_scores(TopkShared &sh, const float *
 
 // kFromScores: the first level, reading f32 scores. Otherwise a later level,
 // reading the previous level's 64-bit key lists.
-template <bool kFromScores>
+// kPerLater: candidates per thread on a later level (8, or 4 when every row
+// of the level has at most 4096).
+template <bool kFromScores, int kPerLater = kTopkPerThreadLater>
 __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs a) {
-  constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kTopkPerThreadLater;
+  constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kPerLater;
   constexpr uint32_t kChunk = kTopkThreads * kPer;
   __shared__ TopkShared sh;
 
@@ -460,7 +467,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
   const bool final_level = (a.final_mask >> r) & 1u;
 
   sh.hist[tid] = 0;
-  if (tid == 0) sh.thr = 0xFFFFFFFFu;
+  sh.cursor[tid] = 0;
+  if (tid == 0) { sh.thr = 0xFFFFFFFFu; sh.count = 0; sh.lo = 0; sh.viol = 0; }
 
   // Candidate e of this thread sits at position begin + tid + 1024 * e.
   // Loads are unconditional, from positions clamped into the row (every row
@@ -556,7 +564,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     auto select_chunk = [&](uint32_t total, uint32_t need, uint32_t gmin, uint32_t gmax, const auto &emit) {
       // Threshold T from the sample (every key when the chunk is small).
       uint32_t thr = 1;
-      if (end - begin > kSmallChunk) {
+      const bool sampled = end - begin > kSmallChunk;
+      if (sampled) {
         const float smin = ord_score(gmin), smax = ord_score(gmax);
         const float range = smax - smin;
         const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
@@ -578,6 +587,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
         if (lane == 0) atomicMin(&sh.thr, t);
         __syncthreads();
         thr = sh.thr;
+      }
+      if constexpr (!kFromScores) {
+        if (!sampled) {
+          // Every valid key stays: select over the candidates as loaded, on
+          // the shared arrays as the kernel initialised them.
+          counting_select<kPer, false, true>(sh, c, total, need, gmin, gmax, emit);
+          return;
+        }
       }
       // Compaction: keys with score bits >= T go to the wave's region, in
       // candidate order; the running count is wave-uniform.
@@ -632,9 +649,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     // wave's floor key; the result stands unless some floor lies above the
     // last selected key (or the row has fewer than 512 candidates and a wave
     // left keys out).
-    __syncthreads();
-    if (tid == 0) sh.viol = 0;
-    __syncthreads();
+    __syncthreads();   // the result is complete in sh.fin (viol was cleared at the start)
     const uint64_t klast = need > 0 ? sh.fin[need - 1] : 0ull;
     auto violates = [&](uint32_t f) {
       return f != 0 && (need < static_cast<uint32_t>(kTopK) || (static_cast<uint64_t>(f) << 32) > klast);
@@ -657,6 +672,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
 hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s) {
   if (a.from_scores)
     hipLaunchKernelGGL(topk_level_kernel<true>, dim3(blocks), dim3(kTopkThreads), 0, s, a);
+  else if (a.per_thread == 4)
+    hipLaunchKernelGGL((topk_level_kernel<false, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
   else
     hipLaunchKernelGGL(topk_level_kernel<false>, dim3(blocks), dim3(kTopkThreads), 0, s, a);
   return hipGetLastError();
