@@ -103,7 +103,7 @@ struct TopkShared {
   __attribute__((aligned(16))) uint32_t wvalid[kWaves];     // per-wave candidate statistics
   __attribute__((aligned(16))) uint32_t wmin1[kWaves];
   __attribute__((aligned(16))) uint32_t wmaxo[kWaves];
-  uint64_t fin[kTopK];                                          // checked final level: result before the check
+  __attribute__((aligned(16))) uint32_t wfloor[kWaves];
   uint32_t count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
 };
 
@@ -498,12 +498,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     for (int e = 0; e < kPer; ++e)
       if (begin + tid + kTopkThreads * e >= end) keyv[e] = 0;
   }
-  // A checked final level needs the row's floors at the end; their first
-  // 1024 are loaded now, with the candidates.
-  uint32_t floor0 = 0;
+  // A checked final level compares the row's highest floor with the last
+  // selected key; the floors are loaded now, with the candidates.
+  const bool check_row = !kFromScores && final_level && ((a.check_mask >> r) & 1u);
+  uint32_t floor_hi = 0;
   if constexpr (!kFromScores) {
-    if (final_level && ((a.check_mask >> r) & 1u) && a.floor_count[r] > 0)
-      floor0 = a.floors[a.floor_begin[r] + min(tid, a.floor_count[r] - 1)];
+    if (check_row && a.floor_count[r] > 0) {
+      floor_hi = a.floors[a.floor_begin[r] + min(tid, a.floor_count[r] - 1)];
+      for (uint32_t b = tid + kTopkThreads; b < a.floor_count[r]; b += kTopkThreads)
+        floor_hi = max(floor_hi, a.floors[a.floor_begin[r] + b]);
+    }
   }
   auto run = [&](const auto &c) {
     // Count and extreme score bits of the valid keys. A missing key has high
@@ -522,31 +526,40 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     nvalid = wave_sum(nvalid);
     omin1 = wave_min(omin1);
     omax = wave_max(omax);
+    const uint32_t wfloor = check_row ? wave_max(floor_hi) : 0u;
     if (lane == 0) {
       sh.wvalid[wave] = nvalid;
       sh.wmin1[wave] = omin1;
       sh.wmaxo[wave] = omax;
+      sh.wfloor[wave] = wfloor;
     }
     __syncthreads();
-    uint32_t total = 0, min1 = 0xFFFFFFFFu, gmax = 0;
+    uint32_t total = 0, min1 = 0xFFFFFFFFu, gmax = 0, max_floor = 0;
 #pragma unroll
     for (int v = 0; v < kWaves / 4; ++v) {
       const u32x4 n4 = reinterpret_cast<const u32x4 *>(sh.wvalid)[v];
       const u32x4 l4 = reinterpret_cast<const u32x4 *>(sh.wmin1)[v];
       const u32x4 h4 = reinterpret_cast<const u32x4 *>(sh.wmaxo)[v];
+      const u32x4 f4 = reinterpret_cast<const u32x4 *>(sh.wfloor)[v];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         total += n4[k];
         min1 = min(min1, l4[k]);
         gmax = max(gmax, h4[k]);
+        max_floor = max(max_floor, f4[k]);
       }
     }
     const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
     const uint32_t gmin = min1 + 1u;
 
-    // A checked final level keeps its result in LDS until the floors allow it.
-    // (Fused-indexer candidates are lists, so only later levels check.)
-    const bool check = !kFromScores && final_level && ((a.check_mask >> r) & 1u);
+    // A checked final level writes its result as it goes: a key that a wave
+    // of the fused indexer did not write ranks below that wave's floor key,
+    // so the result stands unless the row's highest floor lies above the last
+    // selected key (or the row has fewer than 512 candidates and some wave
+    // left keys out); then the row is selected again from its scores, which
+    // rewrites every slot. (Fused-indexer candidates are lists, so only later
+    // levels check.)
+    const bool check = check_row;
     auto emit_out = [&](uint32_t pos, uint64_t kk) {
       if (final_level) {
         a.indices[a.out_offset[r] + pos] =
@@ -556,8 +569,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
       }
     };
     auto emit = [&](uint32_t pos, uint64_t kk) {
-      if (check) sh.fin[pos] = kk;
-      else emit_out(pos, kk);
+      emit_out(pos, kk);
+      if (check && pos + 1 == static_cast<uint32_t>(kTopK) && (static_cast<uint64_t>(max_floor) << 32) > kk)
+        sh.viol = 1;
     };
     // Best `need` of this chunk's candidates (total valid, score bits in
     // [gmin, gmax]), in rank order through emit(pos, key).
@@ -645,25 +659,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
     if (total > 0) select_chunk(total, need, gmin, gmax, emit);
     if constexpr (kFromScores) return;
     if (!check) return;
-    // A key that a wave of the fused indexer did not write ranks below that
-    // wave's floor key; the result stands unless some floor lies above the
-    // last selected key (or the row has fewer than 512 candidates and a wave
-    // left keys out).
-    __syncthreads();   // the result is complete in sh.fin (viol was cleared at the start)
-    const uint64_t klast = need > 0 ? sh.fin[need - 1] : 0ull;
-    auto violates = [&](uint32_t f) {
-      return f != 0 && (need < static_cast<uint32_t>(kTopK) || (static_cast<uint64_t>(f) << 32) > klast);
-    };
-    uint32_t viol = (tid < a.floor_count[r] && violates(floor0)) ? 1u : 0u;
-    for (uint32_t b = tid + kTopkThreads; b < a.floor_count[r]; b += kTopkThreads)
-      viol |= violates(a.floors[a.floor_begin[r] + b]) ? 1u : 0u;
-    if (__ballot(viol != 0) != 0 && lane == 0) atomicOr(&sh.viol, 1u);
-    __syncthreads();
-    if (sh.viol == 0) {
-      for (uint32_t t = tid; t < kTopK; t += kTopkThreads) emit_out(t, sh.fin[t]);
-    } else {
+    // The output stores of every wave land before the barrier, so that a
+    // reselection below rewrites them rather than racing them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();   // the last rank's verdict (viol was cleared at the start)
+    if ((need < static_cast<uint32_t>(kTopK) && max_floor != 0) || sh.viol != 0)
       select_from_scores(sh, a.scores + static_cast<uint64_t>(r) * a.score_stride, a.fallback_count[r], emit_out);
-    }
   };
   if constexpr (kFromScores) run(OrdCand<kPer>{ordv, begin + tid});
   else run(KeyCand<kPer>{keyv});
