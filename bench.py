@@ -2,12 +2,14 @@
 
 One step = the whole path for every row of the workload: indexer score ->
 top-512 -> gather of the selected KV rows -> sparse attention with sinks.
-The headline runs it as two C-ABI calls on one stream:
-ds_rows_indexer_topk (scores and top-512, the first selection stage in the
-indexer's epilogue) and ds_rows_sparse_attn_direct (gather fused into the
-attention). The three-call form (separate ds_rows_indexer_score and
-ds_rows_topk) and the four-call form (ds_rows_gather, then
-ds_rows_sparse_attn) compute the same outputs and are timed beside it.
+The headline runs it as one C-ABI call, ds_rows_indexer_topk_attn: the
+indexer with the first selection stage in its epilogue, then the final
+selection level inside the attention's workgroups (gather fused), then the
+attention's combine. The two-call form (ds_rows_indexer_topk, then
+ds_rows_sparse_attn_direct), the three-call form (separate
+ds_rows_indexer_score and ds_rows_topk) and the four-call form
+(ds_rows_gather, then ds_rows_sparse_attn) compute the same outputs and are
+timed beside it.
 Default workload: 8 rows x 32768 cached keys (64 heads x 128 indexer, top-512,
 64 heads x 512 attention), seeded synthetic inputs resident in HBM.
 
@@ -300,9 +302,10 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0
 
-    # Headline: score + top-k in one call, then attention with the gather
-    # fused in.
-    ms_per_step, wall = timed("step_fused")
+    # Headline: the one-call decode core.
+    ms_per_step, wall = timed("step_one")
+    # Score + top-k in one call, then attention with the gather fused in.
+    ms_two, _ = timed("step_fused")
     # Separate score and top-k calls, then the same attention.
     ms_three, _ = timed("step_direct")
     # The four-call path (gather, then attention on the gathered rows).
@@ -369,9 +372,11 @@ def main():
         },
         "keys_per_s": keys_per_s,
         "step_algorithmic_gb_per_s": step_bytes(inp) / (ms_per_step * 1e-3) / 1e9,
-        "pipeline": "ds_rows_indexer_topk (first top-k stage in the indexer) -> ds_rows_sparse_attn_direct "
-                    "(gather fused)",
-        "per_call_ms": per_call,
+        "pipeline": "ds_rows_indexer_topk_attn (indexer with the first top-k stage; final top-k level inside the "
+                    "attention workgroups, gather fused; combine)",
+        "two_call_pipeline": {
+            "calls": "ds_rows_indexer_topk -> ds_rows_sparse_attn_direct",
+            "ms_per_step": ms_two, "rows_per_s": inp.rows / (ms_two * 1e-3), "per_call_ms": per_call},
         "three_call_pipeline": {
             "calls": "ds_rows_indexer_score -> ds_rows_topk -> ds_rows_sparse_attn_direct",
             "ms_per_step": ms_three, "rows_per_s": inp.rows / (ms_three * 1e-3), "per_call_ms": per_call_three},

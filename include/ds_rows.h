@@ -306,6 +306,44 @@ ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows,
                                      float *out, size_t out_elems,
                                      void *stream);
 
+/* ---- ds_rows_indexer_topk_attn ------------------------------------------
+ * The decode core in one call: ds_rows_indexer_topk on irows followed by
+ * ds_rows_sparse_attn_direct on srows reading the indices it wrote, with the
+ * same scores, indices and output bit for bit. Sources: the pages' rows
+ * dispatches run back to back ([host 0.21] dispatch_deepseek_indexer_*_rows
+ * and dispatch_deepseek_sparse_attention_rows; [shader 0.18]
+ * deepseek_indexer_topk_finalize_rows_i32 and
+ * deepseek_sparse_attention_score_rows_bf16).
+ * When ds_rows_indexer_topk would keep the first selection stage in the
+ * indexer (every row has at least 16384 visible keys) and each row has at
+ * most 8192 candidates (up to 65536 keys), the final selection level runs
+ * inside the attention's workgroups: each repeats its row's selection and
+ * reads its slots' indices from LDS, which removes a kernel boundary and the
+ * attention's index load. Otherwise the two calls run as they are.
+ *   irows, idx_q, weights, scores, idx_workspace, indices
+ *              as ds_rows_indexer_topk (idx_workspace sized by
+ *              ds_rows_indexer_topk_workspace_bytes(irows))
+ *   srows, q, sinks, scale, attn_workspace, out
+ *              as ds_rows_sparse_attn_direct (attn_workspace sized by
+ *              ds_rows_attn_workspace_bytes(srows)); srows must list the
+ *              same rows in the same order, each with width <= 512 and
+ *              index_offset equal to irows' output_offset (the attention
+ *              reads the first `width` of the 512 selected slots of its
+ *              row; all 512 are written to indices)
+ * Checks: those of both calls, plus the row correspondence above. */
+ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_sparse_rows *srows,
+                                    const void *idx_q, size_t idx_q_elems,
+                                    const float *weights, size_t weights_elems,
+                                    float *scores, size_t scores_elems,
+                                    void *idx_workspace, size_t idx_workspace_bytes,
+                                    int32_t *indices, size_t indices_elems,
+                                    const void *q, size_t q_elems,
+                                    const float *sinks, size_t sinks_elems,
+                                    float scale,
+                                    void *attn_workspace, size_t attn_workspace_bytes,
+                                    float *out, size_t out_elems,
+                                    void *stream);
+
 /* ---- ds_rows_compressor -------------------------------------------------
  * One decode token of the learned KV compressor per row, each row with its
  * own recurrent state ([shader 0.18] deepseek_compressor_rows_bf16;

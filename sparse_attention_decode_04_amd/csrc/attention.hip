@@ -39,60 +39,15 @@
 //     out = sum_c e^(m_c - m) O_c / Z in a fixed chunk order.
 // All splits depend only on the row's own width, so rows are independent
 // bit for bit, and both variants give the same bits.
-#include "device_common.hpp"
-#include "ds_rows_internal.hpp"
+#include "attn_chunk.hpp"
 
 namespace ds {
 
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-// Slot states: -inf mask / -1 index = sentinel, NaN mask / bad index = bad.
-enum : uint32_t { kLive = 0, kSkip = 1, kBad = 2 };
-
-__device__ __forceinline__ uint32_t mask_state(uint16_t m) {
-  if (m == kBf16NegInf) return kSkip;
-  if ((m & 0x7FFFu) > 0x7F80u) return kBad;
-  return kLive;
-}
-
-__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-__device__ __forceinline__ bool any_nonfinite(u32x4 v) {
-  bool bad = false;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) bad |= bf16_bits_nonfinite(v[k] & 0xFFFFu) || bf16_bits_nonfinite(v[k] >> 16);
-  return bad;
-}
-// Transposing 8-byte LDS read (see the header comment for its lane layout).
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(p));
-}
-
-constexpr int kChunkThreads = 512;              // 8 waves
-constexpr int kHg = kHeads / kAttnHeadGroups;   // heads per phase-1 workgroup (16)
-constexpr int kRowStride = kDim + 8;            // bf16 per LDS row of q and of the chunk's rows: 1040 B
-constexpr int kRedStride = kAttnChunk + 1;      // padded f32 row of the logits
-constexpr int kPStride = kAttnChunk + 8;        // bf16 per LDS head row of p~: 144 B
 constexpr int kCombineThreads = 256;
-static_assert(kHg == 16, "one MFMA row tile of heads per workgroup");
 
-// ---------------------------------------------------------------- phase 1
 template <bool kDirect>
 __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kAttnChunk * kRowStride];   // the chunk's rows, slot-major
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kHg * kRowStride];       // this group's query heads
-  __shared__ float red[2 * kHg * kRedStride];                                      // logits, one plane per K half
-  __shared__ __attribute__((aligned(16))) uint16_t phi[kHg * kPStride];            // p~ hi
-  __shared__ __attribute__((aligned(16))) uint16_t plo[kHg * kPStride];            // p~ lo
-  __shared__ uint32_t state[kAttnChunk];
-
+  __shared__ AttnChunkShared sm;
   // Row r runs on XCD r (consecutive workgroups go to consecutive XCDs), so
   // the head groups and chunks of a row share one L2: the four head groups
   // of a chunk read the same selected rows.
@@ -101,161 +56,7 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
   const uint32_t hg = rest % kAttnHeadGroups;
   const uint32_t c = rest / kAttnHeadGroups;
   if (r >= a.rows || c >= a.chunks[r]) return;
-  const uint32_t width = a.width[r];
-  const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid & 63;
-  const uint32_t wave = tid >> 6;
-
-  // Loads: thread t moves features 64 (t % 8) .. +64 of slot t / 8, and
-  // features 16 (t % 32) .. +16 of query head t / 32 of the group, each byte
-  // once. They are unconditional (a slot past the width reads the row's last
-  // slot, a sentinel or bad index reads KV row 0) and masked afterwards, so
-  // they are all in flight at once. The slot's index (or mask entry) goes
-  // first: the KV row load depends on it, and loads complete in issue order.
-  const uint32_t sl = tid >> 3;            // slot within the chunk
-  const uint32_t fp = 64 * (tid & 7);      // this thread's 64 features of it
-  const uint32_t slot = c * kAttnChunk + sl;
-  const uint32_t cslot = min(slot, width - 1);
-  int32_t raw_index = 0;
-  uint16_t raw_mask = 0;
-  if (kDirect) raw_index = a.indices[a.index_offset[r] + cslot];
-  else raw_mask = a.mask[a.slot_base[r] + cslot];
-  const uint32_t qh = tid >> 5;            // query head within the group (and the softmax head)
-  const uint32_t qf = 16 * (tid & 31);
-  const uint16_t *qrow = a.q + (static_cast<uint64_t>(a.q_row[r]) * kHeads + kHg * hg + qh) * kDim + qf;
-  const u32x4 qv0 = load16(qrow), qv1 = load16(qrow + 8);
-  uint32_t st;
-  const uint16_t *src;
-  if (kDirect) {
-    const int32_t i = slot < width ? raw_index : -1;
-    const bool ok = i >= 0 && static_cast<uint32_t>(i) < a.kv_len[r];
-    st = ok ? kLive : ((slot < width && i != -1) ? kBad : kSkip);
-    src = a.kv[r] + static_cast<uint64_t>(ok ? i : 0) * kDim;
-  } else {
-    st = slot < width ? mask_state(raw_mask) : kSkip;
-    src = a.gathered + (a.slot_base[r] + cslot) * kDim;
-  }
-  const bool use = kDirect ? st == kLive : slot < width;
-  // The sink of the softmax head, stored with the chunk statistics so that
-  // phase 2 gets it in the same load.
-  const float sink_h = a.sinks[kHg * hg + qh];
-  u32x4 gb[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) gb[s] = load16(src + fp + 8 * s);
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    if (!use) gb[s] = u32x4{0, 0, 0, 0};
-  *reinterpret_cast<u32x4 *>(&q_lds[qh * kRowStride + qf]) = qv0;
-  *reinterpret_cast<u32x4 *>(&q_lds[qh * kRowStride + qf + 8]) = qv1;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(&vt[sl * kRowStride + fp + 8 * s]) = gb[s];
-  if (kDirect) {
-    // Gather semantics: a non-finite element makes the row invalid. The eight
-    // threads of a slot are eight consecutive lanes.
-    bool nf = false;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) nf |= any_nonfinite(gb[s]);
-    nf = ((__ballot(nf) >> (lane & 56u)) & 0xFFull) != 0;
-    if (st == kLive && nf) st = kBad;
-  }
-  if ((tid & 7) == 0) state[sl] = st;
-  __syncthreads();
-
-  // Logits on MFMA 16x16x32 (M = 16 heads, N = 16 slots, K = 32 features):
-  // wave w takes slots 16 (w % 4) .. +16 and features 256 (w / 4) .. +256
-  // (eight steps); lane l reads row l % 16 at features 32 j + 8 (l / 16) of
-  // step j. The two halves of K go to two planes, added in the softmax.
-  {
-    const uint32_t col = lane & 15;
-    const uint32_t grp = lane >> 4;
-    const uint32_t ts = 16 * (wave & 3), kh = wave >> 2;
-    const uint16_t *qa = &q_lds[col * kRowStride + 256 * kh + 8 * grp];
-    const uint16_t *kb = &vt[(ts + col) * kRowStride + 256 * kh + 8 * grp];
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      acc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(qa + 32 * j)),
-                   as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + 32 * j)), acc);
-    // D lane l: slot ts + l % 16, heads 4 (l / 16) + i.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[(kh * kHg + 4 * grp + i) * kRedStride + ts + col] = acc[i];
-  }
-  __syncthreads();
-
-  // Softmax statistics. Thread t: head t / 32, slots 2 (t % 32) .. +2.
-  {
-    const uint32_t head = qh;
-    const uint32_t part = tid & 31;
-    float lv[2];
-    uint32_t sj[2];
-    bool bad = false;
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t s = 2 * part + j;
-      lv[j] = (red[head * kRedStride + s] + red[(kHg + head) * kRedStride + s]) * a.scale;
-      sj[j] = state[s];
-      const bool live = sj[j] == kLive;
-      bad |= (sj[j] == kBad) || (live && !__builtin_isfinite(lv[j]));
-      if (live && __builtin_isfinite(lv[j])) mx = fmaxf(mx, lv[j]);
-    }
-    mx = half_max(mx);
-    bad = half_any(bad);
-    float ssum = 0.0f;
-    uint32_t hi2 = 0, lo2 = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bool live = sj[j] == kLive && __builtin_isfinite(lv[j]);
-      const float p = live ? expf(lv[j] - mx) : 0.0f;
-      ssum += p;
-      const uint16_t h = bf16_rne_bits(p);
-      const uint16_t l = bf16_rne_bits(p - bf16_bits_to_float(h));
-      hi2 |= static_cast<uint32_t>(h) << (16 * j);
-      lo2 |= static_cast<uint32_t>(l) << (16 * j);
-    }
-    ssum = half_sum(ssum);
-    *reinterpret_cast<uint32_t *>(&phi[head * kPStride + 2 * part]) = hi2;
-    *reinterpret_cast<uint32_t *>(&plo[head * kPStride + 2 * part]) = lo2;
-    if (part == 0)
-      a.stats[a.stat_base[r] + static_cast<uint64_t>(c) * kHeads + kHg * hg + head] =
-          make_float4(mx, ssum, bad ? 1.0f : 0.0f, sink_h);
-  }
-  __syncthreads();
-
-  // O_c = p~ . G_c for the group's 16 heads: wave w's 64 features, K = 64
-  // slots (MFMA 16x16x32: M = 16 heads, N = 16 features, K = 32 slots).
-  const uint32_t li = lane & 15;
-  const uint32_t lg = lane >> 4;
-  f32x4 o[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint32_t off = li * kPStride + 32 * ks + 8 * lg;   // head li, slots 32 ks + 8 lg ..+8
-    const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&phi[off]));
-    const bf16x8 alo = as_bf16x8(*reinterpret_cast<const u32x4 *>(&plo[off]));
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      // Lane li of group lg receives features n0 + li of slots s0 .. s0+3
-      // and s0+4 .. s0+7 (s0 = 32 ks + 8 lg): it addresses slot s0 + li/4
-      // (+4), features n0 + 4 (li % 4) .. +4.
-      const uint32_t n0 = 64 * wave + 16 * nt;
-      const uint32_t s0 = 32 * ks + 8 * lg;
-      const s16x4 b0 = lds_read_tr16(&vt[(s0 + li / 4) * kRowStride + n0 + 4 * (li % 4)]);
-      const s16x4 b1 = lds_read_tr16(&vt[(s0 + 4 + li / 4) * kRowStride + n0 + 4 * (li % 4)]);
-      const s16x8 b8 = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      const bf16x8 b = __builtin_bit_cast(bf16x8, b8);
-      o[nt] = mfma16(ahi, b, o[nt]);
-      o[nt] = mfma16(alo, b, o[nt]);
-    }
-  }
-  // D lane l of tile nt: feature 64 wave + 16 nt + l % 16, heads 4 (l / 16) + i.
-  float *dst = a.opart + a.part_base[r] + (static_cast<uint64_t>(c) * kHeads + kHg * hg) * kDim;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dst[(4 * lg + i) * kDim + 64 * wave + 16 * nt + li] = o[nt][i];
+  attn_chunk_body<kDirect>(sm, a, r, hg, c, [&](uint32_t slot) { return a.indices[a.index_offset[r] + slot]; });
 }
 
 // ---------------------------------------------------------------- phase 2

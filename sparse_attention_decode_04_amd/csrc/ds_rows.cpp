@@ -451,9 +451,9 @@ ds_status ds_rows_gather(const ds_sparse_rows *rows, const int32_t *indices, siz
 namespace {
 
 // Both attention entry points after their own operand checks.
-ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool direct, const void *q,
-                           const float *sinks, const void *gathered, const void *mask, const int32_t *indices,
-                           float scale, void *workspace, float *out, void *stream) {
+ds::AttnArgs attention_args(const ds_sparse_rows *rows, const SparsePlan &p, const void *q, const float *sinks,
+                            const void *gathered, const void *mask, const int32_t *indices, float scale,
+                            void *workspace, float *out) {
   ds::AttnArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.sinks = sinks;
@@ -477,12 +477,23 @@ ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool
     a.stat_base[r] = p.stat_base[r];
     a.part_base[r] = p.part_base[r];
   }
-  // Block b of either phase serves row b % 8 (one XCD per row); phase 1 has
-  // kAttnHeadGroups workgroups per (row, chunk).
+  return a;
+}
+
+// Block b of either phase serves row b % 8 (one XCD per row); phase 1 has
+// kAttnHeadGroups workgroups per (row, chunk).
+uint32_t attention_blocks(const SparsePlan &p) {
   uint32_t max_chunks = 0;
   for (uint32_t r = 0; r < p.rows; ++r) max_chunks = std::max(max_chunks, p.chunks[r]);
+  return ds::kXcds * max_chunks * ds::kAttnHeadGroups;
+}
+
+ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool direct, const void *q,
+                           const float *sinks, const void *gathered, const void *mask, const int32_t *indices,
+                           float scale, void *workspace, float *out, void *stream) {
+  const ds::AttnArgs a = attention_args(rows, p, q, sinks, gathered, mask, indices, scale, workspace, out);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = ds::launch_attn_chunks(a, direct, ds::kXcds * max_chunks * ds::kAttnHeadGroups, s);
+  hipError_t e = ds::launch_attn_chunks(a, direct, attention_blocks(p), s);
   if (e != hipSuccess) return hip_fail(e, "attention chunk launch");
   e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
   return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
@@ -537,6 +548,85 @@ ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows, const void *q, 
   }
   DS_TRY(cap(indices_elems, p.index_end, "indices", "elements"));
   return launch_attention(rows, p, true, q, sinks, nullptr, nullptr, indices, scale, workspace, out, stream);
+}
+
+ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_sparse_rows *srows, const void *idx_q,
+                                    size_t idx_q_elems, const float *weights, size_t weights_elems, float *scores,
+                                    size_t scores_elems, void *idx_workspace, size_t idx_workspace_bytes,
+                                    int32_t *indices, size_t indices_elems, const void *q, size_t q_elems,
+                                    const float *sinks, size_t sinks_elems, float scale, void *attn_workspace,
+                                    size_t attn_workspace_bytes, float *out, size_t out_elems, void *stream) {
+  IndexerPlan p;
+  DS_TRY(check_indexer(irows, &p));
+  DS_TRY(check_indexer_operands(irows, p, idx_q, idx_q_elems, weights, weights_elems, scores, scores_elems));
+  DS_TRY(need(idx_workspace, "indexer top-k workspace"));
+  DS_TRY(need(indices, "indexer output"));
+  DS_TRY(cap(idx_workspace_bytes, indexer_topk_workspace_bytes(p), "indexer top-k workspace", "bytes"));
+  DS_TRY(cap(indices_elems, p.indices_end, "indexer output", "elements"));
+  SparsePlan sp;
+  DS_TRY(check_sparse(srows, &sp));
+  DS_TRY(check_attention_common(sp, q, q_elems, sinks, sinks_elems, scale, attn_workspace, attn_workspace_bytes, out,
+                                out_elems));
+  for (uint32_t r = 0; r < sp.rows; ++r) {
+    if (!srows->kv[r]) return fail("row %u: kv must not be null", r);
+    DS_TRY(cap(srows->kv_elems[r], uint64_t(srows->kv_len[r]) * DS_HEAD_DIM, "kv", "elements"));
+  }
+  if (sp.rows != p.rows) return fail("the indexer table has %u rows, the sparse table %u", p.rows, sp.rows);
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    if (srows->width[r] > DS_TOP_K) return fail("row %u: width must be at most %d (the selected slots)", r, DS_TOP_K);
+    if (srows->index_offset[r] != irows->output_offset[r])
+      return fail("row %u: index_offset must equal the indexer's output_offset", r);
+  }
+
+  // One kernel for the final level and the attention when the indexer keeps
+  // the first stage (every row long enough) and each row's candidates fit
+  // one workgroup; otherwise the two calls, with the same results.
+  uint32_t max_count = 0;
+  for (uint32_t r = 0; r < p.rows; ++r)
+    max_count = std::max(max_count, (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand);
+  if (!fused_rows(p) || max_count > ds::kTopkChunkLater) {
+    DS_TRY(ds_rows_indexer_topk(irows, idx_q, idx_q_elems, weights, weights_elems, scores, scores_elems,
+                                idx_workspace, idx_workspace_bytes, indices, indices_elems, stream));
+    return ds_rows_sparse_attn_direct(srows, q, q_elems, sinks, sinks_elems, indices, indices_elems, scale,
+                                      attn_workspace, attn_workspace_bytes, out, out_elems, stream);
+  }
+  char *ws = static_cast<char *>(idx_workspace);
+  uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
+  uint32_t *floors = reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p));
+  DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, cand, floors, stream));
+
+  // The final level, as run_topk_levels sets it up for the fused candidates
+  // (one chunk per row, checked against the floors).
+  ds::TopkLevelArgs t{};
+  t.scores = scores;
+  t.score_stride = p.max_kv;
+  t.in = cand;
+  t.indices = indices;
+  t.rows = p.rows;
+  t.from_scores = 0;
+  t.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
+  t.floors = floors;
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    const uint32_t blocks = p.blk_begin[r + 1] - p.blk_begin[r];
+    t.count[r] = blocks * ds::kIdxCand;
+    t.in_base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
+    t.offset[r] = irows->offset[r];
+    t.out_offset[r] = irows->output_offset[r];
+    t.final_mask |= 1u << r;
+    t.check_mask |= 1u << r;
+    t.floor_begin[r] = p.blk_begin[r] * ds::kIdxFloors;
+    t.floor_count[r] = blocks * ds::kIdxFloors;
+    t.fallback_count[r] = p.visible[r];
+    t.blk_begin[r] = r;
+  }
+  for (uint32_t r = p.rows; r <= ds::kRowsMax; ++r) t.blk_begin[r] = p.rows;
+  const ds::AttnArgs a =
+      attention_args(srows, sp, q, sinks, nullptr, nullptr, indices, scale, attn_workspace, out);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = ds::launch_topk_attn(t, a, attention_blocks(sp), s);
+  if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
+  e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
+  return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
 }
 
 const char *ds_rows_last_error(void) { return g_error.c_str(); }

@@ -155,6 +155,13 @@ struct AttnArgs {
 hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs &a, uint32_t blocks, hipStream_t s);
 
+// ------------------------------------------------ final top-k + attention
+// One 1024-thread workgroup per attention chunk (blocks as the attention's
+// phase 1): each runs its row's final top-k level over the fused indexer's
+// candidates (t: a single final, checked level) and then its attention chunk
+// on the indices it selected (a: the direct variant's arguments).
+hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t blocks, hipStream_t s);
+
 
 // ---------------------------------------------------------- multi-query indexer
 // query_len (1..8) consecutive queries per row; one workgroup of 8 waves per

@@ -78,6 +78,11 @@ class DeviceRows:
     def indexer_candidates(self, stream=None):
         ds.indexer_candidates(self.itab, self.dev.idx_q, self.dev.idx_w, self.scores, self.fused_ws, stream)
 
+    def indexer_topk_attn(self, stream=None):
+        ds.indexer_topk_attn(self.itab, self.stab, self.dev.idx_q, self.dev.idx_w, self.scores, self.fused_ws,
+                             self.indices, self.dev.attn_q, self.dev.sinks, self.scale, self.attn_ws, self.out,
+                             stream)
+
     def gather(self, stream=None):
         ds.gather(self.stab, self.indices, self.gathered, self.mask, stream)
 
@@ -108,6 +113,12 @@ class DeviceRows:
         top-512), then attention reading the selected KV rows directly."""
         self.indexer_topk(stream)
         self.sparse_attn_direct(stream)
+
+    def step_one(self, stream=None):
+        """The decode core in one call (ds_rows_indexer_topk_attn): the fused
+        indexer, then the final top-k level inside the attention's
+        workgroups, then the combine."""
+        self.indexer_topk_attn(stream)
 
     # host copies, per selected row
     def results(self) -> list[dict]:

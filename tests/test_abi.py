@@ -44,7 +44,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert set(names) == set(ds.FUNCTIONS)
     out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (ds_rows_\w+)", out))
@@ -265,6 +265,34 @@ def test_sparse_capacity_checks(lib):
     expect_invalid(call_direct(lib, t, ws=ds.attn_workspace_bytes(t) - 1), "attention workspace holds")
     expect_invalid(call_direct(lib, t, scale=float("nan")), "scale must be finite and positive")
     expect_invalid(call_direct(lib, stab((10, 10), q_row=[1, 1])), "used twice")
+
+
+def call_step(lib, it, st, q=BIG, w=BIG, s=BIG, ws=BIG, idx=BIG, aq=BIG, sinks=64, scale=0.0441941738, aws=BIG,
+              out=BIG):
+    return lib.ds_rows_indexer_topk_attn(ctypes.byref(it), ctypes.byref(st), FAKE, q, FAKE, w, FAKE, s, FAKE, ws,
+                                         FAKE, idx, FAKE, aq, FAKE, sinks, ctypes.c_float(scale), FAKE, aws,
+                                         FAKE, out, None)
+
+
+def test_indexer_topk_attn_checks(lib):
+    # the two tables must describe the same rows: count, width <= 512 and the
+    # attention's index_offset equal to the indexer's output_offset
+    it = itab((20000, 30000), out_off=(0, 512), q_row=(0, 1))
+    st = stab((20000, 30000), width=(512, 512), index_offset=(0, 512), q_row=(0, 1))
+    expect_invalid(call_step(lib, it, stab((20000,), width=(512,))), "the indexer table has 2 rows, the sparse table 1")
+    expect_invalid(call_step(lib, it, stab((20000, 30000), width=(512, 513), index_offset=(0, 512), q_row=(0, 1))),
+                   "row 1: width must be at most 512")
+    expect_invalid(call_step(lib, it, stab((20000, 30000), width=(512, 512), index_offset=(0, 1024), q_row=(0, 1))),
+                   "row 1: index_offset must equal the indexer's output_offset")
+    # and the checks of both calls
+    expect_invalid(call_step(lib, it, st, ws=ds.indexer_topk_workspace_bytes(it) - 1), "indexer top-k workspace holds")
+    expect_invalid(call_step(lib, it, st, idx=1023), "indexer output holds")
+    expect_invalid(call_step(lib, it, st, aws=ds.attn_workspace_bytes(st) - 1), "attention workspace holds")
+    expect_invalid(call_step(lib, it, st, scale=float("inf")), "scale must be finite and positive")
+    expect_invalid(call_step(lib, it, stab((20000, 30000), width=(512, 512), index_offset=(0, 512), q_row=(0, 1),
+                                          kv_elems=[20000 * 512, 30000 * 512 - 1])), "kv holds")
+    expect_invalid(call_step(lib, itab((20000, 30000), out_off=(0, 512), q_row=(0, 1), keys_elems=[1, 1]), st),
+                   "kv holds")
 
 
 def test_binding_rejects_host_tensors():

@@ -1,0 +1,184 @@
+"""GPU parity of the one-call decode core (ds_rows_indexer_topk_attn).
+
+The call must give the scores, indices and attention output of
+ds_rows_indexer_topk followed by ds_rows_sparse_attn_direct bit for bit,
+whether the final top-k level runs inside the attention's workgroups (every
+row at least 16384 visible keys and at most 65536 keys) or the two calls run
+as they are; on the small workloads the output is also checked against the
+oracle. Sources: docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal"
+(deepseek_indexer_topk_finalize_rows_i32, deepseek_sparse_attention_score_rows_bf16)
+and "mlx-native 0.21.0 src/ops/deepseek_rows.rs" (the rows dispatches run back
+to back). The selected set, its order and the attention's arithmetic are the
+same code either way, so equality is exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ds_oracle as O
+from sparse_attention_decode_04_amd import inputs as I
+from sparse_attention_decode_04_amd import ds_rows as ds
+from sparse_attention_decode_04_amd.runner import DeviceInputs, DeviceRows
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "no HIP device"
+    ds.load()
+    yield
+
+
+def one_and_two(dev, rows=None, width=None):
+    one = DeviceRows(dev, rows=rows, width=width)
+    one.step_one()
+    two = DeviceRows(dev, rows=rows, width=width)
+    two.step_fused()
+    return one.results(), two.results()
+
+
+def check_equal(a, b, label):
+    for r in range(len(a)):
+        assert np.array_equal(a[r]["scores"].view(np.uint32), b[r]["scores"].view(np.uint32)), (label, r, "scores")
+        assert np.array_equal(a[r]["indices"], b[r]["indices"]), (label, r, "indices")
+        assert np.array_equal(a[r]["out"].view(np.uint32), b[r]["out"].view(np.uint32)), (label, r, "out")
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
+def test_step_config_parity(cid):
+    say(f"generating config {cid}: {I.CONFIG_NAMES[cid]}")
+    inp = I.make_config(cid)
+    dev = DeviceInputs(inp)
+    say(f"config {cid}: one call vs indexer_topk + sparse_attn_direct")
+    a, b = one_and_two(dev)
+    check_equal(a, b, f"config {cid}")
+    if cid in (0, 1):
+        orc = O.decode_rows(inp)
+        for r in range(inp.rows):
+            np.testing.assert_array_equal(a[r]["indices"], orc[r]["indices"], err_msg=f"config {cid} row {r}")
+            err = np.abs(a[r]["out"].astype(np.float64) - orc[r]["out"].astype(np.float64))
+            assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (cid, r, err.max(), err.mean())
+
+
+def test_step_ties_fall_back_inside_the_kernel():
+    # all-zero indexer keys: every floor lies above the 512th candidate and
+    # each workgroup selects its row again from the scores
+    kv_len = [17000, 20000, 40000]
+    inp = I.small_rows(41, kv_len)
+    for k in inp.idx_keys:
+        k[:] = 0
+    say("one call: all-zero keys", kv_len)
+    a, b = one_and_two(DeviceInputs(inp))
+    check_equal(a, b, "ties")
+    for r in range(len(kv_len)):
+        np.testing.assert_array_equal(a[r]["indices"], np.arange(512))
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_step_sorted_scores_fall_back_inside_the_kernel(sign):
+    kv_len = [16384, 40000, 65536]
+    inp = I.small_rows(43, kv_len)
+    inp.idx_q[:] = 0
+    inp.idx_w[:] = 0
+    inp.idx_q[:, 0, 0] = I.int_to_bf16_bits(np.array(256))
+    inp.idx_q[:, 0, 1] = I.int_to_bf16_bits(np.array(1))
+    inp.idx_w[:, 0] = sign
+    for k in inp.idx_keys:
+        j = np.arange(k.shape[0])
+        k[:] = 0
+        k[:, 0] = I.int_to_bf16_bits(j // 256)
+        k[:, 1] = I.int_to_bf16_bits(j % 256)
+    say("one call: scores sorted by position, sign", sign)
+    a, b = one_and_two(DeviceInputs(inp))
+    check_equal(a, b, f"sorted {sign}")
+    for r, n in enumerate(kv_len):
+        exp = np.arange(n - 1, n - 513, -1) if sign > 0 else np.arange(512)
+        np.testing.assert_array_equal(a[r]["indices"], exp)
+
+
+def test_step_widths_below_512_write_every_index():
+    # the attention reads the first `width` selected slots; all 512 indices
+    # are still written
+    kv_len = [20000, 30000, 17000]
+    inp = I.small_rows(45, kv_len)
+    dev = DeviceInputs(inp)
+    width = [300, 512, 1]
+    say("one call: widths", width)
+    a, b = one_and_two(dev, width=width)
+    check_equal(a, b, "widths")
+    for r in range(len(kv_len)):
+        assert np.all(a[r]["indices"] != -7), r
+
+
+def test_step_rows_past_65536_keys_take_the_two_calls():
+    kv_len = [70000, 20000]
+    inp = I.small_rows(47, kv_len)
+    say("one call with a 70000-key row")
+    a, b = one_and_two(DeviceInputs(inp))
+    check_equal(a, b, "long row")
+
+
+def test_step_short_row_takes_the_two_calls():
+    kv_len = [600, 40000]
+    inp = I.small_rows(48, kv_len)
+    say("one call with a short row")
+    a, b = one_and_two(DeviceInputs(inp))
+    check_equal(a, b, "short row")
+
+
+def test_step_rows_independent_and_non_finite_kv():
+    # rows of a multi-row call equal one-row calls; a non-finite element in a
+    # selected KV row zeroes that row's output in both forms
+    kv_len = [20000, 33000, 18000]
+    inp = I.small_rows(49, kv_len)
+    dev = DeviceInputs(inp)
+    probe = DeviceRows(dev)
+    probe.step_one()
+    res = probe.results()
+    assert all(x["indices"].min() >= 0 for x in res)       # offsets 0, every slot selected
+    kv0 = dev.kv[0].view(-1, 512)
+    kv2 = dev.kv[2].view(-1, 512)
+    kv0[int(res[0]["indices"][5]), 17] = 0x7FC0            # bf16 NaN
+    kv2[int(res[2]["indices"][300]), 3] = 0x7F80           # bf16 +inf
+    say("one call: non-finite selected KV rows, multi vs single rows")
+    a, b = one_and_two(dev)
+    check_equal(a, b, "non-finite kv")
+    assert not a[0]["out"].any() and not a[2]["out"].any() and a[1]["out"].any()
+    for r in range(len(kv_len)):
+        one = DeviceRows(dev, rows=[r])
+        one.step_one()
+        o = one.results()[0]
+        assert np.array_equal(o["indices"], a[r]["indices"]), r
+        assert np.array_equal(o["out"].view(np.uint32), a[r]["out"].view(np.uint32)), r
+
+
+def test_step_graph_replay_matches_eager():
+    inp = I.make_config(3)
+    dev = DeviceInputs(inp)
+    eager = DeviceRows(dev)
+    eager.step_one()
+    ref = eager.results()
+    g_run = DeviceRows(dev)
+    g_run.step_one()                                   # warm-up before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_run.step_one()
+    say("one call: graph replays vs eager")
+    for rep in range(3):
+        g_run.out.zero_()
+        g_run.indices.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = g_run.results()
+        check_equal(got, ref, f"replay {rep}")
+        eager.step_one()
+        torch.cuda.synchronize()
