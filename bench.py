@@ -251,6 +251,11 @@ def main():
 
     import torch
 
+    # Every launch and event goes to one stream of the bench's own (default
+    # priority), as a serving loop would use: work on the legacy null stream
+    # measured about 1 us more per step.
+    torch.cuda.set_stream(torch.cuda.Stream())
+
     if args.copy_calibration:
         n = 64 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

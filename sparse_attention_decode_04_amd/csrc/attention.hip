@@ -55,8 +55,12 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
   const uint32_t rest = blockIdx.x / kXcds;
   const uint32_t hg = rest % kAttnHeadGroups;
   const uint32_t c = rest / kAttnHeadGroups;
-  if (r >= a.rows || c >= a.chunks[r]) return;
-  attn_chunk_body<kDirect>(sm, a, r, hg, c, [&](uint32_t slot) { return a.indices[a.index_offset[r] + slot]; });
+  uint32_t rows = a.rows, chunks = a.chunks[r], ioff = a.index_offset[r];
+  uint64_t ibits = reinterpret_cast<uint64_t>(a.indices);
+  const AttnRow ar = attn_row<kDirect>(a, r, rows, chunks, ibits, ioff);   // one batch of argument loads
+  if (r >= rows || c >= chunks) return;
+  const int32_t *const idx = global_ptr<const int32_t>(ibits) + ioff;
+  attn_chunk_body<kDirect>(sm, ar, hg, c, [&](uint32_t slot) { return idx[slot]; });
 }
 
 // ---------------------------------------------------------------- phase 2
@@ -66,13 +70,18 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   constexpr int kVec = kAttnDimChunk / 4 / 4;   // f32x4 per thread
   const uint32_t r = blockIdx.x % kXcds;
   const uint32_t dc = blockIdx.x / kXcds;
-  if (r >= a.rows) return;
-  const uint32_t nch = a.chunks[r];
+  // The row's arguments in one batch of scalar loads (one wait).
+  uint32_t rows = a.rows, nch = a.chunks[r], q_row = a.q_row[r];
+  uint64_t sbits = reinterpret_cast<uint64_t>(a.stats), sbase = a.stat_base[r];
+  uint64_t pbits = reinterpret_cast<uint64_t>(a.opart), pbase = a.part_base[r];
+  uint64_t obits = reinterpret_cast<uint64_t>(a.out);
+  asm volatile("" : "+s"(rows), "+s"(nch), "+s"(q_row), "+s"(sbits), "+s"(sbase), "+s"(pbits), "+s"(pbase), "+s"(obits));
+  if (r >= rows) return;
   const uint32_t tid = threadIdx.x;
   const uint32_t head = tid >> 2;
   const uint32_t d0 = kAttnDimChunk * dc + 4 * kVec * (tid & 3);
-  const float4 *stats = a.stats + a.stat_base[r] + head;
-  const float *op = a.opart + a.part_base[r] + static_cast<uint64_t>(head) * kDim + d0;
+  const float4 *stats = global_ptr<const float4>(sbits) + sbase + head;
+  const float *op = global_ptr<const float>(pbits) + pbase + static_cast<uint64_t>(head) * kDim + d0;
   constexpr int kB = 8;   // chunks per batch of loads
   auto stat_at = [&](uint32_t cc) { return stats[static_cast<uint64_t>(min(cc, nch - 1)) * kHeads]; };
   auto part_at = [&](uint32_t cc, int h) {
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     }
   }
   const float invz = bad ? 0.0f : 1.0f / z;
-  float *dst = a.out + (static_cast<uint64_t>(a.q_row[r]) * kHeads + head) * kDim + d0;
+  float *dst = global_ptr<float>(obits) + (static_cast<uint64_t>(q_row) * kHeads + head) * kDim + d0;
 #pragma unroll
   for (int h = 0; h < kVec; ++h) {
     f32x4 v;

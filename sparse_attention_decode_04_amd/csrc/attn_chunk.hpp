@@ -58,80 +58,137 @@ struct AttnChunkShared {
   uint32_t state[kAttnChunk];
 };
 
+// One row's arguments of phase 1, read in one batch (see LevelRow: each
+// read on its own would cost a dependent scalar-load round trip).
+struct AttnRow {
+  const uint16_t *rows;     // direct: the row's KV; gathered: its gathered rows
+  const uint16_t *mask;     // gathered: the row's mask entries
+  const uint16_t *q;        // the row's query [64, 512]
+  const float *sinks;
+  float4 *stats;            // the row's chunk statistics
+  float *opart;             // the row's chunk outputs
+  uint32_t width;
+  uint32_t kv_len;
+  float scale;
+};
+
+// Row r's AttnRow; x0, x1 (32-bit), x2 (64-bit) and x3 (32-bit) are more
+// arguments of the caller read in the same batch (in as values read from the
+// arguments, out unchanged).
+template <bool kDirect>
+__device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, uint32_t r, uint32_t &x0, uint32_t &x1, uint64_t &x2,
+                                            uint32_t &x3) {
+  uint64_t rows = reinterpret_cast<uint64_t>(kDirect ? a.kv[r] : a.gathered);
+  uint64_t mask = reinterpret_cast<uint64_t>(a.mask), slot_base = kDirect ? 0 : a.slot_base[r];
+  uint64_t q = reinterpret_cast<uint64_t>(a.q), sinks = reinterpret_cast<uint64_t>(a.sinks);
+  uint64_t stats = reinterpret_cast<uint64_t>(a.stats), stat_base = a.stat_base[r];
+  uint64_t opart = reinterpret_cast<uint64_t>(a.opart), part_base = a.part_base[r];
+  uint32_t q_row = a.q_row[r], width = a.width[r], kv_len = a.kv_len[r], scale = __float_as_uint(a.scale);
+  asm volatile("" : "+s"(rows), "+s"(mask), "+s"(slot_base), "+s"(q), "+s"(sinks), "+s"(stats), "+s"(stat_base),
+               "+s"(opart), "+s"(part_base), "+s"(q_row), "+s"(width), "+s"(kv_len), "+s"(scale), "+s"(x0), "+s"(x1),
+               "+s"(x2), "+s"(x3));
+  AttnRow ar;
+  ar.rows = global_ptr<const uint16_t>(rows) + slot_base * kDim;
+  ar.mask = global_ptr<const uint16_t>(mask) + slot_base;
+  ar.q = global_ptr<const uint16_t>(q) + static_cast<uint64_t>(q_row) * kHeads * kDim;
+  ar.sinks = global_ptr<const float>(sinks);
+  ar.stats = global_ptr<float4>(stats) + stat_base;
+  ar.opart = global_ptr<float>(opart) + part_base;
+  ar.width = width;
+  ar.kv_len = kv_len;
+  ar.scale = __uint_as_float(scale);
+  return ar;
+}
+
 // Phase 1 for (row r, head group hg, chunk c) by the first kChunkThreads
 // threads of the workgroup; further waves of a wider workgroup only take
 // part in the barriers. raw_index_at(slot) gives the direct variant the
 // index of one of the row's slots (slot < width).
 template <bool kDirect, class RawIndex>
-__device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnArgs &a, uint32_t r, uint32_t hg,
-                                                uint32_t c, const RawIndex &raw_index_at) {
+__device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnRow &a, uint32_t hg, uint32_t c,
+                                                const RawIndex &raw_index_at) {
   uint16_t *const vt = sm.vt;
   uint16_t *const q_lds = sm.q_lds;
   float *const red = sm.red;
   uint16_t *const phi = sm.phi;
   uint16_t *const plo = sm.plo;
   uint32_t *const state = sm.state;
-  const uint32_t width = a.width[r];
+  const uint32_t width = a.width;
   const uint32_t tid = threadIdx.x;
   const bool active = tid < static_cast<uint32_t>(kChunkThreads);   // wave-uniform
   const uint32_t lane = tid & 63;
-  const uint32_t wave = tid >> 6;
+  // Wave-uniform (as a scalar, so that slot and row arithmetic stays scalar).
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t qh = tid >> 5;            // query head within the group (and the softmax head)
   float sink_h = 0.0f;
 
   if (active) {
-    // Loads: thread t moves features 64 (t % 8) .. +64 of slot t / 8, and
-    // features 16 (t % 32) .. +16 of query head t / 32 of the group, each byte
-    // once. They are unconditional (a slot past the width reads the row's last
-    // slot, a sentinel or bad index reads KV row 0) and masked afterwards, so
-    // they are all in flight at once. The slot's index (or mask entry) goes
-    // first: the KV row load depends on it, and loads complete in issue order.
-    const uint32_t sl = tid >> 3;            // slot within the chunk
-    const uint32_t fp = 64 * (tid & 7);      // this thread's 64 features of it
-    const uint32_t slot = c * kAttnChunk + sl;
-    const uint32_t cslot = min(slot, width - 1);
-    int32_t raw_index = 0;
-    uint16_t raw_mask = 0;
-    if (kDirect) raw_index = raw_index_at(cslot);
-    else raw_mask = a.mask[a.slot_base[r] + cslot];
-    const uint32_t qf = 16 * (tid & 31);
-    const uint16_t *qrow = a.q + (static_cast<uint64_t>(a.q_row[r]) * kHeads + kHg * hg + qh) * kDim + qf;
-    const u32x4 qv0 = load16(qrow), qv1 = load16(qrow + 8);
-    uint32_t st;
-    const uint16_t *src;
-    if (kDirect) {
-      const int32_t i = slot < width ? raw_index : -1;
-      const bool ok = i >= 0 && static_cast<uint32_t>(i) < a.kv_len[r];
-      st = ok ? kLive : ((slot < width && i != -1) ? kBad : kSkip);
-      src = a.kv[r] + static_cast<uint64_t>(ok ? i : 0) * kDim;
-    } else {
-      st = slot < width ? mask_state(raw_mask) : kSkip;
-      src = a.gathered + (a.slot_base[r] + cslot) * kDim;
+    // Loads: wave w moves slots 8w .. 8w + 7 of the chunk and query heads
+    // 2w, 2w + 1 of the group, one whole 1 KiB row per load instruction
+    // (lane l: features 8l .. 8l + 8), each byte once. They are
+    // unconditional (a slot past the width reads the row's last slot, a
+    // sentinel or bad index reads KV row 0) and masked afterwards, so they
+    // are all in flight at once. The slots' indices (or mask entries) come
+    // first: the row loads depend on them.
+    const uint32_t s0 = c * kAttnChunk + 8 * wave;   // first slot of this wave
+    int32_t raw_index[8];
+    uint16_t raw_mask[8];
+  #pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t cslot = min(s0 + s, width - 1);
+      // Every lane reads the same slot: the value is wave-uniform.
+      if (kDirect) raw_index[s] = __builtin_amdgcn_readfirstlane(raw_index_at(cslot));
+      else raw_mask[s] = a.mask[cslot];
     }
-    const bool use = kDirect ? st == kLive : slot < width;
+    // The row's fields once, out of the loop below.
+    const uint32_t kv_len = a.kv_len;
+    const uint16_t *const kv_row0 = a.rows;
+    uint32_t st[8];
+    bool use[8];
+    const uint16_t *src[8];
+  #pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t slot = s0 + s;
+      if (kDirect) {
+        const int32_t i = slot < width ? raw_index[s] : -1;
+        const bool ok = i >= 0 && static_cast<uint32_t>(i) < kv_len;
+        st[s] = ok ? kLive : ((slot < width && i != -1) ? kBad : kSkip);
+        src[s] = kv_row0 + static_cast<uint64_t>(ok ? i : 0) * kDim;
+      } else {
+        st[s] = slot < width ? mask_state(raw_mask[s]) : kSkip;
+        src[s] = kv_row0 + static_cast<uint64_t>(min(slot, width - 1)) * kDim;
+      }
+      use[s] = kDirect ? st[s] == kLive : slot < width;
+    }
+    u32x4 gb[8];
+  #pragma unroll
+    for (int s = 0; s < 8; ++s) gb[s] = load16(src[s] + 8 * lane);
+    const uint16_t *qbase = a.q + (kHg * hg + 2 * wave) * kDim + 8 * lane;
+    const u32x4 qv0 = load16(qbase), qv1 = load16(qbase + kDim);
     // The sink of the softmax head, stored with the chunk statistics so that
     // phase 2 gets it in the same load.
     sink_h = a.sinks[kHg * hg + qh];
-    u32x4 gb[8];
-  #pragma unroll
-    for (int s = 0; s < 8; ++s) gb[s] = load16(src + fp + 8 * s);
+    // Every load is issued before any of their results is used (the
+    // scheduler would otherwise pull the masking of the first rows up
+    // between the loads, with a wait for them that holds back the rest).
+    __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
     for (int s = 0; s < 8; ++s)
-      if (!use) gb[s] = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4 *>(&q_lds[qh * kRowStride + qf]) = qv0;
-    *reinterpret_cast<u32x4 *>(&q_lds[qh * kRowStride + qf + 8]) = qv1;
+      if (!use[s]) gb[s] = u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4 *>(&q_lds[(2 * wave) * kRowStride + 8 * lane]) = qv0;
+    *reinterpret_cast<u32x4 *>(&q_lds[(2 * wave + 1) * kRowStride + 8 * lane]) = qv1;
   #pragma unroll
-    for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(&vt[sl * kRowStride + fp + 8 * s]) = gb[s];
+    for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(&vt[(8 * wave + s) * kRowStride + 8 * lane]) = gb[s];
     if (kDirect) {
-      // Gather semantics: a non-finite element makes the row invalid. The eight
-      // threads of a slot are eight consecutive lanes.
-      bool nf = false;
+      // Gather semantics: a non-finite element makes the row invalid.
   #pragma unroll
-      for (int s = 0; s < 8; ++s) nf |= any_nonfinite(gb[s]);
-      nf = ((__ballot(nf) >> (lane & 56u)) & 0xFFull) != 0;
-      if (st == kLive && nf) st = kBad;
+      for (int s = 0; s < 8; ++s)
+        if (st[s] == kLive && __ballot(any_nonfinite(gb[s])) != 0) st[s] = kBad;
     }
-    if ((tid & 7) == 0) state[sl] = st;
+    if (lane == 0) {
+  #pragma unroll
+      for (int s = 0; s < 8; ++s) state[8 * wave + s] = st[s];
+    }
   }
   __syncthreads();
 
@@ -194,7 +251,7 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnA
       *reinterpret_cast<uint32_t *>(&phi[head * kPStride + 2 * part]) = hi2;
       *reinterpret_cast<uint32_t *>(&plo[head * kPStride + 2 * part]) = lo2;
       if (part == 0)
-        a.stats[a.stat_base[r] + static_cast<uint64_t>(c) * kHeads + kHg * hg + head] =
+        a.stats[static_cast<uint64_t>(c) * kHeads + kHg * hg + head] =
             make_float4(mx, ssum, bad ? 1.0f : 0.0f, sink_h);
     }
   }
@@ -229,7 +286,7 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnA
       }
     }
     // D lane l of tile nt: feature 64 wave + 16 nt + l % 16, heads 4 (l / 16) + i.
-    float *dst = a.opart + a.part_base[r] + (static_cast<uint64_t>(c) * kHeads + kHg * hg) * kDim;
+    float *dst = a.opart + (static_cast<uint64_t>(c) * kHeads + kHg * hg) * kDim;
   #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
   #pragma unroll

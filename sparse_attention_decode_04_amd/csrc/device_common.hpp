@@ -161,6 +161,14 @@ __device__ __forceinline__ bool half_any(bool f) {
 
 // Row of a multi-row launch owning workgroup `b`: the last r with
 // blk_begin[r] <= b. Entries past the last row hold the total block count.
+// A device pointer handed over as its integer bits (to pass it through an
+// empty asm statement), rebuilt as a global-memory pointer so that accesses
+// through it stay global (not flat) loads and stores.
+template <class T>
+__device__ __forceinline__ T *global_ptr(uint64_t bits) {
+  return (T *)((__attribute__((address_space(1))) T *)bits);
+}
+
 __device__ __forceinline__ uint32_t row_of_block(const uint32_t *blk_begin, uint32_t b) {
   uint32_t r = 0;
 #pragma unroll

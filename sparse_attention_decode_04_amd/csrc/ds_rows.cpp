@@ -212,8 +212,9 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
     a.visible[r] = p.visible[r];
     a.q_row[r] = rows->q_row[r];
   }
-  const hipError_t e = ds::launch_indexer_score(a, p.blk_begin[ds::kRowsMax], cand != nullptr,
-                                                static_cast<hipStream_t>(stream));
+  uint32_t max_row_blocks = 1;
+  for (uint32_t r = 0; r < p.rows; ++r) max_row_blocks = std::max(max_row_blocks, p.blk_begin[r + 1] - p.blk_begin[r]);
+  const hipError_t e = ds::launch_indexer_score(a, max_row_blocks, cand != nullptr, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
 }
 

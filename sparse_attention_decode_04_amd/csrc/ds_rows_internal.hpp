@@ -54,7 +54,8 @@ struct IndexerArgs {
   uint64_t *cand;                   // fused: kIdxCand keys per block (0 = none)
   uint32_t *floors;                 // fused: kIdxFloors floors per block (one per wave)
 };
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, bool fused, hipStream_t s);
+// Grid (max_row_blocks, a.rows): workgroup (x, r) is row r's x-th block.
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s);
 
 // ------------------------------------------------------------------ top-k
 // One selection level: every workgroup reduces a chunk of one row's

@@ -62,9 +62,10 @@ static_assert((kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile + kIdxRing - 
 // One wave's candidates (fused stage, see above): o[e] are the score bits
 // (0 = not valid) of the lane's kept keys, kidx[e] their key indices.
 __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint32_t (&o)[4],
-                                                const uint32_t (&kidx)[4], uint32_t wave, uint32_t lane) {
-  const uint64_t slot0 = static_cast<uint64_t>(blockIdx.x) * kIdxCand + wave * kIdxWaveCand;
-  const uint64_t floor_at = static_cast<uint64_t>(blockIdx.x) * kIdxFloors + wave;
+                                                const uint32_t (&kidx)[4], uint32_t block, uint32_t wave,
+                                                uint32_t lane) {
+  const uint64_t slot0 = static_cast<uint64_t>(block) * kIdxCand + wave * kIdxWaveCand;
+  const uint64_t floor_at = static_cast<uint64_t>(block) * kIdxFloors + wave;
   auto count_ge = [&](uint32_t t) -> uint32_t {   // keys of the wave with score bits >= t
     uint32_t c = 0;
 #pragma unroll
@@ -108,19 +109,33 @@ template <bool kFused>
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs a) {
   __shared__ u32x4 q_lds[kHeads * kIdxDim / 8];   // 16 KiB
 
-  const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
-  const uint32_t n = a.kv_len[r];
-  const uint32_t visible = a.visible[r];
+  // Grid: (workgroups of the longest row, rows). Row r is blockIdx.y, known
+  // at launch, so every argument of the row is read in one batch of scalar
+  // loads (a row found from the block index would first wait for the block
+  // table). Workgroups past the row's own count have no keys and end after
+  // the common set-up, before any store.
+  const uint32_t r = blockIdx.y;
+  uint32_t blk0 = a.blk_begin[r], blk1 = a.blk_begin[r + 1], n = a.kv_len[r], visible = a.visible[r];
+  uint32_t qr = a.q_row[r];
+  uint64_t kbits = reinterpret_cast<uint64_t>(a.keys[r]), qbits = reinterpret_cast<uint64_t>(a.q),
+           wbits = reinterpret_cast<uint64_t>(a.w), sbits = reinterpret_cast<uint64_t>(a.scores);
+  uint64_t sstride = a.score_stride;
+  // One use of them all: the compiler issues these scalar loads together and
+  // waits once, rather than in dependent batches ahead of their first uses.
+  asm volatile("" : "+s"(blk0), "+s"(blk1), "+s"(n), "+s"(visible), "+s"(qr), "+s"(kbits), "+s"(qbits), "+s"(wbits),
+               "+s"(sbits), "+s"(sstride));
+  const uint16_t *const keys = global_ptr<const uint16_t>(kbits);
+  const uint32_t nblk = blk1 - blk0;
+  const bool live = blockIdx.x < nblk;   // uniform
+  const uint32_t block = blk0 + blockIdx.x;   // workgroup index in the candidate layout
   // Tiles of 16 keys are dealt round robin over the row's waves: wave w of
   // the row's workgroup b takes tiles t0 = 4b + w, t0 + S, t0 + 2S, ...
   // (S = 4 x the row's workgroups), so at any time the row's waves read
   // neighbouring tiles.
-  const uint32_t nblk = a.blk_begin[r + 1] - a.blk_begin[r];
   const uint32_t tstride = kIdxWaves * nblk;
-  const uint16_t *__restrict__ keys = a.keys[r];
-  const uint16_t *__restrict__ q = a.q + static_cast<uint64_t>(a.q_row[r]) * kHeads * kIdxDim;
-  const float *__restrict__ w = a.w + static_cast<uint64_t>(a.q_row[r]) * kHeads;
-  float *__restrict__ scores = a.scores + static_cast<uint64_t>(r) * a.score_stride;
+  const uint16_t *__restrict__ q = global_ptr<const uint16_t>(qbits) + static_cast<uint64_t>(qr) * kHeads * kIdxDim;
+  const float *__restrict__ w = global_ptr<const float>(wbits) + static_cast<uint64_t>(qr) * kHeads;
+  float *__restrict__ scores = global_ptr<float>(sbits) + static_cast<uint64_t>(r) * sstride;
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -137,8 +152,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   const float wv = w[tid & (kHeads - 1)];
 
   const uint32_t tiles = (n + kIdxTile - 1) / kIdxTile;
-  const uint32_t t0 = kIdxWaves * (blockIdx.x - a.blk_begin[r]) + wave;
-  const uint32_t mine = tiles > t0 ? (tiles - t0 + tstride - 1) / tstride : 0;
+  const uint32_t t0 = kIdxWaves * blockIdx.x + wave;
+  const uint32_t mine = live && tiles > t0 ? (tiles - t0 + tstride - 1) / tstride : 0;
   auto key_of = [&](uint32_t i) { return (t0 + tstride * i) * kIdxTile + col; };
   auto load_tile = [&](uint32_t i, u32x4 (&kb)[4]) {
     const uint32_t key = min(key_of(i), n - 1);   // tail: clamp, not stored
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
 #pragma unroll
     for (int i = 0; i < 4; ++i) wt[m][i] = w_lds[16 * m + 4 * grp + i];
   }
-  if (!kFused && mine == 0) return;   // (in the fused stage every wave writes its floor)
+  if (!live || (!kFused && mine == 0)) return;   // (in the fused stage every wave of a row writes its floor)
 
   // Tiles go in groups of 4: each lane keeps its head group's partial sum of
   // the group's tiles, then two lane-row swaps finish all four head sums at
@@ -220,15 +235,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
       const uint32_t i = 4 * (groups - 1 - e) + grp;   // (unused when groups <= e: fifo[e] is 0)
       kidx[e] = key_of(i);
     }
-    wave_candidates(a, fifo, kidx, wave, lane);
+    wave_candidates(a, fifo, kidx, block, wave, lane);
   }
 }
 
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t blocks, bool fused, hipStream_t s) {
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s) {
+  const dim3 grid(max_row_blocks, a.rows);
   if (fused)
-    hipLaunchKernelGGL(indexer_score_kernel<true>, dim3(blocks), dim3(kIdxThreads), 0, s, a);
+    hipLaunchKernelGGL(indexer_score_kernel<true>, grid, dim3(kIdxThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(indexer_score_kernel<false>, dim3(blocks), dim3(kIdxThreads), 0, s, a);
+    hipLaunchKernelGGL(indexer_score_kernel<false>, grid, dim3(kIdxThreads), 0, s, a);
   return hipGetLastError();
 }
 

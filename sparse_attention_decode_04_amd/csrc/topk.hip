@@ -53,8 +53,10 @@ template <bool kFromScores, int kPerLater = kTopkPerThreadLater>
 __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs a) {
   __shared__ TopkShared sh;
   const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
-  select_level<kFromScores, kPerLater>(sh, a, r, blockIdx.x - a.blk_begin[r],
-                                       [&](uint32_t pos, int32_t index) { a.indices[a.out_offset[r] + pos] = index; });
+  uint32_t blk0 = a.blk_begin[r], out_offset = a.out_offset[r];
+  const LevelRow lr = level_row(a, r, blk0, out_offset);
+  int32_t *const indices = a.indices + out_offset;
+  select_level<kFromScores, kPerLater>(sh, lr, blockIdx.x - blk0, [&](uint32_t pos, int32_t index) { indices[pos] = index; });
 }
 
 hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s) {

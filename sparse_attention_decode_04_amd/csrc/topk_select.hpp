@@ -120,6 +120,16 @@ struct KeyCand {
   }
 };
 
+// A caller's hook into the counting select: once the lowest bin that holds a
+// selected key is known, touch(key_of) is called with key_of(e) giving this
+// thread's candidate e if it lies in that bin or above (else 0). Those keys
+// are a superset of the selected ones, known before their ranks are; the
+// attention uses the hook to start fetching the rows it will read.
+struct NoTouch {
+  template <class KeyOf>
+  __device__ __forceinline__ void operator()(const KeyOf &) const {}
+};
+
 // Best `need` of the workgroup's candidates (kPer per thread, read through
 // `c`; their score bits lie in [omin, omax]), emitted in rank order through
 // emit(pos, key). kSample: pre-filter the histogram by a sampled lower bin
@@ -127,9 +137,10 @@ struct KeyCand {
 // kFresh: hist, cursor, count and lo still hold the zeros written at the
 // start of the kernel (published by a barrier since), and no earlier reader
 // of the shared arrays remains, so they are not cleared again.
-template <int kPer, bool kSample, bool kFresh = false, class Cand, class Emit>
+template <int kPer, bool kSample, bool kFresh = false, class Cand, class Emit, class Touch = NoTouch>
 __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, uint32_t total, uint32_t need,
-                                                uint32_t omin, uint32_t omax, const Emit &emit) {
+                                                uint32_t omin, uint32_t omax, const Emit &emit,
+                                                const Touch &touch = Touch{}) {
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   if constexpr (!kFresh) {
@@ -206,6 +217,7 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
     __syncthreads();
   }
   if (kept <= kTopkSortCap && maxbin <= kFastBinMax) {
+    touch([&](int e) { return in_range(bin_at(e), d) ? c.vkey(e) : 0ull; });
     // Scatter the keys of bins >= d grouped by bin, then rank within bins.
     c.fence();
 #pragma unroll
@@ -407,25 +419,75 @@ __device__ __forceinline__ void select_from_scores(TopkShared &sh, const float *
   if (tid < kTopK) emit(tid, tid < need ? sh.cand[tid] : 0ull);
 }
 
+// One row's arguments of a selection level. They are read in one batch at
+// the start of the kernel: the level's first loads (candidates, floors)
+// depend on several of them, and read one by one they cost a chain of
+// dependent scalar-load round trips.
+struct LevelRow {
+  const uint64_t *in;        // the row's input lists (later levels)
+  const float *scores;       // the row's scores
+  const uint32_t *floors;    // the row's block floors (checked final level)
+  uint64_t *out;             // the row's output lists (levels before the final one)
+  uint32_t count;            // candidates of the row at this level
+  uint32_t floor_count;
+  uint32_t fallback_count;   // scores to select from when the check fails
+  int32_t offset;
+  bool final_level;
+  bool check;                // final level over fused-indexer candidates: check the floors
+};
+
+// Row r's LevelRow. x0 and x1 are two more 32-bit arguments of the caller,
+// read in the same batch (each goes in as a value read from the arguments and
+// comes out unchanged).
+__device__ __forceinline__ LevelRow level_row(const TopkLevelArgs &a, uint32_t r, uint32_t &x0, uint32_t &x1) {
+  uint64_t in = reinterpret_cast<uint64_t>(a.in), in_base = a.in_base[r];
+  uint64_t sc = reinterpret_cast<uint64_t>(a.scores), stride = a.score_stride;
+  uint64_t fl = reinterpret_cast<uint64_t>(a.floors);
+  uint64_t out = reinterpret_cast<uint64_t>(a.out), out_base = a.out_base[r];
+  uint32_t floor_begin = a.floor_begin[r];
+  uint32_t count = a.count[r], fc = a.floor_count[r], fb = a.fallback_count[r];
+  uint32_t off = static_cast<uint32_t>(a.offset[r]);
+  uint32_t fmask = a.final_mask, cmask = a.check_mask;
+  // One use of every loaded value, before any arithmetic on them: the scalar
+  // loads issue together, with one wait.
+  asm volatile("" : "+s"(in), "+s"(in_base), "+s"(sc), "+s"(stride), "+s"(fl), "+s"(out), "+s"(out_base),
+               "+s"(floor_begin), "+s"(count), "+s"(fc), "+s"(fb), "+s"(off), "+s"(fmask), "+s"(cmask), "+s"(x0),
+               "+s"(x1));
+  LevelRow lr;
+  lr.in = global_ptr<const uint64_t>(in) + in_base;
+  lr.scores = global_ptr<const float>(sc) + r * stride;
+  lr.floors = global_ptr<const uint32_t>(fl) + floor_begin;
+  lr.out = global_ptr<uint64_t>(out) + out_base;
+  lr.count = count;
+  lr.floor_count = fc;
+  lr.fallback_count = fb;
+  lr.offset = static_cast<int32_t>(off);
+  lr.final_level = ((fmask >> r) & 1u) != 0;
+  lr.check = lr.final_level && ((cmask >> r) & 1u) != 0;
+  return lr;
+}
+
 // One workgroup's selection over chunk `chunk` of row r (one top-k level).
 // kFromScores: the first level, reading f32 scores. Otherwise a later level,
 // reading the previous level's 64-bit key lists.
 // kPerLater: candidates per thread on a later level (8, or 4 when every row
 // of the level has at most 4096).
 // emit_final(pos, index): the final level's index of rank pos (index +
-// offset, or -1 for an empty slot).
-template <bool kFromScores, int kPerLater, class EmitFinal>
-__device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs &a, uint32_t r, uint32_t chunk,
-                                             const EmitFinal &emit_final) {
+// offset, or -1 for an empty slot). touch: the counting select's hook (see
+// NoTouch), for the keys that can still rank once the lowest selected bin is
+// known.
+template <bool kFromScores, int kPerLater, class EmitFinal, class Touch = NoTouch>
+__device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr, uint32_t chunk,
+                                             const EmitFinal &emit_final, const Touch &touch = Touch{}) {
   constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kPerLater;
   constexpr uint32_t kChunk = kTopkThreads * kPer;
 
   const uint32_t begin = chunk * kChunk;
-  const uint32_t end = min(a.count[r], begin + kChunk);
+  const uint32_t end = min(lr.count, begin + kChunk);
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const uint32_t wave = tid >> 6;
-  const bool final_level = (a.final_mask >> r) & 1u;
+  const bool final_level = lr.final_level;
 
   sh.hist[tid] = 0;
   sh.cursor[tid] = 0;
@@ -441,7 +503,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs
   uint32_t ordv[kFromScores ? kPer : 1];     // score bits, 0 = no candidate
   uint64_t keyv[kFromScores ? 1 : kPer];
   if constexpr (kFromScores) {
-    const char *sc = reinterpret_cast<const char *>(a.scores + static_cast<uint64_t>(r) * a.score_stride);
+    const char *sc = reinterpret_cast<const char *>(lr.scores);
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       ordv[e] = *reinterpret_cast<const uint32_t *>(sc + 4u * min(begin + tid + kTopkThreads * e, lastp));
@@ -451,7 +513,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs
       ordv[e] = p < end ? static_cast<uint32_t>(topk_key(__uint_as_float(ordv[e]), p) >> 32) : 0u;
     }
   } else {
-    const char *in = reinterpret_cast<const char *>(a.in + a.in_base[r]);
+    const char *in = reinterpret_cast<const char *>(lr.in);
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       keyv[e] = *reinterpret_cast<const uint64_t *>(in + 8u * min(begin + tid + kTopkThreads * e, lastp));
@@ -461,13 +523,12 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs
   }
   // A checked final level compares the row's highest floor with the last
   // selected key; the floors are loaded now, with the candidates.
-  const bool check_row = !kFromScores && final_level && ((a.check_mask >> r) & 1u);
+  const bool check_row = !kFromScores && lr.check;
   uint32_t floor_hi = 0;
   if constexpr (!kFromScores) {
-    if (check_row && a.floor_count[r] > 0) {
-      floor_hi = a.floors[a.floor_begin[r] + min(tid, a.floor_count[r] - 1)];
-      for (uint32_t b = tid + kTopkThreads; b < a.floor_count[r]; b += kTopkThreads)
-        floor_hi = max(floor_hi, a.floors[a.floor_begin[r] + b]);
+    if (check_row && lr.floor_count > 0) {
+      floor_hi = lr.floors[min(tid, lr.floor_count - 1)];
+      for (uint32_t b = tid + kTopkThreads; b < lr.floor_count; b += kTopkThreads) floor_hi = max(floor_hi, lr.floors[b]);
     }
   }
   auto run = [&](const auto &c) {
@@ -523,9 +584,9 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs
     const bool check = check_row;
     auto emit_out = [&](uint32_t pos, uint64_t kk) {
       if (final_level) {
-        emit_final(pos, kk != 0 ? static_cast<int32_t>(~static_cast<uint32_t>(kk)) + a.offset[r] : -1);
+        emit_final(pos, kk != 0 ? static_cast<int32_t>(~static_cast<uint32_t>(kk)) + lr.offset : -1);
       } else {
-        a.out[a.out_base[r] + static_cast<uint64_t>(chunk) * kTopK + pos] = kk;
+        lr.out[static_cast<uint64_t>(chunk) * kTopK + pos] = kk;
       }
     };
     auto emit = [&](uint32_t pos, uint64_t kk) {
@@ -566,7 +627,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs
         if (!sampled) {
           // Every valid key stays: select over the candidates as loaded, on
           // the shared arrays as the kernel initialised them.
-          counting_select<kPer, false, true>(sh, c, total, need, gmin, gmax, emit);
+          counting_select<kPer, false, true>(sh, c, total, need, gmin, gmax, emit, touch);
           return;
         }
       }
@@ -602,7 +663,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs
         for (int j = 0; j < kCompactPerLane; ++j)
           kc[j] = lane + 64u * j < wcount ? region[lane + 64 * j] : 0ull;
         counting_select<kCompactPerLane, false>(sh, KeyCand<kCompactPerLane>{kc}, kept, need, max(thr, gmin), gmax,
-                                                emit);
+                                                emit, touch);
       } else if constexpr (kFromScores) {
         // Heavy ties: select over every candidate. The score bits move to LDS
         // (over the compaction regions), which frees their registers.
@@ -619,12 +680,16 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const TopkLevelArgs
     if (total > 0) select_chunk(total, need, gmin, gmax, emit);
     if constexpr (kFromScores) return;
     if (!check) return;
-    // The output stores of every wave land before the barrier, so that a
-    // reselection below rewrites them rather than racing them.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();   // the last rank's verdict (viol was cleared at the start)
-    if ((need < static_cast<uint32_t>(kTopK) && max_floor != 0) || sh.viol != 0)
-      select_from_scores(sh, a.scores + static_cast<uint64_t>(r) * a.score_stride, a.fallback_count[r], emit_out);
+    if ((need < static_cast<uint32_t>(kTopK) && max_floor != 0) || sh.viol != 0) {   // uniform
+      // The output stores of every wave land before the second barrier, so
+      // that the reselection rewrites them rather than racing them. (Waiting
+      // only here keeps loads that a caller issued through `touch` off the
+      // common path.)
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      __syncthreads();
+      select_from_scores(sh, lr.scores, lr.fallback_count, emit_out);
+    }
   };
   if constexpr (kFromScores) run(OrdCand<kPer>{ordv, begin + tid});
   else run(KeyCand<kPer>{keyv});
