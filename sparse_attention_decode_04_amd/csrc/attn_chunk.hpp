@@ -28,11 +28,15 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
+// Whether any of the eight bf16 in v is not finite (exponent bits all ones).
+// Per 32-bit word: the exponent fields of both halves plus 0x80 each carry
+// into bit 15 of their half exactly when they are all ones (no carry crosses
+// into the upper half), so one mask, one add and one test cover two values.
 __device__ __forceinline__ bool any_nonfinite(u32x4 v) {
-  bool bad = false;
+  uint32_t c = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) bad |= bf16_bits_nonfinite(v[k] & 0xFFFFu) || bf16_bits_nonfinite(v[k] >> 16);
-  return bad;
+  for (int k = 0; k < 4; ++k) c |= (v[k] & 0x7F807F80u) + 0x00800080u;
+  return (c & 0x80008000u) != 0;
 }
 // Transposing 8-byte LDS read (see the header comment for its lane layout).
 __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
@@ -102,9 +106,10 @@ __device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, uint32_t r, uint3
 
 // Phase 1 for (row r, head group hg, chunk c) by the first kChunkThreads
 // threads of the workgroup; further waves of a wider workgroup only take
-// part in the barriers. raw_index_at(slot) gives the direct variant the
-// index of one of the row's slots (slot < width).
-template <bool kDirect, class RawIndex>
+// part in the barriers, and in the loads when kLoadThreads (512 or 1024)
+// includes them. raw_index_at(slot) gives the direct variant the index of
+// one of the row's slots (slot < width).
+template <bool kDirect, int kLoadThreads = kChunkThreads, class RawIndex>
 __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnRow &a, uint32_t hg, uint32_t c,
                                                 const RawIndex &raw_index_at) {
   uint16_t *const vt = sm.vt;
@@ -120,21 +125,26 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   // Wave-uniform (as a scalar, so that slot and row arithmetic stays scalar).
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t qh = tid >> 5;            // query head within the group (and the softmax head)
-  float sink_h = 0.0f;
+  // The sink of the softmax head, stored with the chunk statistics so that
+  // phase 2 gets it in the same load.
+  const float sink_h = active ? a.sinks[kHg * hg + qh] : 0.0f;
+  constexpr int kSlots = kAttnChunk / (kLoadThreads / 64);   // slots per loading wave: 8 or 4
+  constexpr int kQHeads = kHg / (kLoadThreads / 64);         // query heads per loading wave: 2 or 1
+  static_assert(kLoadThreads == 512 || kLoadThreads == 1024, "8 or 16 loading waves");
 
-  if (active) {
-    // Loads: wave w moves slots 8w .. 8w + 7 of the chunk and query heads
-    // 2w, 2w + 1 of the group, one whole 1 KiB row per load instruction
+  if (tid < static_cast<uint32_t>(kLoadThreads)) {
+    // Loads: wave w moves kSlots slots (kSlots w ..) of the chunk and kQHeads
+    // query heads of the group, one whole 1 KiB row per load instruction
     // (lane l: features 8l .. 8l + 8), each byte once. They are
     // unconditional (a slot past the width reads the row's last slot, a
     // sentinel or bad index reads KV row 0) and masked afterwards, so they
     // are all in flight at once. The slots' indices (or mask entries) come
     // first: the row loads depend on them.
-    const uint32_t s0 = c * kAttnChunk + 8 * wave;   // first slot of this wave
-    int32_t raw_index[8];
-    uint16_t raw_mask[8];
+    const uint32_t s0 = c * kAttnChunk + kSlots * wave;   // first slot of this wave
+    int32_t raw_index[kSlots];
+    uint16_t raw_mask[kSlots];
   #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
       const uint32_t cslot = min(s0 + s, width - 1);
       // Every lane reads the same slot: the value is wave-uniform.
       if (kDirect) raw_index[s] = __builtin_amdgcn_readfirstlane(raw_index_at(cslot));
@@ -143,11 +153,11 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
     // The row's fields once, out of the loop below.
     const uint32_t kv_len = a.kv_len;
     const uint16_t *const kv_row0 = a.rows;
-    uint32_t st[8];
-    bool use[8];
-    const uint16_t *src[8];
+    uint32_t st[kSlots];
+    bool use[kSlots];
+    const uint16_t *src[kSlots];
   #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
       const uint32_t slot = s0 + s;
       if (kDirect) {
         const int32_t i = slot < width ? raw_index[s] : -1;
@@ -160,34 +170,33 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
       }
       use[s] = kDirect ? st[s] == kLive : slot < width;
     }
-    u32x4 gb[8];
+    u32x4 gb[kSlots];
   #pragma unroll
-    for (int s = 0; s < 8; ++s) gb[s] = load16(src[s] + 8 * lane);
-    const uint16_t *qbase = a.q + (kHg * hg + 2 * wave) * kDim + 8 * lane;
-    const u32x4 qv0 = load16(qbase), qv1 = load16(qbase + kDim);
-    // The sink of the softmax head, stored with the chunk statistics so that
-    // phase 2 gets it in the same load.
-    sink_h = a.sinks[kHg * hg + qh];
+    for (int s = 0; s < kSlots; ++s) gb[s] = load16(src[s] + 8 * lane);
+    const uint16_t *qbase = a.q + (kHg * hg + kQHeads * wave) * kDim + 8 * lane;
+    u32x4 qv[kQHeads];
+  #pragma unroll
+    for (int h = 0; h < kQHeads; ++h) qv[h] = load16(qbase + h * kDim);
     // Every load is issued before any of their results is used (the
     // scheduler would otherwise pull the masking of the first rows up
     // between the loads, with a wait for them that holds back the rest).
     __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < kSlots; ++s)
       if (!use[s]) gb[s] = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4 *>(&q_lds[(2 * wave) * kRowStride + 8 * lane]) = qv0;
-    *reinterpret_cast<u32x4 *>(&q_lds[(2 * wave + 1) * kRowStride + 8 * lane]) = qv1;
   #pragma unroll
-    for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(&vt[(8 * wave + s) * kRowStride + 8 * lane]) = gb[s];
+    for (int h = 0; h < kQHeads; ++h) *reinterpret_cast<u32x4 *>(&q_lds[(kQHeads * wave + h) * kRowStride + 8 * lane]) = qv[h];
+  #pragma unroll
+    for (int s = 0; s < kSlots; ++s) *reinterpret_cast<u32x4 *>(&vt[(kSlots * wave + s) * kRowStride + 8 * lane]) = gb[s];
     if (kDirect) {
       // Gather semantics: a non-finite element makes the row invalid.
   #pragma unroll
-      for (int s = 0; s < 8; ++s)
+      for (int s = 0; s < kSlots; ++s)
         if (st[s] == kLive && __ballot(any_nonfinite(gb[s])) != 0) st[s] = kBad;
     }
     if (lane == 0) {
   #pragma unroll
-      for (int s = 0; s < 8; ++s) state[8 * wave + s] = st[s];
+      for (int s = 0; s < kSlots; ++s) state[kSlots * wave + s] = st[s];
     }
   }
   __syncthreads();

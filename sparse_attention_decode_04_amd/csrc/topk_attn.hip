@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   uint64_t unused64 = 0;
   uint32_t unused32 = 0;
   const AttnRow ar = attn_row<true>(a, r, rows, chunks, unused64, unused32);
-  attn_chunk_body<true>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
+  attn_chunk_body<true, kTopkThreads>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
 #pragma unroll
   for (int l = 0; l < kDim / 64; ++l) asm volatile("" ::"v"(pf[l]));
 }
