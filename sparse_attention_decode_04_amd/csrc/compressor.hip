@@ -75,20 +75,27 @@ __global__ __launch_bounds__((CompShape<kHd, kRatio>::kThreads)) void compressor
   constexpr bool overlap = S::kOverlap;
   constexpr uint32_t P = S::kP, hd = kHd, ratio = kRatio;
   const uint32_t r = blockIdx.x;
-  if (r >= a.rows) return;
+  // The row's arguments in one batch of scalar loads, waited for once (read
+  // one after another they would cost dependent round trips).
+  uint32_t rows = a.rows, pos = a.start_pos[r];
+  uint64_t kvs_bits = reinterpret_cast<uint64_t>(a.kv_state[r]), scs_bits = reinterpret_cast<uint64_t>(a.score_state[r]);
+  uint64_t kv_bits = reinterpret_cast<uint64_t>(a.kv), sc_bits = reinterpret_cast<uint64_t>(a.score);
+  uint64_t ape_bits = reinterpret_cast<uint64_t>(a.ape), out_bits = reinterpret_cast<uint64_t>(a.out);
+  asm volatile("" : "+s"(rows), "+s"(pos), "+s"(kvs_bits), "+s"(scs_bits), "+s"(kv_bits), "+s"(sc_bits), "+s"(ape_bits),
+               "+s"(out_bits));
+  if (r >= rows) return;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t iw = wave % S::kItemWays;                        // item way
   const uint32_t g0 = (wave / S::kItemWays) * S::kMyGroups;       // first group of this thread
-  const uint32_t pos = a.start_pos[r];
   const uint32_t token = pos % ratio;
   const uint32_t slot = (overlap ? ratio : 0) + token;
   const bool emit = (pos + 1) % ratio == 0;
-  float *kvs = a.kv_state[r];
-  float *scs = a.score_state[r];
-  const float *kin = a.kv + static_cast<uint64_t>(r) * P;
-  const float *scin = a.score + static_cast<uint64_t>(r) * P;
-  const float *ape = a.ape + static_cast<uint64_t>(token) * P;
-  uint16_t *out = a.out + static_cast<uint64_t>(r) * hd;
+  float *kvs = global_ptr<float>(kvs_bits);
+  float *scs = global_ptr<float>(scs_bits);
+  const float *kin = global_ptr<const float>(kv_bits) + static_cast<uint64_t>(r) * P;
+  const float *scin = global_ptr<const float>(sc_bits) + static_cast<uint64_t>(r) * P;
+  const float *ape = global_ptr<const float>(ape_bits) + static_cast<uint64_t>(token) * P;
+  uint16_t *out = global_ptr<uint16_t>(out_bits) + static_cast<uint64_t>(r) * hd;
   const bool owns_slot = iw == slot % S::kItemWays;               // this thread's items include the slot
 
   // The token at features f and head_dim + f of each of this thread's groups.

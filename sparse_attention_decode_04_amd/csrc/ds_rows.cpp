@@ -801,7 +801,9 @@ ds_status ds_rows_indexer_score_mq(const ds_indexer_rows *rows, uint32_t query_l
     for (uint32_t t = 0; t < query_len; ++t)
       a.visible[r * ds::kMqMaxQueries + t] = std::min<uint32_t>(rows->kv_len[r], (rows->start_pos[r] + t + 1) / DS_RATIO);
   }
-  const hipError_t e = ds::launch_indexer_mq(a, p.blk_begin[ds::kRowsMax], static_cast<hipStream_t>(stream));
+  uint32_t max_row_blocks = 1;
+  for (uint32_t r = 0; r < p.rows; ++r) max_row_blocks = std::max(max_row_blocks, p.blk_begin[r + 1] - p.blk_begin[r]);
+  const hipError_t e = ds::launch_indexer_mq(a, max_row_blocks, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DS_OK : hip_fail(e, "multi-query indexer launch");
 }
 

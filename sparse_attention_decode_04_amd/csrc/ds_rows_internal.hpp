@@ -184,7 +184,8 @@ struct IndexerMqArgs {
   uint32_t visible[kRowsMax * kMqMaxQueries];   // [r * 8 + t]: min(kv_len, (start_pos + t + 1) / 4)
   uint32_t blk_begin[kRowsMax + 1];
 };
-hipError_t launch_indexer_mq(const IndexerMqArgs &a, uint32_t blocks, hipStream_t s);
+// Grid (max_row_blocks, a.rows): workgroup (x, r) is row r's x-th block.
+hipError_t launch_indexer_mq(const IndexerMqArgs &a, uint32_t max_row_blocks, hipStream_t s);
 
 // -------------------------------------------------------------- compressor
 // One decode token of the learned KV compressor per row; one workgroup per

@@ -57,12 +57,21 @@ __global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a
   constexpr int kTiles = kMqChunk / 16;
   __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][kMqChunkBytes];   // 32 KiB
 
-  const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
-  const uint32_t n = a.kv_len[r];
-  const uint32_t k0 = (blockIdx.x - a.blk_begin[r]) * a.keys_per_block;
-  const uint32_t k_end = min(n, k0 + a.keys_per_block);
-  const uint16_t *__restrict__ keys = a.keys[r];
-  const uint32_t Q = a.query_len;
+  // Grid: (workgroups of the longest row, rows); row r is blockIdx.y, so the
+  // row's arguments are read in one batch of scalar loads, waited for once
+  // (see the single-query indexer). Workgroups past the row's own count end.
+  const uint32_t r = blockIdx.y;
+  uint32_t blk0 = a.blk_begin[r], blk1 = a.blk_begin[r + 1], n = a.kv_len[r], kpb = a.keys_per_block;
+  uint32_t Q = a.query_len, q_row = a.q_row[r];
+  uint64_t kbits = reinterpret_cast<uint64_t>(a.keys[r]), qbits = reinterpret_cast<uint64_t>(a.q),
+           wbits = reinterpret_cast<uint64_t>(a.w), sbits = reinterpret_cast<uint64_t>(a.scores);
+  uint64_t sstride = a.score_stride;
+  asm volatile("" : "+s"(blk0), "+s"(blk1), "+s"(n), "+s"(kpb), "+s"(Q), "+s"(q_row), "+s"(kbits), "+s"(qbits),
+               "+s"(wbits), "+s"(sbits), "+s"(sstride));
+  if (blockIdx.x >= blk1 - blk0) return;   // uniform
+  const uint32_t k0 = blockIdx.x * kpb;
+  const uint32_t k_end = min(n, k0 + kpb);
+  const uint16_t *__restrict__ keys = global_ptr<const uint16_t>(kbits);
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -100,12 +109,12 @@ __global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a
   // [32*grp + 8s, +8)) and the head weights of the D rows of this lane.
   const bool live = wave < Q;   // wave-uniform
   const uint32_t t = live ? wave : 0;
-  const uint64_t qrow = static_cast<uint64_t>(a.q_row[r]) + t;
+  const uint64_t qrow = static_cast<uint64_t>(q_row) + t;
   bf16x8 qa[4][4];
   float wt[4][4];
   {
-    const uint16_t *q = a.q + qrow * kHeads * kIdxDim;
-    const float *w = a.w + qrow * kHeads;
+    const uint16_t *q = global_ptr<const uint16_t>(qbits) + qrow * kHeads * kIdxDim;
+    const float *w = global_ptr<const float>(wbits) + qrow * kHeads;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a
     }
   }
   const uint32_t vis = a.visible[r * kRowsMax + t];
-  float *srow = a.scores + (static_cast<uint64_t>(r) * Q + t) * a.score_stride;
+  float *srow = global_ptr<float>(sbits) + (static_cast<uint64_t>(r) * Q + t) * sstride;
   // Every load issued so far (the query, weights and first chunks) has
   // landed: without this wait the compiler, unsure whether the query's
   // loads are done when the loop starts, would wait for the in-flight
@@ -196,8 +205,8 @@ __global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a
   }
 }
 
-hipError_t launch_indexer_mq(const IndexerMqArgs &a, uint32_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL(indexer_mq_kernel<kMqMaxQueries>, dim3(blocks), dim3(64 * kMqMaxQueries), 0, s, a);
+hipError_t launch_indexer_mq(const IndexerMqArgs &a, uint32_t max_row_blocks, hipStream_t s) {
+  hipLaunchKernelGGL(indexer_mq_kernel<kMqMaxQueries>, dim3(max_row_blocks, a.rows), dim3(64 * kMqMaxQueries), 0, s, a);
   return hipGetLastError();
 }
 
