@@ -19,16 +19,17 @@
 // rows G[t] come either from the gathered operand and its mask (after
 // ds_rows_gather) or, in the direct variant, straight from each row's KV
 // through the indices (the gather fused in).
-//   phase 1, per (row, 64-slot chunk c, group of 16 heads), 8 waves: the
+//   phase 1, per (row, 64-slot chunk c, group of 16 heads), 16 waves: the
 //     group's query heads (16 KiB) and the chunk's rows (64 KiB) are loaded
 //     once each, into LDS (the four head groups of a chunk run on one XCD
 //     and share the rows through its L2); the logits on MFMA 16x16x32
-//     (M = 16 heads, N = 16 slots, K = 32 features; eight waves, each one
-//     slot tile and half the features). Per head: the chunk max m_c,
+//     (M = 16 heads, N = 16 slots, K = 32 features; sixteen waves, each one
+//     slot tile and a quarter of the features). Per head (one wave each):
+//     the chunk max m_c,
 //     p~ = exp(l - m_c) as a bf16 pair (hi = bf16(p~), lo = bf16(p~ - hi):
 //     ~16 significant bits) and s_c = sum p~. Then the chunk's output
 //     O_c = p~ . G_c (16 heads x 512 features, f32) on MFMA 16x16x32
-//     (M = 16 heads, N = 16 features, K = 32 slots), each wave owning 64
+//     (M = 16 heads, N = 16 features, K = 32 slots), each wave owning 32
 //     features. The chunk's rows stay in LDS as loaded (slot-major); the B
 //     operand, 8 consecutive slots of one feature per lane, comes from two
 //     transposing LDS reads (ds_read_b64_tr_b16: within each 16-lane group,

@@ -44,7 +44,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
       (__attribute__((address_space(3))) s16x4 *)(p));
 }
 
-constexpr int kChunkThreads = 512;              // 8 waves
+constexpr int kChunkThreads = 1024;             // 16 waves
 constexpr int kHg = kHeads / kAttnHeadGroups;   // heads per phase-1 workgroup (16)
 constexpr int kRowStride = kDim + 8;            // bf16 per LDS row of q and of the chunk's rows: 1040 B
 constexpr int kRedStride = kAttnChunk + 1;      // padded f32 row of the logits
@@ -56,7 +56,7 @@ static_assert(kHg == 16, "one MFMA row tile of heads per workgroup");
 struct AttnChunkShared {
   __attribute__((aligned(16))) uint16_t vt[kAttnChunk * kRowStride];   // the chunk's rows, slot-major
   __attribute__((aligned(16))) uint16_t q_lds[kHg * kRowStride];       // this group's query heads
-  float red[2 * kHg * kRedStride];                                      // logits, one plane per K half
+  float red[(kChunkThreads / 256) * kHg * kRedStride];                  // logits, one plane per K part
   __attribute__((aligned(16))) uint16_t phi[kHg * kPStride];            // p~ hi
   __attribute__((aligned(16))) uint16_t plo[kHg * kPStride];            // p~ lo
   uint32_t state[kAttnChunk];
@@ -105,11 +105,10 @@ __device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, uint32_t r, uint3
 }
 
 // Phase 1 for (row r, head group hg, chunk c) by the first kChunkThreads
-// threads of the workgroup; further waves of a wider workgroup only take
-// part in the barriers, and in the loads when kLoadThreads (512 or 1024)
-// includes them. raw_index_at(slot) gives the direct variant the index of
-// one of the row's slots (slot < width).
-template <bool kDirect, int kLoadThreads = kChunkThreads, class RawIndex>
+// threads of the workgroup (further waves of a wider workgroup would only
+// take part in the barriers). raw_index_at(slot) gives the direct variant the
+// index of one of the row's slots (slot < width).
+template <bool kDirect, class RawIndex>
 __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnRow &a, uint32_t hg, uint32_t c,
                                                 const RawIndex &raw_index_at) {
   uint16_t *const vt = sm.vt;
@@ -124,15 +123,16 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   const uint32_t lane = tid & 63;
   // Wave-uniform (as a scalar, so that slot and row arithmetic stays scalar).
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t qh = tid >> 5;            // query head within the group (and the softmax head)
+  constexpr int kTph = kChunkThreads / kHg;   // softmax threads per head: 32 or 64
+  const uint32_t qh = tid / kTph;              // the softmax head of this thread
   // The sink of the softmax head, stored with the chunk statistics so that
   // phase 2 gets it in the same load.
   const float sink_h = active ? a.sinks[kHg * hg + qh] : 0.0f;
-  constexpr int kSlots = kAttnChunk / (kLoadThreads / 64);   // slots per loading wave: 8 or 4
-  constexpr int kQHeads = kHg / (kLoadThreads / 64);         // query heads per loading wave: 2 or 1
-  static_assert(kLoadThreads == 512 || kLoadThreads == 1024, "8 or 16 loading waves");
+  constexpr int kSlots = kAttnChunk / (kChunkThreads / 64);   // slots per wave: 8 or 4
+  constexpr int kQHeads = kHg / (kChunkThreads / 64);         // query heads per wave: 2 or 1
+  static_assert(kChunkThreads == 512 || kChunkThreads == 1024, "8 or 16 waves");
 
-  if (tid < static_cast<uint32_t>(kLoadThreads)) {
+  if (active) {
     // Loads: wave w moves kSlots slots (kSlots w ..) of the chunk and kQHeads
     // query heads of the group, one whole 1 KiB row per load instruction
     // (lane l: features 8l .. 8l + 8), each byte once. They are
@@ -203,18 +203,21 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
 
   if (active) {
     // Logits on MFMA 16x16x32 (M = 16 heads, N = 16 slots, K = 32 features):
-    // wave w takes slots 16 (w % 4) .. +16 and features 256 (w / 4) .. +256
-    // (eight steps); lane l reads row l % 16 at features 32 j + 8 (l / 16) of
-    // step j. The two halves of K go to two planes, added in the softmax.
+    // wave w takes slots 16 (w % 4) .. +16 and K part w / 4 of kKParts
+    // (kKLen features, kKLen / 32 steps); lane l reads row l % 16 at features
+    // 32 j + 8 (l / 16) of step j. Each part goes to its own plane; the
+    // softmax adds the planes in part order.
     {
+      constexpr int kKParts = kChunkThreads / 256;   // 2 or 4
+      constexpr int kKLen = kDim / kKParts;
       const uint32_t col = lane & 15;
       const uint32_t grp = lane >> 4;
       const uint32_t ts = 16 * (wave & 3), kh = wave >> 2;
-      const uint16_t *qa = &q_lds[col * kRowStride + 256 * kh + 8 * grp];
-      const uint16_t *kb = &vt[(ts + col) * kRowStride + 256 * kh + 8 * grp];
+      const uint16_t *qa = &q_lds[col * kRowStride + kKLen * kh + 8 * grp];
+      const uint16_t *kb = &vt[(ts + col) * kRowStride + kKLen * kh + 8 * grp];
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < kKLen / 32; ++j)
         acc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4 *>(qa + 32 * j)),
                      as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + 32 * j)), acc);
       // D lane l: slot ts + l % 16, heads 4 (l / 16) + i.
@@ -225,29 +228,40 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   __syncthreads();
 
   if (active) {
-    // Softmax statistics. Thread t: head t / 32, slots 2 (t % 32) .. +2.
+    // Softmax statistics. Thread t: head t / kTph, slots kSpt (t % kTph) ..
+    // + kSpt (with 16 waves: one wave per head, one slot per thread).
     {
+      constexpr int kKParts = kChunkThreads / 256;
+      constexpr int kSpt = kAttnChunk / kTph;   // slots per thread: 2 or 1
       const uint32_t head = qh;
-      const uint32_t part = tid & 31;
-      float lv[2];
-      uint32_t sj[2];
+      const uint32_t part = tid % kTph;
+      float lv[kSpt];
+      uint32_t sj[kSpt];
       bool bad = false;
       float mx = -__builtin_inff();
   #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t s = 2 * part + j;
-        lv[j] = (red[head * kRedStride + s] + red[(kHg + head) * kRedStride + s]) * a.scale;
+      for (int j = 0; j < kSpt; ++j) {
+        const uint32_t s = kSpt * part + j;
+        float l = red[head * kRedStride + s];
+  #pragma unroll
+        for (int k = 1; k < kKParts; ++k) l += red[(k * kHg + head) * kRedStride + s];
+        lv[j] = l * a.scale;
         sj[j] = state[s];
         const bool live = sj[j] == kLive;
         bad |= (sj[j] == kBad) || (live && !__builtin_isfinite(lv[j]));
         if (live && __builtin_isfinite(lv[j])) mx = fmaxf(mx, lv[j]);
       }
-      mx = half_max(mx);
-      bad = half_any(bad);
+      if constexpr (kTph == 32) {
+        mx = half_max(mx);
+        bad = half_any(bad);
+      } else {
+        mx = wave_max_f(mx);
+        bad = __ballot(bad) != 0;
+      }
       float ssum = 0.0f;
       uint32_t hi2 = 0, lo2 = 0;
   #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kSpt; ++j) {
         const bool live = sj[j] == kLive && __builtin_isfinite(lv[j]);
         const float p = live ? expf(lv[j] - mx) : 0.0f;
         ssum += p;
@@ -256,9 +270,15 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
         hi2 |= static_cast<uint32_t>(h) << (16 * j);
         lo2 |= static_cast<uint32_t>(l) << (16 * j);
       }
-      ssum = half_sum(ssum);
-      *reinterpret_cast<uint32_t *>(&phi[head * kPStride + 2 * part]) = hi2;
-      *reinterpret_cast<uint32_t *>(&plo[head * kPStride + 2 * part]) = lo2;
+      if constexpr (kTph == 32) {
+        ssum = half_sum(ssum);
+        *reinterpret_cast<uint32_t *>(&phi[head * kPStride + 2 * part]) = hi2;
+        *reinterpret_cast<uint32_t *>(&plo[head * kPStride + 2 * part]) = lo2;
+      } else {
+        ssum = wave_sum_f(ssum);
+        phi[head * kPStride + part] = static_cast<uint16_t>(hi2);
+        plo[head * kPStride + part] = static_cast<uint16_t>(lo2);
+      }
       if (part == 0)
         a.stats[static_cast<uint64_t>(c) * kHeads + kHg * hg + head] =
             make_float4(mx, ssum, bad ? 1.0f : 0.0f, sink_h);
@@ -267,24 +287,26 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   __syncthreads();
 
   if (active) {
-    // O_c = p~ . G_c for the group's 16 heads: wave w's 64 features, K = 64
+    // O_c = p~ . G_c for the group's 16 heads: wave w's kFpw features, K = 64
     // slots (MFMA 16x16x32: M = 16 heads, N = 16 features, K = 32 slots).
+    constexpr int kFpw = kDim / (kChunkThreads / 64);   // features per wave: 64 or 32
+    constexpr int kNt = kFpw / 16;
     const uint32_t li = lane & 15;
     const uint32_t lg = lane >> 4;
-    f32x4 o[4];
+    f32x4 o[kNt];
   #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint32_t off = li * kPStride + 32 * ks + 8 * lg;   // head li, slots 32 ks + 8 lg ..+8
       const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&phi[off]));
       const bf16x8 alo = as_bf16x8(*reinterpret_cast<const u32x4 *>(&plo[off]));
   #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNt; ++nt) {
         // Lane li of group lg receives features n0 + li of slots s0 .. s0+3
         // and s0+4 .. s0+7 (s0 = 32 ks + 8 lg): it addresses slot s0 + li/4
         // (+4), features n0 + 4 (li % 4) .. +4.
-        const uint32_t n0 = 64 * wave + 16 * nt;
+        const uint32_t n0 = kFpw * wave + 16 * nt;
         const uint32_t s0 = 32 * ks + 8 * lg;
         const s16x4 b0 = lds_read_tr16(&vt[(s0 + li / 4) * kRowStride + n0 + 4 * (li % 4)]);
         const s16x4 b1 = lds_read_tr16(&vt[(s0 + 4 + li / 4) * kRowStride + n0 + 4 * (li % 4)]);
@@ -294,13 +316,13 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
         o[nt] = mfma16(alo, b, o[nt]);
       }
     }
-    // D lane l of tile nt: feature 64 wave + 16 nt + l % 16, heads 4 (l / 16) + i.
+    // D lane l of tile nt: feature kFpw wave + 16 nt + l % 16, heads 4 (l / 16) + i.
     float *dst = a.opart + (static_cast<uint64_t>(c) * kHeads + kHg * hg) * kDim;
   #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < kNt; ++nt)
   #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dst[(4 * lg + i) * kDim + 64 * wave + 16 * nt + li] = o[nt][i];
+        dst[(4 * lg + i) * kDim + kFpw * wave + 16 * nt + li] = o[nt][i];
   }
 }
 

@@ -159,8 +159,20 @@ __device__ __forceinline__ bool half_any(bool f) {
   return ((m >> (__lane_id() & 32u)) & 0xFFFFFFFFull) != 0;
 }
 
-// Row of a multi-row launch owning workgroup `b`: the last r with
-// blk_begin[r] <= b. Entries past the last row hold the total block count.
+// Whole-wave float reductions, the result in every lane: the half-wave
+// reduction, then the two halves (v_permlane32_swap), so that every lane ends
+// with the same bits.
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v = half_sum(v);
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = half_max(v);
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
 // A device pointer handed over as its integer bits (to pass it through an
 // empty asm statement), rebuilt as a global-memory pointer so that accesses
 // through it stay global (not flat) loads and stores.
@@ -168,6 +180,9 @@ template <class T>
 __device__ __forceinline__ T *global_ptr(uint64_t bits) {
   return (T *)((__attribute__((address_space(1))) T *)bits);
 }
+
+// Row of a multi-row launch owning workgroup `b`: the last r with
+// blk_begin[r] <= b. Entries past the last row hold the total block count.
 
 __device__ __forceinline__ uint32_t row_of_block(const uint32_t *blk_begin, uint32_t b) {
   uint32_t r = 0;

@@ -121,7 +121,7 @@ struct GatherArgs {
 hipError_t launch_gather(const GatherArgs &a, uint32_t blocks, hipStream_t s);
 
 // -------------------------------------------------------------- attention
-// Phase 1 (chunk): one workgroup of 8 waves per (row, 64-slot chunk, group
+// Phase 1 (chunk): one workgroup of 16 waves per (row, 64-slot chunk, group
 // of 16 heads) computes the logits scale * q . G for its heads, per head the chunk max
 // m_c, p~ = exp(l - m_c), s_c = sum p~ and a bad flag, and the chunk's part
 // of the output, O_c = p~ . G (64 heads x 512 dims, f32), on MFMA. G comes

@@ -17,8 +17,8 @@
 // boundary) and keeps the indices of its own 64 slots in LDS; the
 // workgroups of head group 0 also write their slots to the index output (the
 // last chunk's also the slots past the row's width).
-// The selection's LDS is then reused for the chunk's attention, which the
-// first eight waves compute as the attention kernel does, its indices read
+// The selection's LDS is then reused for the chunk's attention, which all
+// sixteen waves compute as the attention kernel does, its indices read
 // from LDS instead of memory. This removes a kernel boundary and the
 // attention's dependent index load (two HBM round trips become one).
 // The remaining round trip, for the selected KV rows, is started during the
@@ -88,7 +88,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   uint64_t unused64 = 0;
   uint32_t unused32 = 0;
   const AttnRow ar = attn_row<true>(a, r, rows, chunks, unused64, unused32);
-  attn_chunk_body<true, kTopkThreads>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
+  static_assert(kTopkThreads == kChunkThreads, "the attention chunk uses every thread of the workgroup");
+  attn_chunk_body<true>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
 #pragma unroll
   for (int l = 0; l < kDim / 64; ++l) asm volatile("" ::"v"(pf[l]));
 }
