@@ -21,15 +21,6 @@
 // sixteen waves compute as the attention kernel does, its indices read
 // from LDS instead of memory. This removes a kernel boundary and the
 // attention's dependent index load (two HBM round trips become one).
-// The remaining round trip, for the selected KV rows, is started during the
-// selection: as soon as the lowest selected score bin is known (the keys at
-// or above it, a few more than 512, hold every selected key), the row's
-// workgroups each load one word of every 128-byte line of their share of
-// those rows, which brings them into the row's L2 (all of a row's
-// workgroups run on one XCD) while the ranks are still being computed. The
-// words are kept in registers and consumed by an empty asm statement at the
-// end, so the loads are neither dropped by the compiler nor waited for
-// before then.
 #include "attn_chunk.hpp"
 #include "topk_select.hpp"
 
@@ -56,42 +47,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   // last chunk also every slot past the row's width.
   const uint32_t out_end = c + 1 == chunks ? static_cast<uint32_t>(kTopK) : lo + kAttnChunk;
   int32_t *const out = t.indices + t.out_offset[r];
-  // Prefetch share: candidate e of thread tid (pair p = kPerLater tid + e)
-  // belongs to the row's workgroup p mod nwg, so each pair is fetched by one
-  // workgroup and each thread fetches at most one row.
-  const uint32_t nwg = chunks * kAttnHeadGroups;
-  const uint32_t j = c * kAttnHeadGroups + hg;
-  const uint32_t e_mine = (j + nwg - (kPerLater * threadIdx.x) % nwg) % nwg;   // >= kPerLater: none
-  uint32_t pf[kDim / 64];
-#pragma unroll
-  for (int l = 0; l < kDim / 64; ++l) pf[l] = 0;
-  auto touch = [&](const auto &key_of) {
-    uint64_t kk = 0;
-#pragma unroll
-    for (int e = 0; e < kPerLater; ++e)
-      if (static_cast<uint32_t>(e) == e_mine) kk = key_of(e);
-    const int64_t i = static_cast<int64_t>(static_cast<int32_t>(~static_cast<uint32_t>(kk))) + lr.offset;
-    if (kk != 0 && i >= 0 && i < static_cast<int64_t>(a.kv_len[r])) {
-      const uint32_t *row = reinterpret_cast<const uint32_t *>(a.kv[r] + static_cast<uint64_t>(i) * kDim);
-#pragma unroll
-      for (int l = 0; l < kDim / 64; ++l) pf[l] = row[32 * l];   // one word per 128-byte line
-    }
-  };
-  select_level<false, kPerLater>(
-      u.sel, lr, 0,
-      [&](uint32_t pos, int32_t index) {
-        if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
-        if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
-      },
-      touch);
+  select_level<false, kPerLater>(u.sel, lr, 0, [&](uint32_t pos, int32_t index) {
+    if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
+    if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
+  });
   __syncthreads();   // the chunk's indices are in place; the selection's LDS is free
   uint64_t unused64 = 0;
   uint32_t unused32 = 0;
   const AttnRow ar = attn_row<true>(a, r, rows, chunks, unused64, unused32);
   static_assert(kTopkThreads == kChunkThreads, "the attention chunk uses every thread of the workgroup");
   attn_chunk_body<true>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
-#pragma unroll
-  for (int l = 0; l < kDim / 64; ++l) asm volatile("" ::"v"(pf[l]));
 }
 
 hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t blocks, hipStream_t s) {

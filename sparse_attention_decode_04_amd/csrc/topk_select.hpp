@@ -120,16 +120,6 @@ struct KeyCand {
   }
 };
 
-// A caller's hook into the counting select: once the lowest bin that holds a
-// selected key is known, touch(key_of) is called with key_of(e) giving this
-// thread's candidate e if it lies in that bin or above (else 0). Those keys
-// are a superset of the selected ones, known before their ranks are; the
-// attention uses the hook to start fetching the rows it will read.
-struct NoTouch {
-  template <class KeyOf>
-  __device__ __forceinline__ void operator()(const KeyOf &) const {}
-};
-
 // Best `need` of the workgroup's candidates (kPer per thread, read through
 // `c`; their score bits lie in [omin, omax]), emitted in rank order through
 // emit(pos, key). kSample: pre-filter the histogram by a sampled lower bin
@@ -137,10 +127,9 @@ struct NoTouch {
 // kFresh: hist, cursor, count and lo still hold the zeros written at the
 // start of the kernel (published by a barrier since), and no earlier reader
 // of the shared arrays remains, so they are not cleared again.
-template <int kPer, bool kSample, bool kFresh = false, class Cand, class Emit, class Touch = NoTouch>
+template <int kPer, bool kSample, bool kFresh = false, class Cand, class Emit>
 __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, uint32_t total, uint32_t need,
-                                                uint32_t omin, uint32_t omax, const Emit &emit,
-                                                const Touch &touch = Touch{}) {
+                                                uint32_t omin, uint32_t omax, const Emit &emit) {
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   if constexpr (!kFresh) {
@@ -217,7 +206,6 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
     __syncthreads();
   }
   if (kept <= kTopkSortCap && maxbin <= kFastBinMax) {
-    touch([&](int e) { return in_range(bin_at(e), d) ? c.vkey(e) : 0ull; });
     // Scatter the keys of bins >= d grouped by bin, then rank within bins.
     c.fence();
 #pragma unroll
@@ -473,12 +461,10 @@ __device__ __forceinline__ LevelRow level_row(const TopkLevelArgs &a, uint32_t r
 // kPerLater: candidates per thread on a later level (8, or 4 when every row
 // of the level has at most 4096).
 // emit_final(pos, index): the final level's index of rank pos (index +
-// offset, or -1 for an empty slot). touch: the counting select's hook (see
-// NoTouch), for the keys that can still rank once the lowest selected bin is
-// known.
-template <bool kFromScores, int kPerLater, class EmitFinal, class Touch = NoTouch>
+// offset, or -1 for an empty slot).
+template <bool kFromScores, int kPerLater, class EmitFinal>
 __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr, uint32_t chunk,
-                                             const EmitFinal &emit_final, const Touch &touch = Touch{}) {
+                                             const EmitFinal &emit_final) {
   constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kPerLater;
   constexpr uint32_t kChunk = kTopkThreads * kPer;
 
@@ -627,7 +613,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
         if (!sampled) {
           // Every valid key stays: select over the candidates as loaded, on
           // the shared arrays as the kernel initialised them.
-          counting_select<kPer, false, true>(sh, c, total, need, gmin, gmax, emit, touch);
+          counting_select<kPer, false, true>(sh, c, total, need, gmin, gmax, emit);
           return;
         }
       }
@@ -663,7 +649,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
         for (int j = 0; j < kCompactPerLane; ++j)
           kc[j] = lane + 64u * j < wcount ? region[lane + 64 * j] : 0ull;
         counting_select<kCompactPerLane, false>(sh, KeyCand<kCompactPerLane>{kc}, kept, need, max(thr, gmin), gmax,
-                                                emit, touch);
+                                                emit);
       } else if constexpr (kFromScores) {
         // Heavy ties: select over every candidate. The score bits move to LDS
         // (over the compaction regions), which frees their registers.
@@ -683,9 +669,8 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
     __syncthreads();   // the last rank's verdict (viol was cleared at the start)
     if ((need < static_cast<uint32_t>(kTopK) && max_floor != 0) || sh.viol != 0) {   // uniform
       // The output stores of every wave land before the second barrier, so
-      // that the reselection rewrites them rather than racing them. (Waiting
-      // only here keeps loads that a caller issued through `touch` off the
-      // common path.)
+      // that the reselection rewrites them rather than racing them (on the
+      // common path nothing waits for them).
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       __syncthreads();
       select_from_scores(sh, lr.scores, lr.fallback_count, emit_out);
