@@ -67,6 +67,65 @@ struct TopkShared {
   uint32_t count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
 };
 
+// Suffix scan of the 1024-bin histogram by the first four waves, four bins
+// per thread (thread t owns bins 1023 - 4t - k, k = 0..3, the top bin
+// first), and the search for the bin d that holds the need-th key: writes
+// sfx[b] (keys in bins above b) for every bin, digit = d, kept (keys in bins
+// >= d), maxbin (largest count of a bin >= d) and hist_total. One barrier
+// inside (the wave totals); the caller's next barrier publishes the results.
+// Four waves with four bins each issue a fraction of the instructions that
+// sixteen waves with one bin each (and a sixteen-way combine) would.
+static_assert(kBins == 4 * 256 && kTopkThreads >= 256, "four waves, four bins per thread");
+__device__ __forceinline__ void scan_digit(TopkShared &sh, uint32_t need, uint32_t tid) {
+  const uint32_t lane = tid & 63, wave = tid >> 6;
+  const bool mine = wave < 4;   // wave-uniform
+  uint32_t v[4] = {0, 0, 0, 0}, sum = 0, m = 0, incl = 0, imax = 0;
+  if (mine) {
+    const u32x4 h4 = reinterpret_cast<const u32x4 *>(sh.hist)[255 - tid];   // bins 1020 - 4t .. 1023 - 4t
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = h4[3 - k];   // bin 1023 - 4t - k
+      sum += v[k];
+      m = max(m, v[k]);
+    }
+    incl = wave_prefix_sum(sum);
+    imax = wave_prefix_max(m);
+    if (lane == 63) { sh.wsum[wave] = incl; sh.wmax[wave] = imax; }
+  }
+  __syncthreads();
+  if (mine) {
+    const u32x4 s4 = reinterpret_cast<const u32x4 *>(sh.wsum)[0];
+    const u32x4 m4 = reinterpret_cast<const u32x4 *>(sh.wmax)[0];
+    uint32_t pre = 0, premax = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool before_me = static_cast<uint32_t>(k) < wave;
+      pre += before_me ? s4[k] : 0u;
+      premax = before_me ? max(premax, m4[k]) : premax;
+      all += s4[k];
+    }
+    // Largest count in the lanes before this one (their bins are all higher).
+    const uint32_t prev_max = __shfl_up(imax, 1);
+    uint32_t above = pre + incl - sum;   // keys in bins above this thread's first bin
+    uint32_t maxge = max(premax, lane > 0 ? prev_max : 0u);
+    u32x4 sfx4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t b = kBins - 1 - 4 * tid - k;
+      maxge = max(maxge, v[k]);
+      sfx4[3 - k] = above;
+      if (above < need && need <= above + v[k]) {
+        sh.digit = b;
+        sh.kept = above + v[k];
+        sh.maxbin = maxge;
+      }
+      above += v[k];
+    }
+    reinterpret_cast<u32x4 *>(sh.sfx)[255 - tid] = sfx4;
+    if (tid == 0) sh.hist_total = all;
+  }
+}
+
 // Candidates of the first level: score bits per candidate (0 = none), index
 // implied by the position begin + tid + 1024 e.
 template <int N>
@@ -184,16 +243,7 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
     for (int e = 0; e < kPer; ++e)
       if (in_range(bin_at(e), lo)) hist_add(sh.hist, bin_at(e), kBins, lane);
     __syncthreads();
-    uint32_t h, above, maxge, all;
-    scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, all);
-    const uint32_t b = kBins - 1 - tid;
-    sh.sfx[b] = above;
-    if (above < need && need <= above + h) {
-      sh.digit = b;
-      sh.kept = above + h;
-      sh.maxbin = maxge;
-    }
-    if (tid == 0) sh.hist_total = all;
+    scan_digit(sh, need, tid);
     __syncthreads();
     if (sh.hist_total >= need || lo == 0) {
       d = sh.digit;
