@@ -35,7 +35,7 @@
 //     transposing LDS reads (ds_read_b64_tr_b16: within each 16-lane group,
 //     lane i receives the i-th 16-bit element of the 8-byte pieces that
 //     lanes 4k + i/4 address, k = 0..3).
-//   phase 2, per (row, 32-feature chunk), 4 waves: m, Z and the bad flag of
+//   phase 2, per (row, 16-feature chunk), 4 waves: m, Z and the bad flag of
 //     each head from the chunk statistics and the sink, then
 //     out = sum_c e^(m_c - m) O_c / Z in a fixed chunk order.
 // All splits depend only on the row's own width, so rows are independent

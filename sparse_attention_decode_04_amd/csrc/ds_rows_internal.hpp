@@ -126,11 +126,11 @@ hipError_t launch_gather(const GatherArgs &a, uint32_t blocks, hipStream_t s);
 // m_c, p~ = exp(l - m_c), s_c = sum p~ and a bad flag, and the chunk's part
 // of the output, O_c = p~ . G (64 heads x 512 dims, f32), on MFMA. G comes
 // from the gathered operand, or (direct) from each row's KV through the
-// indices. Phase 2 (combine): one workgroup per (row, 32-dim chunk) weighs
+// indices. Phase 2 (combine): one workgroup per (row, 16-dim chunk) weighs
 // the chunks with the sink: out = sum_c exp(m_c - m) O_c / Z.
 constexpr int kAttnChunk = 64;      // slots per phase-1 workgroup
 constexpr int kAttnHeadGroups = 4;  // phase-1 workgroups per chunk (16 heads each)
-constexpr int kAttnDimChunk = 32;   // output dims per phase-2 workgroup
+constexpr int kAttnDimChunk = 16;   // output dims per phase-2 workgroup
 
 struct AttnArgs {
   const uint16_t *q;                // bf16 [_, 64, 512]
