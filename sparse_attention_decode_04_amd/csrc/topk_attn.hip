@@ -26,6 +26,48 @@
 
 namespace ds {
 
+// The row's arguments of both parts (its final top-k level and its attention
+// chunk, direct variant) read in one batch of scalar loads at entry, waited
+// for once; rows and chunks are read in the same batch.
+__device__ __forceinline__ void topk_attn_rows(const TopkLevelArgs &t, const AttnArgs &a, uint32_t r, uint32_t &rows,
+                                               uint32_t &chunks, LevelRow &lr, AttnRow &ar) {
+  uint64_t in = reinterpret_cast<uint64_t>(t.in), in_base = t.in_base[r];
+  uint64_t sc = reinterpret_cast<uint64_t>(t.scores), stride = t.score_stride;
+  uint64_t fl = reinterpret_cast<uint64_t>(t.floors);
+  uint32_t floor_begin = t.floor_begin[r], count = t.count[r], fc = t.floor_count[r], fb = t.fallback_count[r];
+  uint32_t off = static_cast<uint32_t>(t.offset[r]), fmask = t.final_mask, cmask = t.check_mask;
+  uint64_t kv = reinterpret_cast<uint64_t>(a.kv[r]), q = reinterpret_cast<uint64_t>(a.q);
+  uint64_t sinks = reinterpret_cast<uint64_t>(a.sinks);
+  uint64_t stats = reinterpret_cast<uint64_t>(a.stats), stat_base = a.stat_base[r];
+  uint64_t opart = reinterpret_cast<uint64_t>(a.opart), part_base = a.part_base[r];
+  uint32_t q_row = a.q_row[r], width = a.width[r], kv_len = a.kv_len[r], scale = __float_as_uint(a.scale);
+  rows = a.rows;
+  chunks = a.chunks[r];
+  asm volatile("" : "+s"(in), "+s"(in_base), "+s"(sc), "+s"(stride), "+s"(fl), "+s"(floor_begin), "+s"(count),
+               "+s"(fc), "+s"(fb), "+s"(off), "+s"(fmask), "+s"(cmask), "+s"(kv), "+s"(q), "+s"(sinks), "+s"(stats),
+               "+s"(stat_base), "+s"(opart), "+s"(part_base), "+s"(q_row), "+s"(width), "+s"(kv_len), "+s"(scale),
+               "+s"(rows), "+s"(chunks));
+  lr.in = global_ptr<const uint64_t>(in) + in_base;
+  lr.scores = global_ptr<const float>(sc) + r * stride;
+  lr.floors = global_ptr<const uint32_t>(fl) + floor_begin;
+  lr.out = nullptr;   // a final level writes indices, not lists
+  lr.count = count;
+  lr.floor_count = fc;
+  lr.fallback_count = fb;
+  lr.offset = static_cast<int32_t>(off);
+  lr.final_level = ((fmask >> r) & 1u) != 0;
+  lr.check = lr.final_level && ((cmask >> r) & 1u) != 0;
+  ar.rows = global_ptr<const uint16_t>(kv);
+  ar.mask = nullptr;   // direct variant
+  ar.q = global_ptr<const uint16_t>(q) + static_cast<uint64_t>(q_row) * kHeads * kDim;
+  ar.sinks = global_ptr<const float>(sinks);
+  ar.stats = global_ptr<float4>(stats) + stat_base;
+  ar.opart = global_ptr<float>(opart) + part_base;
+  ar.width = width;
+  ar.kv_len = kv_len;
+  ar.scale = __uint_as_float(scale);
+}
+
 template <int kPerLater>
 __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t, AttnArgs a) {
   __shared__ union Shared {
@@ -39,8 +81,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   const uint32_t rest = blockIdx.x / kXcds;
   const uint32_t hg = rest % kAttnHeadGroups;
   const uint32_t c = rest / kAttnHeadGroups;
-  uint32_t rows = a.rows, chunks = a.chunks[r];
-  const LevelRow lr = level_row(t, r, rows, chunks);   // one batch of argument loads
+  uint32_t rows, chunks;
+  LevelRow lr;
+  AttnRow ar;
+  topk_attn_rows(t, a, r, rows, chunks, lr, ar);
   if (r >= rows || c >= chunks) return;   // uniform
   const uint32_t lo = c * kAttnChunk;
   // Head group 0 writes the index output: each chunk its own 64 slots, the
@@ -52,9 +96,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
     if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
   });
   __syncthreads();   // the chunk's indices are in place; the selection's LDS is free
-  uint64_t unused64 = 0;
-  uint32_t unused32 = 0;
-  const AttnRow ar = attn_row<true>(a, r, rows, chunks, unused64, unused32);
   static_assert(kTopkThreads == kChunkThreads, "the attention chunk uses every thread of the workgroup");
   attn_chunk_body<true>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
 }
