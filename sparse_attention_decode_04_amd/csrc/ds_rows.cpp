@@ -431,19 +431,16 @@ ds_status ds_rows_gather(const ds_sparse_rows *rows, const int32_t *indices, siz
   a.gathered = static_cast<uint16_t *>(gathered);
   a.mask = static_cast<uint16_t *>(mask);
   a.rows = p.rows;
-  uint32_t blocks = 0;
-  for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
-    a.blk_begin[r] = blocks;
-    if (r >= p.rows) continue;
+  uint32_t max_row_blocks = 1;
+  for (uint32_t r = 0; r < p.rows; ++r) {
     a.kv[r] = static_cast<const uint16_t *>(rows->kv[r]);
     a.kv_len[r] = rows->kv_len[r];
     a.width[r] = rows->width[r];
     a.index_offset[r] = rows->index_offset[r];
     a.slot_base[r] = p.slot_base[r];
-    blocks += div_up(rows->width[r], ds::kGatherSlotsPerBlock);
+    max_row_blocks = std::max(max_row_blocks, div_up(rows->width[r], ds::kGatherSlotsPerBlock));
   }
-  a.blk_begin[ds::kRowsMax] = blocks;
-  const hipError_t e = ds::launch_gather(a, blocks, static_cast<hipStream_t>(stream));
+  const hipError_t e = ds::launch_gather(a, max_row_blocks, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DS_OK : hip_fail(e, "gather launch");
 }
 

@@ -116,9 +116,9 @@ struct GatherArgs {
   uint32_t width[kRowsMax];
   uint32_t index_offset[kRowsMax];
   uint64_t slot_base[kRowsMax];     // sum of widths of the rows before r
-  uint32_t blk_begin[kRowsMax + 1];
 };
-hipError_t launch_gather(const GatherArgs &a, uint32_t blocks, hipStream_t s);
+// Grid (max_row_blocks, a.rows): workgroup (x, r) copies row r's slots 16x ..
+hipError_t launch_gather(const GatherArgs &a, uint32_t max_row_blocks, hipStream_t s);
 
 // -------------------------------------------------------------- attention
 // Phase 1 (chunk): one workgroup of 16 waves per (row, 64-slot chunk, group

@@ -20,14 +20,22 @@
 namespace ds {
 
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
-  const uint32_t r = row_of_block(a.blk_begin, blockIdx.x);
-  const uint32_t width = a.width[r];
-  const uint32_t n = a.kv_len[r];
+  // Grid: (blocks of the widest row, rows); row r is blockIdx.y, so its
+  // arguments are read in one batch of scalar loads, waited for once.
+  // Blocks past the row's width end at once.
+  const uint32_t r = blockIdx.y;
+  uint32_t width = a.width[r], n = a.kv_len[r], ioff = a.index_offset[r];
+  uint64_t kvb = reinterpret_cast<uint64_t>(a.kv[r]), ib = reinterpret_cast<uint64_t>(a.indices);
+  uint64_t gb = reinterpret_cast<uint64_t>(a.gathered), mb = reinterpret_cast<uint64_t>(a.mask), sbase = a.slot_base[r];
+  asm volatile("" : "+s"(width), "+s"(n), "+s"(ioff), "+s"(kvb), "+s"(ib), "+s"(gb), "+s"(mb), "+s"(sbase));
+  if (blockIdx.x * kGatherSlotsPerBlock >= width) return;   // uniform
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = threadIdx.x >> 6;
-  const uint32_t slot0 = (blockIdx.x - a.blk_begin[r]) * kGatherSlotsPerBlock + wave * kGatherSlotsPerWave;
-  const uint16_t *__restrict__ kv = a.kv[r];
-  const int32_t *__restrict__ idx = a.indices + a.index_offset[r];
+  const uint32_t slot0 = blockIdx.x * kGatherSlotsPerBlock + wave * kGatherSlotsPerWave;
+  const uint16_t *__restrict__ kv = global_ptr<const uint16_t>(kvb);
+  const int32_t *__restrict__ idx = global_ptr<const int32_t>(ib) + ioff;
+  uint16_t *const gathered = global_ptr<uint16_t>(gb);
+  uint16_t *const mask = global_ptr<uint16_t>(mb);
 
   // Loads are unconditional (clamped to valid slots / KV row 0) and masked
   // afterwards, so all eight rows are in flight together.
@@ -61,16 +69,16 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
       if (bf16_bits_nonfinite(d >> 16)) { d &= 0x0000FFFFu; value_bad = true; }
       v[s][k] = d;
     }
-    const uint64_t out_slot = a.slot_base[r] + slot;
-    store16(a.gathered + out_slot * kDim + 8 * lane, v[s]);
+    const uint64_t out_slot = sbase + slot;
+    store16(gathered + out_slot * kDim + 8 * lane, v[s]);
     const bool any_bad = __ballot(value_bad) != 0;
     if (lane == 0)
-      a.mask[out_slot] = sentinel ? kBf16NegInf : ((index_bad || any_bad) ? kBf16NaN : uint16_t(0));
+      mask[out_slot] = sentinel ? kBf16NegInf : ((index_bad || any_bad) ? kBf16NaN : uint16_t(0));
   }
 }
 
-hipError_t launch_gather(const GatherArgs &a, uint32_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kGatherThreads), 0, s, a);
+hipError_t launch_gather(const GatherArgs &a, uint32_t max_row_blocks, hipStream_t s) {
+  hipLaunchKernelGGL(gather_kernel, dim3(max_row_blocks, a.rows), dim3(kGatherThreads), 0, s, a);
   return hipGetLastError();
 }
 
