@@ -182,12 +182,14 @@ __global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a
       float part[kTiles];
       read_b(0, b0);
       read_b(1, b1);
+      __builtin_amdgcn_s_setprio(1);
       products(b0, acc[0]);
       read_b(2, b0);
       products(b1, acc[1]);
       read_b(3, b1);
       products(b0, acc[2]);
       products(b1, acc[3]);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int kt = 0; kt < kTiles; ++kt) part[kt] = epilogue(acc[kt]);
       // Head sums of the chunk's four tiles at once: lane row g (16 lanes)
