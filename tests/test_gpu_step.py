@@ -182,3 +182,35 @@ def test_step_graph_replay_matches_eager():
         check_equal(got, ref, f"replay {rep}")
         eager.step_one()
         torch.cuda.synchronize()
+
+
+def test_step_permuted_row_subsets_match_full_launch():
+    """Row tables whose entries are not in row order: entry i of a launch
+    holds row sel[i] with that row's own q_row, offsets and buffers, so table
+    index, q_row, index/output offsets and the grid's row index all differ.
+    Every entry must give its row's results of the full launch bit for bit,
+    on the one-call path and on the four-call path (gather kernel)."""
+    kv_len = [20000, 33000, 18000, 24000, 40000]
+    inp = I.small_rows(51, kv_len)
+    dev = DeviceInputs(inp)
+    full = DeviceRows(dev)
+    full.step_one()
+    ref = full.results()
+    four = DeviceRows(dev)
+    four.step()
+    ref4 = four.results()
+    for sel in ([4, 1, 3], [2, 0], [3, 4, 0, 2, 1]):
+        say(f"one call and four calls: rows {sel}")
+        sub = DeviceRows(dev, rows=sel)
+        sub.step_one()
+        got = sub.results()
+        for i, r in enumerate(sel):
+            assert np.array_equal(got[i]["scores"].view(np.uint32), ref[r]["scores"].view(np.uint32)), (sel, r)
+            assert np.array_equal(got[i]["indices"], ref[r]["indices"]), (sel, r)
+            assert np.array_equal(got[i]["out"].view(np.uint32), ref[r]["out"].view(np.uint32)), (sel, r)
+        sub4 = DeviceRows(dev, rows=sel)
+        sub4.step()
+        got4 = sub4.results()
+        for i, r in enumerate(sel):
+            assert np.array_equal(got4[i]["gathered"], ref4[r]["gathered"]), (sel, r)
+            assert np.array_equal(got4[i]["out"].view(np.uint32), ref4[r]["out"].view(np.uint32)), (sel, r)
