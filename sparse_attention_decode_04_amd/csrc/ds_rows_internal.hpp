@@ -29,8 +29,9 @@ constexpr int kIdxTile = 16;
 constexpr uint32_t kIdxMaxKeysPerBlock = 1024;
 // Fused top-k stage (ds_rows_indexer_topk): every wave of the indexer also
 // writes up to kIdxWaveCand candidate keys of its own 256 keys (those at or
-// above its kIdxWaveKeep-th best score, or every valid key when it has at
-// most kIdxWaveCand) and a 32-bit floor: 0 when it wrote every valid key,
+// above a threshold keeping kIdxWaveKeep to kIdxWaveCand of them, or every
+// valid key when it has at most kIdxWaveCand) and a 32-bit floor: 0 when it
+// wrote every valid key,
 // otherwise score bits T such that all of its unwritten keys lie below the
 // key T << 32 (0xFFFFFFFF, above every valid key, when ties at its threshold
 // exceed the room).

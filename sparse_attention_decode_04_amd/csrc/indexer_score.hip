@@ -37,8 +37,10 @@
 // (deepseek_indexer_topk_block_rows_i32). Here every wave keeps, from the 256
 // scores it just computed (still in its registers: after each group of 4
 // tiles every lane holds one score, lane row g that of tile g), only the
-// keys at or above its 24th best score bits: a bitwise search with ballot counts finds that
-// threshold T without LDS or barriers. It writes those keys (at most 32) and
+// keys at or above a threshold T that keeps 24 to 32 of them (the 24th best
+// score bits when ties allow no such T): a search over T's bits with ballot
+// counts, two bits per step and stopping at the first T in range, finds it
+// without LDS or barriers. It writes those keys (at most 32) and
 // the floor T: all of its other keys lie below the key T << 32; the final top-k
 // level uses the floors to prove that no unkept key can reach the row's top
 // 512, and selects from the scores again when one could.
@@ -74,16 +76,27 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
   };
   const uint32_t nvalid = count_ge(1u);
   uint32_t thr = 1;   // keep every valid key
+  uint32_t kept = nvalid;
   if (nvalid > kIdxWaveCand) {
-    // Largest T with at least kIdxWaveKeep keys at or above it: the
-    // kIdxWaveKeep-th best score bits.
+    // T is built from the top two bits at a time (three candidate values per
+    // step, whose counts are independent and overlap in latency), each time
+    // taking the largest value that still has at least kIdxWaveKeep keys at
+    // or above it. It stops as soon as the accepted T keeps at most
+    // kIdxWaveCand keys; otherwise it ends at the kIdxWaveKeep-th best score
+    // bits. Any T that keeps at most kIdxWaveCand keys is a valid floor: the
+    // final level's check compares the floors with its 512th key, so which
+    // one is taken changes no index.
     thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = thr | (1u << bit);
-      if (count_ge(c) >= kIdxWaveKeep) thr = c;
+    kept = 256;   // count_ge(0); replaced at the first accepted step (count_ge(1) = nvalid > kIdxWaveKeep)
+    for (int b = 30; b >= 0; b -= 2) {
+      const uint32_t t1 = thr | (1u << b), t2 = thr | (2u << b), t3 = thr | (3u << b);
+      const uint32_t n1 = count_ge(t1), n2 = count_ge(t2), n3 = count_ge(t3);
+      if (n3 >= kIdxWaveKeep) { thr = t3; kept = n3; }
+      else if (n2 >= kIdxWaveKeep) { thr = t2; kept = n2; }
+      else if (n1 >= kIdxWaveKeep) { thr = t1; kept = n1; }
+      if (kept <= kIdxWaveCand) break;   // uniform
     }
   }
-  const uint32_t kept = count_ge(thr);
   if (kept > kIdxWaveCand) {
     // Ties at the threshold overflow the room: write nothing; the floor ~0
     // makes the row fall back to a selection over its scores.
