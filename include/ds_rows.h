@@ -157,9 +157,9 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows,
  * rows_bf16 and deepseek_indexer_topk_{block,merge,finalize}_rows_i32; the
  * pages' block stage keeps each 1024-key block's best 512). Writes the same
  * scores and the same indices as the two calls, bit for bit.
- * Each wave of the indexer keeps, of its 256 keys, those at or above its
- * 24th best score (at most 32; every valid key when it has at most 32) and
- * a floor below which lie all of its other keys; the top-k levels then
+ * Each wave of the indexer keeps, of its 256 keys, those at or above a
+ * threshold that keeps 24 to 32 of them (every valid key when it has at most
+ * 32) and a floor below which lie all of its other keys; the top-k levels then
  * select from those candidates, and a row's result stands only if no floor
  * lies above its 512th key. Otherwise (heavy ties, scores sorted by
  * position) the row is selected again from its scores in the same call,
