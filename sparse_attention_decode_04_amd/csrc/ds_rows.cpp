@@ -280,7 +280,15 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
     uint32_t max_count = 0;
     for (uint32_t r = 0; r < p.rows; ++r)
       if (!done[r]) max_count = std::max(max_count, count[r]);
-    a.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
+    if (a.from_scores) {
+      // The first level reads scores: short rows take a chunk sized to them
+      // (every row then fits one chunk; 32 per thread otherwise).
+      a.per_thread = ds::kTopkPerThreadFirst;
+      for (uint32_t per : {4u, 8u, 16u})
+        if (max_count <= ds::kTopkThreads * per) { a.per_thread = per; break; }
+    } else {
+      a.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
+    }
     const hipError_t e = ds::launch_topk_level(a, blocks, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     bool all = true;

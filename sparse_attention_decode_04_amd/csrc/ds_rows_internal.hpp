@@ -80,7 +80,8 @@ struct TopkLevelArgs {
   int32_t *indices;                 // final output
   uint32_t rows;
   uint32_t from_scores;             // 1 on the first level
-  uint32_t per_thread;              // later levels: 4 when every row has <= 4096 candidates, else 8
+  uint32_t per_thread;              // candidates per thread: first level 4/8/16 when every row has <= 1024x that
+                                    // many scores, else 32; later levels 4 when every row has <= 4096, else 8
   uint32_t final_mask;              // bit r: this level emits row r's indices
   uint32_t count[kRowsMax];         // candidates of row r at this level
   uint64_t in_base[kRowsMax];       // element offset of row r's input in `in`

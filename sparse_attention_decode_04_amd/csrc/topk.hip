@@ -60,9 +60,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(TopkLevelArgs 
 }
 
 hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_t s) {
-  if (a.from_scores)
-    hipLaunchKernelGGL(topk_level_kernel<true>, dim3(blocks), dim3(kTopkThreads), 0, s, a);
-  else if (a.per_thread == 4)
+  if (a.from_scores) {
+    if (a.per_thread == 4)
+      hipLaunchKernelGGL((topk_level_kernel<true, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
+    else if (a.per_thread == 8)
+      hipLaunchKernelGGL((topk_level_kernel<true, 8>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
+    else if (a.per_thread == 16)
+      hipLaunchKernelGGL((topk_level_kernel<true, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((topk_level_kernel<true, kTopkPerThreadFirst>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
+  } else if (a.per_thread == 4)
     hipLaunchKernelGGL((topk_level_kernel<false, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
   else
     hipLaunchKernelGGL(topk_level_kernel<false>, dim3(blocks), dim3(kTopkThreads), 0, s, a);

@@ -508,14 +508,16 @@ __device__ __forceinline__ LevelRow level_row(const TopkLevelArgs &a, uint32_t r
 // One workgroup's selection over chunk `chunk` of row r (one top-k level).
 // kFromScores: the first level, reading f32 scores. Otherwise a later level,
 // reading the previous level's 64-bit key lists.
-// kPerLater: candidates per thread on a later level (8, or 4 when every row
-// of the level has at most 4096).
+// kPer: candidates per thread, so that a chunk holds 1024 kPer of them: on
+// the first level 32, or 4, 8 or 16 when every row of the level fits one
+// such chunk (short rows: less work per thread); on later levels 8, or 4
+// when every row of the level has at most 4096.
 // emit_final(pos, index): the final level's index of rank pos (index +
 // offset, or -1 for an empty slot).
-template <bool kFromScores, int kPerLater, class EmitFinal>
+template <bool kFromScores, int kPer, class EmitFinal>
 __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr, uint32_t chunk,
                                              const EmitFinal &emit_final) {
-  constexpr int kPer = kFromScores ? kTopkPerThreadFirst : kPerLater;
+  static_assert(kPer <= kTopkPerThreadFirst, "the first level's LDS holds 32 score slots per thread");
   constexpr uint32_t kChunk = kTopkThreads * kPer;
 
   const uint32_t begin = chunk * kChunk;
