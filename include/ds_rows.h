@@ -319,7 +319,10 @@ ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows,
  * most 8192 candidates (up to 65536 keys), the final selection level runs
  * inside the attention's workgroups: each repeats its row's selection and
  * reads its slots' indices from LDS, which removes a kernel boundary and the
- * attention's index load. Otherwise the two calls run as they are.
+ * attention's index load. When instead every row has at most 16384 visible
+ * keys, the score kernel runs alone and the one selection level, over the
+ * scores, runs inside the attention's workgroups in the same way. Otherwise
+ * the two calls run as they are.
  *   irows, idx_q, weights, scores, idx_workspace, indices
  *              as ds_rows_indexer_topk (idx_workspace sized by
  *              ds_rows_indexer_topk_workspace_bytes(irows))

@@ -584,6 +584,41 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
       return fail("row %u: index_offset must equal the indexer's output_offset", r);
   }
 
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const ds::AttnArgs a =
+      attention_args(srows, sp, q, sinks, nullptr, nullptr, indices, scale, attn_workspace, out);
+  ds::TopkLevelArgs t{};
+  t.scores = scores;
+  t.score_stride = p.max_kv;
+  t.indices = indices;
+  t.rows = p.rows;
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    t.offset[r] = irows->offset[r];
+    t.out_offset[r] = irows->output_offset[r];
+    t.final_mask |= 1u << r;
+    t.blk_begin[r] = r;
+  }
+  for (uint32_t r = p.rows; r <= ds::kRowsMax; ++r) t.blk_begin[r] = p.rows;
+
+  // Rows too short for the indexer's first stage whose visible scores all fit
+  // one selection chunk (at most 16384): the score kernel, then the one level
+  // from the scores inside the attention's workgroups, with the chunk size
+  // ds_rows_indexer_topk would take.
+  uint32_t max_visible = 0;
+  for (uint32_t r = 0; r < p.rows; ++r) max_visible = std::max(max_visible, p.visible[r]);
+  if (!fused_rows(p) && max_visible <= ds::kTopkThreads * 16) {
+    DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, nullptr, nullptr, stream));
+    t.from_scores = 1;
+    t.per_thread = 16;
+    for (uint32_t per : {4u, 8u})
+      if (max_visible <= ds::kTopkThreads * per) { t.per_thread = per; break; }
+    for (uint32_t r = 0; r < p.rows; ++r) t.count[r] = p.visible[r];
+    hipError_t e = ds::launch_topk_attn(t, a, attention_blocks(sp), s);
+    if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
+    e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
+    return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
+  }
+
   // One kernel for the final level and the attention when the indexer keeps
   // the first stage (every row long enough) and each row's candidates fit
   // one workgroup; otherwise the two calls, with the same results.
@@ -603,12 +638,7 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
 
   // The final level, as run_topk_levels sets it up for the fused candidates
   // (one chunk per row, checked against the floors).
-  ds::TopkLevelArgs t{};
-  t.scores = scores;
-  t.score_stride = p.max_kv;
   t.in = cand;
-  t.indices = indices;
-  t.rows = p.rows;
   t.from_scores = 0;
   t.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
   t.floors = floors;
@@ -616,19 +646,11 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
     const uint32_t blocks = p.blk_begin[r + 1] - p.blk_begin[r];
     t.count[r] = blocks * ds::kIdxCand;
     t.in_base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
-    t.offset[r] = irows->offset[r];
-    t.out_offset[r] = irows->output_offset[r];
-    t.final_mask |= 1u << r;
     t.check_mask |= 1u << r;
     t.floor_begin[r] = p.blk_begin[r] * ds::kIdxFloors;
     t.floor_count[r] = blocks * ds::kIdxFloors;
     t.fallback_count[r] = p.visible[r];
-    t.blk_begin[r] = r;
   }
-  for (uint32_t r = p.rows; r <= ds::kRowsMax; ++r) t.blk_begin[r] = p.rows;
-  const ds::AttnArgs a =
-      attention_args(srows, sp, q, sinks, nullptr, nullptr, indices, scale, attn_workspace, out);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = ds::launch_topk_attn(t, a, attention_blocks(sp), s);
   if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
   e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);

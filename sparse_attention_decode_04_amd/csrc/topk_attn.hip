@@ -1,10 +1,11 @@
 // A row's final top-k level and its sparse attention in one kernel.
 //
-// What is computed is exactly ds_rows_indexer_topk's last level (the best 512
-// of the fused indexer's candidates in rank order, checked against the
-// waves' floors, with the reselection from scores when a floor could hide a
-// ranking key) followed by phase 1 of ds_rows_sparse_attn_direct on those
-// indices. Sources: docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal",
+// What is computed is exactly ds_rows_indexer_topk's last level followed by
+// phase 1 of ds_rows_sparse_attn_direct on its indices. That level is either
+// the best 512 of the fused indexer's candidates in rank order, checked
+// against the waves' floors, with the reselection from scores when a floor
+// could hide a ranking key, or, for rows whose visible scores all fit one
+// selection chunk, the best 512 of the scores themselves. Sources: docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal",
 // kernels deepseek_indexer_topk_finalize_rows_i32 (the final indices) and
 // deepseek_sparse_attention_score_rows_bf16 (the attention reading the KV
 // through them); "mlx-native 0.21.0 src/ops/deepseek_rows.rs", the rows
@@ -68,7 +69,7 @@ __device__ __forceinline__ void topk_attn_rows(const TopkLevelArgs &t, const Att
   ar.scale = __uint_as_float(scale);
 }
 
-template <int kPerLater>
+template <bool kFromScores, int kPer>
 __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t, AttnArgs a) {
   __shared__ union Shared {
     TopkShared sel;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   // last chunk also every slot past the row's width.
   const uint32_t out_end = c + 1 == chunks ? static_cast<uint32_t>(kTopK) : lo + kAttnChunk;
   int32_t *const out = t.indices + t.out_offset[r];
-  select_level<false, kPerLater>(u.sel, lr, 0, [&](uint32_t pos, int32_t index) {
+  select_level<kFromScores, kPer>(u.sel, lr, 0, [&](uint32_t pos, int32_t index) {
     if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
     if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
   });
@@ -101,10 +102,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
 }
 
 hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t blocks, hipStream_t s) {
-  if (t.per_thread == 4)
-    hipLaunchKernelGGL(topk_attn_kernel<4>, dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+  if (t.from_scores) {
+    // The scores of every row fit one chunk of 4, 8 or 16 per thread.
+    if (t.per_thread == 4)
+      hipLaunchKernelGGL((topk_attn_kernel<true, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+    else if (t.per_thread == 8)
+      hipLaunchKernelGGL((topk_attn_kernel<true, 8>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+    else
+      hipLaunchKernelGGL((topk_attn_kernel<true, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+  } else if (t.per_thread == 4)
+    hipLaunchKernelGGL((topk_attn_kernel<false, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
   else
-    hipLaunchKernelGGL(topk_attn_kernel<kTopkPerThreadLater>, dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+    hipLaunchKernelGGL((topk_attn_kernel<false, kTopkPerThreadLater>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
   return hipGetLastError();
 }
 

@@ -263,3 +263,27 @@ def test_widths_other_than_512():
         check_row(got, dict(indices=rows_idx[r], gathered=g, sentinel=sent, slot_bad=bad, out=o),
                   f"width {width[r]}", scores=False)
         base += width[r]
+
+
+@pytest.mark.parametrize("ternary", [False, True])
+@pytest.mark.parametrize("longest", [4096, 4097, 8192, 8193, 16384, 16385])
+def test_first_level_sizes_at_their_edges(longest, ternary):
+    # The first top-k level takes 4, 8, 16 or 32 score slots per thread by the
+    # call's longest row (at most 4096, 8192, 16384 keys, or more): each edge
+    # from both sides, with a shorter row and a row past 512 beside it, through
+    # the four calls and the one call; ternary keys give heavy ties.
+    kv_len = [longest, 700, longest - 1500]
+    inp = I.small_rows(50 + longest % 97 + 7 * ternary, kv_len, ternary=ternary)
+    say("first-level size edge", kv_len, "ternary" if ternary else "integer")
+    orc = O.decode_rows(inp)
+    dev = DeviceInputs(inp)
+    run = DeviceRows(dev)
+    run.step()
+    got = run.results()
+    for r in range(inp.rows):
+        check_row(got[r], orc[r], f"edge {longest} row {r}")
+    one = DeviceRows(dev)
+    one.step_one()
+    got1 = one.results()
+    for r in range(inp.rows):
+        check_row(got1[r], orc[r], f"edge {longest} row {r} one call", gathered=False)

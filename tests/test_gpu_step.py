@@ -2,9 +2,10 @@
 
 The call must give the scores, indices and attention output of
 ds_rows_indexer_topk followed by ds_rows_sparse_attn_direct bit for bit,
-whether the final top-k level runs inside the attention's workgroups (every
-row at least 16384 visible keys and at most 65536 keys) or the two calls run
-as they are; on the small workloads the output is also checked against the
+whether the final top-k level runs inside the attention's workgroups (from
+the fused indexer's candidates when every row has at least 16384 visible keys
+and at most 65536 keys, from the scores when every row has at most 16384
+visible keys) or the two calls run as they are; on the small workloads the output is also checked against the
 oracle. Sources: docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal"
 (deepseek_indexer_topk_finalize_rows_i32, deepseek_sparse_attention_score_rows_bf16)
 and "mlx-native 0.21.0 src/ops/deepseek_rows.rs" (the rows dispatches run back
@@ -132,6 +133,32 @@ def test_step_short_row_takes_the_two_calls():
     say("one call with a short row")
     a, b = one_and_two(DeviceInputs(inp))
     check_equal(a, b, "short row")
+
+
+def test_step_short_rows_select_from_scores_inside_the_kernel():
+    # every row's visible scores fit one selection chunk (at most 16384): the
+    # one level from the scores runs inside the attention's workgroups. Causal
+    # limits inside the cache (one row with nothing visible), offsets (a row
+    # whose indices pass its cache, which the attention zeroes), widths below
+    # 512 and non-finite indexer keys.
+    kv_len = [5000, 300, 20000, 9000, 64]
+    start_pos = [4 * 1000 + 2, 2, 4 * 16384 - 1, 4 * 8192 + 1, 4 * 64 - 1]
+    offset = [0, 0, 12345, 3, 0]
+    inp = I.small_rows(49, kv_len, start_pos=start_pos, offset=offset)
+    keys = inp.idx_keys[3]
+    keys[3, 5] = 0x7FC0
+    keys[6, :] = 0x7F80
+    dev = DeviceInputs(inp)
+    width = [512, 300, 200, 1, 64]
+    say("one call, short rows: causal limits, offsets, widths, non-finite keys")
+    a, b = one_and_two(dev, width=width)
+    check_equal(a, b, "short rows")
+    for r in range(len(kv_len)):
+        assert np.all(a[r]["indices"] != -7), r
+    assert np.all(a[1]["indices"] == -1)
+    orc = O.decode_rows(inp)
+    for r in (0, 4):
+        np.testing.assert_array_equal(a[r]["indices"], orc[r]["indices"], err_msg=f"short row {r}")
 
 
 def test_step_rows_independent_and_non_finite_kv():
