@@ -321,7 +321,10 @@ ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows,
  * reads its slots' indices from LDS, which removes a kernel boundary and the
  * attention's index load. When instead every row has at most 16384 visible
  * keys, the score kernel runs alone and the one selection level, over the
- * scores, runs inside the attention's workgroups in the same way. Otherwise
+ * scores, runs inside the attention's workgroups in the same way. When the
+ * indexer keeps the first stage but a row has more candidates, the selection
+ * passes of ds_rows_indexer_topk run, and the last runs inside the
+ * attention's workgroups if every row reaches it in the same pass. Otherwise
  * the two calls run as they are.
  *   irows, idx_q, weights, scores, idx_workspace, indices
  *              as ds_rows_indexer_topk (idx_workspace sized by

@@ -229,8 +229,12 @@ struct TopkInput {
 };
 
 // Selection levels until every row has one list; the last writes indices.
+// With attn set, a final level over lists that every row reaches in the same
+// pass runs inside the attention's workgroups instead (then the combine), and
+// *attn_done says so.
 ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, const float *scores,
-                          const TopkInput &in, uint64_t *bank0, uint64_t *bank1, int32_t *indices, void *stream) {
+                          const TopkInput &in, uint64_t *bank0, uint64_t *bank1, int32_t *indices, void *stream,
+                          const ds::AttnArgs *attn = nullptr, uint32_t attn_blocks = 0, bool *attn_done = nullptr) {
   uint64_t *bank[2] = {bank0, bank1};
   const bool from_lists = in.lists != nullptr;
   const uint32_t first_chunk = from_lists ? ds::kTopkChunkLater : ds::kTopkChunkFirst;
@@ -288,6 +292,16 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
         if (max_count <= ds::kTopkThreads * per) { a.per_thread = per; break; }
     } else {
       a.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
+    }
+    bool every_row_final = true;
+    for (uint32_t r = 0; r < p.rows; ++r) every_row_final &= !done[r] && chunks[r] == 1;
+    if (attn && !a.from_scores && every_row_final) {
+      hipError_t e = ds::launch_topk_attn(a, *attn, attn_blocks, s);
+      if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
+      e = ds::launch_attn_combine(*attn, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
+      if (e != hipSuccess) return hip_fail(e, "attention reduce launch");
+      *attn_done = true;
+      return DS_OK;
     }
     const hipError_t e = ds::launch_topk_level(a, blocks, s);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
@@ -625,6 +639,29 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
   uint32_t max_count = 0;
   for (uint32_t r = 0; r < p.rows; ++r)
     max_count = std::max(max_count, (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand);
+  if (fused_rows(p) && max_count > ds::kTopkChunkLater) {
+    // Rows past one workgroup's candidates: ds_rows_indexer_topk's levels,
+    // the last inside the attention's workgroups when every row reaches it
+    // in the same pass; otherwise the attention call follows.
+    char *ws = static_cast<char *>(idx_workspace);
+    uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
+    uint32_t *floors = reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p));
+    uint64_t *bank = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
+    DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, cand, floors, stream));
+    TopkInput in{};
+    in.lists = cand;
+    in.floors = floors;
+    for (uint32_t r = 0; r < p.rows; ++r) {
+      in.count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand;
+      in.base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
+    }
+    bool attn_done = false;
+    DS_TRY(run_topk_levels(irows, p, scores, in, bank, bank + p.fused_bank, indices, stream, &a,
+                           attention_blocks(sp), &attn_done));
+    if (attn_done) return DS_OK;
+    return ds_rows_sparse_attn_direct(srows, q, q_elems, sinks, sinks_elems, indices, indices_elems, scale,
+                                      attn_workspace, attn_workspace_bytes, out, out_elems, stream);
+  }
   if (!fused_rows(p) || max_count > ds::kTopkChunkLater) {
     DS_TRY(ds_rows_indexer_topk(irows, idx_q, idx_q_elems, weights, weights_elems, scores, scores_elems,
                                 idx_workspace, idx_workspace_bytes, indices, indices_elems, stream));

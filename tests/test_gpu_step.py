@@ -1,16 +1,19 @@
 """GPU parity of the one-call decode core (ds_rows_indexer_topk_attn).
 
-The call must give the scores, indices and attention output of
-ds_rows_indexer_topk followed by ds_rows_sparse_attn_direct bit for bit,
-whether the final top-k level runs inside the attention's workgroups (from
-the fused indexer's candidates when every row has at least 16384 visible keys
-and at most 65536 keys, from the scores when every row has at most 16384
-visible keys) or the two calls run as they are; on the small workloads the output is also checked against the
-oracle. Sources: docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal"
-(deepseek_indexer_topk_finalize_rows_i32, deepseek_sparse_attention_score_rows_bf16)
-and "mlx-native 0.21.0 src/ops/deepseek_rows.rs" (the rows dispatches run back
-to back). The selected set, its order and the attention's arithmetic are the
-same code either way, so equality is exact.
+The call
+must give the scores, indices and attention output of ds_rows_indexer_topk
+followed by ds_rows_sparse_attn_direct bit for bit, whether the final top-k
+level runs inside the attention's workgroups (from the fused indexer's
+candidates when every row has at least 16384 visible keys and at most 65536
+keys, from the scores when every row has at most 16384 visible keys, or over
+lists when every row reaches its final level in the same later pass) or the
+two calls run as they are; on the small workloads the output is also checked
+against the oracle. Sources: docs.rs "mlx-native 0.18.0
+src/shaders/deepseek_rows.metal" (deepseek_indexer_topk_finalize_rows_i32,
+deepseek_sparse_attention_score_rows_bf16) and "mlx-native 0.21.0
+src/ops/deepseek_rows.rs" (the rows dispatches run back to back). The selected
+set, its order and the attention's arithmetic are the same code either way, so
+equality is exact.
 """
 import numpy as np
 import pytest
@@ -125,6 +128,21 @@ def test_step_rows_past_65536_keys_take_the_two_calls():
     say("one call with a 70000-key row")
     a, b = one_and_two(DeviceInputs(inp))
     check_equal(a, b, "long row")
+
+
+def test_step_rows_past_65536_keys_final_level_inside_the_kernel():
+    # both rows need a second selection pass, which is then every row's final
+    # level: it runs inside the attention's workgroups
+    kv_len = [70000, 90000]
+    inp = I.small_rows(51, kv_len)
+    say("one call with two rows past 65536 keys")
+    a, b = one_and_two(DeviceInputs(inp))
+    check_equal(a, b, "long rows, same final pass")
+    orc = O.decode_rows(inp)
+    for r in range(len(kv_len)):
+        np.testing.assert_array_equal(a[r]["indices"], orc[r]["indices"], err_msg=f"long row {r}")
+        err = np.abs(a[r]["out"].astype(np.float64) - orc[r]["out"].astype(np.float64))
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (r, err.max(), err.mean())
 
 
 def test_step_short_row_takes_the_two_calls():
