@@ -1,14 +1,13 @@
 """GPU parity of the one-call decode core (ds_rows_indexer_topk_attn).
 
-The call
-must give the scores, indices and attention output of ds_rows_indexer_topk
-followed by ds_rows_sparse_attn_direct bit for bit, whether the final top-k
-level runs inside the attention's workgroups (from the fused indexer's
-candidates when every row has at least 16384 visible keys and at most 65536
-keys, from the scores when every row has at most 16384 visible keys, or over
-lists when every row reaches its final level in the same later pass) or the
-two calls run as they are; on the small workloads the output is also checked
-against the oracle. Sources: docs.rs "mlx-native 0.18.0
+The call must give the scores, indices and attention output of
+ds_rows_indexer_topk followed by ds_rows_sparse_attn_direct bit for bit,
+whether the final top-k level runs inside the attention's workgroups (from the
+fused indexer's candidates when every row has at least 16384 visible keys and
+at most 65536 keys, from the scores when every row has at most 16384 visible
+keys, or over lists when every row reaches its final level in the same later
+pass) or the two calls run as they are; on the small workloads the output is
+also checked against the oracle. Sources: docs.rs "mlx-native 0.18.0
 src/shaders/deepseek_rows.metal" (deepseek_indexer_topk_finalize_rows_i32,
 deepseek_sparse_attention_score_rows_bf16) and "mlx-native 0.21.0
 src/ops/deepseek_rows.rs" (the rows dispatches run back to back). The selected
