@@ -32,7 +32,9 @@
  *     it follows; a call checks that each buffer is large enough.
  *   - All argument checks run before anything is enqueued. A failed check
  *     returns DS_ERR_INVALID_ARGUMENT, enqueues nothing and leaves a
- *     message readable through ds_rows_last_error(). A failed launch returns
+ *     message readable through ds_rows_last_error(). After the arguments,
+ *     a call that would launch checks the current HIP device (DS_ERR_DEVICE
+ *     if there is none or it is not a gfx950). A failed launch returns
  *     DS_ERR_HIP.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
  *     stream) of the current HIP device and the call returns without
@@ -62,16 +64,24 @@ extern "C" {
 
 typedef enum {
   DS_OK = 0,
-  DS_ERR_INVALID_ARGUMENT = 1,
-  DS_ERR_HIP = 2
+  DS_ERR_INVALID_ARGUMENT = 1,  /* a check on the arguments failed */
+  DS_ERR_HIP = 2,               /* the HIP runtime refused a launch */
+  DS_ERR_DEVICE = 3             /* no current HIP device, or it is not a
+                                   gfx950 (the kernels are built for it
+                                   alone); nothing was enqueued */
 } ds_status;
+
+/* Largest kv_len of a row: the selection kernels address a row's entries
+ * with 32-bit byte offsets of 8-byte keys. */
+#define DS_KV_LEN_MAX ((1u << 30) - 1)
 
 /* Per-row table of the indexer calls; the fields of the pages'
  * DeepSeekIndexerRow ([host 0.21] DeepSeekIndexerRow,
  * dispatch_deepseek_indexer_rows). Entries [rows, DS_ROWS_MAX) are ignored. */
 typedef struct {
   uint32_t rows;                        /* 1..DS_ROWS_MAX */
-  uint32_t kv_len[DS_ROWS_MAX];         /* cached compressed keys, > 0 */
+  uint32_t kv_len[DS_ROWS_MAX];         /* cached compressed keys, in
+                                           [1, DS_KV_LEN_MAX] */
   uint32_t start_pos[DS_ROWS_MAX];      /* absolute query position; keys
                                            j >= min(kv_len, (start_pos+1)/4)
                                            are causally hidden; requires
@@ -226,15 +236,16 @@ ds_status ds_rows_indexer_score_mq(const ds_indexer_rows *rows, uint32_t query_l
  * Gathers, for slot t < width[r] of row r with i = indices[index_offset[r]+t]
  * ([shader 0.18] deepseek_sparse_attention_gather_rows_bf16):
  *   i == -1               gathered row = 0, mask = -inf   (sentinel)
- *   i < -1 or i >= kv_len gathered row = 0, mask = NaN    (bad index)
+ *   i < -1 or i >= kv_len gathered row = 0, mask = 0, invalid[r] = 1
  *   otherwise             gathered row = kv_r[i] bit for bit, with every
- *                         non-finite element replaced by +0; mask = NaN if
- *                         any element was non-finite, else 0.
- * A NaN mask entry marks the row invalid: ds_rows_sparse_attn then zeroes
- * the row's whole output.
+ *                         non-finite element replaced by +0 (and then
+ *                         invalid[r] = 1); mask = 0
+ * invalid[r] (entry r of the call's table, not q_row) is written for every
+ * row: 1 if any of its slots was bad, else 0. The caller need not clear it.
  *   indices   device i32, indices_elems >= max(index_offset + width)
  *   gathered  device bf16 [sum(width), 512], rows concatenated in row order
  *   mask      device bf16 [sum(width)]
+ *   invalid   device u32 [rows], invalid_elems >= rows
  * Checks: those of [host 0.21] sparse_params / sparse_io_checks on the table
  * (rows, kv_len and width non-zero, unique q_row, kv capacity, index range),
  * output capacities, and non-null pointers. */
@@ -242,38 +253,44 @@ ds_status ds_rows_gather(const ds_sparse_rows *rows,
                          const int32_t *indices, size_t indices_elems,
                          void *gathered, size_t gathered_elems,
                          void *mask, size_t mask_elems,
+                         uint32_t *invalid, size_t invalid_elems,
                          void *stream);
 
 /* ---- ds_rows_sparse_attn ------------------------------------------------
  * Attention of each row's query over its gathered rows, keys = values, with
  * a learned sink logit per head shared by all rows ([shader 0.18]
  * deepseek_sparse_attention_score_rows_bf16 / _reduce_rows_bf16 /
- * _sanitize_rows_bf16; [host 0.21] dispatch_deepseek_sparse_attention_flash_rows):
- *   l[h,t]  = scale * q[h] . G[t]          for slots t whose mask is not -inf
+ * _sanitize_rows_bf16; [host 0.21] dispatch_deepseek_sparse_attention_flash_rows,
+ * whose flash kernel takes the gathered rows, an additive mask and the
+ * per-row invalid flags):
+ *   l[h,t]  = scale * q[h] . G[t] + mask[t]   for slots t whose mask is not -inf
  *   m       = max(sink[h], max_t l[h,t])
  *   Z       = exp(sink[h]-m) + sum_t exp(l[h,t]-m)
  *   out[h]  = sum_t exp(l[h,t]-m)/Z * G[t]       (f32 [64,512] per row)
- * out[q_row[r], h, :] is zeroed when the row has a NaN mask entry, when
- * sink[h] or a live logit l[h,t] is not finite, or when Z is not in (0,inf);
- * any other non-finite output element is zeroed. Logits accumulate in f32
- * from exact bf16 products; the softmax weights enter the weighted sum as a
- * bf16 hi+lo pair (relative error ~2^-16) with f32 accumulation.
+ * out[q_row[r], h, :] is zeroed when invalid[r] != 0, when sink[h] or a
+ * live logit l[h,t] is not finite, or when Z is not in (0,inf); any other
+ * non-finite output element is zeroed. Logits accumulate in f32 from exact
+ * bf16 products; the softmax weights enter the weighted sum as a bf16 hi+lo
+ * pair (relative error ~2^-16) with f32 accumulation.
  *   q          device bf16 [q_rows, 64, 512], q_elems >= (max q_row+1)*32768
  *   sinks      device f32 [64]
  *   gathered   device bf16, as written by ds_rows_gather
- *   mask       device bf16, as written by ds_rows_gather
+ *   mask       device bf16 [sum(width)]: 0 or -inf as ds_rows_gather writes
+ *              it (any entry other than -inf is added to its logit)
+ *   invalid    device u32 [rows], as written by ds_rows_gather
  *   scale      finite and > 0 (1/sqrt(512) for the decode core)
  *   workspace  device scratch, workspace_bytes >= ds_rows_attn_workspace_bytes
  *              (contents on entry do not matter; clobbered)
  *   out        device f32 [q_rows, 64, 512], out_elems >= (max q_row+1)*32768
  * Checks: those of [host 0.21] sparse_params / sparse_io_checks on the table,
- * gathered/mask capacities, scale, sinks and workspace capacity (the KV
- * pointers of the table are not used by this call). */
+ * gathered/mask/invalid capacities, scale, sinks and workspace capacity (the
+ * KV pointers of the table are not used by this call). */
 ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows,
                               const void *q, size_t q_elems,
                               const float *sinks, size_t sinks_elems,
                               const void *gathered, size_t gathered_elems,
                               const void *mask, size_t mask_elems,
+                              const uint32_t *invalid, size_t invalid_elems,
                               float scale,
                               void *workspace, size_t workspace_bytes,
                               float *out, size_t out_elems,

@@ -11,9 +11,11 @@
 //   m = max(sink[h], max_t l), Z = e^(sink-m) + sum_t e^(l-m)
 //   out[h] = sum_t e^(l-m)/Z * G[t]
 // with the pages' fail-closed rule: a row with a bad slot (bad index or a
-// non-finite KV element), a head whose sink or any live logit is not finite,
-// or a denominator outside (0, inf) is written as zeros; other non-finite
-// outputs are zeroed.
+// non-finite KV element; the gathered variant has the gather's per-row
+// invalid flag), a head whose sink or any live logit is not finite, or a
+// denominator outside (0, inf) is written as zeros; other non-finite outputs
+// are zeroed. The gathered variant adds the mask entry of each slot it keeps
+// (mask not -inf) to the slot's logit, as an additive attention mask.
 //
 // Two launches (split over the selected slots, then a combine). The selected
 // rows G[t] come either from the gathered operand and its mask (after
@@ -49,13 +51,11 @@ constexpr int kCombineThreads = 256;
 template <bool kDirect>
 __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
   __shared__ AttnChunkShared sm;
-  // Row r runs on XCD r (consecutive workgroups go to consecutive XCDs), so
-  // the head groups and chunks of a row share one L2: the four head groups
-  // of a chunk read the same selected rows.
-  const uint32_t r = blockIdx.x % kXcds;
-  const uint32_t rest = blockIdx.x / kXcds;
-  const uint32_t hg = rest % kAttnHeadGroups;
-  const uint32_t c = rest / kAttnHeadGroups;
+  // Grid (x, row): the four head groups of a chunk run on one XCD and read
+  // the chunk's selected rows through its L2 (see attn_block).
+  const uint32_t r = blockIdx.y;
+  uint32_t c, hg;
+  attn_block(blockIdx.x, c, hg);
   uint32_t rows = a.rows, chunks = a.chunks[r], ioff = a.index_offset[r];
   uint64_t ibits = reinterpret_cast<uint64_t>(a.indices);
   const AttnRow ar = attn_row<kDirect>(a, r, rows, chunks, ibits, ioff);   // one batch of argument loads
@@ -66,11 +66,11 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- phase 2
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
-  // Row r on XCD r (block b = 8 dc + r), as in phase 1. Thread t: head t / 4,
-  // dims d0 .. d0 + 4 kVec of the workgroup's kAttnDimChunk.
+  // Grid (dim chunk, row). Thread t: head t / 4, dims d0 .. d0 + 4 kVec of
+  // the workgroup's kAttnDimChunk.
   constexpr int kVec = kAttnDimChunk / 4 / 4;   // f32x4 per thread
-  const uint32_t r = blockIdx.x % kXcds;
-  const uint32_t dc = blockIdx.x / kXcds;
+  const uint32_t r = blockIdx.y;
+  const uint32_t dc = blockIdx.x;
   // The row's arguments in one batch of scalar loads (one wait).
   uint32_t rows = a.rows, nch = a.chunks[r], q_row = a.q_row[r];
   uint64_t sbits = reinterpret_cast<uint64_t>(a.stats), sbase = a.stat_base[r];
@@ -156,16 +156,17 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   }
 }
 
-hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s) {
+hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t max_chunks, hipStream_t s) {
+  const dim3 grid(kXcds * kAttnHeadGroups * ((max_chunks + kXcds - 1) / kXcds), a.rows);
   if (direct)
-    hipLaunchKernelGGL(attn_chunk_kernel<true>, dim3(blocks), dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_chunk_kernel<true>, grid, dim3(kChunkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_chunk_kernel<false>, dim3(blocks), dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_chunk_kernel<false>, grid, dim3(kChunkThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_combine(const AttnArgs &a, uint32_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(blocks), dim3(kCombineThreads), 0, s, a);
+hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(kDim / kAttnDimChunk, a.rows), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -13,13 +13,14 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// Slot states: -inf mask / -1 index = sentinel, NaN mask / bad index = bad.
+// Slot states: -inf mask / -1 index = sentinel (dropped), bad index or a
+// non-finite KV element (direct variant) = bad (the row is zeroed).
 enum : uint32_t { kLive = 0, kSkip = 1, kBad = 2 };
 
-__device__ __forceinline__ uint32_t mask_state(uint16_t m) {
-  if (m == kBf16NegInf) return kSkip;
-  if ((m & 0x7FFFu) > 0x7F80u) return kBad;
-  return kLive;
+// Workgroup (x, r) of the phase-1 grid: chunk c and head group hg of row r.
+__device__ __forceinline__ void attn_block(uint32_t x, uint32_t &c, uint32_t &hg) {
+  hg = (x / kXcds) % kAttnHeadGroups;
+  c = kXcds * (x / (kXcds * kAttnHeadGroups)) + x % kXcds;
 }
 
 __device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
@@ -60,6 +61,7 @@ struct AttnChunkShared {
   __attribute__((aligned(16))) uint16_t phi[kHg * kPStride];            // p~ hi
   __attribute__((aligned(16))) uint16_t plo[kHg * kPStride];            // p~ lo
   uint32_t state[kAttnChunk];
+  float madd[kAttnChunk];   // gathered variant: the mask value added to a live slot's logit
 };
 
 // One row's arguments of phase 1, read in one batch (see LevelRow: each
@@ -67,6 +69,7 @@ struct AttnChunkShared {
 struct AttnRow {
   const uint16_t *rows;     // direct: the row's KV; gathered: its gathered rows
   const uint16_t *mask;     // gathered: the row's mask entries
+  const uint32_t *invalid;  // gathered: the row's invalid flag
   const uint16_t *q;        // the row's query [64, 512]
   const float *sinks;
   float4 *stats;            // the row's chunk statistics
@@ -84,16 +87,18 @@ __device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, uint32_t r, uint3
                                             uint32_t &x3) {
   uint64_t rows = reinterpret_cast<uint64_t>(kDirect ? a.kv[r] : a.gathered);
   uint64_t mask = reinterpret_cast<uint64_t>(a.mask), slot_base = kDirect ? 0 : a.slot_base[r];
+  uint64_t inv = reinterpret_cast<uint64_t>(a.invalid);
   uint64_t q = reinterpret_cast<uint64_t>(a.q), sinks = reinterpret_cast<uint64_t>(a.sinks);
   uint64_t stats = reinterpret_cast<uint64_t>(a.stats), stat_base = a.stat_base[r];
   uint64_t opart = reinterpret_cast<uint64_t>(a.opart), part_base = a.part_base[r];
   uint32_t q_row = a.q_row[r], width = a.width[r], kv_len = a.kv_len[r], scale = __float_as_uint(a.scale);
-  asm volatile("" : "+s"(rows), "+s"(mask), "+s"(slot_base), "+s"(q), "+s"(sinks), "+s"(stats), "+s"(stat_base),
+  asm volatile("" : "+s"(rows), "+s"(mask), "+s"(slot_base), "+s"(inv), "+s"(q), "+s"(sinks), "+s"(stats), "+s"(stat_base),
                "+s"(opart), "+s"(part_base), "+s"(q_row), "+s"(width), "+s"(kv_len), "+s"(scale), "+s"(x0), "+s"(x1),
                "+s"(x2), "+s"(x3));
   AttnRow ar;
   ar.rows = global_ptr<const uint16_t>(rows) + slot_base * kDim;
   ar.mask = global_ptr<const uint16_t>(mask) + slot_base;
+  ar.invalid = global_ptr<const uint32_t>(inv) + r;
   ar.q = global_ptr<const uint16_t>(q) + static_cast<uint64_t>(q_row) * kHeads * kDim;
   ar.sinks = global_ptr<const float>(sinks);
   ar.stats = global_ptr<float4>(stats) + stat_base;
@@ -128,6 +133,9 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   // The sink of the softmax head, stored with the chunk statistics so that
   // phase 2 gets it in the same load.
   const float sink_h = active ? a.sinks[kHg * hg + qh] : 0.0f;
+  // Gathered variant: the row's invalid flag, read by every thread with its
+  // other first loads and used in the softmax.
+  const bool row_invalid = !kDirect && active && *a.invalid != 0;
   constexpr int kSlots = kAttnChunk / (kChunkThreads / 64);   // slots per wave: 8 or 4
   constexpr int kQHeads = kHg / (kChunkThreads / 64);         // query heads per wave: 2 or 1
   static_assert(kChunkThreads == 512 || kChunkThreads == 1024, "8 or 16 waves");
@@ -165,7 +173,7 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
         st[s] = ok ? kLive : ((slot < width && i != -1) ? kBad : kSkip);
         src[s] = kv_row0 + static_cast<uint64_t>(ok ? i : 0) * kDim;
       } else {
-        st[s] = slot < width ? mask_state(raw_mask[s]) : kSkip;
+        st[s] = (slot < width && raw_mask[s] != kBf16NegInf) ? kLive : kSkip;
         src[s] = kv_row0 + static_cast<uint64_t>(min(slot, width - 1)) * kDim;
       }
       use[s] = kDirect ? st[s] == kLive : slot < width;
@@ -197,6 +205,10 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
     if (lane == 0) {
   #pragma unroll
       for (int s = 0; s < kSlots; ++s) state[kSlots * wave + s] = st[s];
+      if (!kDirect) {
+  #pragma unroll
+        for (int s = 0; s < kSlots; ++s) sm.madd[kSlots * wave + s] = bf16_bits_to_float(raw_mask[s]);
+      }
     }
   }
   __syncthreads();
@@ -231,13 +243,18 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
     // Softmax statistics. Thread t: head t / kTph, slots kSpt (t % kTph) ..
     // + kSpt (with 16 waves: one wave per head, one slot per thread).
     {
+      // No contraction here: each logit is rounded once as scale * sum (plus
+      // the mask entry in the gathered variant) before it is compared and
+      // exponentiated, so that both variants give the same bits (a fused
+      // multiply-subtract into the exponent would round differently).
+#pragma clang fp contract(off)
       constexpr int kKParts = kChunkThreads / 256;
       constexpr int kSpt = kAttnChunk / kTph;   // slots per thread: 2 or 1
       const uint32_t head = qh;
       const uint32_t part = tid % kTph;
       float lv[kSpt];
       uint32_t sj[kSpt];
-      bool bad = false;
+      bool bad = row_invalid;
       float mx = -__builtin_inff();
   #pragma unroll
       for (int j = 0; j < kSpt; ++j) {
@@ -246,6 +263,7 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   #pragma unroll
         for (int k = 1; k < kKParts; ++k) l += red[(k * kHg + head) * kRedStride + s];
         lv[j] = l * a.scale;
+        if (!kDirect) lv[j] += sm.madd[s];   // additive mask: 0 for every slot ds_rows_gather keeps
         sj[j] = state[s];
         const bool live = sj[j] == kLive;
         bad |= (sj[j] == kBad) || (live && !__builtin_isfinite(lv[j]));

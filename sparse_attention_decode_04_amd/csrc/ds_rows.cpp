@@ -1,18 +1,23 @@
 // C ABI of the multi-row sparse-attention decode core: argument checks,
 // per-row tables, workspace layout and kernel launches.
 //
-// The checks restate those of the host dispatch code on docs.rs
-// "mlx-native 0.21.0 src/ops/deepseek_rows.rs": check_rows, sparse_params,
-// sparse_io_checks, dispatch_deepseek_indexer_rows (causal length, offset
-// range, disjoint outputs) and its `require` capacity checks. Every check runs
-// before anything is enqueued, so a failed call has no effect on the device.
+// The checks cover what the host dispatch code on docs.rs "mlx-native 0.21.0
+// src/ops/deepseek_rows.rs" requires of its rows dispatches (row count,
+// per-row lengths and positions, the causal length, the index range, disjoint
+// outputs, unique query rows, buffer capacities), organised here as one pass
+// over each table's fields followed by the cross-row checks (sorted ranges,
+// distinct query rows). Every check runs before anything is enqueued, so a
+// failed call has no effect on the device.
 #include "ds_rows.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
+#include <utility>
 
 #include "ds_rows_internal.hpp"
 
@@ -35,8 +40,56 @@ ds_status hip_fail(hipError_t e, const char *what) {
   return DS_ERR_HIP;
 }
 
+// The current device must be a gfx950 (the only target the kernels are built
+// for). The answer is cached per device id; hipGetDevice itself is cheap.
+ds_status check_device() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    g_error = std::string("ds_rows: no current HIP device (") + hipGetErrorString(e) + ")";
+    return DS_ERR_DEVICE;
+  }
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> verdict[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+  int v = dev < kMaxDevices ? verdict[dev].load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      g_error = "ds_rows: cannot read the properties of HIP device " + std::to_string(dev);
+      return DS_ERR_DEVICE;
+    }
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (v == 2) g_error = std::string("ds_rows: HIP device ") + std::to_string(dev) + " is " + prop.gcnArchName +
+                          "; the kernels are built for gfx950 only";
+    if (dev < kMaxDevices) verdict[dev].store(v, std::memory_order_relaxed);
+  } else if (v == 2) {
+    g_error = "ds_rows: HIP device " + std::to_string(dev) + " is not a gfx950; the kernels are built for it only";
+  }
+  return v == 1 ? DS_OK : DS_ERR_DEVICE;
+}
+
 uint32_t div_up(uint64_t a, uint64_t b) { return static_cast<uint32_t>((a + b - 1) / b); }
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+ds_status check_row_count(uint32_t rows) {
+  if (rows < 1 || rows > DS_ROWS_MAX) return fail("row table has rows = %u; a call takes 1 to %d rows", rows, DS_ROWS_MAX);
+  return DS_OK;
+}
+
+// Table rows a and b whose [start, start + len) ranges intersect, if any:
+// sort the starts, then compare neighbours.
+bool overlapping_pair(const uint64_t *start, uint64_t len, uint32_t n, uint32_t *a, uint32_t *b) {
+  std::pair<uint64_t, uint32_t> s[DS_ROWS_MAX];
+  for (uint32_t i = 0; i < n; ++i) s[i] = {start[i], i};
+  std::sort(s, s + n);
+  for (uint32_t i = 1; i < n; ++i)
+    if (s[i].first < s[i - 1].first + len) {
+      *a = std::min(s[i - 1].second, s[i].second);
+      *b = std::max(s[i - 1].second, s[i].second);
+      return true;
+    }
+  return false;
+}
 
 // ------------------------------------------------------------ indexer table
 struct IndexerPlan {
@@ -54,26 +107,33 @@ struct IndexerPlan {
 
 constexpr uint32_t kIndexerKeysPerBlock = 1024;
 
+// One indexer row's fields: length, position, causal length and index range.
+// Returns the keys visible to the row's query in *visible.
+ds_status check_indexer_row(uint32_t r, uint32_t kv_len, uint32_t start_pos, int32_t offset, uint32_t *visible) {
+  if (kv_len == 0) return fail("indexer row %u: kv_len is 0; every row needs at least one key", r);
+  if (kv_len > DS_KV_LEN_MAX)
+    return fail("indexer row %u: kv_len %u is above DS_KV_LEN_MAX = 2^30 - 1", r, kv_len);
+  if (start_pos == UINT32_MAX)
+    return fail("indexer row %u: start_pos 4294967295 has no next position; it must be at most 2^32 - 2", r);
+  const uint32_t causal = (start_pos + 1) / DS_RATIO;
+  if (causal > kv_len)
+    return fail("indexer row %u: start_pos %u makes %u keys visible but kv_len is only %u", r, start_pos, causal,
+                kv_len);
+  if (offset < 0) return fail("indexer row %u: offset %d is negative (index -1 marks an empty slot)", r, offset);
+  if (causal > 0 && int64_t(offset) + int64_t(causal) - 1 > int64_t(INT32_MAX))
+    return fail("indexer row %u: the largest emitted index, offset %d + %u - 1, does not fit in int32", r, offset,
+                causal);
+  *visible = causal;
+  return DS_OK;
+}
+
 ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
-  if (!t) return fail("null indexer row table");
-  if (t->rows == 0 || t->rows > DS_ROWS_MAX) return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, t->rows);
+  if (!t) return fail("indexer row table is null");
+  if (const ds_status st = check_row_count(t->rows)) return st;
   p->rows = t->rows;
   for (uint32_t r = 0; r < t->rows; ++r) {
-    if (t->kv_len[r] == 0) return fail("indexer row %u: kv_len must be nonzero", r);
-    if (t->start_pos[r] == UINT32_MAX) return fail("indexer row %u: indexer position overflows", r);
-    const uint32_t causal = (t->start_pos[r] + 1) / DS_RATIO;
-    if (t->kv_len[r] < causal)
-      return fail("indexer row %u: kv_len %u is shorter than %u causal compressed entries", r, t->kv_len[r], causal);
-    if (t->offset[r] < 0)
-      return fail("indexer row %u: offset must be nonnegative; -1 is reserved for the sentinel", r);
-    if (causal > 0 && int64_t(t->offset[r]) + int64_t(causal) - 1 > int64_t(INT32_MAX))
-      return fail("indexer row %u: offset plus compressed index exceeds i32", r);
-    for (uint32_t o = 0; o < r; ++o) {
-      const uint64_t a0 = t->output_offset[r], a1 = a0 + DS_TOP_K;
-      const uint64_t b0 = t->output_offset[o], b1 = b0 + DS_TOP_K;
-      if (a0 < b1 && b0 < a1) return fail("indexer outputs of two rows overlap (rows %u and %u)", o, r);
-    }
-    p->visible[r] = std::min<uint32_t>(t->kv_len[r], causal);
+    if (const ds_status st = check_indexer_row(r, t->kv_len[r], t->start_pos[r], t->offset[r], &p->visible[r]))
+      return st;
     p->max_kv = std::max<uint64_t>(p->max_kv, t->kv_len[r]);
     p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + 1);
     p->indices_end = std::max<uint64_t>(p->indices_end, uint64_t(t->output_offset[r]) + DS_TOP_K);
@@ -85,6 +145,12 @@ ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
     if (fchunks > 1) p->fused_bank += uint64_t(fchunks) * DS_TOP_K;
   }
   for (uint32_t r = t->rows; r < ds::kRowsMax; ++r) p->blk_begin[r + 1] = p->blk_begin[r];
+  uint64_t starts[DS_ROWS_MAX];
+  for (uint32_t r = 0; r < t->rows; ++r) starts[r] = t->output_offset[r];
+  uint32_t a, b;
+  if (overlapping_pair(starts, DS_TOP_K, t->rows, &a, &b))
+    return fail("indexer rows %u and %u: their 512-index output ranges at %u and %u intersect", a, b,
+                t->output_offset[a], t->output_offset[b]);
   return DS_OK;
 }
 
@@ -132,26 +198,33 @@ struct SparsePlan {
   uint64_t stat_base[ds::kRowsMax] = {};
   uint64_t part_base[ds::kRowsMax] = {};
   uint64_t stat_elems = 0, part_elems = 0;
+  uint32_t max_chunks = 0;
 };
 
 ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
-  if (!t) return fail("null sparse row table");
-  if (t->rows == 0 || t->rows > DS_ROWS_MAX) return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, t->rows);
+  if (!t) return fail("sparse row table is null");
+  if (const ds_status st = check_row_count(t->rows)) return st;
   p->rows = t->rows;
   for (uint32_t r = 0; r < t->rows; ++r) {
-    if (t->kv_len[r] == 0 || t->width[r] == 0) return fail("row %u: kv_len and width must be nonzero", r);
-    for (uint32_t o = 0; o < r; ++o)
-      if (t->q_row[o] == t->q_row[r]) return fail("row %u: q_row %u is used twice", r, t->q_row[r]);
+    if (t->kv_len[r] == 0) return fail("sparse row %u: kv_len is 0; every row needs at least one KV row", r);
+    if (t->width[r] == 0) return fail("sparse row %u: width is 0; every row attends to at least one slot", r);
     p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + 1);
     p->index_end = std::max<uint64_t>(p->index_end, uint64_t(t->index_offset[r]) + t->width[r]);
     p->slot_base[r] = p->slots;
     p->slots += t->width[r];
     p->chunks[r] = div_up(t->width[r], ds::kAttnChunk);
+    p->max_chunks = std::max(p->max_chunks, p->chunks[r]);
     p->stat_base[r] = p->stat_elems;
     p->stat_elems += uint64_t(ds::kHeads) * p->chunks[r];
     p->part_base[r] = p->part_elems;
     p->part_elems += uint64_t(ds::kHeads) * ds::kDim * p->chunks[r];
   }
+  // Each row writes its own query row of the output: no two may share one.
+  uint64_t qr[DS_ROWS_MAX];
+  for (uint32_t r = 0; r < t->rows; ++r) qr[r] = t->q_row[r];
+  uint32_t a, b;
+  if (overlapping_pair(qr, 1, t->rows, &a, &b))
+    return fail("sparse rows %u and %u both use q_row %u (each row writes its own output row)", a, b, t->q_row[a]);
   return DS_OK;
 }
 
@@ -234,7 +307,7 @@ struct TopkInput {
 // *attn_done says so.
 ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, const float *scores,
                           const TopkInput &in, uint64_t *bank0, uint64_t *bank1, int32_t *indices, void *stream,
-                          const ds::AttnArgs *attn = nullptr, uint32_t attn_blocks = 0, bool *attn_done = nullptr) {
+                          const ds::AttnArgs *attn = nullptr, uint32_t attn_chunks = 0, bool *attn_done = nullptr) {
   uint64_t *bank[2] = {bank0, bank1};
   const bool from_lists = in.lists != nullptr;
   const uint32_t first_chunk = from_lists ? ds::kTopkChunkLater : ds::kTopkChunkFirst;
@@ -296,10 +369,10 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
     bool every_row_final = true;
     for (uint32_t r = 0; r < p.rows; ++r) every_row_final &= !done[r] && chunks[r] == 1;
     if (attn && !a.from_scores && every_row_final) {
-      hipError_t e = ds::launch_topk_attn(a, *attn, attn_blocks, s);
+      hipError_t e = ds::launch_topk_attn(a, *attn, attn_chunks, s);
       if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
-      e = ds::launch_attn_combine(*attn, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
-      if (e != hipSuccess) return hip_fail(e, "attention reduce launch");
+      e = ds::launch_attn_combine(*attn, s);
+      if (e != hipSuccess) return hip_fail(e, "attention combine launch");
       *attn_done = true;
       return DS_OK;
     }
@@ -359,6 +432,7 @@ ds_status ds_rows_indexer_score(const ds_indexer_rows *rows, const void *q, size
   IndexerPlan p;
   DS_TRY(check_indexer(rows, &p));
   DS_TRY(check_indexer_operands(rows, p, q, q_elems, weights, weights_elems, scores, scores_elems));
+  DS_TRY(check_device());
   return launch_indexer(rows, p, q, weights, scores, nullptr, nullptr, stream);
 }
 
@@ -373,6 +447,7 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows, const float *scores, size_t 
   DS_TRY(cap(scores_elems, p.rows * p.max_kv, "indexer scores", "elements"));
   DS_TRY(cap(workspace_bytes, ws, "indexer top-k scratch", "bytes"));
   DS_TRY(cap(indices_elems, p.indices_end, "indexer output", "elements"));
+  DS_TRY(check_device());
 
   TopkInput in{};
   for (uint32_t r = 0; r < p.rows; ++r) in.count[r] = p.visible[r];
@@ -394,6 +469,7 @@ ds_status ds_rows_indexer_candidates(const ds_indexer_rows *rows, const void *q,
   DS_TRY(check_indexer_operands(rows, p, q, q_elems, weights, weights_elems, scores, scores_elems));
   DS_TRY(need(workspace, "indexer top-k workspace"));
   DS_TRY(cap(workspace_bytes, indexer_topk_workspace_bytes(p), "indexer top-k workspace", "bytes"));
+  DS_TRY(check_device());
   char *ws = static_cast<char *>(workspace);
   return launch_indexer(rows, p, q, weights, scores, reinterpret_cast<uint64_t *>(ws),
                         reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p)), stream);
@@ -409,6 +485,7 @@ ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_
   DS_TRY(need(indices, "indexer output"));
   DS_TRY(cap(workspace_bytes, indexer_topk_workspace_bytes(p), "indexer top-k workspace", "bytes"));
   DS_TRY(cap(indices_elems, p.indices_end, "indexer output", "elements"));
+  DS_TRY(check_device());
 
   if (!fused_rows(p)) {
     DS_TRY(launch_indexer(rows, p, q, weights, scores, nullptr, nullptr, stream));
@@ -434,24 +511,29 @@ ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_
 }
 
 ds_status ds_rows_gather(const ds_sparse_rows *rows, const int32_t *indices, size_t indices_elems, void *gathered,
-                         size_t gathered_elems, void *mask, size_t mask_elems, void *stream) {
+                         size_t gathered_elems, void *mask, size_t mask_elems, uint32_t *invalid,
+                         size_t invalid_elems, void *stream) {
   SparsePlan p;
   DS_TRY(check_sparse(rows, &p));
   DS_TRY(need(indices, "indices"));
   DS_TRY(need(gathered, "gathered_kv"));
   DS_TRY(need(mask, "mask"));
+  DS_TRY(need(invalid, "invalid"));
   for (uint32_t r = 0; r < p.rows; ++r) {
-    if (!rows->kv[r]) return fail("row %u: kv must not be null", r);
+    if (!rows->kv[r]) return fail("sparse row %u: kv must not be null", r);
     DS_TRY(cap(rows->kv_elems[r], uint64_t(rows->kv_len[r]) * DS_HEAD_DIM, "kv", "elements"));
   }
   DS_TRY(cap(indices_elems, p.index_end, "indices", "elements"));
   DS_TRY(cap(gathered_elems, p.slots * DS_HEAD_DIM, "gathered_kv", "elements"));
   DS_TRY(cap(mask_elems, p.slots, "mask", "elements"));
+  DS_TRY(cap(invalid_elems, p.rows, "invalid", "elements"));
+  DS_TRY(check_device());
 
   ds::GatherArgs a{};
   a.indices = indices;
   a.gathered = static_cast<uint16_t *>(gathered);
   a.mask = static_cast<uint16_t *>(mask);
+  a.invalid = invalid;
   a.rows = p.rows;
   uint32_t max_row_blocks = 1;
   for (uint32_t r = 0; r < p.rows; ++r) {
@@ -472,13 +554,14 @@ namespace {
 
 // Both attention entry points after their own operand checks.
 ds::AttnArgs attention_args(const ds_sparse_rows *rows, const SparsePlan &p, const void *q, const float *sinks,
-                            const void *gathered, const void *mask, const int32_t *indices, float scale,
-                            void *workspace, float *out) {
+                            const void *gathered, const void *mask, const uint32_t *invalid,
+                            const int32_t *indices, float scale, void *workspace, float *out) {
   ds::AttnArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.sinks = sinks;
   a.gathered = static_cast<const uint16_t *>(gathered);
   a.mask = static_cast<const uint16_t *>(mask);
+  a.invalid = invalid;
   a.indices = indices;
   char *ws = static_cast<char *>(workspace);
   a.stats = reinterpret_cast<float4 *>(ws);
@@ -500,29 +583,21 @@ ds::AttnArgs attention_args(const ds_sparse_rows *rows, const SparsePlan &p, con
   return a;
 }
 
-// Block b of either phase serves row b % 8 (one XCD per row); phase 1 has
-// kAttnHeadGroups workgroups per (row, chunk).
-uint32_t attention_blocks(const SparsePlan &p) {
-  uint32_t max_chunks = 0;
-  for (uint32_t r = 0; r < p.rows; ++r) max_chunks = std::max(max_chunks, p.chunks[r]);
-  return ds::kXcds * max_chunks * ds::kAttnHeadGroups;
-}
-
 ds_status launch_attention(const ds_sparse_rows *rows, const SparsePlan &p, bool direct, const void *q,
-                           const float *sinks, const void *gathered, const void *mask, const int32_t *indices,
-                           float scale, void *workspace, float *out, void *stream) {
-  const ds::AttnArgs a = attention_args(rows, p, q, sinks, gathered, mask, indices, scale, workspace, out);
+                           const float *sinks, const void *gathered, const void *mask, const uint32_t *invalid,
+                           const int32_t *indices, float scale, void *workspace, float *out, void *stream) {
+  const ds::AttnArgs a = attention_args(rows, p, q, sinks, gathered, mask, invalid, indices, scale, workspace, out);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = ds::launch_attn_chunks(a, direct, attention_blocks(p), s);
+  hipError_t e = ds::launch_attn_chunks(a, direct, p.max_chunks, s);
   if (e != hipSuccess) return hip_fail(e, "attention chunk launch");
-  e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
-  return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
+  e = ds::launch_attn_combine(a, s);
+  return e == hipSuccess ? DS_OK : hip_fail(e, "attention combine launch");
 }
 
 ds_status check_attention_common(const SparsePlan &p, const void *q, size_t q_elems, const float *sinks,
                                  size_t sinks_elems, float scale, void *workspace, size_t workspace_bytes,
                                  float *out, size_t out_elems) {
-  if (!std::isfinite(scale) || scale <= 0.0f) return fail("scale must be finite and positive");
+  if (!(std::isfinite(scale) && scale > 0.0f)) return fail("scale %g is not a finite value above 0", double(scale));
   DS_TRY(need(q, "q"));
   DS_TRY(need(sinks, "sinks"));
   DS_TRY(need(workspace, "attention workspace"));
@@ -540,8 +615,8 @@ extern "C" {
 
 ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows, const void *q, size_t q_elems, const float *sinks,
                               size_t sinks_elems, const void *gathered, size_t gathered_elems, const void *mask,
-                              size_t mask_elems, float scale, void *workspace, size_t workspace_bytes, float *out,
-                              size_t out_elems, void *stream) {
+                              size_t mask_elems, const uint32_t *invalid, size_t invalid_elems, float scale,
+                              void *workspace, size_t workspace_bytes, float *out, size_t out_elems, void *stream) {
   SparsePlan p;
   DS_TRY(check_sparse(rows, &p));
   DS_TRY(check_attention_common(p, q, q_elems, sinks, sinks_elems, scale, workspace, workspace_bytes, out,
@@ -550,7 +625,10 @@ ds_status ds_rows_sparse_attn(const ds_sparse_rows *rows, const void *q, size_t 
   DS_TRY(need(mask, "mask"));
   DS_TRY(cap(gathered_elems, p.slots * DS_HEAD_DIM, "gathered_kv", "elements"));
   DS_TRY(cap(mask_elems, p.slots, "mask", "elements"));
-  return launch_attention(rows, p, false, q, sinks, gathered, mask, nullptr, scale, workspace, out, stream);
+  DS_TRY(need(invalid, "invalid"));
+  DS_TRY(cap(invalid_elems, p.rows, "invalid", "elements"));
+  DS_TRY(check_device());
+  return launch_attention(rows, p, false, q, sinks, gathered, mask, invalid, nullptr, scale, workspace, out, stream);
 }
 
 ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows, const void *q, size_t q_elems, const float *sinks,
@@ -563,11 +641,12 @@ ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows, const void *q, 
                                 out_elems));
   DS_TRY(need(indices, "indices"));
   for (uint32_t r = 0; r < p.rows; ++r) {
-    if (!rows->kv[r]) return fail("row %u: kv must not be null", r);
+    if (!rows->kv[r]) return fail("sparse row %u: kv must not be null", r);
     DS_TRY(cap(rows->kv_elems[r], uint64_t(rows->kv_len[r]) * DS_HEAD_DIM, "kv", "elements"));
   }
   DS_TRY(cap(indices_elems, p.index_end, "indices", "elements"));
-  return launch_attention(rows, p, true, q, sinks, nullptr, nullptr, indices, scale, workspace, out, stream);
+  DS_TRY(check_device());
+  return launch_attention(rows, p, true, q, sinks, nullptr, nullptr, nullptr, indices, scale, workspace, out, stream);
 }
 
 ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_sparse_rows *srows, const void *idx_q,
@@ -588,19 +667,22 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
   DS_TRY(check_attention_common(sp, q, q_elems, sinks, sinks_elems, scale, attn_workspace, attn_workspace_bytes, out,
                                 out_elems));
   for (uint32_t r = 0; r < sp.rows; ++r) {
-    if (!srows->kv[r]) return fail("row %u: kv must not be null", r);
+    if (!srows->kv[r]) return fail("sparse row %u: kv must not be null", r);
     DS_TRY(cap(srows->kv_elems[r], uint64_t(srows->kv_len[r]) * DS_HEAD_DIM, "kv", "elements"));
   }
-  if (sp.rows != p.rows) return fail("the indexer table has %u rows, the sparse table %u", p.rows, sp.rows);
+  if (sp.rows != p.rows) return fail("the indexer table has %u rows but the sparse table %u", p.rows, sp.rows);
   for (uint32_t r = 0; r < p.rows; ++r) {
-    if (srows->width[r] > DS_TOP_K) return fail("row %u: width must be at most %d (the selected slots)", r, DS_TOP_K);
+    if (srows->width[r] > DS_TOP_K)
+      return fail("sparse row %u: width %u is above the %d selected slots", r, srows->width[r], DS_TOP_K);
     if (srows->index_offset[r] != irows->output_offset[r])
-      return fail("row %u: index_offset must equal the indexer's output_offset", r);
+      return fail("sparse row %u: index_offset %u differs from the indexer row's output_offset %u", r,
+                  srows->index_offset[r], irows->output_offset[r]);
   }
+  DS_TRY(check_device());
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const ds::AttnArgs a =
-      attention_args(srows, sp, q, sinks, nullptr, nullptr, indices, scale, attn_workspace, out);
+      attention_args(srows, sp, q, sinks, nullptr, nullptr, nullptr, indices, scale, attn_workspace, out);
   ds::TopkLevelArgs t{};
   t.scores = scores;
   t.score_stride = p.max_kv;
@@ -627,10 +709,10 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
     for (uint32_t per : {4u, 8u})
       if (max_visible <= ds::kTopkThreads * per) { t.per_thread = per; break; }
     for (uint32_t r = 0; r < p.rows; ++r) t.count[r] = p.visible[r];
-    hipError_t e = ds::launch_topk_attn(t, a, attention_blocks(sp), s);
+    hipError_t e = ds::launch_topk_attn(t, a, sp.max_chunks, s);
     if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
-    e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
-    return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
+    e = ds::launch_attn_combine(a, s);
+    return e == hipSuccess ? DS_OK : hip_fail(e, "attention combine launch");
   }
 
   // One kernel for the final level and the attention when the indexer keeps
@@ -657,7 +739,7 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
     }
     bool attn_done = false;
     DS_TRY(run_topk_levels(irows, p, scores, in, bank, bank + p.fused_bank, indices, stream, &a,
-                           attention_blocks(sp), &attn_done));
+                           sp.max_chunks, &attn_done));
     if (attn_done) return DS_OK;
     return ds_rows_sparse_attn_direct(srows, q, q_elems, sinks, sinks_elems, indices, indices_elems, scale,
                                       attn_workspace, attn_workspace_bytes, out, out_elems, stream);
@@ -688,10 +770,10 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
     t.floor_count[r] = blocks * ds::kIdxFloors;
     t.fallback_count[r] = p.visible[r];
   }
-  hipError_t e = ds::launch_topk_attn(t, a, attention_blocks(sp), s);
+  hipError_t e = ds::launch_topk_attn(t, a, sp.max_chunks, s);
   if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
-  e = ds::launch_attn_combine(a, ds::kXcds * (DS_HEAD_DIM / ds::kAttnDimChunk), s);
-  return e == hipSuccess ? DS_OK : hip_fail(e, "attention reduce launch");
+  e = ds::launch_attn_combine(a, s);
+  return e == hipSuccess ? DS_OK : hip_fail(e, "attention combine launch");
 }
 
 const char *ds_rows_last_error(void) { return g_error.c_str(); }
@@ -707,9 +789,9 @@ bool compressor_shape_ok(uint32_t ratio, uint32_t head_dim) {
   return (ratio == 4 && (head_dim == 128 || head_dim == 512)) || (ratio == 128 && head_dim == 512);
 }
 
-bool ranges_overlap(const void *a, uint64_t an, const void *b, uint64_t bn) {
-  const auto a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-  return a0 < b0 + bn && b0 < a0 + an;
+ds_status compressor_shape_error(uint32_t ratio, uint32_t head_dim) {
+  return fail("compressor shape (ratio %u, head_dim %u) is unsupported; supported are ratio 4 with head_dim 128 "
+              "or 512, and ratio 128 with head_dim 512", ratio, head_dim);
 }
 
 }  // namespace
@@ -718,7 +800,7 @@ extern "C" {
 
 size_t ds_rows_compressor_state_elems(uint32_t ratio, uint32_t head_dim) {
   if (!compressor_shape_ok(ratio, head_dim)) {
-    fail("compressor (ratio, head_dim) must be (4,128), (4,512) or (128,512), got (%u,%u)", ratio, head_dim);
+    compressor_shape_error(ratio, head_dim);
     return 0;
   }
   const uint64_t coff = ratio == 4 ? 2 : 1;
@@ -729,32 +811,39 @@ ds_status ds_rows_compressor(const ds_compressor_rows *rows, uint32_t ratio, uin
                              const float *kv, size_t kv_elems, const float *score, size_t score_elems,
                              const float *ape, size_t ape_elems, const float *norm, size_t norm_elems, void *output,
                              size_t output_elems, void *stream) {
-  if (!rows) return fail("null compressor row table");
-  if (rows->rows == 0 || rows->rows > DS_ROWS_MAX)
-    return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, rows->rows);
-  if (!compressor_shape_ok(ratio, head_dim))
-    return fail("compressor (ratio, head_dim) must be (4,128), (4,512) or (128,512), got (%u,%u)", ratio, head_dim);
-  if (!std::isfinite(epsilon) || epsilon <= 0.0f) return fail("compressor epsilon must be finite and positive");
+  if (!rows) return fail("compressor row table is null");
+  DS_TRY(check_row_count(rows->rows));
+  if (!compressor_shape_ok(ratio, head_dim)) return compressor_shape_error(ratio, head_dim);
+  if (!(std::isfinite(epsilon) && epsilon > 0.0f))
+    return fail("compressor epsilon %g is not a finite value above 0", double(epsilon));
   const uint64_t coff = ratio == 4 ? 2 : 1;
   const uint64_t proj = coff * head_dim;
   const uint64_t state = coff * ratio * proj;
   const uint32_t n = rows->rows;
   for (uint32_t r = 0; r < n; ++r) {
-    if (rows->start_pos[r] == 0 || rows->start_pos[r] == UINT32_MAX)
-      return fail("compressor row %u: position must be in 1..u32::MAX, got %u", r, rows->start_pos[r]);
+    // start_pos 0 would have no earlier token; the largest position leaves no
+    // next one.
+    if (rows->start_pos[r] < 1 || rows->start_pos[r] > UINT32_MAX - 1)
+      return fail("compressor row %u: start_pos %u is outside [1, 2^32 - 2]", r, rows->start_pos[r]);
     if (!rows->kv_state[r]) return fail("compressor row %u: kv_state must not be null", r);
     if (!rows->score_state[r]) return fail("compressor row %u: score_state must not be null", r);
     DS_TRY(cap(rows->kv_state_elems[r], state, "kv_state", "elements"));
     DS_TRY(cap(rows->score_state_elems[r], state, "score_state", "elements"));
   }
-  // Every state buffer of every row is written: all must be disjoint.
-  for (uint32_t r = 0; r < 2 * n; ++r) {
-    const void *pr = r < n ? rows->kv_state[r] : rows->score_state[r - n];
-    for (uint32_t o = 0; o < r; ++o) {
-      const void *po = o < n ? rows->kv_state[o] : rows->score_state[o - n];
-      if (ranges_overlap(pr, state * sizeof(float), po, state * sizeof(float)))
-        return fail("compressor states overlap (state buffers %u and %u)", o, r);
+  // Every state buffer of every row is written: all 2n byte ranges must be
+  // disjoint (kv states are buffers 0..n-1, score states n..2n-1).
+  {
+    std::pair<uintptr_t, uint32_t> b[2 * DS_ROWS_MAX];
+    for (uint32_t r = 0; r < n; ++r) {
+      b[r] = {reinterpret_cast<uintptr_t>(rows->kv_state[r]), r};
+      b[n + r] = {reinterpret_cast<uintptr_t>(rows->score_state[r]), n + r};
     }
+    std::sort(b, b + 2 * n);
+    for (uint32_t i = 1; i < 2 * n; ++i)
+      if (b[i].first < b[i - 1].first + state * sizeof(float))
+        return fail("compressor state buffers %u and %u share memory (buffers 0..rows-1 are the kv states, "
+                    "rows..2 rows-1 the score states)", std::min(b[i - 1].second, b[i].second),
+                    std::max(b[i - 1].second, b[i].second));
   }
   DS_TRY(need(kv, "kv"));
   DS_TRY(need(score, "score"));
@@ -766,6 +855,7 @@ ds_status ds_rows_compressor(const ds_compressor_rows *rows, uint32_t ratio, uin
   DS_TRY(cap(ape_elems, ratio * proj, "ape", "elements"));
   DS_TRY(cap(norm_elems, head_dim, "norm", "elements"));
   DS_TRY(cap(output_elems, uint64_t(n) * head_dim, "output", "elements"));
+  DS_TRY(check_device());
 
   ds::CompressorArgs a{};
   a.kv = kv;
@@ -803,18 +893,19 @@ struct MqPlan {
 // The row-table checks that concern scoring (rows, kv_len, positions and the
 // causal length of the last query); offsets and output offsets are not used.
 ds_status check_mq(const ds_indexer_rows *t, uint32_t query_len, MqPlan *p) {
-  if (!t) return fail("null indexer row table");
-  if (t->rows == 0 || t->rows > DS_ROWS_MAX) return fail("rows must be 1..=%d, got %u", DS_ROWS_MAX, t->rows);
-  if (query_len == 0 || query_len > uint32_t(ds::kMqMaxQueries))
-    return fail("query_len must be 1..=%d, got %u", ds::kMqMaxQueries, query_len);
+  if (!t) return fail("indexer row table is null");
+  DS_TRY(check_row_count(t->rows));
+  if (query_len < 1 || query_len > uint32_t(ds::kMqMaxQueries))
+    return fail("query_len %u is outside [1, %d]", query_len, ds::kMqMaxQueries);
   p->rows = t->rows;
   for (uint32_t r = 0; r < t->rows; ++r) {
-    if (t->kv_len[r] == 0) return fail("indexer row %u: kv_len must be nonzero", r);
     if (uint64_t(t->start_pos[r]) + query_len > UINT32_MAX)
-      return fail("indexer row %u: indexer position overflows", r);
-    const uint32_t causal = (t->start_pos[r] + query_len) / DS_RATIO;   // the last query's
-    if (t->kv_len[r] < causal)
-      return fail("indexer row %u: kv_len %u is shorter than %u causal compressed entries", r, t->kv_len[r], causal);
+      return fail("indexer row %u: the last query's position start_pos %u + %u is past 2^32 - 2", r,
+                  t->start_pos[r], query_len - 1);
+    // The row's fields as for one query at the last query's position; the
+    // offset is not used by the scores.
+    uint32_t visible;
+    DS_TRY(check_indexer_row(r, t->kv_len[r], t->start_pos[r] + query_len - 1, 0, &visible));
     p->max_kv = std::max<uint64_t>(p->max_kv, t->kv_len[r]);
     p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + query_len);
     p->blk_begin[r + 1] = p->blk_begin[r] + div_up(t->kv_len[r], kMqKeysPerBlock);
@@ -848,6 +939,7 @@ ds_status ds_rows_indexer_score_mq(const ds_indexer_rows *rows, uint32_t query_l
   DS_TRY(cap(q_elems, p.q_rows * DS_HEADS * DS_INDEXER_DIM, "indexer q", "elements"));
   DS_TRY(cap(weights_elems, p.q_rows * DS_HEADS, "indexer weights", "elements"));
   DS_TRY(cap(scores_elems, uint64_t(p.rows) * query_len * p.max_kv, "indexer scores", "elements"));
+  DS_TRY(check_device());
 
   ds::IndexerMqArgs a{};
   a.q = static_cast<const uint16_t *>(q);

@@ -8,6 +8,8 @@
 
 #include <cstdint>
 
+#include "ds_rows.h"
+
 namespace ds {
 
 constexpr int kRowsMax = 8;
@@ -103,7 +105,8 @@ hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_
 
 // ----------------------------------------------------------------- gather
 // One workgroup of 2 waves copies 16 slots; one wave moves one 1 KiB row per
-// slot, eight slots in flight.
+// slot, eight slots in flight. A first small kernel clears invalid[0 .. rows),
+// which the gather's workgroups then set with atomic ORs.
 constexpr int kGatherThreads = 128;
 constexpr int kGatherSlotsPerWave = 8;
 constexpr int kGatherSlotsPerBlock = (kGatherThreads / 64) * kGatherSlotsPerWave;
@@ -113,6 +116,7 @@ struct GatherArgs {
   const int32_t *indices;
   uint16_t *gathered;               // bf16 [sum(width), 512]
   uint16_t *mask;                   // bf16 [sum(width)]
+  uint32_t *invalid;                // u32 [rows]
   uint32_t rows;
   uint32_t kv_len[kRowsMax];
   uint32_t width[kRowsMax];
@@ -120,6 +124,7 @@ struct GatherArgs {
   uint64_t slot_base[kRowsMax];     // sum of widths of the rows before r
 };
 // Grid (max_row_blocks, a.rows): workgroup (x, r) copies row r's slots 16x ..
+// (after the clearing kernel).
 hipError_t launch_gather(const GatherArgs &a, uint32_t max_row_blocks, hipStream_t s);
 
 // -------------------------------------------------------------- attention
@@ -139,6 +144,7 @@ struct AttnArgs {
   const float *sinks;               // f32 [64]
   const uint16_t *gathered;         // bf16 [sum(width), 512] (gathered variant)
   const uint16_t *mask;             // bf16 [sum(width)] (gathered variant)
+  const uint32_t *invalid;          // u32 [rows] (gathered variant): nonzero zeroes the row
   const int32_t *indices;           // i32 (direct variant)
   const uint16_t *kv[kRowsMax];     // bf16 [kv_len, 512] per row (direct variant)
   float4 *stats;                    // (m_c, s_c, bad, sink): row r at stat_base[r], [chunks][64]
@@ -155,15 +161,20 @@ struct AttnArgs {
   uint64_t stat_base[kRowsMax];
   uint64_t part_base[kRowsMax];
 };
-hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t blocks, hipStream_t s);
-hipError_t launch_attn_combine(const AttnArgs &a, uint32_t blocks, hipStream_t s);
+// Phase-1 grid (32 * ceil(max_chunks / 8), rows): workgroup (x, r) serves
+// chunk 8 (x / 32) + x % 8 of row r with head group (x / 8) % 4. Workgroups go
+// to the 8 XCDs by linear id, so the four head groups of a chunk share one
+// XCD (and its L2, where they read the chunk's rows). Phase-2 grid
+// (512 / kAttnDimChunk, rows).
+hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t max_chunks, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s);
 
 // ------------------------------------------------ final top-k + attention
 // One 1024-thread workgroup per attention chunk (blocks as the attention's
 // phase 1): each runs its row's final top-k level over the fused indexer's
 // candidates (t: a single final, checked level) and then its attention chunk
 // on the indices it selected (a: the direct variant's arguments).
-hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t blocks, hipStream_t s);
+hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t max_chunks, hipStream_t s);
 
 
 // ---------------------------------------------------------- multi-query indexer

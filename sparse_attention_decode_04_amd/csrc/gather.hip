@@ -3,17 +3,16 @@
 // Source: docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal",
 // kernel deepseek_sparse_attention_gather_rows_bf16: per slot, a -1 index is
 // a sentinel (zero row, mask -inf), an index outside [0, kv_len) is bad (zero
-// row, row invalid), otherwise the KV row is copied bit for bit with
+// row, mask 0, row invalid), otherwise the KV row is copied bit for bit with
 // non-finite elements replaced by zero (and the row marked invalid).
 //
-// Differences from the pages' kernel (one thread per element, a relaxed
-// atomic store into a caller-zeroed per-row flag): one wave moves one
-// 1 KiB row as 64 lanes x 16 bytes, eight rows in flight per wave, with the
-// wave's eight indices read by eight lanes and broadcast; and the "row
-// invalid" state is carried per slot in the mask as NaN, written with a plain
-// store by the wave that saw it. The mask therefore needs no zeroed workspace
-// and no atomics; the attention call treats any NaN mask entry of a row as
-// the row's invalid flag.
+// Differences from the pages' kernel (one thread per element; a relaxed
+// atomic store into a per-row flag the caller has cleared): one wave moves
+// one 1 KiB row as 64 lanes x 16 bytes, eight rows in flight per wave, with
+// the wave's eight indices read by eight lanes and broadcast; the per-row
+// flag is cleared by a first one-workgroup kernel of the same call (so the
+// caller need not), and each wave that saw a bad slot sets it with one atomic
+// OR.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 
@@ -27,7 +26,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   uint32_t width = a.width[r], n = a.kv_len[r], ioff = a.index_offset[r];
   uint64_t kvb = reinterpret_cast<uint64_t>(a.kv[r]), ib = reinterpret_cast<uint64_t>(a.indices);
   uint64_t gb = reinterpret_cast<uint64_t>(a.gathered), mb = reinterpret_cast<uint64_t>(a.mask), sbase = a.slot_base[r];
-  asm volatile("" : "+s"(width), "+s"(n), "+s"(ioff), "+s"(kvb), "+s"(ib), "+s"(gb), "+s"(mb), "+s"(sbase));
+  uint64_t vb = reinterpret_cast<uint64_t>(a.invalid);
+  asm volatile("" : "+s"(width), "+s"(n), "+s"(ioff), "+s"(kvb), "+s"(ib), "+s"(gb), "+s"(mb), "+s"(sbase), "+s"(vb));
   if (blockIdx.x * kGatherSlotsPerBlock >= width) return;   // uniform
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = threadIdx.x >> 6;
@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
     const bool ok = sel[s] >= 0 && static_cast<uint32_t>(sel[s]) < n;
     if (!ok) v[s] = u32x4{0, 0, 0, 0};
   }
+  bool row_bad = false;   // wave-uniform
 #pragma unroll
   for (int s = 0; s < kGatherSlotsPerWave; ++s) {
     const uint32_t slot = slot0 + s;
@@ -71,13 +72,22 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
     }
     const uint64_t out_slot = sbase + slot;
     store16(gathered + out_slot * kDim + 8 * lane, v[s]);
-    const bool any_bad = __ballot(value_bad) != 0;
-    if (lane == 0)
-      mask[out_slot] = sentinel ? kBf16NegInf : ((index_bad || any_bad) ? kBf16NaN : uint16_t(0));
+    row_bad |= index_bad || __ballot(value_bad) != 0;
+    if (lane == 0) mask[out_slot] = sentinel ? kBf16NegInf : uint16_t(0);
   }
+  if (row_bad && lane == 0) atomicOr(global_ptr<uint32_t>(vb) + r, 1u);
+}
+
+// invalid[0 .. rows) = 0, ahead of the gather in the same stream.
+__global__ __launch_bounds__(64) void clear_flags_kernel(uint32_t *flags, uint32_t n) {
+  if (threadIdx.x < n) flags[threadIdx.x] = 0;
 }
 
 hipError_t launch_gather(const GatherArgs &a, uint32_t max_row_blocks, hipStream_t s) {
+  static_assert(kRowsMax <= 64, "one clearing workgroup");
+  hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(64), 0, s, a.invalid, a.rows);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gather_kernel, dim3(max_row_blocks, a.rows), dim3(kGatherThreads), 0, s, a);
   return hipGetLastError();
 }

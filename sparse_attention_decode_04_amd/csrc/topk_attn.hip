@@ -60,6 +60,7 @@ __device__ __forceinline__ void topk_attn_rows(const TopkLevelArgs &t, const Att
   lr.check = lr.final_level && ((cmask >> r) & 1u) != 0;
   ar.rows = global_ptr<const uint16_t>(kv);
   ar.mask = nullptr;   // direct variant
+  ar.invalid = nullptr;
   ar.q = global_ptr<const uint16_t>(q) + static_cast<uint64_t>(q_row) * kHeads * kDim;
   ar.sinks = global_ptr<const float>(sinks);
   ar.stats = global_ptr<float4>(stats) + stat_base;
@@ -77,11 +78,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   } u;
   __shared__ int32_t slot_index[kAttnChunk];
 
-  // Row r on XCD r, as in the attention kernel.
-  const uint32_t r = blockIdx.x % kXcds;
-  const uint32_t rest = blockIdx.x / kXcds;
-  const uint32_t hg = rest % kAttnHeadGroups;
-  const uint32_t c = rest / kAttnHeadGroups;
+  // Grid (x, row), as the attention's phase 1.
+  const uint32_t r = blockIdx.y;
+  uint32_t c, hg;
+  attn_block(blockIdx.x, c, hg);
   uint32_t rows, chunks;
   LevelRow lr;
   AttnRow ar;
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   attn_chunk_body<true>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
 }
 
-hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t blocks, hipStream_t s) {
+hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t max_chunks, hipStream_t s) {
+  const dim3 blocks(kXcds * kAttnHeadGroups * ((max_chunks + kXcds - 1) / kXcds), a.rows);
   if (t.from_scores) {
     // The scores of every row fit one chunk of 4, 8 or 16 per thread.
     if (t.per_thread == 4)

@@ -101,9 +101,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ds_rows_topk.argtypes = [P(IndexerRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                  c_void_p, c_size_t, c_void_p]
     lib.ds_rows_gather.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
-                                   c_void_p, c_size_t, c_void_p]
+                                   c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     lib.ds_rows_sparse_attn.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
-                                        c_void_p, c_size_t, c_void_p, c_size_t, c_float,
+                                        c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t, c_float,
                                         c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     lib.ds_rows_sparse_attn_direct.argtypes = [P(SparseRows), c_void_p, c_size_t, c_void_p, c_size_t,
                                                c_void_p, c_size_t, c_float, c_void_p, c_size_t,
@@ -312,22 +312,24 @@ def indexer_candidates(t: IndexerRows, q, weights, scores, workspace, stream=Non
     _check(load().ds_rows_indexer_candidates(ctypes.byref(t), qa, qn, wa, wn, sa, sn, ka, kb, _stream(stream)))
 
 
-def gather(t: SparseRows, indices, gathered, mask, stream=None):
+def gather(t: SparseRows, indices, gathered, mask, invalid, stream=None):
     ia, inn = _dev(indices, 4)
     ga, gn = _dev(gathered, 2)
     ma, mn = _dev(mask, 2)
-    _check(load().ds_rows_gather(ctypes.byref(t), ia, inn, ga, gn, ma, mn, _stream(stream)))
+    va, vn = _dev(invalid, 4)
+    _check(load().ds_rows_gather(ctypes.byref(t), ia, inn, ga, gn, ma, mn, va, vn, _stream(stream)))
 
 
-def sparse_attn(t: SparseRows, q, sinks, gathered, mask, scale, workspace, out, stream=None):
+def sparse_attn(t: SparseRows, q, sinks, gathered, mask, invalid, scale, workspace, out, stream=None):
     qa, qn = _dev(q, 2)
     sa, sn = _dev(sinks, 4)
     ga, gn = _dev(gathered, 2)
     ma, mn = _dev(mask, 2)
+    va, vn = _dev(invalid, 4)
     wa = _addr(workspace)
     wb = workspace.numel() * workspace.element_size()
     oa, on = _dev(out, 4)
-    _check(load().ds_rows_sparse_attn(ctypes.byref(t), qa, qn, sa, sn, ga, gn, ma, mn, float(scale),
+    _check(load().ds_rows_sparse_attn(ctypes.byref(t), qa, qn, sa, sn, ga, gn, ma, mn, va, vn, float(scale),
                                       wa, wb, oa, on, _stream(stream)))
 
 

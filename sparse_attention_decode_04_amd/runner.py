@@ -61,6 +61,7 @@ class DeviceRows:
         self.indices = torch.full((R_all * TOP_K,), -7, dtype=torch.int32, device=d)
         self.gathered = torch.empty(ds.gathered_elems(self.stab), dtype=torch.int16, device=d)
         self.mask = torch.empty(ds.mask_elems(self.stab), dtype=torch.int16, device=d)
+        self.invalid = torch.full((len(self.rows),), 7, dtype=torch.int32, device=d)
         self.attn_ws = torch.empty(ds.attn_workspace_bytes(self.stab), dtype=torch.uint8, device=d)
         self.out = torch.zeros(R_all * HEADS * HEAD_DIM, dtype=torch.float32, device=d)
         self.scale = inp.scale
@@ -84,10 +85,10 @@ class DeviceRows:
                              stream)
 
     def gather(self, stream=None):
-        ds.gather(self.stab, self.indices, self.gathered, self.mask, stream)
+        ds.gather(self.stab, self.indices, self.gathered, self.mask, self.invalid, stream)
 
     def sparse_attn(self, stream=None):
-        ds.sparse_attn(self.stab, self.dev.attn_q, self.dev.sinks, self.gathered, self.mask,
+        ds.sparse_attn(self.stab, self.dev.attn_q, self.dev.sinks, self.gathered, self.mask, self.invalid,
                        self.scale, self.attn_ws, self.out, stream)
 
     def sparse_attn_direct(self, stream=None):
@@ -129,6 +130,7 @@ class DeviceRows:
         idx = self.indices.cpu().numpy()
         gathered = self.gathered.cpu().numpy().view(np.uint16)
         mask = self.mask.cpu().numpy().view(np.uint16)
+        invalid = self.invalid.cpu().numpy().view(np.uint32)
         out = self.out.cpu().numpy().reshape(inp.rows, HEADS, HEAD_DIM)
         res, base = [], 0
         for i, r in enumerate(self.rows):
@@ -139,6 +141,7 @@ class DeviceRows:
                 indices=idx[TOP_K * r: TOP_K * (r + 1)],
                 gathered=gathered[base * HEAD_DIM:(base + w) * HEAD_DIM].reshape(w, HEAD_DIM),
                 mask=mask[base: base + w],
+                invalid=int(invalid[i]),
                 out=out[r],
             ))
             base += w

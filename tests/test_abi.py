@@ -4,8 +4,9 @@ queries are right, and every argument check fires before anything is
 enqueued (so these calls use fake, never-dereferenced device addresses and
 never reach a launch).
 
-Checks restated from docs.rs "mlx-native 0.21.0 src/ops/deepseek_rows.rs":
-check_rows, sparse_params, sparse_io_checks, dispatch_deepseek_indexer_rows.
+The checked conditions are those the host dispatch code on docs.rs
+"mlx-native 0.21.0 src/ops/deepseek_rows.rs" requires of its rows dispatches;
+the messages are this library's own.
 """
 import ctypes
 import os
@@ -22,6 +23,7 @@ HEADER = os.path.join(ROOT, "include", "ds_rows.h")
 FAKE = 0x100000            # never dereferenced: every call below fails its checks
 BIG = 1 << 40
 INVALID = 1
+DEVICE = 3
 
 
 @pytest.fixture(scope="module")
@@ -123,12 +125,12 @@ def call_fused(lib, t, q=BIG, w=BIG, s=BIG, ws=BIG, idx=BIG, wsp=FAKE):
     return lib.ds_rows_indexer_topk(ctypes.byref(t), FAKE, q, FAKE, w, FAKE, s, wsp, ws, FAKE, idx, None)
 
 
-def call_gather(lib, t, idx=BIG, g=BIG, m=BIG):
-    return lib.ds_rows_gather(ctypes.byref(t), FAKE, idx, FAKE, g, FAKE, m, None)
+def call_gather(lib, t, idx=BIG, g=BIG, m=BIG, inv=BIG, invp=FAKE):
+    return lib.ds_rows_gather(ctypes.byref(t), FAKE, idx, FAKE, g, FAKE, m, invp, inv, None)
 
 
-def call_attn(lib, t, scale=0.0441941738, q=BIG, sinks=64, g=BIG, m=BIG, ws=BIG, out=BIG):
-    return lib.ds_rows_sparse_attn(ctypes.byref(t), FAKE, q, FAKE, sinks, FAKE, g, FAKE, m,
+def call_attn(lib, t, scale=0.0441941738, q=BIG, sinks=64, g=BIG, m=BIG, inv=BIG, ws=BIG, out=BIG, invp=FAKE):
+    return lib.ds_rows_sparse_attn(ctypes.byref(t), FAKE, q, FAKE, sinks, FAKE, g, FAKE, m, invp, inv,
                                    ctypes.c_float(scale), FAKE, ws, FAKE, out, None)
 
 
@@ -186,27 +188,53 @@ def test_size_queries(lib):
 def test_rows_out_of_range(lib, rows):
     t = itab((10,) * 8)
     t.rows = rows
-    expect_invalid(call_score(lib, t), "rows must be 1..=8")
-    expect_invalid(call_topk(lib, t), "rows must be 1..=8")
+    msg = f"row table has rows = {rows}; a call takes 1 to 8 rows"
+    expect_invalid(call_score(lib, t), msg)
+    expect_invalid(call_topk(lib, t), msg)
     s = stab((10,) * 8)
     s.rows = rows
-    expect_invalid(call_gather(lib, s), "rows must be 1..=8")
-    expect_invalid(call_attn(lib, s), "rows must be 1..=8")
+    expect_invalid(call_gather(lib, s), msg)
+    expect_invalid(call_attn(lib, s), msg)
 
 
 def test_indexer_row_checks(lib):
-    expect_invalid(call_score(lib, itab((10, 0))), "row 1: kv_len must be nonzero")
-    expect_invalid(call_score(lib, itab((10,), start_pos=[4 * 11 - 1])), "shorter than 11 causal")
-    expect_invalid(call_score(lib, itab((10,), start_pos=[0xFFFFFFFF])), "position overflows")
-    expect_invalid(call_score(lib, itab((10,), offset=[-1])), "offset must be nonnegative")
-    expect_invalid(call_score(lib, itab((10,), offset=[2 ** 31 - 9])), "exceeds i32")
+    expect_invalid(call_score(lib, itab((10, 0))), "indexer row 1: kv_len is 0")
+    expect_invalid(call_score(lib, itab((10,), start_pos=[4 * 11 - 1])), "makes 11 keys visible but kv_len is only 10")
+    expect_invalid(call_score(lib, itab((10,), start_pos=[0xFFFFFFFF])), "must be at most 2^32 - 2")
+    expect_invalid(call_score(lib, itab((10,), offset=[-1])), "offset -1 is negative")
+    expect_invalid(call_score(lib, itab((10,), offset=[2 ** 31 - 9])), "does not fit in int32")
     # offset + causal - 1 == INT32_MAX is allowed, one more is not
     assert ds.scores_elems(itab((10,), offset=[2 ** 31 - 9])) == 0
     assert ds.scores_elems(itab((10,), offset=[2 ** 31 - 10])) == 10
     # no visible key: any offset is fine
     assert ds.scores_elems(itab((10,), start_pos=[2], offset=[2 ** 31 - 1])) == 10
-    expect_invalid(call_topk(lib, itab((10, 10), out_off=[0, 511])), "overlap")
+    expect_invalid(call_topk(lib, itab((10, 10), out_off=[0, 511])), "rows 0 and 1: their 512-index output ranges")
+    expect_invalid(call_topk(lib, itab((10, 10, 10), out_off=[1024, 3000, 1100])), "rows 0 and 2")
     assert ds.scores_elems(itab((10, 10), out_off=[512, 0])) == 20
+
+
+def test_kv_len_limit(lib):
+    # The selection kernels address a row's 8-byte keys with 32-bit byte
+    # offsets: kv_len must stay below 2^30, in every indexer entry point.
+    top = 2 ** 30 - 1
+    assert ds.scores_elems(itab((top,))) == top
+    for n in (2 ** 30, 2 ** 32 - 1):
+        t = itab((10, n))
+        assert ds.scores_elems(t) == 0
+        assert "indexer row 1: kv_len %d is above DS_KV_LEN_MAX = 2^30 - 1" % n in ds.last_error()
+        expect_invalid(call_score(lib, t), "is above DS_KV_LEN_MAX")
+        expect_invalid(call_topk(lib, t), "is above DS_KV_LEN_MAX")
+        expect_invalid(call_fused(lib, t), "is above DS_KV_LEN_MAX")
+        expect_invalid(call_mq(lib, itab((n,), start_pos=[8]), 2), "is above DS_KV_LEN_MAX")
+
+
+def test_valid_call_without_a_device_enqueues_nothing(lib):
+    # Arguments that pass every check reach the device check, which fails on
+    # a host without a HIP device: DS_ERR_DEVICE, and no launch is attempted.
+    t = itab((100,))
+    assert call_score(lib, t) == DEVICE
+    assert "HIP device" in ds.last_error()
+    assert call_gather(lib, stab((100,))) == DEVICE
 
 
 def test_fused_indexer_topk_checks(lib):
@@ -218,7 +246,7 @@ def test_fused_indexer_topk_checks(lib):
     expect_invalid(call_fused(lib, t, ws=need - 1), "indexer top-k workspace holds")
     expect_invalid(call_fused(lib, t, wsp=None), "indexer top-k workspace must not be null")
     expect_invalid(call_fused(lib, itab((10, 10), out_off=[0, 1024]), idx=1535), "indexer output holds")
-    expect_invalid(call_fused(lib, itab((10, 0))), "row 1: kv_len must be nonzero")
+    expect_invalid(call_fused(lib, itab((10, 0))), "indexer row 1: kv_len is 0")
     expect_invalid(call_fused(lib, itab((10,), keys_elems=[10 * 128 - 1])), "indexer kv holds")
     expect_invalid(lib.ds_rows_indexer_candidates(ctypes.byref(t), FAKE, BIG, FAKE, BIG, FAKE, BIG, FAKE, need - 1,
                                                   None), "indexer top-k workspace holds")
@@ -239,15 +267,16 @@ def test_indexer_capacity_checks(lib):
 # -------------------------------------------------------- sparse-row checks
 
 def test_sparse_row_checks(lib):
-    expect_invalid(call_gather(lib, stab((10, 0), width=(10, 1))), "kv_len and width must be nonzero")
-    expect_invalid(call_gather(lib, stab((10, 10), width=(10, 0))), "kv_len and width must be nonzero")
-    expect_invalid(call_attn(lib, stab((10, 10), q_row=[2, 2])), "q_row 2 is used twice")
+    expect_invalid(call_gather(lib, stab((10, 0), width=(10, 1))), "sparse row 1: kv_len is 0")
+    expect_invalid(call_gather(lib, stab((10, 10), width=(10, 0))), "sparse row 1: width is 0")
+    expect_invalid(call_attn(lib, stab((10, 10), q_row=[2, 2])), "sparse rows 0 and 1 both use q_row 2")
+    expect_invalid(call_attn(lib, stab((10, 10, 10), q_row=[4, 1, 4])), "sparse rows 0 and 2 both use q_row 4")
     expect_invalid(call_gather(lib, stab((10,), kv_elems=[10 * 512 - 1])), "kv holds")
     for bad in (float("nan"), float("inf"), 0.0, -1.0):
-        expect_invalid(call_attn(lib, stab((10,)), scale=bad), "scale must be finite and positive")
+        expect_invalid(call_attn(lib, stab((10,)), scale=bad), "is not a finite value above 0")
     s = stab((10,))
     s.rows = 9
-    expect_invalid(call_direct(lib, s), "rows must be 1..=8")
+    expect_invalid(call_direct(lib, s), "row table has rows = 9")
 
 
 def test_sparse_capacity_checks(lib):
@@ -255,6 +284,10 @@ def test_sparse_capacity_checks(lib):
     expect_invalid(call_gather(lib, t, idx=4029), "indices holds")
     expect_invalid(call_gather(lib, t, g=542 * 512 - 1), "gathered_kv holds")
     expect_invalid(call_gather(lib, t, m=541), "mask holds")
+    expect_invalid(call_gather(lib, t, inv=1), "invalid holds 1 elements, needs 2")
+    expect_invalid(call_gather(lib, t, invp=None), "invalid must not be null")
+    expect_invalid(call_attn(lib, t, inv=1), "invalid holds 1 elements, needs 2")
+    expect_invalid(call_attn(lib, t, invp=None), "invalid must not be null")
     expect_invalid(call_attn(lib, t, q=6 * 64 * 512 - 1), "q holds")
     expect_invalid(call_attn(lib, t, out=6 * 64 * 512 - 1), "output holds")
     expect_invalid(call_attn(lib, t, sinks=63), "sinks holds")
@@ -263,8 +296,8 @@ def test_sparse_capacity_checks(lib):
     expect_invalid(call_direct(lib, t, idx=4029), "indices holds")
     expect_invalid(call_direct(lib, stab((10,), kv_elems=[10 * 512 - 1])), "kv holds")
     expect_invalid(call_direct(lib, t, ws=ds.attn_workspace_bytes(t) - 1), "attention workspace holds")
-    expect_invalid(call_direct(lib, t, scale=float("nan")), "scale must be finite and positive")
-    expect_invalid(call_direct(lib, stab((10, 10), q_row=[1, 1])), "used twice")
+    expect_invalid(call_direct(lib, t, scale=float("nan")), "scale nan is not a finite value above 0")
+    expect_invalid(call_direct(lib, stab((10, 10), q_row=[1, 1])), "both use q_row 1")
 
 
 def call_step(lib, it, st, q=BIG, w=BIG, s=BIG, ws=BIG, idx=BIG, aq=BIG, sinks=64, scale=0.0441941738, aws=BIG,
@@ -279,16 +312,16 @@ def test_indexer_topk_attn_checks(lib):
     # attention's index_offset equal to the indexer's output_offset
     it = itab((20000, 30000), out_off=(0, 512), q_row=(0, 1))
     st = stab((20000, 30000), width=(512, 512), index_offset=(0, 512), q_row=(0, 1))
-    expect_invalid(call_step(lib, it, stab((20000,), width=(512,))), "the indexer table has 2 rows, the sparse table 1")
+    expect_invalid(call_step(lib, it, stab((20000,), width=(512,))), "the indexer table has 2 rows but the sparse table 1")
     expect_invalid(call_step(lib, it, stab((20000, 30000), width=(512, 513), index_offset=(0, 512), q_row=(0, 1))),
-                   "row 1: width must be at most 512")
+                   "sparse row 1: width 513 is above the 512 selected slots")
     expect_invalid(call_step(lib, it, stab((20000, 30000), width=(512, 512), index_offset=(0, 1024), q_row=(0, 1))),
-                   "row 1: index_offset must equal the indexer's output_offset")
+                   "sparse row 1: index_offset 1024 differs from the indexer row's output_offset 512")
     # and the checks of both calls
     expect_invalid(call_step(lib, it, st, ws=ds.indexer_topk_workspace_bytes(it) - 1), "indexer top-k workspace holds")
     expect_invalid(call_step(lib, it, st, idx=1023), "indexer output holds")
     expect_invalid(call_step(lib, it, st, aws=ds.attn_workspace_bytes(st) - 1), "attention workspace holds")
-    expect_invalid(call_step(lib, it, st, scale=float("inf")), "scale must be finite and positive")
+    expect_invalid(call_step(lib, it, st, scale=float("inf")), "scale inf is not a finite value above 0")
     expect_invalid(call_step(lib, it, stab((20000, 30000), width=(512, 512), index_offset=(0, 512), q_row=(0, 1),
                                           kv_elems=[20000 * 512, 30000 * 512 - 1])), "kv holds")
     expect_invalid(call_step(lib, itab((20000, 30000), out_off=(0, 512), q_row=(0, 1), keys_elems=[1, 1]), st),
@@ -304,9 +337,9 @@ def test_binding_rejects_host_tensors():
 
 
 # ---------------------------------------------------------------- compressor
-# Checks restated from dispatch_deepseek_compressor_rows ("mlx-native 0.21.0
-# src/ops/deepseek_rows.rs"): rows, supported shapes, epsilon, positions,
-# state capacities, disjoint states, operand capacities.
+# The conditions dispatch_deepseek_compressor_rows ("mlx-native 0.21.0
+# src/ops/deepseek_rows.rs") requires: rows, supported shapes, epsilon,
+# positions, state capacities, disjoint states, operand capacities.
 
 def ctab(start_pos=(7,), ratio=4, head_dim=128, state_elems=None, kv_addr=None, sc_addr=None):
     R = len(start_pos)
@@ -328,31 +361,34 @@ def test_compressor_sizes(lib):
     assert ds.compressor_state_elems(4, 512) == 8 * 1024
     assert ds.compressor_state_elems(128, 512) == 128 * 512
     assert ds.compressor_state_elems(128, 128) == 0
-    assert "must be (4,128), (4,512) or (128,512)" in ds.last_error()
+    assert "compressor shape (ratio 128, head_dim 128) is unsupported" in ds.last_error()
 
 
 def test_compressor_checks(lib):
-    expect_invalid(call_comp(lib, ctab(), ratio=4, head_dim=256), "must be (4,128), (4,512) or (128,512)")
-    expect_invalid(call_comp(lib, ctab(), ratio=128, head_dim=128), "got (128,128)")
+    expect_invalid(call_comp(lib, ctab(), ratio=4, head_dim=256), "shape (ratio 4, head_dim 256) is unsupported")
+    expect_invalid(call_comp(lib, ctab(), ratio=128, head_dim=128), "(ratio 128, head_dim 128)")
     for bad in (0.0, -1e-6, float("nan"), float("inf")):
-        expect_invalid(call_comp(lib, ctab(), eps=bad), "epsilon must be finite and positive")
-    expect_invalid(call_comp(lib, ctab((7, 0))), "row 1: position must be in 1..u32::MAX, got 0")
-    expect_invalid(call_comp(lib, ctab((0xFFFFFFFF,))), "position must be in 1..u32::MAX")
+        expect_invalid(call_comp(lib, ctab(), eps=bad), "compressor epsilon")
+        assert "is not a finite value above 0" in ds.last_error()
+    expect_invalid(call_comp(lib, ctab((7, 0))), "compressor row 1: start_pos 0 is outside [1, 2^32 - 2]")
+    expect_invalid(call_comp(lib, ctab((0xFFFFFFFF,))), "start_pos 4294967295 is outside")
     t = ctab()
     t.rows = 9
-    expect_invalid(call_comp(lib, t), "rows must be 1..=8")
+    expect_invalid(call_comp(lib, t), "rows = 9")
     t.rows = 0
-    expect_invalid(call_comp(lib, t), "rows must be 1..=8")
+    expect_invalid(call_comp(lib, t), "rows = 0")
     expect_invalid(call_comp(lib, ctab(state_elems=[2047])), "kv_state holds 2047 elements, needs 2048")
     t = ctab()
     t.score_state_elems[0] = 100
     expect_invalid(call_comp(lib, t), "score_state holds")
     # states of different rows, or a row's two states, must not overlap
     expect_invalid(call_comp(lib, ctab((7, 11), kv_addr=[FAKE, FAKE + 4096],
-                                       sc_addr=[FAKE + 0x1000000, FAKE + 0x2000000])), "compressor states overlap")
-    expect_invalid(call_comp(lib, ctab((7,), kv_addr=[FAKE], sc_addr=[FAKE + 2048 * 4 - 4])), "states overlap")
+                                       sc_addr=[FAKE + 0x1000000, FAKE + 0x2000000])),
+                   "compressor state buffers 0 and 1 share memory")
+    expect_invalid(call_comp(lib, ctab((7,), kv_addr=[FAKE], sc_addr=[FAKE + 2048 * 4 - 4])),
+                   "state buffers 0 and 1 share memory")
     call_comp(lib, ctab((7,), kv_addr=[FAKE], sc_addr=[FAKE + 2048 * 4]), kv=0)   # adjacent is fine...
-    assert "states overlap" not in ds.last_error()                                 # ...it fails on kv
+    assert "share memory" not in ds.last_error()                                   # ...it fails on kv
     t2 = ctab((7, 11))
     expect_invalid(call_comp(lib, t2, kv=2 * 256 - 1), "kv holds 511")
     expect_invalid(call_comp(lib, t2, score=2 * 256 - 1), "score holds")
@@ -374,12 +410,12 @@ def test_mq_sizes_and_checks(lib):
     t = itab((100, 50), start_pos=[4 * 100 - 8, 4 * 50 - 8], q_row=[3, 0])
     assert ds.indexer_mq_scores_elems(t, 8) == 2 * 8 * 100
     assert ds.indexer_mq_scores_elems(t, 9) == 0
-    assert "query_len must be 1..=8, got 9" in ds.last_error()
-    expect_invalid(call_mq(lib, t, 0), "query_len must be 1..=8, got 0")
+    assert "query_len 9 is outside [1, 8]" in ds.last_error()
+    expect_invalid(call_mq(lib, t, 0), "query_len 0 is outside [1, 8]")
     # the last query (start_pos + 7) must still fit the cache
     expect_invalid(call_mq(lib, itab((100,), start_pos=[4 * 100 - 4]), 8),
-                   "kv_len 100 is shorter than 101 causal compressed entries")
-    expect_invalid(call_mq(lib, itab((100,), start_pos=[0xFFFFFFFF - 3]), 4), "indexer position overflows")
+                   "makes 101 keys visible but kv_len is only 100")
+    expect_invalid(call_mq(lib, itab((100,), start_pos=[0xFFFFFFFF - 3]), 4), "is past 2^32 - 2")
     # queries q_row .. q_row + 7: max q_row 3 -> 11 query rows
     expect_invalid(call_mq(lib, t, 8, q=11 * 64 * 128 - 1), "indexer q holds")
     expect_invalid(call_mq(lib, t, 8, w=11 * 64 - 1), "indexer weights holds")

@@ -4,7 +4,8 @@ Every test runs the library through its C ABI (via the ctypes binding) on
 seeded synthetic inputs and compares each step's output with the oracle:
   indexer scores   exact (integer-valued inputs make every f32 score exact)
   top-k indices    exact, in rank order
-  gathered rows    bit for bit; mask state (0 / -inf sentinel / NaN bad) exact
+  gathered rows    bit for bit; mask (0, or -inf for a sentinel) and the
+                   per-row invalid flag exact
   attention out    max-abs <= 1e-2 and mean-abs <= 1e-3 against the oracle's
                    float64 result rounded to f32
 and checks that each row of a multi-row launch equals a one-row launch on
@@ -54,7 +55,6 @@ def config(cid):
 def mask_expected(orc):
     m = np.zeros(orc["sentinel"].shape[0], np.uint16)
     m[orc["sentinel"]] = 0xFF80
-    m[orc["slot_bad"]] = 0x7FC0
     return m
 
 
@@ -65,6 +65,7 @@ def check_row(got, orc, label, scores=True, gathered=True):
     if gathered:
         np.testing.assert_array_equal(got["gathered"], orc["gathered"], err_msg=f"{label} gathered")
         np.testing.assert_array_equal(got["mask"], mask_expected(orc), err_msg=f"{label} mask")
+        assert got["invalid"] == int(bool(orc["slot_bad"].any())), f"{label} invalid flag"
     err = np.abs(got["out"].astype(np.float64) - orc["out"].astype(np.float64))
     say(f"  {label}: out max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, label
@@ -74,6 +75,7 @@ def bitwise_equal(a, b, label):
     for k in ("scores", "indices", "gathered", "mask"):
         assert np.array_equal(np.ascontiguousarray(a[k]).view(np.uint8),
                               np.ascontiguousarray(b[k]).view(np.uint8)), f"{label} {k}"
+    assert a["invalid"] == b["invalid"], f"{label} invalid"
     assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32)), f"{label} out"
 
 
@@ -216,6 +218,9 @@ def test_fail_closed_injections():
         orc = dict(indices=idx[r], gathered=g, sentinel=sent, slot_bad=bad, out=out)
         got[r]["indices"] = idx[r]
         check_row(got[r], orc, f"inject row {r}", scores=False)
+    assert [g["invalid"] for g in got] == [0, 1, 1, 0, 1]
+    # bad slots keep mask 0 (only sentinels are -inf), as the pages' gather writes it
+    assert got[1]["mask"][7] == 0 and got[4]["mask"][487] == 0 and got[0]["mask"][5] == 0xFF80
     assert np.all(got[1]["out"] == 0) and np.all(got[2]["out"] == 0) and np.all(got[4]["out"] == 0)
     assert np.all(got[3]["out"][7] == 0) and np.all(got[0]["out"][11] == 0)
     assert np.all(np.abs(got[0]["out"][10]) > 0)
@@ -239,6 +244,7 @@ def test_widths_other_than_512():
     d_idx = torch.from_numpy(idx).cuda()
     gathered = torch.empty(ds.gathered_elems(t), dtype=torch.int16, device="cuda")
     mask = torch.empty(ds.mask_elems(t), dtype=torch.int16, device="cuda")
+    invalid = torch.full((3,), 5, dtype=torch.int32, device="cuda")
     ws = torch.empty(ds.attn_workspace_bytes(t), dtype=torch.uint8, device="cuda")
     out = torch.zeros(3 * 64 * 512, dtype=torch.float32, device="cuda")
     say("widths", width, "direct")
@@ -247,11 +253,12 @@ def test_widths_other_than_512():
     o_direct = out.cpu().numpy().reshape(3, 64, 512).copy()
     out.zero_()
     say("widths", width, "gather + attention")
-    ds.gather(t, d_idx, gathered, mask)
-    ds.sparse_attn(t, dev.attn_q, dev.sinks, gathered, mask, inp.scale, ws, out)
+    ds.gather(t, d_idx, gathered, mask, invalid)
+    ds.sparse_attn(t, dev.attn_q, dev.sinks, gathered, mask, invalid, inp.scale, ws, out)
     torch.cuda.synchronize()
     g_all = gathered.cpu().numpy().view(np.uint16).reshape(-1, 512)
     m_all = mask.cpu().numpy().view(np.uint16)
+    v_all = invalid.cpu().numpy()
     o_all = out.cpu().numpy().reshape(3, 64, 512)
     assert np.array_equal(o_all.view(np.uint32), o_direct.view(np.uint32))
     base = 0
@@ -259,7 +266,7 @@ def test_widths_other_than_512():
         g, sent, bad, inv = O.gather_row(inp.kv[r], rows_idx[r], kv_len[r])
         o = O.sparse_attention_row(inp.attn_q[r], inp.sinks, g, sent, inv, inp.scale)
         got = dict(indices=rows_idx[r], gathered=g_all[base: base + width[r]],
-                   mask=m_all[base: base + width[r]], out=o_all[r])
+                   mask=m_all[base: base + width[r]], invalid=int(v_all[r]), out=o_all[r])
         check_row(got, dict(indices=rows_idx[r], gathered=g, sentinel=sent, slot_bad=bad, out=o),
                   f"width {width[r]}", scores=False)
         base += width[r]
