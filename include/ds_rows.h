@@ -367,6 +367,34 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
                                     float *out, size_t out_elems,
                                     void *stream);
 
+/* ---- ds_rows_indexer_topk_attn_noalloc ----------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same
+ * computation, results and checks as ds_rows_indexer_topk_attn, with both
+ * workspaces taken from a device array the library holds on each GPU it runs
+ * on (DS_NOALLOC_SCRATCH_BYTES, kept until the process ends) instead of
+ * caller buffers. The caller still passes every input and output. Nothing is
+ * allocated or freed by the call.
+ * The array must hold ds_rows_indexer_topk_workspace_bytes(irows), rounded up
+ * to 256, plus ds_rows_attn_workspace_bytes(srows); a larger call fails with
+ * DS_ERR_INVALID_ARGUMENT before anything is enqueued (8 rows of 512 slots
+ * fit up to 911360 keys each; one row up to 13.7 million keys). The array
+ * needs no clearing: no kernel depends on its contents at entry.
+ * Calls on one GPU share its array: calls that overlap in time (e.g. on two
+ * streams) race and must be serialised by the caller. The first call on a
+ * device looks up the array's device address (DS_ERR_HIP if that fails). */
+#define DS_NOALLOC_SCRATCH_BYTES (16u << 20)
+ds_status ds_rows_indexer_topk_attn_noalloc(const ds_indexer_rows *irows, const ds_sparse_rows *srows,
+                                            const void *idx_q, size_t idx_q_elems,
+                                            const float *weights, size_t weights_elems,
+                                            float *scores, size_t scores_elems,
+                                            int32_t *indices, size_t indices_elems,
+                                            const void *q, size_t q_elems,
+                                            const float *sinks, size_t sinks_elems,
+                                            float scale,
+                                            float *out, size_t out_elems,
+                                            void *stream);
+
 /* ---- ds_rows_compressor -------------------------------------------------
  * One decode token of the learned KV compressor per row, each row with its
  * own recurrent state ([shader 0.18] deepseek_compressor_rows_bf16;

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libds_rows.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["indexer_score.hip", "indexer_mq.hip", "topk.hip", "gather.hip", "attention.hip", "compressor.hip",
-           "topk_attn.hip", "ds_rows.cpp"]
+           "topk_attn.hip", "noalloc.hip", "ds_rows.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

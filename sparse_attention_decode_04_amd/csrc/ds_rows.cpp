@@ -394,6 +394,16 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
 
 }  // namespace
 
+ds_status ds::record_error(ds_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = std::string("ds_rows: ") + buf;
+  return st;
+}
+
 extern "C" {
 
 

@@ -12,6 +12,10 @@
 
 namespace ds {
 
+// Records the calling thread's last-error message ("ds_rows: " + the
+// formatted text) and returns `st`.
+ds_status record_error(ds_status st, const char *fmt, ...);
+
 constexpr int kRowsMax = 8;
 constexpr int kHeads = 64;
 constexpr int kIdxDim = 128;

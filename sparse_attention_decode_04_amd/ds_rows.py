@@ -29,6 +29,7 @@ FUNCTIONS = (
     "ds_rows_last_error", "ds_rows_version", "ds_rows_indexer_topk_workspace_bytes", "ds_rows_indexer_topk",
     "ds_rows_indexer_candidates", "ds_rows_compressor_state_elems", "ds_rows_compressor",
     "ds_rows_indexer_mq_scores_elems", "ds_rows_indexer_score_mq", "ds_rows_indexer_topk_attn",
+    "ds_rows_indexer_topk_attn_noalloc",
 )
 
 
@@ -116,6 +117,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                               c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t,
                                               c_void_p, c_size_t, c_void_p, c_size_t, c_float,
                                               c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
+    lib.ds_rows_indexer_topk_attn_noalloc.argtypes = [P(IndexerRows), P(SparseRows), c_void_p, c_size_t,
+                                                      c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t,
+                                                      c_void_p, c_size_t, c_void_p, c_size_t, c_float,
+                                                      c_void_p, c_size_t, c_void_p]
     lib.ds_rows_indexer_mq_scores_elems.argtypes = [P(IndexerRows), c_uint32]
     lib.ds_rows_indexer_mq_scores_elems.restype = c_size_t
     lib.ds_rows_indexer_score_mq.argtypes = [P(IndexerRows), c_uint32, c_void_p, c_size_t, c_void_p, c_size_t,
@@ -127,7 +132,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     for f in ("ds_rows_indexer_score", "ds_rows_topk", "ds_rows_gather", "ds_rows_sparse_attn",
               "ds_rows_sparse_attn_direct", "ds_rows_indexer_topk", "ds_rows_indexer_candidates",
-              "ds_rows_compressor", "ds_rows_indexer_score_mq", "ds_rows_indexer_topk_attn"):
+              "ds_rows_compressor", "ds_rows_indexer_score_mq", "ds_rows_indexer_topk_attn",
+              "ds_rows_indexer_topk_attn_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
@@ -301,6 +307,22 @@ def indexer_topk_attn(it: IndexerRows, st: SparseRows, idx_q, weights, scores, i
     _check(load().ds_rows_indexer_topk_attn(ctypes.byref(it), ctypes.byref(st), qa, qn, wa, wn, sa, sn, ka, kb,
                                             ia, inn, aqa, aqn, ska, skn, float(scale), awa, awb, oa, on,
                                             _stream(stream)))
+
+
+def indexer_topk_attn_noalloc(it: IndexerRows, st: SparseRows, idx_q, weights, scores, indices,
+                              q, sinks, scale, out, stream=None):
+    """ds_rows_indexer_topk_attn with the library's own device scratch array
+    in place of the two workspaces."""
+    qa, qn = _dev(idx_q, 2)
+    wa, wn = _dev(weights, 4)
+    sa, sn = _dev(scores, 4)
+    ia, inn = _dev(indices, 4)
+    aqa, aqn = _dev(q, 2)
+    ska, skn = _dev(sinks, 4)
+    oa, on = _dev(out, 4)
+    _check(load().ds_rows_indexer_topk_attn_noalloc(ctypes.byref(it), ctypes.byref(st), qa, qn, wa, wn, sa, sn,
+                                                    ia, inn, aqa, aqn, ska, skn, float(scale), oa, on,
+                                                    _stream(stream)))
 
 
 def indexer_candidates(t: IndexerRows, q, weights, scores, workspace, stream=None):

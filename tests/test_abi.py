@@ -46,7 +46,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert set(names) == set(ds.FUNCTIONS)
     out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (ds_rows_\w+)", out))
