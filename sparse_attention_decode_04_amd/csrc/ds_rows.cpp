@@ -162,7 +162,7 @@ uint64_t fused_cand_bytes(const IndexerPlan &p) {
   return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxCand * sizeof(uint64_t));
 }
 uint64_t fused_floor_bytes(const IndexerPlan &p) {
-  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxFloors * sizeof(uint32_t));
+  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxFloors * sizeof(uint64_t));
 }
 uint64_t fused_workspace_bytes(const IndexerPlan &p) {
   return fused_cand_bytes(p) + fused_floor_bytes(p) + 2 * p.fused_bank * sizeof(uint64_t);
@@ -268,7 +268,7 @@ ds_status check_indexer_operands(const ds_indexer_rows *rows, const IndexerPlan 
 
 // Indexer launch; with cand/floors set, also the fused top-k stage.
 ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, const void *q, const float *weights,
-                         float *scores, uint64_t *cand, uint32_t *floors, void *stream) {
+                         float *scores, uint64_t *cand, uint64_t *floors, void *stream) {
   ds::IndexerArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.w = weights;
@@ -296,7 +296,7 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
 // base per row, with the block floors to check on the final level).
 struct TopkInput {
   const uint64_t *lists = nullptr;
-  const uint32_t *floors = nullptr;
+  const uint64_t *floors = nullptr;
   uint32_t count[ds::kRowsMax] = {};
   uint64_t base[ds::kRowsMax] = {};
 };
@@ -482,7 +482,7 @@ ds_status ds_rows_indexer_candidates(const ds_indexer_rows *rows, const void *q,
   DS_TRY(check_device());
   char *ws = static_cast<char *>(workspace);
   return launch_indexer(rows, p, q, weights, scores, reinterpret_cast<uint64_t *>(ws),
-                        reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p)), stream);
+                        reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p)), stream);
 }
 
 ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_t q_elems, const float *weights,
@@ -506,7 +506,7 @@ ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_
   }
   char *ws = static_cast<char *>(workspace);
   uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
-  uint32_t *floors = reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p));
+  uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
   uint64_t *bank = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
   DS_TRY(launch_indexer(rows, p, q, weights, scores, cand, floors, stream));
 
@@ -737,7 +737,7 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
     // in the same pass; otherwise the attention call follows.
     char *ws = static_cast<char *>(idx_workspace);
     uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
-    uint32_t *floors = reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p));
+    uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
     uint64_t *bank = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
     DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, cand, floors, stream));
     TopkInput in{};
@@ -762,7 +762,7 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
   }
   char *ws = static_cast<char *>(idx_workspace);
   uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
-  uint32_t *floors = reinterpret_cast<uint32_t *>(ws + fused_cand_bytes(p));
+  uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
   DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, cand, floors, stream));
 
   // The final level, as run_topk_levels sets it up for the fused candidates

@@ -35,12 +35,11 @@ constexpr int kIdxTile = 16;
 constexpr uint32_t kIdxMaxKeysPerBlock = 1024;
 // Fused top-k stage (ds_rows_indexer_topk): every wave of the indexer also
 // writes up to kIdxWaveCand candidate keys of its own 256 keys (those at or
-// above a threshold keeping kIdxWaveKeep to kIdxWaveCand of them, or every
-// valid key when it has at most kIdxWaveCand) and a 32-bit floor: 0 when it
-// wrote every valid key,
-// otherwise score bits T such that all of its unwritten keys lie below the
-// key T << 32 (0xFFFFFFFF, above every valid key, when ties at its threshold
-// exceed the room).
+// above a threshold keeping kIdxWaveKeep to kIdxWaveCand of them; every valid
+// key when it has at most kIdxWaveCand; when ties at its threshold T overflow,
+// the keys above T and the lowest-index ties) and a 64-bit floor, a key that
+// no unwritten key of the wave exceeds: 0 when it wrote every valid key,
+// T << 32 after a clean threshold, else the key of its best unwritten tie.
 constexpr uint32_t kIdxWaveKeep = 24;
 constexpr uint32_t kIdxWaveCand = 32;
 constexpr uint32_t kIdxCand = (kIdxThreads / 64) * kIdxWaveCand;   // 128 per block
@@ -59,7 +58,7 @@ struct IndexerArgs {
   uint32_t q_row[kRowsMax];
   uint32_t blk_begin[kRowsMax + 1]; // first block of each row; [rows..] = total
   uint64_t *cand;                   // fused: kIdxCand keys per block (0 = none)
-  uint32_t *floors;                 // fused: kIdxFloors floors per block (one per wave)
+  uint64_t *floors;                 // fused: kIdxFloors floors per block (one per wave)
 };
 // Grid (max_row_blocks, a.rows): workgroup (x, r) is row r's x-th block.
 hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s);
@@ -100,7 +99,7 @@ struct TopkLevelArgs {
   // that an unwritten key could rank; otherwise the row is selected again from
   // its `fallback_count` scores.
   uint32_t check_mask;
-  const uint32_t *floors;
+  const uint64_t *floors;
   uint32_t floor_begin[kRowsMax];
   uint32_t floor_count[kRowsMax];
   uint32_t fallback_count[kRowsMax];

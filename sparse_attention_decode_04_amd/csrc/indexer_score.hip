@@ -37,13 +37,16 @@
 // (deepseek_indexer_topk_block_rows_i32). Here every wave keeps, from the 256
 // scores it just computed (still in its registers: after each group of 4
 // tiles every lane holds one score, lane row g that of tile g), only the
-// keys at or above a threshold T that keeps 24 to 32 of them (the 24th best
-// score bits when ties allow no such T): a search over T's bits with ballot
-// counts, two bits per step and stopping at the first T in range, finds it
-// without LDS or barriers. It writes those keys (at most 32) and
-// the floor T: all of its other keys lie below the key T << 32; the final top-k
-// level uses the floors to prove that no unkept key can reach the row's top
-// 512, and selects from the scores again when one could.
+// keys at or above a threshold T that keeps 24 to 32 of them: a search over
+// T's bits with ballot counts, two bits per step and stopping at the first T
+// in range, finds it without LDS or barriers. When ties at the 24th best
+// score bits T leave no such threshold, it keeps every key above T and, of
+// the keys tied at T, the lowest indices (ties rank by lower index) up to 32
+// in all. It writes those keys and a 64-bit floor: a key no better than any
+// key it did not write (T << 32 after a clean threshold; the exact key of its
+// best unwritten tie otherwise). The final top-k level uses the floors to
+// prove that no unkept key can reach the row's top 512, and selects from the
+// scores again when one could.
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 #include "select_common.hpp"
@@ -62,7 +65,9 @@ static_assert((kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile + kIdxRing - 
               "groups of 4 tiles per wave fit the queue");
 
 // One wave's candidates (fused stage, see above): o[e] are the score bits
-// (0 = not valid) of the lane's kept keys, kidx[e] their key indices.
+// (0 = not valid) of the lane's four queued keys, kidx[e] their key indices.
+// Key indices increase with (3 - e, lane): e = 3 holds the wave's first group
+// of tiles, and within a group lane row g holds tile g of the group.
 __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint32_t (&o)[4],
                                                 const uint32_t (&kidx)[4], uint32_t block, uint32_t wave,
                                                 uint32_t lane) {
@@ -85,7 +90,8 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
     // kIdxWaveCand keys; otherwise it ends at the kIdxWaveKeep-th best score
     // bits. Any T that keeps at most kIdxWaveCand keys is a valid floor: the
     // final level's check compares the floors with its 512th key, so which
-    // one is taken changes no index.
+    // one is taken changes no index. If none keeps at most kIdxWaveCand, T
+    // ends as the kIdxWaveKeep-th best score bits (ties at T overflow).
     thr = 0;
     kept = 256;   // count_ge(0); replaced at the first accepted step (count_ge(1) = nvalid > kIdxWaveKeep)
     for (int b = 30; b >= 0; b -= 2) {
@@ -97,25 +103,47 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
       if (kept <= kIdxWaveCand) break;   // uniform
     }
   }
-  if (kept > kIdxWaveCand) {
-    // Ties at the threshold overflow the room: write nothing; the floor ~0
-    // makes the row fall back to a selection over its scores.
-    if (lane < kIdxWaveCand) a.cand[slot0 + lane] = 0;
-    if (lane == 0) a.floors[floor_at] = 0xFFFFFFFFu;
-    return;
+  auto prefix = [](uint64_t mask) {   // set lanes of `mask` below this lane
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+  };
+  // Which queued keys this lane writes: those at or above T, or, when the
+  // keys tied at T overflow the room, those above T and the first `room`
+  // ties in key-index order (e = 3 .. 0, lanes ascending).
+  bool take[4];
+  uint64_t floor = static_cast<uint64_t>(thr) << 32;   // after a clean threshold
+  if (kept <= kIdxWaveCand) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) take[e] = o[e] >= thr;
+    if (kept == nvalid) floor = 0;
+  } else {
+    uint32_t room = kIdxWaveCand - count_ge(thr + 1);   // slots left for ties at T (> 0)
+    uint32_t first_unkept = 0xFFFFFFFFu;                // index of the best unwritten tie
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      const bool tie = o[e] == thr;
+      const uint64_t m = __ballot(tie);
+      const uint32_t pos = prefix(m);
+      take[e] = o[e] > thr || (tie && pos < room);
+      const uint64_t first = __ballot(tie && pos == room);   // the first tie past the room, if in this e
+      if (first != 0 && first_unkept == 0xFFFFFFFFu)
+        first_unkept = __shfl(kidx[e], static_cast<int>(__builtin_ctzll(first)));
+      const uint32_t n = static_cast<uint32_t>(__popcll(m));
+      room = n >= room ? 0u : room - n;
+    }
+    kept = kIdxWaveCand;
+    floor = (static_cast<uint64_t>(thr) << 32) | static_cast<uint32_t>(~first_unkept);
   }
   uint32_t base = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const bool in = o[e] >= thr;
-    const uint64_t mask = __ballot(in);
-    const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-    if (in) a.cand[slot0 + pos] = (static_cast<uint64_t>(o[e]) << 32) | static_cast<uint32_t>(~kidx[e]);
+    const uint64_t mask = __ballot(take[e]);
+    const uint32_t pos = base + prefix(mask);
+    if (take[e]) a.cand[slot0 + pos] = (static_cast<uint64_t>(o[e]) << 32) | static_cast<uint32_t>(~kidx[e]);
     base += static_cast<uint32_t>(__popcll(mask));
   }
   if (lane >= kept && lane < kIdxWaveCand) a.cand[slot0 + lane] = 0;   // unused slots
-  if (lane == 0) a.floors[floor_at] = kept == nvalid ? 0u : thr;
+  if (lane == 0) a.floors[floor_at] = floor;
 }
 
 template <bool kFused>

@@ -50,7 +50,7 @@ __device__ __forceinline__ void topk_attn_rows(const TopkLevelArgs &t, const Att
                "+s"(rows), "+s"(chunks));
   lr.in = global_ptr<const uint64_t>(in) + in_base;
   lr.scores = global_ptr<const float>(sc) + r * stride;
-  lr.floors = global_ptr<const uint32_t>(fl) + floor_begin;
+  lr.floors = global_ptr<const uint64_t>(fl) + floor_begin;
   lr.out = nullptr;   // a final level writes indices, not lists
   lr.count = count;
   lr.floor_count = fc;

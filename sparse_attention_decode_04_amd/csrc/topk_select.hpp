@@ -12,7 +12,7 @@
 namespace ds {
 
 constexpr int kBins = 1024;
-constexpr uint32_t kFastBinMax = 64;
+constexpr uint32_t kFastBinMax = 256;   // largest bin the counting select ranks by comparisons
 constexpr uint32_t kSampleMin = 64;
 constexpr int kWaves = kTopkThreads / 64;
 constexpr uint32_t kCompactPerWave = 512;                  // compaction capacity of one wave
@@ -63,7 +63,8 @@ struct TopkShared {
   __attribute__((aligned(16))) uint32_t wvalid[kWaves];     // per-wave candidate statistics
   __attribute__((aligned(16))) uint32_t wmin1[kWaves];
   __attribute__((aligned(16))) uint32_t wmaxo[kWaves];
-  __attribute__((aligned(16))) uint32_t wfloor[kWaves];
+  __attribute__((aligned(16))) uint64_t wfloor[kWaves];
+  uint64_t wkmin[kWaves], wkmax[kWaves];                     // radix fallback: key range per wave
   uint32_t count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
 };
 
@@ -278,9 +279,39 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
   // ---- fallback: radix select on the 64-bit keys, then bitonic sort ------
   uint64_t thr = 1;
   if (total > kTopkSortCap) {
+    // The passes start at the highest byte in which the smallest and the
+    // largest candidate differ: heavy ties (equal scores) share their upper
+    // bytes, which a pass would only confirm.
+    uint64_t kmin = ~0ull, kmax = 0;
+    c.fence();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const uint64_t kk = c.key(e);
+      if (kk != 0) { kmin = min(kmin, kk); kmax = max(kmax, kk); }
+    }
+    {
+      const uint32_t hmin = wave_min(static_cast<uint32_t>(kmin >> 32));
+      const uint32_t lmin = wave_min(static_cast<uint32_t>(kmin >> 32) == hmin ? static_cast<uint32_t>(kmin) : ~0u);
+      const uint32_t hmax = wave_max(static_cast<uint32_t>(kmax >> 32));
+      const uint32_t lmax = wave_max(static_cast<uint32_t>(kmax >> 32) == hmax ? static_cast<uint32_t>(kmax) : 0u);
+      if (lane == 0) {
+        sh.wkmin[tid >> 6] = (static_cast<uint64_t>(hmin) << 32) | lmin;
+        sh.wkmax[tid >> 6] = (static_cast<uint64_t>(hmax) << 32) | lmax;
+      }
+    }
+    __syncthreads();
+    kmin = ~0ull;
+    kmax = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      kmin = min(kmin, sh.wkmin[w]);
+      kmax = max(kmax, sh.wkmax[w]);
+    }
+    const uint64_t diff = kmin ^ kmax;   // nonzero: more than kTopkSortCap distinct keys
+    const int top = diff == 0 ? 0 : (63 - __builtin_clzll(diff)) / 8 * 8;
     uint32_t left = kTopK;          // ranks still to fill below the prefix
-    uint64_t prefix = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    uint64_t prefix = top == 56 ? 0ull : (kmax >> (top + 8)) << (top + 8);   // the common upper bytes
+    for (int shift = top; shift >= 0; shift -= 8) {
       __syncthreads();
       if (tid < 256) sh.hist[tid] = 0;
       __syncthreads();
@@ -464,7 +495,7 @@ __device__ __forceinline__ void select_from_scores(TopkShared &sh, const float *
 struct LevelRow {
   const uint64_t *in;        // the row's input lists (later levels)
   const float *scores;       // the row's scores
-  const uint32_t *floors;    // the row's block floors (checked final level)
+  const uint64_t *floors;    // the row's wave floors (checked final level)
   uint64_t *out;             // the row's output lists (levels before the final one)
   uint32_t count;            // candidates of the row at this level
   uint32_t floor_count;
@@ -494,7 +525,7 @@ __device__ __forceinline__ LevelRow level_row(const TopkLevelArgs &a, uint32_t r
   LevelRow lr;
   lr.in = global_ptr<const uint64_t>(in) + in_base;
   lr.scores = global_ptr<const float>(sc) + r * stride;
-  lr.floors = global_ptr<const uint32_t>(fl) + floor_begin;
+  lr.floors = global_ptr<const uint64_t>(fl) + floor_begin;
   lr.out = global_ptr<uint64_t>(out) + out_base;
   lr.count = count;
   lr.floor_count = fc;
@@ -562,7 +593,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
   // A checked final level compares the row's highest floor with the last
   // selected key; the floors are loaded now, with the candidates.
   const bool check_row = !kFromScores && lr.check;
-  uint32_t floor_hi = 0;
+  uint64_t floor_hi = 0;
   if constexpr (!kFromScores) {
     if (check_row && lr.floor_count > 0) {
       floor_hi = lr.floors[min(tid, lr.floor_count - 1)];
@@ -586,7 +617,12 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
     nvalid = wave_sum(nvalid);
     omin1 = wave_min(omin1);
     omax = wave_max(omax);
-    const uint32_t wfloor = check_row ? wave_max(floor_hi) : 0u;
+    uint64_t wfloor = 0;
+    if (check_row) {   // 64-bit wave maximum: the high words, then the low words of the lanes holding it
+      const uint32_t hi = wave_max(static_cast<uint32_t>(floor_hi >> 32));
+      const uint32_t lo = wave_max(static_cast<uint32_t>(floor_hi >> 32) == hi ? static_cast<uint32_t>(floor_hi) : 0u);
+      wfloor = (static_cast<uint64_t>(hi) << 32) | lo;
+    }
     if (lane == 0) {
       sh.wvalid[wave] = nvalid;
       sh.wmin1[wave] = omin1;
@@ -594,19 +630,19 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
       sh.wfloor[wave] = wfloor;
     }
     __syncthreads();
-    uint32_t total = 0, min1 = 0xFFFFFFFFu, gmax = 0, max_floor = 0;
+    uint32_t total = 0, min1 = 0xFFFFFFFFu, gmax = 0;
+    uint64_t max_floor = 0;
 #pragma unroll
     for (int v = 0; v < kWaves / 4; ++v) {
       const u32x4 n4 = reinterpret_cast<const u32x4 *>(sh.wvalid)[v];
       const u32x4 l4 = reinterpret_cast<const u32x4 *>(sh.wmin1)[v];
       const u32x4 h4 = reinterpret_cast<const u32x4 *>(sh.wmaxo)[v];
-      const u32x4 f4 = reinterpret_cast<const u32x4 *>(sh.wfloor)[v];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         total += n4[k];
         min1 = min(min1, l4[k]);
         gmax = max(gmax, h4[k]);
-        max_floor = max(max_floor, f4[k]);
+        max_floor = max(max_floor, sh.wfloor[4 * v + k]);
       }
     }
     const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
@@ -629,7 +665,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
     };
     auto emit = [&](uint32_t pos, uint64_t kk) {
       emit_out(pos, kk);
-      if (check && pos + 1 == static_cast<uint32_t>(kTopK) && (static_cast<uint64_t>(max_floor) << 32) > kk)
+      if (check && pos + 1 == static_cast<uint32_t>(kTopK) && max_floor > kk)
         sh.viol = 1;
     };
     // Best `need` of this chunk's candidates (total valid, score bits in

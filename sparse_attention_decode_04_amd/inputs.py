@@ -262,3 +262,37 @@ def mq_workload(query_len: int = 8) -> MultiQueryInputs:
     """The measured multi-query workload: 8 rows x 32768 keys, query_len
     queries per row."""
     return make_mq(MQ_SEED_BASE + query_len, [32768] * 8, query_len)
+
+
+# ---------------------------------------------------------------------------
+# Score distributions that defeat the fused indexer's per-wave candidates
+# ---------------------------------------------------------------------------
+# Used to time the one-call step's exact reselection path on the throughput
+# shape (8 rows x 32768 keys):
+#   "ties":   every indexer key is zero, so every score is 0 (the top 512 are
+#             the lowest indices, all in the first waves);
+#   "sorted": each query is one-hot on feature 0 with unit head weights and
+#             key j holds bf16(4 j / kv_len) in feature 0 (zeros elsewhere),
+#             so scores never decrease with the position and the top 512 sit
+#             in the last waves (bf16 rounding leaves runs of equal scores).
+# Everything else is the config-2 recipe (same seed and order).
+FALLBACK_KINDS = ("ties", "sorted")
+
+
+def fallback_workload(kind: str) -> RowsInputs:
+    inp = make_config(2)
+    if kind == "ties":
+        for k in inp.idx_keys:
+            k[:] = 0
+    elif kind == "sorted":
+        inp.idx_q[:] = 0
+        inp.idx_q[:, :, 0] = int_to_bf16_bits(np.ones(1))[0]
+        inp.idx_w[:] = 1.0
+        for k in inp.idx_keys:
+            n = k.shape[0]
+            k[:] = 0
+            k[:, 0] = f32_to_bf16_bits(np.arange(n, dtype=np.float32) * np.float32(4.0 / n))
+    else:
+        raise ValueError(kind)
+    inp.extra["fallback"] = kind
+    return inp

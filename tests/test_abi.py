@@ -155,21 +155,21 @@ def test_size_queries(lib):
     # top-k lists: only rows longer than one 32768-key chunk need the banks
     assert ds.topk_workspace_bytes(t) == 2 * 8 * 512 * (3 + 2)
     assert ds.topk_workspace_bytes(itab((1000, 32768))) == 0
-    # fused: 128 candidate keys and four u32 floors per 1024-key block (each
+    # fused: 128 candidate keys and four u64 floors per 1024-key block (each
     # region 256-byte aligned), plus two list banks for rows whose candidates
     # exceed one 8192-key chunk (rows over 65536 keys): here the 70000-key
     # row, 69 blocks -> 8832 candidates -> 2 chunks of 512
     blocks = 1 + 69 + 32 + 33
-    assert ds.indexer_topk_workspace_bytes(t) == blocks * 128 * 8 + 2304 + 2 * 2 * 512 * 8
+    assert ds.indexer_topk_workspace_bytes(t) == blocks * 128 * 8 + 4352 + 2 * 2 * 512 * 8
     big = itab((200000,))
     nb = 196
     cand = -(-nb * 128 * 8 // 256) * 256
-    floors = -(-nb * 4 * 4 // 256) * 256
+    floors = -(-nb * 4 * 8 // 256) * 256
     chunks = -(-nb * 128 // 8192)
     assert ds.indexer_topk_workspace_bytes(big) == cand + floors + 2 * chunks * 512 * 8
     # the size covers both of the call's paths: a lone 1000-key row (which
     # takes the separate score and top-k kernels) still gets the fused
-    # stage's candidates (one block: 1 KiB) and floors (16 B -> 256)
+    # stage's candidates (one block: 1 KiB) and floors (32 B -> 256)
     assert ds.indexer_topk_workspace_bytes(itab((1000,))) == 1024 + 256
     s = stab((1000, 37, 1), width=(512, 37, 1))
     assert ds.gathered_elems(s) == (512 + 37 + 1) * 512

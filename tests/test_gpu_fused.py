@@ -1,13 +1,13 @@
 """GPU parity of the fused score + top-512 call (ds_rows_indexer_topk).
 
-The fused call keeps, per 1024-key block of the indexer, only the keys of the
-block's top score bins plus a floor, selects from those candidates, and
-selects again from the scores when a floor shows that the candidates may miss
-a key of the top 512. Its scores and indices must equal the oracle exactly and
-the separate calls (ds_rows_indexer_score + ds_rows_topk) bit for bit, on the
-workloads (where the candidates suffice) and on inputs built to defeat the
-candidates (ties across blocks, scores sorted by position), which take the
-in-call fallback. The first top-k stage on the pages keeps each block's best
+The fused call keeps, per 256-key wave of the indexer, only the wave's best
+keys (with ties at its threshold, the lowest indices) plus a floor, selects
+from those candidates, and selects again from the scores when a floor shows
+that the candidates may miss a key of the top 512. Its scores and indices must
+equal the oracle exactly and the separate calls (ds_rows_indexer_score +
+ds_rows_topk) bit for bit: on the workloads, on heavy ties and scores sorted
+by position (the tie-aware candidates hold the top 512), and on inputs whose
+best keys all belong to one wave, which must take the in-call reselection. The first top-k stage on the pages keeps each block's best
 512 (docs.rs "mlx-native 0.18.0 src/shaders/deepseek_rows.metal",
 deepseek_indexer_topk_block_rows_i32); the selected set and its order are
 unique, so any correct staging gives these results.
@@ -36,6 +36,35 @@ def gpu():
     assert torch.cuda.is_available(), "no HIP device"
     ds.load()
     yield
+
+
+def one_wave_holds_the_top(seed, kv_len):
+    """Inputs whose 256 best scores belong to the keys that one wave of the
+    fused indexer scores. The kernel deals 16-key tiles round robin over a
+    row's 4 x ceil(n / 1024) waves, so its first wave takes tiles 0, S, 2S, ...
+    (S = 4 ceil(n / 1024)); that wave writes at most 32 of its keys, all of
+    them in the row's top 512, so its floor lies above the 512th key and the
+    row must be selected again from its scores. Scores are 256 * a + b for
+    key entries a (feature 0) and b (feature 1), exact integers."""
+    inp = I.small_rows(seed, kv_len)
+    inp.idx_q[:] = 0
+    inp.idx_w[:] = 0
+    inp.idx_q[:, 0, 0] = I.int_to_bf16_bits(np.array(256))
+    inp.idx_q[:, 0, 1] = I.int_to_bf16_bits(np.array(1))
+    inp.idx_w[:, 0] = 1.0
+    for k in inp.idx_keys:
+        n = k.shape[0]
+        j = np.arange(n)
+        wave0 = (j // 16) % (4 * -(-n // 1024)) == 0
+        assert wave0.sum() == 256
+        a = (j // 256) % 150
+        b = j % 256
+        a[wave0] = 200
+        b[wave0] = np.arange(256)
+        k[:] = 0
+        k[:, 0] = I.int_to_bf16_bits(a)
+        k[:, 1] = I.int_to_bf16_bits(b)
+    return inp
 
 
 def fused_and_separate(dev, rows=None):
@@ -97,10 +126,11 @@ def test_fused_multi_row_equals_single_row():
         assert np.array_equal(m[r]["scores"].view(np.uint32), o["scores"].view(np.uint32)), r
 
 
-def test_fused_ties_across_blocks_fall_back():
-    # every score 0: each block keeps its lowest indices, the floors of later
-    # blocks sit above the 512th key and the row is selected from its scores
-    # (every row long enough for the fused stage)
+def test_fused_ties_across_blocks():
+    # every score 0: each wave keeps its 32 lowest-index keys and a floor at
+    # its best unwritten one; the floors stay below the 512th key, so the
+    # candidates give the answer (every row long enough for the fused stage;
+    # the 131072-key row takes two selection levels)
     kv_len = [17000, 20000, 131072]
     inp = I.small_rows(7, kv_len)
     for k in inp.idx_keys:
@@ -130,9 +160,8 @@ def sorted_scores(seed, kv_len, sign):
 
 
 @pytest.mark.parametrize("sign", [1.0, -1.0])
-def test_fused_sorted_scores_fall_back(sign):
-    # ascending: the top 512 are the last keys, all in the last blocks;
-    # descending: the first keys. Either way the blocks' candidates miss some.
+def test_fused_sorted_scores(sign):
+    # ascending: the top 512 are the last keys; descending: the first keys.
     kv_len = [16384, 40000, 65536]
     inp = sorted_scores(13, kv_len, sign)
     say("fused: scores sorted by position, sign", sign, kv_len)
@@ -141,6 +170,18 @@ def test_fused_sorted_scores_fall_back(sign):
     for r, n in enumerate(kv_len):
         exp = np.arange(n - 1, n - 513, -1) if sign > 0 else np.arange(512)
         np.testing.assert_array_equal(got[r]["indices"], exp)
+
+
+def test_fused_one_wave_holding_the_top_is_selected_again():
+    kv_len = [17000, 20000, 40000]
+    inp = one_wave_holds_the_top(15, kv_len)
+    say("fused: the 256 best keys of each row in one indexer wave", kv_len)
+    got, sep = fused_and_separate(DeviceInputs(inp))
+    check_scores_indices(got, sep, inp, "one wave")
+    for r, n in enumerate(kv_len):
+        j = np.arange(n)
+        wave0 = j[(j // 16) % (4 * -(-n // 1024)) == 0]
+        np.testing.assert_array_equal(got[r]["indices"][:256], wave0[::-1])
 
 
 def test_fused_causal_offset_and_non_finite():

@@ -71,9 +71,9 @@ def test_step_config_parity(cid):
             assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (cid, r, err.max(), err.mean())
 
 
-def test_step_ties_fall_back_inside_the_kernel():
-    # all-zero indexer keys: every floor lies above the 512th candidate and
-    # each workgroup selects its row again from the scores
+def test_step_ties_inside_the_kernel():
+    # all-zero indexer keys: every wave keeps its lowest-index ties, and its
+    # floor (its best unwritten tie) stays below the 512th candidate
     kv_len = [17000, 20000, 40000]
     inp = I.small_rows(41, kv_len)
     for k in inp.idx_keys:
@@ -85,8 +85,24 @@ def test_step_ties_fall_back_inside_the_kernel():
         np.testing.assert_array_equal(a[r]["indices"], np.arange(512))
 
 
+def test_step_one_wave_holding_the_top_is_selected_again_inside_the_kernel():
+    # the 256 best keys of each row belong to one indexer wave: its floor lies
+    # above the 512th candidate and each workgroup selects its row again from
+    # the scores (the one-call path's reselection)
+    from test_gpu_fused import one_wave_holds_the_top
+    kv_len = [17000, 20000, 40000]
+    inp = one_wave_holds_the_top(47, kv_len)
+    say("one call: the 256 best keys of each row in one indexer wave", kv_len)
+    a, b = one_and_two(DeviceInputs(inp))
+    check_equal(a, b, "one wave")
+    for r in range(len(kv_len)):
+        exp = O.topk_select(O.indexer_scores(inp.idx_q[r], inp.idx_w[r], inp.idx_keys[r], inp.start_pos[r]),
+                            kv_len[r])
+        np.testing.assert_array_equal(a[r]["indices"], exp)
+
+
 @pytest.mark.parametrize("sign", [1.0, -1.0])
-def test_step_sorted_scores_fall_back_inside_the_kernel(sign):
+def test_step_sorted_scores_inside_the_kernel(sign):
     kv_len = [16384, 40000, 65536]
     inp = I.small_rows(43, kv_len)
     inp.idx_q[:] = 0
