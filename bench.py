@@ -440,14 +440,16 @@ def main():
                 "p90": float(np.percentile(d, 90)), "min": float(d.min()), "max": float(d.max()),
                 "steps": steps}
 
-    def in_step_ms(runs, first_kernel_call, n):
+    def in_step_ms(runs, extra_runs, first_kernel_call, n):
         """Duration of the step's first kernel (the indexer) as it runs inside
         the step: the time of n one-call steps each followed by one more
         launch of that kernel alone, minus the time of n one-call steps, over
         n. Each extra launch starts after a step's attention kernels and is
-        followed by the next step's indexer, as in the timed loop, and both
-        regions are single HIP event pairs on the launch stream (a pair around
-        one launch would add the event's own dispatch latency)."""
+        followed by the next step's indexer, as in the timed loop; it reads
+        input copies of its own (extra_runs, rotating), so that it warms no
+        cache for the steps. Both regions are single HIP event pairs on the
+        launch stream (a pair around one launch would add the event's own
+        dispatch latency)."""
         def region(extra):
             for i in range(len(runs)):
                 runs[i].step_one()
@@ -457,7 +459,7 @@ def main():
             for i in range(n):
                 runs[i % len(runs)].step_one()
                 if extra:
-                    getattr(runs[(i + 1) % len(runs)], first_kernel_call)()
+                    getattr(extra_runs[i % len(extra_runs)], first_kernel_call)()
             e1.record(stream)
             torch.cuda.synchronize()
             return e0.elapsed_time(e1)
@@ -531,7 +533,9 @@ def main():
     ms_four, _ = timed(runs, "step", args.steps, args.warmup)
 
     n_idx = max(args.steps, 50)
-    idx_in_mean = in_step_ms(runs, first_call, n_idx)
+    extra_runs = device_copies(inp, args.copies)
+    idx_in_mean = in_step_ms(runs, extra_runs, first_call, n_idx)
+    del extra_runs
     idx_b2b = back_to_back_ms(runs, first_call, n_idx)
     per_call = per_call_ms(runs, ("indexer_topk", "sparse_attn_direct"), args.steps)
     per_call_three = per_call_ms(runs, ("indexer_score", "topk", "sparse_attn_direct"), args.steps)
@@ -590,8 +594,9 @@ def main():
             "kernel": ("indexer_score_kernel<true> (indexer with the fused top-k candidate stage)" if fused
                        else "indexer_score_kernel<false>"),
             "kernel_ms": idx_in_mean,
-            "timing": "in step: (n one-call steps each followed by one more launch of the indexer kernel alone) "
-                      "minus (n one-call steps), over n = %d, HIP events on the launch stream" % n_idx,
+            "timing": "in step: (n one-call steps each followed by one more launch of the indexer kernel alone, on "
+                      "input copies of its own) minus (n one-call steps), over n = %d, HIP events on the launch "
+                      "stream" % n_idx,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
@@ -640,7 +645,9 @@ def main():
             spread = per_step_us(cruns, "step_one", steps)
             cfused = fused_route(cinp.kv_len)
             cfirst = "indexer_candidates" if cfused else "indexer_score"
-            c_in = in_step_ms(cruns, cfirst, max(steps, 20))
+            cextra = device_copies(cinp, ncopies)
+            c_in = in_step_ms(cruns, cextra, cfirst, max(steps, 20))
+            del cextra
             cb, _ = indexer_bytes_flops(cinp.kv_len, cfused)
             out["configs"][str(cid)] = {
                 "workload": I.CONFIG_NAMES[cid], "rows": cinp.rows, "keys": sum(cinp.kv_len),

@@ -99,42 +99,25 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
 #pragma unroll
     for (int h = 0; h < kVec; ++h) pv[i][h] = part_at(i, h);
 
-  // m, the bad flag and Z over all chunks, with the sink.
-  const float sink = x[0].w;   // phase 1 stores the head's sink with every statistic
-  bool bad = !__builtin_isfinite(sink);
-  float m = bad ? 0.0f : sink;
-  auto take_max = [&](const float4 &s) {
-    bad |= s.z != 0.0f;
-    if (s.y > 0.0f) m = fmaxf(m, s.x);
-  };
-#pragma unroll
-  for (int i = 0; i < kB; ++i)
-    if (static_cast<uint32_t>(i) < nch) take_max(x[i]);
-  for (uint32_t cc = kB; cc < nch; ++cc) take_max(stat_at(cc));
-  float z = bad ? 0.0f : expf(sink - m);
-  auto weight = [&](const float4 &s) { return s.y > 0.0f ? expf(s.x - m) : 0.0f; };
-#pragma unroll
-  for (int i = 0; i < kB; ++i)
-    if (static_cast<uint32_t>(i) < nch) z += x[i].y * weight(x[i]);
-  for (uint32_t cc = kB; cc < nch; ++cc) {
-    const float4 s = stat_at(cc);
-    z += s.y * weight(s);
-  }
-  bad |= !(z > 0.0f && __builtin_isfinite(z));
+  // m, the bad flag and Z over all chunks, with the sink (phase 1 stores the
+  // head's sink with every statistic).
+  const HeadNorm hn = head_norm<kB>(x[0].w, nch, [&](uint32_t cc) { return x[cc]; }, stat_at);
 
+  // acc = sum_c exp(m_c - m) O_c in chunk order, over the row's chunks only.
   f32x4 acc[kVec];
 #pragma unroll
   for (int h = 0; h < kVec; ++h) acc[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < kB; ++i) {
-    const float w = static_cast<uint32_t>(i) < nch ? weight(x[i]) : 0.0f;
+    if (static_cast<uint32_t>(i) >= nch) break;
+    const float w = chunk_weight(x[i], hn.m);
 #pragma unroll
     for (int h = 0; h < kVec; ++h)
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(w, pv[i][h][k], acc[h][k]);
   }
   for (uint32_t cc = kB; cc < nch; ++cc) {
-    const float w = weight(stat_at(cc));
+    const float w = chunk_weight(stat_at(cc), hn.m);
 #pragma unroll
     for (int h = 0; h < kVec; ++h) {
       const f32x4 q = part_at(cc, h);
@@ -142,16 +125,12 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
       for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(w, q[k], acc[h][k]);
     }
   }
-  const float invz = bad ? 0.0f : 1.0f / z;
   float *dst = global_ptr<float>(obits) + (static_cast<uint64_t>(q_row) * kHeads + head) * kDim + d0;
 #pragma unroll
   for (int h = 0; h < kVec; ++h) {
     f32x4 v;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float u = acc[h][k] * invz;
-      v[k] = (!bad && __builtin_isfinite(u)) ? u : 0.0f;
-    }
+    for (int k = 0; k < 4; ++k) v[k] = head_out(acc[h][k], hn.invz, hn.bad);
     *reinterpret_cast<f32x4 *>(dst + 4 * h) = v;
   }
 }

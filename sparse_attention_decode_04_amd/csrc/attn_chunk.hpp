@@ -109,6 +109,54 @@ __device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, uint32_t r, uint3
   return ar;
 }
 
+// The softmax normaliser of one head over its row's chunks, from each
+// chunk's statistics s_c = (m_c, sum_c, bad_c, sink) in chunk order:
+// m = max(sink, m_c of chunks with a live slot), Z = exp(sink - m) +
+// sum_c sum_c exp(m_c - m); the head is bad when the sink, a chunk or Z is.
+// Every multiply-add is an explicit fmaf (the combine's bits do not depend
+// on how the compiler contracts the code around it).
+struct HeadNorm {
+  float m, invz;   // invz = 1/Z, or 0 for a bad head
+  bool bad;
+};
+__device__ __forceinline__ float chunk_weight(const float4 &s, float m) { return s.y > 0.0f ? expf(s.x - m) : 0.0f; }
+// first_at(cc) gives the statistics of the first kUnrolled chunks (called
+// with compile-time cc, so statistics held in register arrays stay in
+// registers), later_at(cc) those of the rest; chunks are taken in order.
+template <int kUnrolled, class FirstAt, class LaterAt>
+__device__ __forceinline__ HeadNorm head_norm(float sink, uint32_t nch, const FirstAt &first_at,
+                                              const LaterAt &later_at) {
+  bool bad = !__builtin_isfinite(sink);
+  float m = bad ? 0.0f : sink;
+  auto take_max = [&](const float4 &s) {
+    bad |= s.z != 0.0f;
+    if (s.y > 0.0f) m = fmaxf(m, s.x);
+  };
+#pragma unroll
+  for (int cc = 0; cc < kUnrolled; ++cc)
+    if (static_cast<uint32_t>(cc) < nch) take_max(first_at(cc));
+  for (uint32_t cc = kUnrolled; cc < nch; ++cc) take_max(later_at(cc));
+  float z = bad ? 0.0f : expf(sink - m);
+#pragma unroll
+  for (int cc = 0; cc < kUnrolled; ++cc)
+    if (static_cast<uint32_t>(cc) < nch) {
+      const float4 s = first_at(cc);
+      z = fmaf(s.y, chunk_weight(s, m), z);
+    }
+  for (uint32_t cc = kUnrolled; cc < nch; ++cc) {
+    const float4 s = later_at(cc);
+    z = fmaf(s.y, chunk_weight(s, m), z);
+  }
+  bad |= !(z > 0.0f && __builtin_isfinite(z));
+  return HeadNorm{m, bad ? 0.0f : 1.0f / z, bad};
+}
+// One output element from its weighted sum: acc / Z, zeroed for a bad head
+// or a non-finite value.
+__device__ __forceinline__ float head_out(float acc, float invz, bool bad) {
+  const float u = acc * invz;
+  return (!bad && __builtin_isfinite(u)) ? u : 0.0f;
+}
+
 // Phase 1 for (row r, head group hg, chunk c) by the first kChunkThreads
 // threads of the workgroup (further waves of a wider workgroup would only
 // take part in the barriers). raw_index_at(slot) gives the direct variant the

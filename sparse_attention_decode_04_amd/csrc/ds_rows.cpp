@@ -302,9 +302,10 @@ struct TopkInput {
 };
 
 // Selection levels until every row has one list; the last writes indices.
-// With attn set, a final level over lists that every row reaches in the same
-// pass runs inside the attention's workgroups instead (then the combine), and
-// *attn_done says so.
+// With attn set, the pass over lists in which every row that is still
+// selecting reaches its final level runs inside the attention's workgroups
+// instead (rows that finished in earlier passes read their indices there),
+// followed by the attention's combine, and *attn_done says so.
 ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, const float *scores,
                           const TopkInput &in, uint64_t *bank0, uint64_t *bank1, int32_t *indices, void *stream,
                           const ds::AttnArgs *attn = nullptr, uint32_t attn_chunks = 0, bool *attn_done = nullptr) {
@@ -334,12 +335,13 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
     uint64_t out_elems = 0;
     for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
       a.blk_begin[r] = blocks;
-      if (r >= p.rows || done[r]) continue;
+      if (r >= p.rows) continue;
+      a.offset[r] = rows->offset[r];
+      a.out_offset[r] = rows->output_offset[r];   // (also where a finished row's indices are)
+      if (done[r]) continue;
       a.count[r] = count[r];
       a.in_base[r] = in_base[r];
       a.out_base[r] = out_elems;
-      a.offset[r] = rows->offset[r];
-      a.out_offset[r] = rows->output_offset[r];
       if (chunks[r] == 1) {
         a.final_mask |= 1u << r;
         if (from_lists) {
@@ -367,7 +369,7 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
       a.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
     }
     bool every_row_final = true;
-    for (uint32_t r = 0; r < p.rows; ++r) every_row_final &= !done[r] && chunks[r] == 1;
+    for (uint32_t r = 0; r < p.rows; ++r) every_row_final &= done[r] || chunks[r] == 1;
     if (attn && !a.from_scores && every_row_final) {
       hipError_t e = ds::launch_topk_attn(a, *attn, attn_chunks, s);
       if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
@@ -725,65 +727,37 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
     return e == hipSuccess ? DS_OK : hip_fail(e, "attention combine launch");
   }
 
-  // One kernel for the final level and the attention when the indexer keeps
-  // the first stage (every row long enough) and each row's candidates fit
-  // one workgroup; otherwise the two calls, with the same results.
-  uint32_t max_count = 0;
-  for (uint32_t r = 0; r < p.rows; ++r)
-    max_count = std::max(max_count, (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand);
-  if (fused_rows(p) && max_count > ds::kTopkChunkLater) {
-    // Rows past one workgroup's candidates: ds_rows_indexer_topk's levels,
-    // the last inside the attention's workgroups when every row reaches it
-    // in the same pass; otherwise the attention call follows.
+  // Otherwise ds_rows_indexer_topk's kernels (the fused indexer and selection
+  // passes over its candidates when every row is long enough, else the score
+  // kernel and passes over the scores), with the last selection pass inside
+  // the attention's workgroups whenever it is a pass over lists; when the
+  // only pass is over the scores, ds_rows_sparse_attn_direct follows.
+  TopkInput in{};
+  uint64_t *bank0, *bank1;
+  if (fused_rows(p)) {
     char *ws = static_cast<char *>(idx_workspace);
     uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
     uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
-    uint64_t *bank = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
+    bank0 = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
+    bank1 = bank0 + p.fused_bank;
     DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, cand, floors, stream));
-    TopkInput in{};
     in.lists = cand;
     in.floors = floors;
     for (uint32_t r = 0; r < p.rows; ++r) {
       in.count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand;
       in.base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
     }
-    bool attn_done = false;
-    DS_TRY(run_topk_levels(irows, p, scores, in, bank, bank + p.fused_bank, indices, stream, &a,
-                           sp.max_chunks, &attn_done));
-    if (attn_done) return DS_OK;
-    return ds_rows_sparse_attn_direct(srows, q, q_elems, sinks, sinks_elems, indices, indices_elems, scale,
-                                      attn_workspace, attn_workspace_bytes, out, out_elems, stream);
+  } else {
+    bank0 = static_cast<uint64_t *>(idx_workspace);
+    bank1 = bank0 + p.topk_bank;
+    DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, nullptr, nullptr, stream));
+    for (uint32_t r = 0; r < p.rows; ++r) in.count[r] = p.visible[r];
   }
-  if (!fused_rows(p) || max_count > ds::kTopkChunkLater) {
-    DS_TRY(ds_rows_indexer_topk(irows, idx_q, idx_q_elems, weights, weights_elems, scores, scores_elems,
-                                idx_workspace, idx_workspace_bytes, indices, indices_elems, stream));
-    return ds_rows_sparse_attn_direct(srows, q, q_elems, sinks, sinks_elems, indices, indices_elems, scale,
-                                      attn_workspace, attn_workspace_bytes, out, out_elems, stream);
-  }
-  char *ws = static_cast<char *>(idx_workspace);
-  uint64_t *cand = reinterpret_cast<uint64_t *>(ws);
-  uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
-  DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, cand, floors, stream));
-
-  // The final level, as run_topk_levels sets it up for the fused candidates
-  // (one chunk per row, checked against the floors).
-  t.in = cand;
-  t.from_scores = 0;
-  t.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
-  t.floors = floors;
-  for (uint32_t r = 0; r < p.rows; ++r) {
-    const uint32_t blocks = p.blk_begin[r + 1] - p.blk_begin[r];
-    t.count[r] = blocks * ds::kIdxCand;
-    t.in_base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
-    t.check_mask |= 1u << r;
-    t.floor_begin[r] = p.blk_begin[r] * ds::kIdxFloors;
-    t.floor_count[r] = blocks * ds::kIdxFloors;
-    t.fallback_count[r] = p.visible[r];
-  }
-  hipError_t e = ds::launch_topk_attn(t, a, sp.max_chunks, s);
-  if (e != hipSuccess) return hip_fail(e, "top-k and attention launch");
-  e = ds::launch_attn_combine(a, s);
-  return e == hipSuccess ? DS_OK : hip_fail(e, "attention combine launch");
+  bool attn_done = false;
+  DS_TRY(run_topk_levels(irows, p, scores, in, bank0, bank1, indices, stream, &a, sp.max_chunks, &attn_done));
+  if (attn_done) return DS_OK;
+  return ds_rows_sparse_attn_direct(srows, q, q_elems, sinks, sinks_elems, indices, indices_elems, scale,
+                                    attn_workspace, attn_workspace_bytes, out, out_elems, stream);
 }
 
 const char *ds_rows_last_error(void) { return g_error.c_str(); }

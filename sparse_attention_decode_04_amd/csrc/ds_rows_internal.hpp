@@ -176,7 +176,9 @@ hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s);
 // One 1024-thread workgroup per attention chunk (blocks as the attention's
 // phase 1): each runs its row's final top-k level over the fused indexer's
 // candidates (t: a single final, checked level) and then its attention chunk
-// on the indices it selected (a: the direct variant's arguments).
+// on the indices it selected (a: the direct variant's arguments); rows that
+// are not final at this level (clear in t.final_mask) read their indices from
+// t.indices. The attention's combine kernel follows.
 hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t max_chunks, hipStream_t s);
 
 

@@ -1,7 +1,8 @@
 // A row's final top-k level and its sparse attention in one kernel.
 //
 // What is computed is exactly ds_rows_indexer_topk's last level followed by
-// phase 1 of ds_rows_sparse_attn_direct on its indices. That level is either
+// ds_rows_sparse_attn_direct on its indices (rows whose selection ended in
+// an earlier pass read their indices from the output). That level is either
 // the best 512 of the fused indexer's candidates in rank order, checked
 // against the waves' floors, with the reselection from scores when a floor
 // could hide a ranking key, or, for rows whose visible scores all fit one
@@ -22,6 +23,11 @@
 // sixteen waves compute as the attention kernel does, its indices read
 // from LDS instead of memory. This removes a kernel boundary and the
 // attention's dependent index load (two HBM round trips become one).
+// The attention's combine kernel follows. (Combining in this kernel, by the
+// last workgroup of each (row, head group) to finish, with the chunk results
+// passed through agent-scope stores and loads and an arrival counter, was
+// measured slower: 26.6 us for final level + attention + combine against
+// about 18 us with the separate kernel, at 8 rows x 32768 keys.)
 #include "attn_chunk.hpp"
 #include "topk_select.hpp"
 
@@ -92,10 +98,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   // last chunk also every slot past the row's width.
   const uint32_t out_end = c + 1 == chunks ? static_cast<uint32_t>(kTopK) : lo + kAttnChunk;
   int32_t *const out = t.indices + t.out_offset[r];
-  select_level<kFromScores, kPer>(u.sel, lr, 0, [&](uint32_t pos, int32_t index) {
-    if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
-    if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
-  });
+  if (lr.final_level) {   // uniform
+    select_level<kFromScores, kPer>(u.sel, lr, 0, [&](uint32_t pos, int32_t index) {
+      if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
+      if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
+    });
+  } else if (threadIdx.x < static_cast<uint32_t>(kAttnChunk)) {
+    // The row finished its selection in an earlier pass: its indices are in
+    // the output already.
+    slot_index[threadIdx.x] = out[min(lo + threadIdx.x, static_cast<uint32_t>(kTopK) - 1)];
+  }
   __syncthreads();   // the chunk's indices are in place; the selection's LDS is free
   static_assert(kTopkThreads == kChunkThreads, "the attention chunk uses every thread of the workgroup");
   attn_chunk_body<true>(u.att, ar, hg, c, [&](uint32_t slot) { return slot_index[slot - lo]; });
