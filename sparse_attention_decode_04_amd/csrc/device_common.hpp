@@ -173,6 +173,22 @@ __device__ __forceinline__ float wave_max_f(float v) {
   return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
 }
 
+// max(x, 0) with maxNum's treatment of a NaN input (the result is 0) in one
+// instruction: v_med3_f32(x, 0, +inf) is the median, and for a quiet NaN
+// operand the hardware returns the smallest of the three, 0. (fmaxf costs a
+// second instruction that quiets signalling NaNs first; the values clamped
+// here are MFMA results, never signalling.) A -0 result may come back as
+// either zero, which no use here can tell apart.
+// `inf` is +inf held in a register the compiler cannot see into (see
+// opaque_inf), so that it emits the med3 rather than folding it back into a
+// max with the quieting instruction.
+__device__ __forceinline__ float opaque_inf() {
+  float inf = __builtin_inff();
+  asm volatile("" : "+v"(inf));
+  return inf;
+}
+__device__ __forceinline__ float relu_num(float x, float inf) { return __builtin_amdgcn_fmed3f(x, 0.0f, inf); }
+
 // A device pointer handed over as its integer bits (to pass it through an
 // empty asm statement), rebuilt as a global-memory pointer so that accesses
 // through it stay global (not flat) loads and stores.

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a
   store_chunk(0, st[0]);
   __syncthreads();
 
+  const float inf = opaque_inf();   // for relu_num
   for (uint32_t c0 = 0; c0 < chunks; c0 += kMqDepth) {
 #pragma unroll
    for (int u = 0; u < kMqDepth; ++u) {
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(64 * kWaves) void indexer_mq_kernel(IndexerMqArgs a
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) part = fmaf(fmaxf(acc[m][j], 0.0f), wt[m][j], part);
+          for (int j = 0; j < 4; ++j) part = fmaf(relu_num(acc[m][j], inf), wt[m][j], part);
         }
         return part;
       };

@@ -54,6 +54,27 @@ def test_ragged_rows(Q):
     check_rows(inp, dev.results())
 
 
+def test_non_finite_keys_and_queries():
+    # NaN and infinite key and query elements: a NaN dot product contributes
+    # 0 through the ReLU (maxNum), an infinite one makes the score non-finite
+    # (-inf), as the oracle computes it
+    kv_len = [300, 130]
+    Q = 3
+    inp = I.make_mq(405, kv_len, Q)
+    k0 = inp.idx_keys[0]
+    k0[3, 5] = 0x7FC0     # NaN
+    k0[4, 9] = 0x7F80     # +inf
+    k0[5, 2] = 0xFF80     # -inf
+    k0[6, :] = 0x7F80     # a whole row of +inf
+    k0[7, 0] = 0x7F80     # +inf and -inf in one row
+    k0[7, 1] = 0xFF80
+    inp.idx_q[Q * 1 + 2, 10, 3] = 0x7FC0    # NaN in a query of row 1
+    say("multi-query indexer: non-finite keys and queries")
+    dev = DeviceMultiQuery(inp)
+    dev.run()
+    check_rows(inp, dev.results())
+
+
 def test_per_query_causal_limits_and_ternary_keys():
     # start positions well inside the cache: each query hides a different
     # number of keys; ternary entries give many zero and tied scores
