@@ -399,15 +399,7 @@ def main():
 
     def device_copies(inp, n):
         base = DeviceInputs(inp)
-        out = [base]
-        for _ in range(n - 1):
-            c = DeviceInputs.__new__(DeviceInputs)
-            c.inp, c.device = inp, base.device
-            c.idx_q, c.idx_w, c.attn_q, c.sinks = (base.idx_q.clone(), base.idx_w.clone(),
-                                                   base.attn_q.clone(), base.sinks.clone())
-            c.keys = [k.clone() for k in base.keys]
-            c.kv = [k.clone() for k in base.kv]
-            out.append(c)
+        out = [base] + [base.clone() for _ in range(n - 1)]
         return [DeviceRows(c) for c in out]
 
     def timed(runs, name, steps, warmup):
@@ -467,6 +459,33 @@ def main():
         without = region(False)
         with_extra2 = region(True)
         return ((with_extra + with_extra2) / 2 - without) / n
+
+    def dispatch_timed_ms(runs, call, n):
+        """Duration of the indexer kernel inside `call` from its own dispatch
+        timestamps: before each of n calls (rotating over the input copies)
+        ds_rows_time_next_indexer arms the call's indexer launch to record its
+        start and end in a pair of HIP events (hipExtLaunchKernel), the
+        timestamps a kernel trace reports. Mean and median in ms, and the mean
+        call time of that armed loop (binding the events to a dispatch adds
+        launch overhead, so the armed calls run with small gaps between
+        kernels, as under a tracer)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:   # a torch event gets its HIP event when first recorded
+            a.record(stream)
+            b.record(stream)
+        for i in range(len(runs)):
+            getattr(runs[i], call)()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            ds.time_next_indexer(evs[i][0], evs[i][1])
+            getattr(runs[i % len(runs)], call)()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        d = np.array([a.elapsed_time(b) for a, b in evs])
+        return float(d.mean()), float(np.median(d)), e0.elapsed_time(e1) / n
 
     def back_to_back_ms(runs, call, n):
         """Mean duration of one `call` from HIP events on the launch stream
@@ -533,10 +552,14 @@ def main():
     ms_four, _ = timed(runs, "step", args.steps, args.warmup)
 
     n_idx = max(args.steps, 50)
+    # The indexer inside the one-call step, from its dispatch timestamps (the
+    # roofline figure), and by difference of unarmed loops (marginal).
+    idx_in_mean, idx_in_median, armed_step_ms = dispatch_timed_ms(runs, "step_one", n_idx)
     extra_runs = device_copies(inp, args.copies)
-    idx_in_mean = in_step_ms(runs, extra_runs, first_call, n_idx)
+    idx_marginal = in_step_ms(runs, extra_runs, first_call, n_idx)
     del extra_runs
     idx_b2b = back_to_back_ms(runs, first_call, n_idx)
+    idx_b2b_disp, _, _ = dispatch_timed_ms(runs, first_call, n_idx)
     per_call = per_call_ms(runs, ("indexer_topk", "sparse_attn_direct"), args.steps)
     per_call_three = per_call_ms(runs, ("indexer_score", "topk", "sparse_attn_direct"), args.steps)
     per_call_four = per_call_ms(runs, ("indexer_score", "topk", "gather", "sparse_attn"), args.steps)
@@ -552,7 +575,7 @@ def main():
     # and the kernel boundaries between them), and the separate direct
     # attention call (phase 1 + combine) by its own events.
     attn_b, attn_f = attention_bytes_flops(kv_len)
-    rest_ms = ms_per_step - idx_in_mean
+    rest_ms = ms_per_step - idx_marginal
     attn_traffic = measured_traffic("attention") if args.config == 2 else None
     attn_direct_ms = per_call["sparse_attn_direct"]
 
@@ -594,9 +617,17 @@ def main():
             "kernel": ("indexer_score_kernel<true> (indexer with the fused top-k candidate stage)" if fused
                        else "indexer_score_kernel<false>"),
             "kernel_ms": idx_in_mean,
-            "timing": "in step: (n one-call steps each followed by one more launch of the indexer kernel alone, on "
-                      "input copies of its own) minus (n one-call steps), over n = %d, HIP events on the launch "
-                      "stream" % n_idx,
+            "kernel_ms_median": idx_in_median,
+            "timing": "in step, from the kernel's own dispatch timestamps: mean over n = %d one-call steps on the "
+                      "rotating copies, each step's indexer launch bound to a pair of HIP events "
+                      "(ds_rows_time_next_indexer / hipExtLaunchKernel), the same timestamps a kernel trace reports" % n_idx,
+            "armed_step_ms": armed_step_ms,
+            "marginal_ms": idx_marginal,
+            "marginal_timing": "(n one-call steps each followed by one more launch of the indexer alone, on input copies "
+                               "of its own) minus (n one-call steps), unarmed, HIP events on the launch stream; the "
+                               "extra launch also puts the next step's indexer behind an indexer, so this leans "
+                               "toward the back-to-back figure",
+            "marginal_frac": idx_bytes / (idx_marginal * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
@@ -607,6 +638,7 @@ def main():
             "bytes_per_launch": idx_bytes,
             "back_to_back_ms": idx_b2b,
             "back_to_back_frac": idx_bytes / (idx_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "back_to_back_dispatch_ms": idx_b2b_disp,
             "mfma_tflops": idx_flops / (idx_in_mean * 1e-3) / 1e12,
             "mfma_frac_of_bf16_peak": idx_flops / (idx_in_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         },
@@ -615,7 +647,8 @@ def main():
             "algorithmic_bytes": attn_b,
             "flops": attn_f,
             "in_step_us": rest_ms * 1e3,
-            "in_step_timing": "one-call step mean minus the in-step indexer mean (includes the kernel boundaries)",
+            "in_step_timing": "one-call step mean minus the indexer's marginal in-step time (unarmed loops; includes "
+                              "the kernel boundaries)",
             "achieved_gb_s": attn_b / (rest_ms * 1e-3) / 1e9,
             "hbm_frac": attn_b / (rest_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "direct_call_us": attn_direct_ms * 1e3,
@@ -645,9 +678,7 @@ def main():
             spread = per_step_us(cruns, "step_one", steps)
             cfused = fused_route(cinp.kv_len)
             cfirst = "indexer_candidates" if cfused else "indexer_score"
-            cextra = device_copies(cinp, ncopies)
-            c_in = in_step_ms(cruns, cextra, cfirst, max(steps, 20))
-            del cextra
+            c_in, _, _ = dispatch_timed_ms(cruns, "step_one", max(steps, 20))
             cb, _ = indexer_bytes_flops(cinp.kv_len, cfused)
             out["configs"][str(cid)] = {
                 "workload": I.CONFIG_NAMES[cid], "rows": cinp.rows, "keys": sum(cinp.kv_len),

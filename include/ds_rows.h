@@ -453,6 +453,21 @@ ds_status ds_rows_compressor(const ds_compressor_rows *rows,
                              void *output, size_t output_elems,
                              void *stream);
 
+/* Timing of one indexer launch, for measurement tools.
+ *
+ * Arms the calling thread's next launch of the indexer kernel (plain or with
+ * the fused top-k stage, made by any entry point above) to record its own
+ * start and end in the two events: `start_event` and `stop_event` are
+ * hipEvent_t handles (passed as void *) that the caller created on the
+ * current device, e.g. with hipEventCreate, and owns. The kernel is then
+ * launched with hipExtLaunchKernel, which ties the events to the dispatch
+ * itself, so no separate event record sits between the indexer and the
+ * kernels around it; hipEventElapsedTime(start, stop) afterwards gives the
+ * kernel's duration where it ran. One arm times one launch; a call that
+ * fails its argument checks leaves the arm in place. Both handles must be
+ * non-null (DS_ERR_INVALID_ARGUMENT otherwise); nothing is enqueued by this call. */
+ds_status ds_rows_time_next_indexer(void *start_event, void *stop_event);
+
 /* Message of the last failed call on this thread ("ds_rows: ..."), or "". */
 const char *ds_rows_last_error(void);
 

@@ -202,9 +202,17 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
       const uint32_t cslot = min(s0 + s, width - 1);
-      // Every lane reads the same slot: the value is wave-uniform.
-      if (kDirect) raw_index[s] = __builtin_amdgcn_readfirstlane(raw_index_at(cslot));
+      // Every lane reads the same slot. The direct variant keeps the index
+      // in a vector register (an opaque per-lane copy), so that the checks
+      // and the 64-bit row address below run on the vector ALUs, each SIMD
+      // for its own waves: as wave-uniform scalar code they would queue
+      // every wave of the workgroup on the compute unit's one scalar ALU.
+      if (kDirect) raw_index[s] = raw_index_at(cslot);
       else raw_mask[s] = a.mask[cslot];
+    }
+    if (kDirect) {
+  #pragma unroll
+      for (int s = 0; s < kSlots; ++s) asm volatile("" : "+v"(raw_index[s]));
     }
     // The row's fields once, out of the loop below.
     const uint32_t kv_len = a.kv_len;

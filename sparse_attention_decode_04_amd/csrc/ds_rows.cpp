@@ -266,6 +266,15 @@ ds_status check_indexer_operands(const ds_indexer_rows *rows, const IndexerPlan 
   return DS_OK;
 }
 
+// The calling thread's armed indexer timing events (ds_rows_time_next_indexer),
+// handed to the next indexer launch and cleared.
+thread_local hipEvent_t t_timer_start = nullptr, t_timer_stop = nullptr;
+void take_indexer_timer(hipEvent_t *start, hipEvent_t *stop) {
+  *start = t_timer_start;
+  *stop = t_timer_stop;
+  t_timer_start = t_timer_stop = nullptr;
+}
+
 // Indexer launch; with cand/floors set, also the fused top-k stage.
 ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, const void *q, const float *weights,
                          float *scores, uint64_t *cand, uint64_t *floors, void *stream) {
@@ -287,7 +296,10 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
   }
   uint32_t max_row_blocks = 1;
   for (uint32_t r = 0; r < p.rows; ++r) max_row_blocks = std::max(max_row_blocks, p.blk_begin[r + 1] - p.blk_begin[r]);
-  const hipError_t e = ds::launch_indexer_score(a, max_row_blocks, cand != nullptr, static_cast<hipStream_t>(stream));
+  hipEvent_t start = nullptr, stop = nullptr;
+  take_indexer_timer(&start, &stop);
+  const hipError_t e =
+      ds::launch_indexer_score(a, max_row_blocks, cand != nullptr, static_cast<hipStream_t>(stream), start, stop);
   return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
 }
 
@@ -758,6 +770,14 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
   if (attn_done) return DS_OK;
   return ds_rows_sparse_attn_direct(srows, q, q_elems, sinks, sinks_elems, indices, indices_elems, scale,
                                     attn_workspace, attn_workspace_bytes, out, out_elems, stream);
+}
+
+ds_status ds_rows_time_next_indexer(void *start_event, void *stop_event) {
+  DS_TRY(need(start_event, "start_event"));
+  DS_TRY(need(stop_event, "stop_event"));
+  t_timer_start = static_cast<hipEvent_t>(start_event);
+  t_timer_stop = static_cast<hipEvent_t>(stop_event);
+  return DS_OK;
 }
 
 const char *ds_rows_last_error(void) { return g_error.c_str(); }

@@ -61,7 +61,10 @@ struct IndexerArgs {
   uint64_t *floors;                 // fused: kIdxFloors floors per block (one per wave)
 };
 // Grid (max_row_blocks, a.rows): workgroup (x, r) is row r's x-th block.
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s);
+// With start/stop events, the launch records its own start and end in them
+// (hipExtLaunchKernel).
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s,
+                                hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // ------------------------------------------------------------------ top-k
 // One selection level: every workgroup reduces a chunk of one row's

@@ -47,6 +47,8 @@
 // best unwritten tie otherwise). The final top-k level uses the floors to
 // prove that no unkept key can reach the row's top 512, and selects from the
 // scores again when one could.
+#include <hip/hip_ext.h>
+
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 #include "select_common.hpp"
@@ -280,12 +282,19 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   }
 }
 
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s) {
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s,
+                                hipEvent_t start, hipEvent_t stop) {
   const dim3 grid(max_row_blocks, a.rows);
-  if (fused)
+  if (start != nullptr) {
+    if (fused)
+      hipExtLaunchKernelGGL(indexer_score_kernel<true>, grid, dim3(kIdxThreads), 0, s, start, stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(indexer_score_kernel<false>, grid, dim3(kIdxThreads), 0, s, start, stop, 0, a);
+  } else if (fused) {
     hipLaunchKernelGGL(indexer_score_kernel<true>, grid, dim3(kIdxThreads), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL(indexer_score_kernel<false>, grid, dim3(kIdxThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ FUNCTIONS = (
     "ds_rows_last_error", "ds_rows_version", "ds_rows_indexer_topk_workspace_bytes", "ds_rows_indexer_topk",
     "ds_rows_indexer_candidates", "ds_rows_compressor_state_elems", "ds_rows_compressor",
     "ds_rows_indexer_mq_scores_elems", "ds_rows_indexer_score_mq", "ds_rows_indexer_topk_attn",
-    "ds_rows_indexer_topk_attn_noalloc",
+    "ds_rows_indexer_topk_attn_noalloc", "ds_rows_time_next_indexer",
 )
 
 
@@ -135,6 +135,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
               "ds_rows_compressor", "ds_rows_indexer_score_mq", "ds_rows_indexer_topk_attn",
               "ds_rows_indexer_topk_attn_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.ds_rows_time_next_indexer.argtypes = [c_void_p, c_void_p]
+    lib.ds_rows_time_next_indexer.restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
     _lib = lib
@@ -390,6 +392,20 @@ def compressor(t: CompressorRows, ratio, head_dim, eps, kv, score, ape, norm, ou
     oa, on = _dev(out, 2)
     _check(load().ds_rows_compressor(ctypes.byref(t), int(ratio), int(head_dim), float(eps), ka, kn, sa, sn,
                                      aa, an, na, nn, oa, on, _stream(stream)))
+
+
+def time_next_indexer(start_event, stop_event):
+    """Arm the calling thread's next indexer launch to record its own start and
+    end in two HIP events (torch.cuda.Event objects with enable_timing=True, or
+    raw hipEvent_t handles as ints). A torch event gets its HIP event when it is
+    first recorded, so it is recorded once here if it has none yet."""
+    def handle(ev):
+        if isinstance(ev, int):
+            return ev
+        if not ev.cuda_event:
+            ev.record()
+        return ev.cuda_event
+    _check(load().ds_rows_time_next_indexer(c_void_p(handle(start_event)), c_void_p(handle(stop_event))))
 
 
 def version() -> str:

@@ -26,8 +26,23 @@ def to_device(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
+def pooled(arrays, device):
+    """One device allocation holding every array (row after row) and a view
+    of each: a cache pool, as a server keeps a layer's cached rows."""
+    flat = [np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else np.ascontiguousarray(a)
+            for a in arrays]
+    pool = torch.from_numpy(np.concatenate([a.reshape(-1) for a in flat])).to(device)
+    views, at = [], 0
+    for a in flat:
+        views.append(pool[at: at + a.size].view(a.shape))
+        at += a.size
+    return pool, views
+
+
 class DeviceInputs:
-    """Device copies of a workload's inputs (shared by any number of runs)."""
+    """Device copies of a workload's inputs (shared by any number of runs).
+    Every row's KV rows sit in one allocation (the per-row tensors are views
+    into it); each row's indexer keys are an allocation of their own."""
 
     def __init__(self, inp: RowsInputs, device="cuda"):
         self.inp = inp
@@ -37,7 +52,19 @@ class DeviceInputs:
         self.keys = [to_device(k, device) for k in inp.idx_keys]
         self.attn_q = to_device(inp.attn_q, device)
         self.sinks = to_device(inp.sinks, device)
-        self.kv = [to_device(k, device) for k in inp.kv]
+        self.kv_pool, self.kv = pooled(inp.kv, device)
+
+    def clone(self) -> "DeviceInputs":
+        """An independent device copy (new allocations, same values)."""
+        c = DeviceInputs.__new__(DeviceInputs)
+        c.inp, c.device = self.inp, self.device
+        c.idx_q, c.idx_w, c.attn_q, c.sinks = (self.idx_q.clone(), self.idx_w.clone(), self.attn_q.clone(),
+                                               self.sinks.clone())
+        c.keys = [k.clone() for k in self.keys]
+        c.kv_pool = self.kv_pool.clone()
+        c.kv = [c.kv_pool[k.storage_offset() - self.kv_pool.storage_offset():][:k.numel()].view(k.shape)
+                for k in self.kv]
+        return c
 
 
 class DeviceRows:

@@ -274,3 +274,31 @@ def test_step_permuted_row_subsets_match_full_launch():
         for i, r in enumerate(sel):
             assert np.array_equal(got4[i]["gathered"], ref4[r]["gathered"]), (sel, r)
             assert np.array_equal(got4[i]["out"].view(np.uint32), ref4[r]["out"].view(np.uint32)), (sel, r)
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_timed_indexer_launch_changes_nothing(cid):
+    """ds_rows_time_next_indexer: the armed step's indexer records its own
+    start and end (a positive duration below a second), the outputs are those
+    of an unarmed step bit for bit, and the arm is used up by that launch."""
+    inp = I.make_config(cid)
+    say(f"config {cid}: timed indexer launch")
+    run = DeviceRows(DeviceInputs(inp))
+    run.step_one()
+    torch.cuda.synchronize()
+    ref_out, ref_idx, ref_sc = run.out.clone(), run.indices.clone(), run.scores.clone()
+    run.out.zero_()
+    run.indices.fill_(-7)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ds.time_next_indexer(start, stop)
+    run.step_one()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop)
+    assert 0.0 < ms < 1000.0, ms
+    assert torch.equal(run.out, ref_out)
+    assert torch.equal(run.indices, ref_idx)
+    assert torch.equal(run.scores, ref_sc)
+    # The arm was consumed: a later step leaves the events as they were.
+    run.step_one()
+    torch.cuda.synchronize()
+    assert start.elapsed_time(stop) == ms
