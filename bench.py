@@ -65,7 +65,7 @@ def parse():
     p.add_argument("--leg", choices=("all", "multi_query", "compressor", "fallback", "stream"), default="all",
                    help="run one leg alone and print its JSON object: the multi-query indexer, the compressor, "
                         "the one-call step on scores that defeat the fused candidates, or plain streaming "
-                        "copies and reads of 64 MiB .. 1 GiB (the achievable HBM rate on this GPU)")
+                        "copies of 64 MiB .. 1 GiB (the achievable HBM rate on this GPU)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 64 MiB device-to-device copy 5 times (reference for the "
                         "FETCH_SIZE / WRITE_SIZE counter scale) and exit")
@@ -316,44 +316,34 @@ def cpu_baseline(headline_inp, seconds, config_inputs):
 
 
 def stream_bench(torch):
-    """Plain device copies (torch copy_, the HIP runtime's blit kernel) and a
-    read-only reduction (torch sum over float32) of 64 MiB, 256 MiB and
-    1 GiB: the HBM rates a simple streaming kernel reaches on this GPU, as
-    a practical ceiling next to the 8 TB/s specification."""
+    """Plain device-to-device copies (torch copy_, the HIP runtime's blit
+    kernel) of 64 MiB, 256 MiB and 1 GiB over rotating buffers: the HBM rate
+    a simple streaming kernel reaches on this GPU (read + write bytes), the
+    practical ceiling next to the 8 TB/s specification."""
     stream = torch.cuda.current_stream()
     res = {}
     for mib in (64, 256, 1024):
         n = mib << 20
         copies = max(2, (2048 // mib))
         src = [torch.ones(n // 4, dtype=torch.float32, device="cuda") for _ in range(copies)]
-        dst = [torch.empty_like(s) for s in src]
+        dst = [torch.empty_like(x) for x in src]
         for i in range(copies):
             dst[i].copy_(src[i])
-            src[i].sum()
         torch.cuda.synchronize()
         reps = 20
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
         for i in range(reps):
             dst[i % copies].copy_(src[i % copies])
         ev[1].record(stream)
-        ev[2].record(stream)
-        acc = torch.zeros((), device="cuda")
-        for i in range(reps):
-            acc += src[i % copies].sum()
-        ev[3].record(stream)
         torch.cuda.synchronize()
         copy_ms = ev[0].elapsed_time(ev[1]) / reps
-        read_ms = ev[2].elapsed_time(ev[3]) / reps
-        res[f"{mib}MiB"] = {
-            "copy_us": copy_ms * 1e3, "copy_gb_s": 2 * n / (copy_ms * 1e-3) / 1e9,
-            "read_us": read_ms * 1e3, "read_gb_s": n / (read_ms * 1e-3) / 1e9,
-            "rotating_buffers": copies}
+        res[f"{mib}MiB"] = {"copy_us": copy_ms * 1e3, "copy_gb_s": 2 * n / (copy_ms * 1e-3) / 1e9,
+                            "rotating_buffers": copies}
         del src, dst
         torch.cuda.empty_cache()
-    return {"timing": "HIP events around 20 back-to-back launches over rotating buffers (2 GiB in total per size)",
-            "copy": "torch copy_ (read + write counted)", "read": "torch sum over float32 (read counted)",
-            "sizes": res}
+    return {"timing": "HIP events around 20 back-to-back copies over rotating buffers (2 GiB in total per size)",
+            "copy": "torch copy_ (read + write counted)", "sizes": res}
 
 
 def main():
@@ -460,19 +450,19 @@ def main():
         with_extra2 = region(True)
         return ((with_extra + with_extra2) / 2 - without) / n
 
-    def dispatch_timed_ms(runs, call, n):
-        """Duration of the indexer kernel inside `call` from its own dispatch
-        timestamps: before each of n calls (rotating over the input copies)
-        ds_rows_time_next_indexer arms the call's indexer launch to record its
-        start and end in a pair of HIP events (hipExtLaunchKernel), the
-        timestamps a kernel trace reports. Mean and median in ms, and the mean
-        call time of that armed loop (binding the events to a dispatch adds
-        launch overhead, so the armed calls run with small gaps between
-        kernels, as under a tracer)."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for a, b in evs:   # a torch event gets its HIP event when first recorded
-            a.record(stream)
-            b.record(stream)
+    def stamped_ms(runs, call, n):
+        """Execution span of the indexer kernel inside `call`, from the
+        wall-clock stamps its workgroups write when armed by
+        ds_rows_time_next_indexer: smallest workgroup start to largest wave
+        end, for each of n calls over the rotating input copies. Each call
+        writes to a zeroed buffer of its own, so nothing but the calls runs in
+        the loop (the armed launch is an ordinary one plus a few stores per
+        workgroup). Mean and median span in ms, and the loop's mean call time."""
+        inp_ = runs[0].dev.inp
+        per = -(-max(inp_.kv_len) // 1024) * inp_.rows * ds.TIMER_STAMPS_PER_WG
+        buf = torch.zeros(n * per, dtype=torch.int64, device="cuda")
+        views = [buf[i * per:(i + 1) * per] for i in range(n)]
+        khz = ds.wall_clock_khz()
         for i in range(len(runs)):
             getattr(runs[i], call)()
         torch.cuda.synchronize()
@@ -480,11 +470,12 @@ def main():
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(n):
-            ds.time_next_indexer(evs[i][0], evs[i][1])
+            ds.time_next_indexer(views[i])
             getattr(runs[i % len(runs)], call)()
         e1.record(stream)
         torch.cuda.synchronize()
-        d = np.array([a.elapsed_time(b) for a, b in evs])
+        host = buf.cpu().numpy().reshape(n, -1)
+        d = np.array([ds.indexer_span_ticks(host[i]) for i in range(n)]) / khz   # ms
         return float(d.mean()), float(np.median(d)), e0.elapsed_time(e1) / n
 
     def back_to_back_ms(runs, call, n):
@@ -551,15 +542,16 @@ def main():
     # The four-call path (gather, then attention on the gathered rows).
     ms_four, _ = timed(runs, "step", args.steps, args.warmup)
 
-    n_idx = max(args.steps, 50)
-    # The indexer inside the one-call step, from its dispatch timestamps (the
-    # roofline figure), and by difference of unarmed loops (marginal).
-    idx_in_mean, idx_in_median, armed_step_ms = dispatch_timed_ms(runs, "step_one", n_idx)
+    n_idx = max(args.steps, 200)
+    # The indexer inside the one-call step: its execution span from the
+    # workgroups' wall-clock stamps (the roofline figure), and by difference of
+    # plain loops (marginal).
+    idx_in_mean, idx_in_median, armed_step_ms = stamped_ms(runs, "step_one", n_idx)
     extra_runs = device_copies(inp, args.copies)
     idx_marginal = in_step_ms(runs, extra_runs, first_call, n_idx)
     del extra_runs
     idx_b2b = back_to_back_ms(runs, first_call, n_idx)
-    idx_b2b_disp, _, _ = dispatch_timed_ms(runs, first_call, n_idx)
+    idx_b2b_span, _, _ = stamped_ms(runs, first_call, n_idx)
     per_call = per_call_ms(runs, ("indexer_topk", "sparse_attn_direct"), args.steps)
     per_call_three = per_call_ms(runs, ("indexer_score", "topk", "sparse_attn_direct"), args.steps)
     per_call_four = per_call_ms(runs, ("indexer_score", "topk", "gather", "sparse_attn"), args.steps)
@@ -618,15 +610,15 @@ def main():
                        else "indexer_score_kernel<false>"),
             "kernel_ms": idx_in_mean,
             "kernel_ms_median": idx_in_median,
-            "timing": "in step, from the kernel's own dispatch timestamps: mean over n = %d one-call steps on the "
-                      "rotating copies, each step's indexer launch bound to a pair of HIP events "
-                      "(ds_rows_time_next_indexer / hipExtLaunchKernel), the same timestamps a kernel trace reports" % n_idx,
-            "armed_step_ms": armed_step_ms,
+            "timing": "in step: mean over n = %d one-call steps on the rotating copies of the indexer's execution "
+                      "span, smallest workgroup start to largest wave end, from the wall-clock stamps its "
+                      "workgroups write (ds_rows_time_next_indexer)" % n_idx,
+            "stamped_loop_step_ms": armed_step_ms,
             "marginal_ms": idx_marginal,
             "marginal_timing": "(n one-call steps each followed by one more launch of the indexer alone, on input copies "
-                               "of its own) minus (n one-call steps), unarmed, HIP events on the launch stream; the "
-                               "extra launch also puts the next step's indexer behind an indexer, so this leans "
-                               "toward the back-to-back figure",
+                               "of its own) minus (n one-call steps), HIP events on the launch stream; the extra "
+                               "launch also puts the next step's indexer behind an indexer, so this measures about "
+                               "the back-to-back duration",
             "marginal_frac": idx_bytes / (idx_marginal * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bound": "hbm",
             "achieved": achieved,
@@ -638,7 +630,7 @@ def main():
             "bytes_per_launch": idx_bytes,
             "back_to_back_ms": idx_b2b,
             "back_to_back_frac": idx_bytes / (idx_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "back_to_back_dispatch_ms": idx_b2b_disp,
+            "back_to_back_span_ms": idx_b2b_span,
             "mfma_tflops": idx_flops / (idx_in_mean * 1e-3) / 1e12,
             "mfma_frac_of_bf16_peak": idx_flops / (idx_in_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         },
@@ -678,7 +670,7 @@ def main():
             spread = per_step_us(cruns, "step_one", steps)
             cfused = fused_route(cinp.kv_len)
             cfirst = "indexer_candidates" if cfused else "indexer_score"
-            c_in, _, _ = dispatch_timed_ms(cruns, "step_one", max(steps, 20))
+            c_in, _, _ = stamped_ms(cruns, "step_one", max(steps, 20))
             cb, _ = indexer_bytes_flops(cinp.kv_len, cfused)
             out["configs"][str(cid)] = {
                 "workload": I.CONFIG_NAMES[cid], "rows": cinp.rows, "keys": sum(cinp.kv_len),

@@ -456,17 +456,27 @@ ds_status ds_rows_compressor(const ds_compressor_rows *rows,
 /* Timing of one indexer launch, for measurement tools.
  *
  * Arms the calling thread's next launch of the indexer kernel (plain or with
- * the fused top-k stage, made by any entry point above) to record its own
- * start and end in the two events: `start_event` and `stop_event` are
- * hipEvent_t handles (passed as void *) that the caller created on the
- * current device, e.g. with hipEventCreate, and owns. The kernel is then
- * launched with hipExtLaunchKernel, which ties the events to the dispatch
- * itself, so no separate event record sits between the indexer and the
- * kernels around it; hipEventElapsedTime(start, stop) afterwards gives the
- * kernel's duration where it ran. One arm times one launch; a call that
- * fails its argument checks leaves the arm in place. Both handles must be
- * non-null (DS_ERR_INVALID_ARGUMENT otherwise); nothing is enqueued by this call. */
-ds_status ds_rows_time_next_indexer(void *start_event, void *stop_event);
+ * the fused top-k stage, made by any entry point above) to write wall-clock
+ * stamps into `stamps`, a device buffer of `stamps_elems` uint64 entries that
+ * the caller owns and fills with zeros beforehand: DS_TIMER_STAMPS_PER_WG
+ * entries per workgroup of the launch's grid (workgroup g of the grid, in
+ * launch order, at g * DS_TIMER_STAMPS_PER_WG), entry 0 its start and
+ * entries 1 .. 4 the ends of its four waves, in ticks of the device's
+ * constant wall clock (hipDeviceAttributeWallClockRate, kHz). The span from
+ * the smallest start to the largest end is the kernel's execution time where
+ * it ran; the launch is an ordinary one (a few extra stores per workgroup),
+ * so the kernels around it run as they would. The grid has
+ * ceil(max kv_len / 1024) x rows workgroups; a launch whose grid needs more
+ * entries than `stamps_elems` fails with DS_ERR_INVALID_ARGUMENT (nothing
+ * enqueued). One arm serves one launch; a call that fails its argument
+ * checks before the launch leaves the arm in place. `stamps` must be
+ * non-null (DS_ERR_INVALID_ARGUMENT otherwise); this call enqueues nothing. */
+#define DS_TIMER_STAMPS_PER_WG 8
+ds_status ds_rows_time_next_indexer(uint64_t *stamps, size_t stamps_elems);
+
+/* Frequency of that wall clock on the current device, in kHz (*khz), from
+ * hipDeviceAttributeWallClockRate. DS_ERR_DEVICE without a current device. */
+ds_status ds_rows_wall_clock_khz(int *khz);
 
 /* Message of the last failed call on this thread ("ds_rows: ..."), or "". */
 const char *ds_rows_last_error(void);

@@ -266,14 +266,10 @@ ds_status check_indexer_operands(const ds_indexer_rows *rows, const IndexerPlan 
   return DS_OK;
 }
 
-// The calling thread's armed indexer timing events (ds_rows_time_next_indexer),
-// handed to the next indexer launch and cleared.
-thread_local hipEvent_t t_timer_start = nullptr, t_timer_stop = nullptr;
-void take_indexer_timer(hipEvent_t *start, hipEvent_t *stop) {
-  *start = t_timer_start;
-  *stop = t_timer_stop;
-  t_timer_start = t_timer_stop = nullptr;
-}
+// The calling thread's armed indexer timing buffer (ds_rows_time_next_indexer),
+// taken by its next indexer launch.
+thread_local uint64_t *t_timer_stamps = nullptr;
+thread_local size_t t_timer_elems = 0;
 
 // Indexer launch; with cand/floors set, also the fused top-k stage.
 ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, const void *q, const float *weights,
@@ -296,10 +292,16 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
   }
   uint32_t max_row_blocks = 1;
   for (uint32_t r = 0; r < p.rows; ++r) max_row_blocks = std::max(max_row_blocks, p.blk_begin[r + 1] - p.blk_begin[r]);
-  hipEvent_t start = nullptr, stop = nullptr;
-  take_indexer_timer(&start, &stop);
-  const hipError_t e =
-      ds::launch_indexer_score(a, max_row_blocks, cand != nullptr, static_cast<hipStream_t>(stream), start, stop);
+  if (t_timer_stamps != nullptr) {
+    const uint64_t need_elems = uint64_t(max_row_blocks) * p.rows * ds::kTimerStamps;
+    if (t_timer_elems < need_elems)
+      return fail("the indexer timing buffer holds %zu entries; this launch's %u x %u workgroups need %llu",
+                  t_timer_elems, max_row_blocks, p.rows, static_cast<unsigned long long>(need_elems));
+    a.stamps = t_timer_stamps;
+    t_timer_stamps = nullptr;
+    t_timer_elems = 0;
+  }
+  const hipError_t e = ds::launch_indexer_score(a, max_row_blocks, cand != nullptr, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
 }
 
@@ -772,12 +774,20 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
                                     attn_workspace, attn_workspace_bytes, out, out_elems, stream);
 }
 
-ds_status ds_rows_time_next_indexer(void *start_event, void *stop_event) {
-  DS_TRY(need(start_event, "start_event"));
-  DS_TRY(need(stop_event, "stop_event"));
-  t_timer_start = static_cast<hipEvent_t>(start_event);
-  t_timer_stop = static_cast<hipEvent_t>(stop_event);
+ds_status ds_rows_time_next_indexer(uint64_t *stamps, size_t stamps_elems) {
+  DS_TRY(need(stamps, "indexer timing stamps"));
+  t_timer_stamps = stamps;
+  t_timer_elems = stamps_elems;
   return DS_OK;
+}
+
+ds_status ds_rows_wall_clock_khz(int *khz) {
+  DS_TRY(need(khz, "khz"));
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ds::record_error(DS_ERR_DEVICE, "no current HIP device");
+  const hipError_t e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  return e == hipSuccess ? DS_OK : ds::record_error(DS_ERR_DEVICE, "the wall clock rate is unavailable (%s)",
+                                                     hipGetErrorString(e));
 }
 
 const char *ds_rows_last_error(void) { return g_error.c_str(); }

@@ -44,6 +44,8 @@ constexpr uint32_t kIdxWaveKeep = 24;
 constexpr uint32_t kIdxWaveCand = 32;
 constexpr uint32_t kIdxCand = (kIdxThreads / 64) * kIdxWaveCand;   // 128 per block
 constexpr uint32_t kIdxFloors = kIdxThreads / 64;                   // 4 per block
+constexpr uint32_t kTimerStamps = DS_TIMER_STAMPS_PER_WG;           // timing stamps per workgroup
+static_assert(kTimerStamps >= 1 + kIdxThreads / 64, "a start and one end per wave");
 
 struct IndexerArgs {
   const uint16_t *keys[kRowsMax];   // bf16 [kv_len, 128] per row
@@ -59,12 +61,11 @@ struct IndexerArgs {
   uint32_t blk_begin[kRowsMax + 1]; // first block of each row; [rows..] = total
   uint64_t *cand;                   // fused: kIdxCand keys per block (0 = none)
   uint64_t *floors;                 // fused: kIdxFloors floors per block (one per wave)
+  uint64_t *stamps;                 // timing (ds_rows_time_next_indexer) or nullptr: per workgroup of the
+                                    // grid, its start and each wave's end (wall clock)
 };
 // Grid (max_row_blocks, a.rows): workgroup (x, r) is row r's x-th block.
-// With start/stop events, the launch records its own start and end in them
-// (hipExtLaunchKernel).
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s,
-                                hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s);
 
 // ------------------------------------------------------------------ top-k
 // One selection level: every workgroup reduces a chunk of one row's

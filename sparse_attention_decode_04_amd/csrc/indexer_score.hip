@@ -47,8 +47,6 @@
 // best unwritten tie otherwise). The final top-k level uses the floors to
 // prove that no unkept key can reach the row's top 512, and selects from the
 // scores again when one could.
-#include <hip/hip_ext.h>
-
 #include "device_common.hpp"
 #include "ds_rows_internal.hpp"
 #include "select_common.hpp"
@@ -163,10 +161,20 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   uint64_t kbits = reinterpret_cast<uint64_t>(a.keys[r]), qbits = reinterpret_cast<uint64_t>(a.q),
            wbits = reinterpret_cast<uint64_t>(a.w), sbits = reinterpret_cast<uint64_t>(a.scores);
   uint64_t sstride = a.score_stride;
+  uint64_t tbits = reinterpret_cast<uint64_t>(a.stamps);
   // One use of them all: the compiler issues these scalar loads together and
   // waits once, rather than in dependent batches ahead of their first uses.
   asm volatile("" : "+s"(blk0), "+s"(blk1), "+s"(n), "+s"(visible), "+s"(qr), "+s"(kbits), "+s"(qbits), "+s"(wbits),
-               "+s"(sbits), "+s"(sstride));
+               "+s"(sbits), "+s"(sstride), "+s"(tbits));
+  // Timing stamps (ds_rows_time_next_indexer): this workgroup's start now,
+  // each wave's end where it leaves.
+  uint64_t *const stamps = tbits != 0 ? global_ptr<uint64_t>(tbits) +
+                                            static_cast<uint64_t>(blockIdx.y * gridDim.x + blockIdx.x) * kTimerStamps
+                                      : nullptr;
+  if (stamps != nullptr && threadIdx.x == 0) stamps[0] = wall_clock64();
+  auto stamp_end = [&]() {
+    if (stamps != nullptr && (threadIdx.x & 63) == 0) stamps[1 + (threadIdx.x >> 6)] = wall_clock64();
+  };
   const uint16_t *const keys = global_ptr<const uint16_t>(kbits);
   const uint32_t nblk = blk1 - blk0;
   const bool live = blockIdx.x < nblk;   // uniform
@@ -227,7 +235,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
 #pragma unroll
     for (int i = 0; i < 4; ++i) wt[m][i] = w_lds[16 * m + 4 * grp + i];
   }
-  if (!live || (!kFused && mine == 0)) return;   // (in the fused stage every wave of a row writes its floor)
+  if (!live || (!kFused && mine == 0)) {   // (in the fused stage every wave of a row writes its floor)
+    stamp_end();
+    return;
+  }
 
   // Tiles go in groups of 4: each lane keeps its head group's partial sum of
   // the group's tiles, then two lane-row swaps finish all four head sums at
@@ -280,21 +291,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
     }
     wave_candidates(a, fifo, kidx, block, wave, lane);
   }
+  stamp_end();
 }
 
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s,
-                                hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s) {
   const dim3 grid(max_row_blocks, a.rows);
-  if (start != nullptr) {
-    if (fused)
-      hipExtLaunchKernelGGL(indexer_score_kernel<true>, grid, dim3(kIdxThreads), 0, s, start, stop, 0, a);
-    else
-      hipExtLaunchKernelGGL(indexer_score_kernel<false>, grid, dim3(kIdxThreads), 0, s, start, stop, 0, a);
-  } else if (fused) {
+  if (fused)
     hipLaunchKernelGGL(indexer_score_kernel<true>, grid, dim3(kIdxThreads), 0, s, a);
-  } else {
+  else
     hipLaunchKernelGGL(indexer_score_kernel<false>, grid, dim3(kIdxThreads), 0, s, a);
-  }
   return hipGetLastError();
 }
 

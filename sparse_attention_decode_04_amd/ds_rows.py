@@ -29,7 +29,7 @@ FUNCTIONS = (
     "ds_rows_last_error", "ds_rows_version", "ds_rows_indexer_topk_workspace_bytes", "ds_rows_indexer_topk",
     "ds_rows_indexer_candidates", "ds_rows_compressor_state_elems", "ds_rows_compressor",
     "ds_rows_indexer_mq_scores_elems", "ds_rows_indexer_score_mq", "ds_rows_indexer_topk_attn",
-    "ds_rows_indexer_topk_attn_noalloc", "ds_rows_time_next_indexer",
+    "ds_rows_indexer_topk_attn_noalloc", "ds_rows_time_next_indexer", "ds_rows_wall_clock_khz",
 )
 
 
@@ -135,8 +135,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
               "ds_rows_compressor", "ds_rows_indexer_score_mq", "ds_rows_indexer_topk_attn",
               "ds_rows_indexer_topk_attn_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
-    lib.ds_rows_time_next_indexer.argtypes = [c_void_p, c_void_p]
+    lib.ds_rows_time_next_indexer.argtypes = [c_void_p, c_size_t]
     lib.ds_rows_time_next_indexer.restype = ctypes.c_int
+    lib.ds_rows_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    lib.ds_rows_wall_clock_khz.restype = ctypes.c_int
     lib.ds_rows_last_error.restype = ctypes.c_char_p
     lib.ds_rows_version.restype = ctypes.c_char_p
     _lib = lib
@@ -394,18 +396,32 @@ def compressor(t: CompressorRows, ratio, head_dim, eps, kv, score, ape, norm, ou
                                      aa, an, na, nn, oa, on, _stream(stream)))
 
 
-def time_next_indexer(start_event, stop_event):
-    """Arm the calling thread's next indexer launch to record its own start and
-    end in two HIP events (torch.cuda.Event objects with enable_timing=True, or
-    raw hipEvent_t handles as ints). A torch event gets its HIP event when it is
-    first recorded, so it is recorded once here if it has none yet."""
-    def handle(ev):
-        if isinstance(ev, int):
-            return ev
-        if not ev.cuda_event:
-            ev.record()
-        return ev.cuda_event
-    _check(load().ds_rows_time_next_indexer(c_void_p(handle(start_event)), c_void_p(handle(stop_event))))
+TIMER_STAMPS_PER_WG = 8
+
+
+def time_next_indexer(stamps):
+    """Arm the calling thread's next indexer launch to write its workgroups'
+    wall-clock stamps into `stamps` (a zero-filled int64 device tensor of at
+    least 8 entries per workgroup: [start, end of wave 0..3, unused x 3])."""
+    addr, n = _dev(stamps, 8)
+    _check(load().ds_rows_time_next_indexer(addr, n))
+
+
+def wall_clock_khz() -> int:
+    """Frequency of the device wall clock the timing stamps count, in kHz."""
+    v = ctypes.c_int(0)
+    _check(load().ds_rows_wall_clock_khz(ctypes.byref(v)))
+    return v.value
+
+
+def indexer_span_ticks(stamps) -> int:
+    """Smallest start to largest end (wall-clock ticks) of a timed launch's
+    stamps (host copy, int64 [..., 8]; workgroups that wrote none are 0)."""
+    import numpy as np
+    a = np.asarray(stamps).reshape(-1, TIMER_STAMPS_PER_WG)
+    starts = a[:, 0][a[:, 0] > 0]
+    ends = a[:, 1:5][a[:, 1:5] > 0]
+    return int(ends.max() - starts.min())
 
 
 def version() -> str:

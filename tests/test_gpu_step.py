@@ -278,9 +278,11 @@ def test_step_permuted_row_subsets_match_full_launch():
 
 @pytest.mark.parametrize("cid", [1, 2])
 def test_timed_indexer_launch_changes_nothing(cid):
-    """ds_rows_time_next_indexer: the armed step's indexer records its own
-    start and end (a positive duration below a second), the outputs are those
-    of an unarmed step bit for bit, and the arm is used up by that launch."""
+    """ds_rows_time_next_indexer: the armed step's indexer writes a start and
+    four wave ends per workgroup (ends after starts, a span below a second),
+    the outputs are those of an unarmed step bit for bit, the arm is used up
+    by that launch, and a buffer too small for the grid is refused before
+    anything is enqueued."""
     inp = I.make_config(cid)
     say(f"config {cid}: timed indexer launch")
     run = DeviceRows(DeviceInputs(inp))
@@ -289,16 +291,34 @@ def test_timed_indexer_launch_changes_nothing(cid):
     ref_out, ref_idx, ref_sc = run.out.clone(), run.indices.clone(), run.scores.clone()
     run.out.zero_()
     run.indices.fill_(-7)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ds.time_next_indexer(start, stop)
+    wgs = -(-max(inp.kv_len) // 1024) * inp.rows
+    stamps = torch.zeros(wgs * ds.TIMER_STAMPS_PER_WG, dtype=torch.int64, device="cuda")
+    ds.time_next_indexer(stamps)
     run.step_one()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop)
-    assert 0.0 < ms < 1000.0, ms
+    st = stamps.cpu().numpy().reshape(wgs, ds.TIMER_STAMPS_PER_WG)
+    assert (st[:, 0] > 0).all()                       # every workgroup started
+    assert (st[:, 1:5] >= st[:, :1]).all()            # ends after starts
+    assert (st[:, 5:] == 0).all()
+    span = ds.indexer_span_ticks(st)
+    assert 0 < span < 10 ** 8, span                   # below a second at 100 MHz
     assert torch.equal(run.out, ref_out)
     assert torch.equal(run.indices, ref_idx)
     assert torch.equal(run.scores, ref_sc)
-    # The arm was consumed: a later step leaves the events as they were.
+    # The arm was used up: a later step writes no stamps.
+    stamps.zero_()
     run.step_one()
     torch.cuda.synchronize()
-    assert start.elapsed_time(stop) == ms
+    assert int(stamps.abs().sum()) == 0
+    # Too small for the grid: refused, outputs untouched, the arm stays.
+    small = torch.zeros(ds.TIMER_STAMPS_PER_WG, dtype=torch.int64, device="cuda")
+    ds.time_next_indexer(small)
+    if wgs > 1:
+        run.out.zero_()
+        with pytest.raises(ds.DsRowsError, match="indexer timing buffer"):
+            run.step_one()
+        torch.cuda.synchronize()
+        assert int(run.out.abs().sum()) == 0 and int(small.abs().sum()) == 0
+        ds.time_next_indexer(stamps)   # replace the arm for the next call
+        run.step_one()
+        torch.cuda.synchronize()
