@@ -70,7 +70,13 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   // the workgroup's kAttnDimChunk.
   constexpr int kVec = kAttnDimChunk / 4 / 4;   // f32x4 per thread
   const uint32_t r = blockIdx.y;
-  const uint32_t dc = blockIdx.x;
+  // Workgroup x of a row runs on XCD x % 8 (the grid's rows are whole
+  // multiples of 8 workgroups). XCD k takes the row's dim chunks 4k .. 4k + 3:
+  // 64 consecutive dims, two whole 128-byte lines of every partial row, so
+  // each line is fetched into one L2 only (with neighbouring chunks on
+  // different XCDs every line was fetched twice, once per half).
+  static_assert(kDim / kAttnDimChunk == 4 * kXcds, "four dim chunks per XCD");
+  const uint32_t dc = 4 * (blockIdx.x % kXcds) + blockIdx.x / kXcds;
   // The row's arguments in one batch of scalar loads (one wait).
   uint32_t rows = a.rows, nch = a.chunks[r], q_row = a.q_row[r];
   uint64_t sbits = reinterpret_cast<uint64_t>(a.stats), sbase = a.stat_base[r];
