@@ -391,12 +391,17 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
       }
     }
     // D lane l of tile nt: feature kFpw wave + 16 nt + l % 16, heads 4 (l / 16) + i.
+    // Non-temporal stores: the chunk outputs are read once, by the combine
+    // kernel, from memory; stored as ordinary write-back lines they waited
+    // in L2 for the end-of-kernel write-back (8 MiB at 8 rows x 512 slots),
+    // which the step then paid for after the last workgroup (34.5 -> 33.8 us
+    // per step at 8 rows x 32768 keys).
     float *dst = a.opart + (static_cast<uint64_t>(c) * kHeads + kHg * hg) * kDim;
   #pragma unroll
     for (int nt = 0; nt < kNt; ++nt)
   #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dst[(4 * lg + i) * kDim + kFpw * wave + 16 * nt + li] = o[nt][i];
+        __builtin_nontemporal_store(o[nt][i], &dst[(4 * lg + i) * kDim + kFpw * wave + 16 * nt + li]);
   }
 }
 

@@ -60,10 +60,8 @@ struct TopkShared {
   __attribute__((aligned(16))) uint32_t wsum[kWaves];
   __attribute__((aligned(16))) uint32_t wmax[kWaves];
   __attribute__((aligned(16))) uint32_t wcount[kWaves];
-  __attribute__((aligned(16))) uint32_t wvalid[kWaves];     // per-wave candidate statistics
-  __attribute__((aligned(16))) uint32_t wmin1[kWaves];
-  __attribute__((aligned(16))) uint32_t wmaxo[kWaves];
-  __attribute__((aligned(16))) uint64_t wfloor[kWaves];
+  uint64_t s_floor;                                          // candidate statistics of the level,
+  uint32_t s_total, s_min1, s_max;                           // combined by LDS atomics
   uint64_t wkmin[kWaves], wkmax[kWaves];                     // radix fallback: key range per wave
   uint32_t count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
 };
@@ -560,7 +558,16 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
 
   sh.hist[tid] = 0;
   sh.cursor[tid] = 0;
-  if (tid == 0) { sh.thr = 0xFFFFFFFFu; sh.count = 0; sh.lo = 0; sh.viol = 0; }
+  if (tid == 0) {
+    sh.thr = 0xFFFFFFFFu;
+    sh.count = 0;
+    sh.lo = 0;
+    sh.viol = 0;
+    sh.s_total = 0;
+    sh.s_min1 = 0xFFFFFFFFu;
+    sh.s_max = 0;
+    sh.s_floor = 0;
+  }
 
   // Candidate e of this thread sits at position begin + tid + 1024 * e.
   // Loads are unconditional, from positions clamped into the row (every row
@@ -600,6 +607,9 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
       for (uint32_t b = tid + kTopkThreads; b < lr.floor_count; b += kTopkThreads) floor_hi = max(floor_hi, lr.floors[b]);
     }
   }
+  // The statistics' starting values are in place before any wave adds to
+  // them (the waves pass this barrier while their loads are in flight).
+  __syncthreads();
   auto run = [&](const auto &c) {
     // Count and extreme score bits of the valid keys. A missing key has high
     // word 0 (every valid key's is nonzero), so it never raises the maximum
@@ -612,8 +622,10 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
       omin1 = min(omin1, o - 1u);
       omax = max(omax, o);
     }
-    // Per-wave totals in LDS slots, combined by every thread after one
-    // barrier (which also publishes the LDS initialisation above).
+    // Per-wave totals, combined across the waves by one LDS atomic per
+    // statistic from each wave; every thread reads the four results after a
+    // barrier (combining sixteen per-wave slots in every thread cost more
+    // than the rest of this phase).
     nvalid = wave_sum(nvalid);
     omin1 = wave_min(omin1);
     omax = wave_max(omax);
@@ -624,27 +636,14 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
       wfloor = (static_cast<uint64_t>(hi) << 32) | lo;
     }
     if (lane == 0) {
-      sh.wvalid[wave] = nvalid;
-      sh.wmin1[wave] = omin1;
-      sh.wmaxo[wave] = omax;
-      sh.wfloor[wave] = wfloor;
+      atomicAdd(&sh.s_total, nvalid);
+      atomicMin(&sh.s_min1, omin1);
+      atomicMax(&sh.s_max, omax);
+      if (check_row) atomicMax(reinterpret_cast<unsigned long long *>(&sh.s_floor), static_cast<unsigned long long>(wfloor));
     }
     __syncthreads();
-    uint32_t total = 0, min1 = 0xFFFFFFFFu, gmax = 0;
-    uint64_t max_floor = 0;
-#pragma unroll
-    for (int v = 0; v < kWaves / 4; ++v) {
-      const u32x4 n4 = reinterpret_cast<const u32x4 *>(sh.wvalid)[v];
-      const u32x4 l4 = reinterpret_cast<const u32x4 *>(sh.wmin1)[v];
-      const u32x4 h4 = reinterpret_cast<const u32x4 *>(sh.wmaxo)[v];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        total += n4[k];
-        min1 = min(min1, l4[k]);
-        gmax = max(gmax, h4[k]);
-        max_floor = max(max_floor, sh.wfloor[4 * v + k]);
-      }
-    }
+    const uint32_t total = sh.s_total, min1 = sh.s_min1, gmax = sh.s_max;
+    const uint64_t max_floor = sh.s_floor;
     const uint32_t need = min(total, static_cast<uint32_t>(kTopK));
     const uint32_t gmin = min1 + 1u;
 
