@@ -459,7 +459,7 @@ def main():
         the loop (the armed launch is an ordinary one plus a few stores per
         workgroup). Mean and median span in ms, and the loop's mean call time."""
         inp_ = runs[0].dev.inp
-        per = -(-max(inp_.kv_len) // 1024) * inp_.rows * ds.TIMER_STAMPS_PER_WG
+        per = -(-max(inp_.kv_len) // 64) * inp_.rows * ds.TIMER_STAMPS_PER_WG   # fits any block size
         buf = torch.zeros(n * per, dtype=torch.int64, device="cuda")
         views = [buf[i * per:(i + 1) * per] for i in range(n)]
         khz = ds.wall_clock_khz()

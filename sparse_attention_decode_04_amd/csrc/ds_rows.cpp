@@ -106,6 +106,23 @@ struct IndexerPlan {
 };
 
 constexpr uint32_t kIndexerKeysPerBlock = 1024;
+// The plain score kernel (no fused stage) takes smaller blocks when a call has
+// few keys: the largest power of two from 1024 down to 64 keys that gives the
+// call at least one workgroup per compute unit. A workgroup streams its keys
+// at a rate set by its own loads in flight, so a call with fewer, longer
+// blocks than compute units (one 1024-key row, or a few long rows among short
+// ones) leaves most of the GPU idle.
+constexpr uint32_t kPlainMinKeysPerBlock = 64;
+constexpr uint64_t kPlainMinBlocks = 256;
+uint32_t plain_keys_per_block(const ds_indexer_rows *rows, uint32_t nrows) {
+  uint32_t kpb = kIndexerKeysPerBlock;
+  for (; kpb > kPlainMinKeysPerBlock; kpb /= 2) {
+    uint64_t blocks = 0;
+    for (uint32_t r = 0; r < nrows; ++r) blocks += div_up(rows->kv_len[r], kpb);
+    if (blocks >= kPlainMinBlocks) break;
+  }
+  return kpb;
+}
 
 // One indexer row's fields: length, position, causal length and index range.
 // Returns the keys visible to the row's query in *visible.
@@ -280,10 +297,17 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
   a.scores = scores;
   a.score_stride = p.max_kv;
   a.rows = p.rows;
-  a.keys_per_block = kIndexerKeysPerBlock;
   a.cand = cand;
   a.floors = floors;
-  for (uint32_t r = 0; r <= ds::kRowsMax; ++r) a.blk_begin[r] = p.blk_begin[r];
+  if (cand != nullptr) {
+    // The fused stage's candidate and floor layout is per 1024-key block.
+    a.keys_per_block = kIndexerKeysPerBlock;
+    for (uint32_t r = 0; r <= ds::kRowsMax; ++r) a.blk_begin[r] = p.blk_begin[r];
+  } else {
+    a.keys_per_block = plain_keys_per_block(rows, p.rows);
+    for (uint32_t r = 0; r < ds::kRowsMax; ++r)
+      a.blk_begin[r + 1] = a.blk_begin[r] + (r < p.rows ? div_up(rows->kv_len[r], a.keys_per_block) : 0);
+  }
   for (uint32_t r = 0; r < p.rows; ++r) {
     a.keys[r] = static_cast<const uint16_t *>(rows->keys[r]);
     a.kv_len[r] = rows->kv_len[r];
@@ -291,7 +315,7 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
     a.q_row[r] = rows->q_row[r];
   }
   uint32_t max_row_blocks = 1;
-  for (uint32_t r = 0; r < p.rows; ++r) max_row_blocks = std::max(max_row_blocks, p.blk_begin[r + 1] - p.blk_begin[r]);
+  for (uint32_t r = 0; r < p.rows; ++r) max_row_blocks = std::max(max_row_blocks, a.blk_begin[r + 1] - a.blk_begin[r]);
   if (t_timer_stamps != nullptr) {
     const uint64_t need_elems = uint64_t(max_row_blocks) * p.rows * ds::kTimerStamps;
     if (t_timer_elems < need_elems)

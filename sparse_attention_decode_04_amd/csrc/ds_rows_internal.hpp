@@ -54,7 +54,7 @@ struct IndexerArgs {
   float *scores;                    // f32 [rows, score_stride]
   uint64_t score_stride;
   uint32_t rows;
-  uint32_t keys_per_block;          // multiple of 4 * kIdxTile
+  uint32_t keys_per_block;          // 1024 with the fused stage; the plain kernel 64 .. 1024 (a power of 2)
   uint32_t kv_len[kRowsMax];
   uint32_t visible[kRowsMax];       // min(kv_len, (start_pos + 1) / 4)
   uint32_t q_row[kRowsMax];

@@ -291,7 +291,15 @@ def test_timed_indexer_launch_changes_nothing(cid):
     ref_out, ref_idx, ref_sc = run.out.clone(), run.indices.clone(), run.scores.clone()
     run.out.zero_()
     run.indices.fill_(-7)
-    wgs = -(-max(inp.kv_len) // 1024) * inp.rows
+    # The grid the header states: 1024-key blocks with the fused stage (every
+    # row has 16384 visible keys or more), else the largest power of two from
+    # 1024 down to 64 that gives the call at least 256 blocks.
+    visible = [min(n, (sp + 1) // 4) for n, sp in zip(inp.kv_len, inp.start_pos)]
+    block = 1024
+    if min(visible) < 16384:
+        while block > 64 and sum(-(-n // block) for n in inp.kv_len) < 256:
+            block //= 2
+    wgs = -(-max(inp.kv_len) // block) * inp.rows
     stamps = torch.zeros(wgs * ds.TIMER_STAMPS_PER_WG, dtype=torch.int64, device="cuda")
     ds.time_next_indexer(stamps)
     run.step_one()
