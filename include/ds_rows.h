@@ -168,8 +168,9 @@ ds_status ds_rows_topk(const ds_indexer_rows *rows,
  * pages' block stage keeps each 1024-key block's best 512). Writes the same
  * scores and the same indices as the two calls, bit for bit.
  * Each wave of the indexer keeps, of its 256 keys, those at or above a
- * threshold that keeps 24 to 32 of them (every valid key when it has at most
- * 32) and a floor below which lie all of its other keys; the top-k levels then
+ * threshold that keeps 24 to 32 of them (6 to 8 when every row has at least
+ * 262144 visible keys; every valid key when it has at most that many) and a
+ * floor below which lie all of its other keys; the top-k levels then
  * select from those candidates, and a row's result stands only if no floor
  * lies above its 512th key. Otherwise (heavy ties, scores sorted by
  * position) the row is selected again from its scores in the same call,
@@ -333,8 +334,9 @@ ds_status ds_rows_sparse_attn_direct(const ds_sparse_rows *rows,
  * deepseek_sparse_attention_score_rows_bf16).
  * When ds_rows_indexer_topk would keep the first selection stage in the
  * indexer (every row has at least 16384 visible keys) and each row has at
- * most 8192 candidates (up to 65536 keys), the final selection level runs
- * inside the attention's workgroups: each repeats its row's selection and
+ * most 16384 candidates (up to 131072 keys, or 524288 when every row has at
+ * least 262144 visible keys), the final selection level runs inside the
+ * attention's workgroups: each repeats its row's selection and
  * reads its slots' indices from LDS, which removes a kernel boundary and the
  * attention's index load. When instead every row has at most 16384 visible
  * keys, the score kernel runs alone and the one selection level, over the

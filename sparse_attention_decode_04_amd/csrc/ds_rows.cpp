@@ -199,6 +199,21 @@ bool fused_rows(const IndexerPlan &p) {
   return true;
 }
 
+// The fused stage's candidates per wave: 8 (of 256 keys, keeping 6 to 8)
+// when every row has at least 262144 visible keys, else 32 (keeping 24 to
+// 32). A wave holds on average 512 * 256 / visible of its row's top 512, at
+// most 0.5 past 262144 keys; that more than 6 of them fall in one wave (which
+// sends the row to the reselection from scores) then has a chance of about
+// 1e-3 per row at 262144 keys and under 1e-6 at 1M. The smaller budget
+// leaves a row of up to 512K keys at most 16384 candidates, which the final
+// selection takes at once.
+uint32_t fused_wave_cand(const IndexerPlan &p) {
+  for (uint32_t r = 0; r < p.rows; ++r)
+    if (p.visible[r] < ds::kIdxLongRow) return ds::kIdxWaveCand;
+  return ds::kIdxWaveCandLong;
+}
+
+
 // Enough for either path (and for ds_rows_indexer_candidates).
 uint64_t indexer_topk_workspace_bytes(const IndexerPlan &p) {
   return std::max(fused_workspace_bytes(p), topk_workspace_bytes(p));
@@ -325,7 +340,8 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
     t_timer_stamps = nullptr;
     t_timer_elems = 0;
   }
-  const hipError_t e = ds::launch_indexer_score(a, max_row_blocks, cand != nullptr, static_cast<hipStream_t>(stream));
+  const hipError_t e = ds::launch_indexer_score(a, max_row_blocks, cand != nullptr ? fused_wave_cand(p) : 0,
+                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
 }
 
@@ -339,6 +355,19 @@ struct TopkInput {
   uint64_t base[ds::kRowsMax] = {};
 };
 
+// The fused indexer's candidates: 4 waves x C slots per 1024-key block.
+TopkInput fused_input(const IndexerPlan &p, const uint64_t *cand, const uint64_t *floors) {
+  TopkInput in{};
+  in.lists = cand;
+  in.floors = floors;
+  const uint32_t per_block = ds::kIdxFloors * fused_wave_cand(p);
+  for (uint32_t r = 0; r < p.rows; ++r) {
+    in.count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * per_block;
+    in.base[r] = uint64_t(p.blk_begin[r]) * per_block;
+  }
+  return in;
+}
+
 // Selection levels until every row has one list; the last writes indices.
 // With attn set, the pass over lists in which every row that is still
 // selecting reaches its final level runs inside the attention's workgroups
@@ -349,14 +378,12 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
                           const ds::AttnArgs *attn = nullptr, uint32_t attn_chunks = 0, bool *attn_done = nullptr) {
   uint64_t *bank[2] = {bank0, bank1};
   const bool from_lists = in.lists != nullptr;
-  const uint32_t first_chunk = from_lists ? ds::kTopkChunkLater : ds::kTopkChunkFirst;
   uint32_t count[ds::kRowsMax] = {}, chunks[ds::kRowsMax] = {};
   uint64_t in_base[ds::kRowsMax] = {};
   bool done[ds::kRowsMax] = {};
   for (uint32_t r = 0; r < p.rows; ++r) {
     count[r] = in.count[r];
     in_base[r] = in.base[r];
-    chunks[r] = std::max<uint32_t>(1, div_up(count[r], first_chunk));
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   for (uint32_t level = 0;; ++level) {
@@ -369,6 +396,17 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
     a.rows = p.rows;
     a.from_scores = (level == 0 && !from_lists) ? 1 : 0;
     a.floors = in.floors;
+    // Candidates per thread, and so the chunk size: the smallest of 4, 8 and
+    // 16 that holds every row still selecting, which makes this the final
+    // level; otherwise chunks of 32768 scores or 8192 list keys.
+    uint32_t max_count = 0;
+    for (uint32_t r = 0; r < p.rows; ++r)
+      if (!done[r]) max_count = std::max(max_count, count[r]);
+    a.per_thread = a.from_scores ? ds::kTopkPerThreadFirst : ds::kTopkPerThreadLater;
+    for (uint32_t per : {4u, 8u, 16u})
+      if (max_count <= ds::kTopkThreads * per) { a.per_thread = per; break; }
+    for (uint32_t r = 0; r < p.rows; ++r)
+      if (!done[r]) chunks[r] = std::max<uint32_t>(1, div_up(count[r], uint64_t(ds::kTopkThreads) * a.per_thread));
     uint32_t blocks = 0;
     uint64_t out_elems = 0;
     for (uint32_t r = 0; r < ds::kRowsMax; ++r) {
@@ -394,18 +432,6 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
       blocks += chunks[r];
     }
     a.blk_begin[ds::kRowsMax] = blocks;
-    uint32_t max_count = 0;
-    for (uint32_t r = 0; r < p.rows; ++r)
-      if (!done[r]) max_count = std::max(max_count, count[r]);
-    if (a.from_scores) {
-      // The first level reads scores: short rows take a chunk sized to them
-      // (every row then fits one chunk; 32 per thread otherwise).
-      a.per_thread = ds::kTopkPerThreadFirst;
-      for (uint32_t per : {4u, 8u, 16u})
-        if (max_count <= ds::kTopkThreads * per) { a.per_thread = per; break; }
-    } else {
-      a.per_thread = max_count <= ds::kTopkThreads * 4 ? 4 : ds::kTopkPerThreadLater;
-    }
     bool every_row_final = true;
     for (uint32_t r = 0; r < p.rows; ++r) every_row_final &= done[r] || chunks[r] == 1;
     if (attn && !a.from_scores && every_row_final) {
@@ -425,7 +451,6 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
       all = false;
       in_base[r] = a.out_base[r];
       count[r] = chunks[r] * DS_TOP_K;
-      chunks[r] = std::max<uint32_t>(1, div_up(count[r], ds::kTopkChunkLater));
     }
     if (all) break;
   }
@@ -549,15 +574,7 @@ ds_status ds_rows_indexer_topk(const ds_indexer_rows *rows, const void *q, size_
   uint64_t *floors = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p));
   uint64_t *bank = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
   DS_TRY(launch_indexer(rows, p, q, weights, scores, cand, floors, stream));
-
-  TopkInput in{};
-  in.lists = cand;
-  in.floors = floors;
-  for (uint32_t r = 0; r < p.rows; ++r) {
-    in.count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand;
-    in.base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
-  }
-  return run_topk_levels(rows, p, scores, in, bank, bank + p.fused_bank, indices, stream);
+  return run_topk_levels(rows, p, scores, fused_input(p, cand, floors), bank, bank + p.fused_bank, indices, stream);
 }
 
 ds_status ds_rows_gather(const ds_sparse_rows *rows, const int32_t *indices, size_t indices_elems, void *gathered,
@@ -779,12 +796,7 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
     bank0 = reinterpret_cast<uint64_t *>(ws + fused_cand_bytes(p) + fused_floor_bytes(p));
     bank1 = bank0 + p.fused_bank;
     DS_TRY(launch_indexer(irows, p, idx_q, weights, scores, cand, floors, stream));
-    in.lists = cand;
-    in.floors = floors;
-    for (uint32_t r = 0; r < p.rows; ++r) {
-      in.count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxCand;
-      in.base[r] = uint64_t(p.blk_begin[r]) * ds::kIdxCand;
-    }
+    in = fused_input(p, cand, floors);
   } else {
     bank0 = static_cast<uint64_t *>(idx_workspace);
     bank1 = bank0 + p.topk_bank;

@@ -34,15 +34,18 @@ constexpr int kIdxThreads = 256;
 constexpr int kIdxTile = 16;
 constexpr uint32_t kIdxMaxKeysPerBlock = 1024;
 // Fused top-k stage (ds_rows_indexer_topk): every wave of the indexer also
-// writes up to kIdxWaveCand candidate keys of its own 256 keys (those at or
-// above a threshold keeping kIdxWaveKeep to kIdxWaveCand of them; every valid
-// key when it has at most kIdxWaveCand; when ties at its threshold T overflow,
-// the keys above T and the lowest-index ties) and a 64-bit floor, a key that
-// no unwritten key of the wave exceeds: 0 when it wrote every valid key,
-// T << 32 after a clean threshold, else the key of its best unwritten tie.
-constexpr uint32_t kIdxWaveKeep = 24;
+// writes up to C candidate keys of its own 256 keys (those at or above a
+// threshold keeping 3C/4 to C of them; every valid key when it has at most C;
+// when ties at its threshold T overflow, the keys above T and the
+// lowest-index ties) and a 64-bit floor, a key that no unwritten key of the
+// wave exceeds: 0 when it wrote every valid key, T << 32 after a clean
+// threshold, else the key of its best unwritten tie. C = kIdxWaveCand, or
+// kIdxWaveCandLong when every row of the call has at least kIdxLongRow
+// visible keys: a row's top 512 then averages at most half a key per wave.
 constexpr uint32_t kIdxWaveCand = 32;
-constexpr uint32_t kIdxCand = (kIdxThreads / 64) * kIdxWaveCand;   // 128 per block
+constexpr uint32_t kIdxWaveCandLong = 8;
+constexpr uint32_t kIdxLongRow = 262144;
+constexpr uint32_t kIdxCand = (kIdxThreads / 64) * kIdxWaveCand;   // candidate slots per block (at most)
 constexpr uint32_t kIdxFloors = kIdxThreads / 64;                   // 4 per block
 constexpr uint32_t kTimerStamps = DS_TIMER_STAMPS_PER_WG;           // timing stamps per workgroup
 static_assert(kTimerStamps >= 1 + kIdxThreads / 64, "a start and one end per wave");
@@ -59,21 +62,25 @@ struct IndexerArgs {
   uint32_t visible[kRowsMax];       // min(kv_len, (start_pos + 1) / 4)
   uint32_t q_row[kRowsMax];
   uint32_t blk_begin[kRowsMax + 1]; // first block of each row; [rows..] = total
-  uint64_t *cand;                   // fused: kIdxCand keys per block (0 = none)
+  uint64_t *cand;                   // fused: 4 C keys per block (0 = none)
   uint64_t *floors;                 // fused: kIdxFloors floors per block (one per wave)
   uint64_t *stamps;                 // timing (ds_rows_time_next_indexer) or nullptr: per workgroup of the
                                     // grid, its start and each wave's end (wall clock)
 };
 // Grid (max_row_blocks, a.rows): workgroup (x, r) is row r's x-th block.
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s);
+// wave_cand: 0 for the plain kernel, else the fused stage's C (kIdxWaveCand
+// or kIdxWaveCandLong).
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, uint32_t wave_cand, hipStream_t s);
 
 // ------------------------------------------------------------------ top-k
 // One selection level: every workgroup reduces a chunk of one row's
 // candidates to that chunk's best 512, sorted best first. Candidates are
 // 64-bit keys (order-preserving score bits << 32 | ~index); 0 = no candidate.
 // The first level reads scores (chunks of 32768); later levels read the
-// previous level's 512-key lists or the fused indexer's candidates (chunks of
-// 8192 keys).
+// previous level's 512-key lists or the fused indexer's candidates: whole,
+// as the final level, when every row still selecting has at most 16384 of
+// them (16 per thread; 32 64-bit keys per thread would not fit the
+// registers), else in chunks of 8192 keys.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkPerThreadFirst = 32;
 constexpr int kTopkPerThreadLater = 8;
@@ -89,8 +96,9 @@ struct TopkLevelArgs {
   int32_t *indices;                 // final output
   uint32_t rows;
   uint32_t from_scores;             // 1 on the first level
-  uint32_t per_thread;              // candidates per thread: first level 4/8/16 when every row has <= 1024x that
-                                    // many scores, else 32; later levels 4 when every row has <= 4096, else 8
+  uint32_t per_thread;              // candidates per thread: 4/8/16, the smallest that holds every row's
+                                    // candidates (a final level), else 32 on the first level (scores) and 8
+                                    // on later ones (lists), in chunks
   uint32_t final_mask;              // bit r: this level emits row r's indices
   uint32_t count[kRowsMax];         // candidates of row r at this level
   uint64_t in_base[kRowsMax];       // element offset of row r's input in `in`

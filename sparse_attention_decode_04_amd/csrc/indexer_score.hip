@@ -37,11 +37,12 @@
 // (deepseek_indexer_topk_block_rows_i32). Here every wave keeps, from the 256
 // scores it just computed (still in its registers: after each group of 4
 // tiles every lane holds one score, lane row g that of tile g), only the
-// keys at or above a threshold T that keeps 24 to 32 of them: a search over
-// T's bits with ballot counts, two bits per step and stopping at the first T
-// in range, finds it without LDS or barriers. When ties at the 24th best
+// keys at or above a threshold T that keeps 3C/4 to C of them (C = 32, or 8
+// when every row has at least 262144 visible keys): a search over T's bits
+// with ballot counts, two bits per step and stopping at the first T in
+// range, finds it without LDS or barriers. When ties at the (3C/4)-th best
 // score bits T leave no such threshold, it keeps every key above T and, of
-// the keys tied at T, the lowest indices (ties rank by lower index) up to 32
+// the keys tied at T, the lowest indices (ties rank by lower index) up to C
 // in all. It writes those keys and a 64-bit floor: a key no better than any
 // key it did not write (T << 32 after a clean threshold; the exact key of its
 // best unwritten tie otherwise). The final top-k level uses the floors to
@@ -64,14 +65,18 @@ static_assert(kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile <= 16, "tiles 
 static_assert((kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile + kIdxRing - 1) / kIdxRing * (kIdxRing / 4) <= 4,
               "groups of 4 tiles per wave fit the queue");
 
-// One wave's candidates (fused stage, see above): o[e] are the score bits
-// (0 = not valid) of the lane's four queued keys, kidx[e] their key indices.
-// Key indices increase with (3 - e, lane): e = 3 holds the wave's first group
-// of tiles, and within a group lane row g holds tile g of the group.
+// One wave's candidates (fused stage, see above), kCand of them at most:
+// o[e] are the score bits (0 = not valid) of the lane's four queued keys,
+// kidx[e] their key indices. Key indices increase with (3 - e, lane): e = 3
+// holds the wave's first group of tiles, and within a group lane row g holds
+// tile g of the group.
+template <uint32_t kCand>
 __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint32_t (&o)[4],
                                                 const uint32_t (&kidx)[4], uint32_t block, uint32_t wave,
                                                 uint32_t lane) {
-  const uint64_t slot0 = static_cast<uint64_t>(block) * kIdxCand + wave * kIdxWaveCand;
+  constexpr uint32_t kKeep = kCand * 3 / 4;
+  static_assert(kCand <= 64 && kKeep >= 1, "one slot per lane");
+  const uint64_t slot0 = static_cast<uint64_t>(block) * (kIdxThreads / 64) * kCand + wave * kCand;
   const uint64_t floor_at = static_cast<uint64_t>(block) * kIdxFloors + wave;
   auto count_ge = [&](uint32_t t) -> uint32_t {   // keys of the wave with score bits >= t
     uint32_t c = 0;
@@ -82,25 +87,25 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
   const uint32_t nvalid = count_ge(1u);
   uint32_t thr = 1;   // keep every valid key
   uint32_t kept = nvalid;
-  if (nvalid > kIdxWaveCand) {
+  if (nvalid > kCand) {
     // T is built from the top two bits at a time (three candidate values per
     // step, whose counts are independent and overlap in latency), each time
-    // taking the largest value that still has at least kIdxWaveKeep keys at
+    // taking the largest value that still has at least kKeep keys at
     // or above it. It stops as soon as the accepted T keeps at most
-    // kIdxWaveCand keys; otherwise it ends at the kIdxWaveKeep-th best score
-    // bits. Any T that keeps at most kIdxWaveCand keys is a valid floor: the
+    // kCand keys; otherwise it ends at the kKeep-th best score
+    // bits. Any T that keeps at most kCand keys is a valid floor: the
     // final level's check compares the floors with its 512th key, so which
-    // one is taken changes no index. If none keeps at most kIdxWaveCand, T
-    // ends as the kIdxWaveKeep-th best score bits (ties at T overflow).
+    // one is taken changes no index. If none keeps at most kCand, T
+    // ends as the kKeep-th best score bits (ties at T overflow).
     thr = 0;
-    kept = 256;   // count_ge(0); replaced at the first accepted step (count_ge(1) = nvalid > kIdxWaveKeep)
+    kept = 256;   // count_ge(0); replaced at the first accepted step (count_ge(1) = nvalid > kKeep)
     for (int b = 30; b >= 0; b -= 2) {
       const uint32_t t1 = thr | (1u << b), t2 = thr | (2u << b), t3 = thr | (3u << b);
       const uint32_t n1 = count_ge(t1), n2 = count_ge(t2), n3 = count_ge(t3);
-      if (n3 >= kIdxWaveKeep) { thr = t3; kept = n3; }
-      else if (n2 >= kIdxWaveKeep) { thr = t2; kept = n2; }
-      else if (n1 >= kIdxWaveKeep) { thr = t1; kept = n1; }
-      if (kept <= kIdxWaveCand) break;   // uniform
+      if (n3 >= kKeep) { thr = t3; kept = n3; }
+      else if (n2 >= kKeep) { thr = t2; kept = n2; }
+      else if (n1 >= kKeep) { thr = t1; kept = n1; }
+      if (kept <= kCand) break;   // uniform
     }
   }
   auto prefix = [](uint64_t mask) {   // set lanes of `mask` below this lane
@@ -112,12 +117,12 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
   // ties in key-index order (e = 3 .. 0, lanes ascending).
   bool take[4];
   uint64_t floor = static_cast<uint64_t>(thr) << 32;   // after a clean threshold
-  if (kept <= kIdxWaveCand) {
+  if (kept <= kCand) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) take[e] = o[e] >= thr;
     if (kept == nvalid) floor = 0;
   } else {
-    uint32_t room = kIdxWaveCand - count_ge(thr + 1);   // slots left for ties at T (> 0)
+    uint32_t room = kCand - count_ge(thr + 1);   // slots left for ties at T (> 0)
     uint32_t first_unkept = 0xFFFFFFFFu;                // index of the best unwritten tie
 #pragma unroll
     for (int e = 3; e >= 0; --e) {
@@ -131,7 +136,7 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
       const uint32_t n = static_cast<uint32_t>(__popcll(m));
       room = n >= room ? 0u : room - n;
     }
-    kept = kIdxWaveCand;
+    kept = kCand;
     floor = (static_cast<uint64_t>(thr) << 32) | static_cast<uint32_t>(~first_unkept);
   }
   uint32_t base = 0;
@@ -142,12 +147,15 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
     if (take[e]) a.cand[slot0 + pos] = (static_cast<uint64_t>(o[e]) << 32) | static_cast<uint32_t>(~kidx[e]);
     base += static_cast<uint32_t>(__popcll(mask));
   }
-  if (lane >= kept && lane < kIdxWaveCand) a.cand[slot0 + lane] = 0;   // unused slots
+  if (lane >= kept && lane < kCand) a.cand[slot0 + lane] = 0;   // unused slots
   if (lane == 0) a.floors[floor_at] = floor;
 }
 
-template <bool kFused>
+// kCand: 0 for the plain kernel (scores only), else the fused stage's
+// per-wave candidate budget.
+template <uint32_t kCand>
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs a) {
+  constexpr bool kFused = kCand != 0;
   __shared__ u32x4 q_lds[kHeads * kIdxDim / 8];   // 16 KiB
 
   // Grid: (workgroups of the longest row, rows). Row r is blockIdx.y, known
@@ -289,17 +297,19 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
       const uint32_t i = 4 * (groups - 1 - e) + grp;   // (unused when groups <= e: fifo[e] is 0)
       kidx[e] = key_of(i);
     }
-    wave_candidates(a, fifo, kidx, block, wave, lane);
+    wave_candidates<kCand>(a, fifo, kidx, block, wave, lane);
   }
   stamp_end();
 }
 
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, bool fused, hipStream_t s) {
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, uint32_t wave_cand, hipStream_t s) {
   const dim3 grid(max_row_blocks, a.rows);
-  if (fused)
-    hipLaunchKernelGGL(indexer_score_kernel<true>, grid, dim3(kIdxThreads), 0, s, a);
+  if (wave_cand == kIdxWaveCand)
+    hipLaunchKernelGGL(indexer_score_kernel<kIdxWaveCand>, grid, dim3(kIdxThreads), 0, s, a);
+  else if (wave_cand == kIdxWaveCandLong)
+    hipLaunchKernelGGL(indexer_score_kernel<kIdxWaveCandLong>, grid, dim3(kIdxThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(indexer_score_kernel<false>, grid, dim3(kIdxThreads), 0, s, a);
+    hipLaunchKernelGGL(indexer_score_kernel<0>, grid, dim3(kIdxThreads), 0, s, a);
   return hipGetLastError();
 }
 

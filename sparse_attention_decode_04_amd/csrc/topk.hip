@@ -44,7 +44,8 @@
 // pays for every cold instruction-cache line it executes.
 // Levels repeat on the lists until each row has one; the last level writes
 // index + offset, or -1 for empty slots. A row of n visible keys needs one
-// level up to 32768 keys, two up to 512K and three up to 8M.
+// level up to 32768 keys, two up to 1M (the second takes its up to 32 lists
+// whole) and three beyond.
 #include "topk_select.hpp"
 
 namespace ds {
@@ -71,6 +72,8 @@ hipError_t launch_topk_level(const TopkLevelArgs &a, uint32_t blocks, hipStream_
       hipLaunchKernelGGL((topk_level_kernel<true, kTopkPerThreadFirst>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
   } else if (a.per_thread == 4)
     hipLaunchKernelGGL((topk_level_kernel<false, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
+  else if (a.per_thread == 16)
+    hipLaunchKernelGGL((topk_level_kernel<false, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, a);
   else
     hipLaunchKernelGGL(topk_level_kernel<false>, dim3(blocks), dim3(kTopkThreads), 0, s, a);
   return hipGetLastError();

@@ -125,6 +125,8 @@ hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t 
       hipLaunchKernelGGL((topk_attn_kernel<true, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
   } else if (t.per_thread == 4)
     hipLaunchKernelGGL((topk_attn_kernel<false, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+  else if (t.per_thread == 16)
+    hipLaunchKernelGGL((topk_attn_kernel<false, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
   else
     hipLaunchKernelGGL((topk_attn_kernel<false, kTopkPerThreadLater>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
   return hipGetLastError();
