@@ -144,6 +144,17 @@ ds_status check_indexer_row(uint32_t r, uint32_t kv_len, uint32_t start_pos, int
   return DS_OK;
 }
 
+// Scores per thread of a selection level over scores whose rows hold up to
+// max_count of them: 4, 8 or 16 when every row fits one chunk (the final
+// level); else chunks of 16384 (16 per thread: twice the workgroups at half
+// the work of 32768) as long as every row's lists then still fit one final
+// level of 4 per thread (at most 8 chunks), else chunks of 32768.
+uint32_t scores_per_thread(uint32_t max_count) {
+  for (uint32_t per : {4u, 8u, 16u})
+    if (max_count <= ds::kTopkThreads * per) return per;
+  return max_count <= 8u * ds::kTopkThreads * 16 ? 16u : static_cast<uint32_t>(ds::kTopkPerThreadFirst);
+}
+
 ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
   if (!t) return fail("indexer row table is null");
   if (const ds_status st = check_row_count(t->rows)) return st;
@@ -154,14 +165,21 @@ ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
     p->max_kv = std::max<uint64_t>(p->max_kv, t->kv_len[r]);
     p->q_rows = std::max<uint64_t>(p->q_rows, uint64_t(t->q_row[r]) + 1);
     p->indices_end = std::max<uint64_t>(p->indices_end, uint64_t(t->output_offset[r]) + DS_TOP_K);
-    const uint32_t chunks = std::max<uint32_t>(1, div_up(p->visible[r], ds::kTopkChunkFirst));
-    if (chunks > 1) p->topk_bank += uint64_t(chunks) * DS_TOP_K;
     const uint32_t blocks = div_up(t->kv_len[r], kIndexerKeysPerBlock);
     p->blk_begin[r + 1] = p->blk_begin[r] + blocks;
     const uint32_t fchunks = div_up(uint64_t(blocks) * ds::kIdxCand, ds::kTopkChunkLater);
     if (fchunks > 1) p->fused_bank += uint64_t(fchunks) * DS_TOP_K;
   }
   for (uint32_t r = t->rows; r < ds::kRowsMax; ++r) p->blk_begin[r + 1] = p->blk_begin[r];
+  // The list banks of a selection from the scores: the first level's chunks
+  // of every row it splits (later levels write fewer lists).
+  uint32_t max_visible = 0;
+  for (uint32_t r = 0; r < t->rows; ++r) max_visible = std::max(max_visible, p->visible[r]);
+  const uint64_t first_chunk = uint64_t(ds::kTopkThreads) * scores_per_thread(max_visible);
+  for (uint32_t r = 0; r < t->rows; ++r) {
+    const uint32_t chunks = std::max<uint32_t>(1, div_up(p->visible[r], first_chunk));
+    if (chunks > 1) p->topk_bank += uint64_t(chunks) * DS_TOP_K;
+  }
   uint64_t starts[DS_ROWS_MAX];
   for (uint32_t r = 0; r < t->rows; ++r) starts[r] = t->output_offset[r];
   uint32_t a, b;
@@ -398,13 +416,18 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
     a.floors = in.floors;
     // Candidates per thread, and so the chunk size: the smallest of 4, 8 and
     // 16 that holds every row still selecting, which makes this the final
-    // level; otherwise chunks of 32768 scores or 8192 list keys.
+    // level; otherwise chunks of scores (see scores_per_thread) or of 8192
+    // list keys.
     uint32_t max_count = 0;
     for (uint32_t r = 0; r < p.rows; ++r)
       if (!done[r]) max_count = std::max(max_count, count[r]);
-    a.per_thread = a.from_scores ? ds::kTopkPerThreadFirst : ds::kTopkPerThreadLater;
-    for (uint32_t per : {4u, 8u, 16u})
-      if (max_count <= ds::kTopkThreads * per) { a.per_thread = per; break; }
+    if (a.from_scores) {
+      a.per_thread = scores_per_thread(max_count);   // (the banks are sized by the same rule)
+    } else {
+      a.per_thread = ds::kTopkPerThreadLater;
+      for (uint32_t per : {4u, 8u, 16u})
+        if (max_count <= ds::kTopkThreads * per) { a.per_thread = per; break; }
+    }
     for (uint32_t r = 0; r < p.rows; ++r)
       if (!done[r]) chunks[r] = std::max<uint32_t>(1, div_up(count[r], uint64_t(ds::kTopkThreads) * a.per_thread));
     uint32_t blocks = 0;

@@ -152,9 +152,14 @@ def expect_invalid(status, *fragments):
 def test_size_queries(lib):
     t = itab((1000, 70000, 32768, 32769))
     assert ds.scores_elems(t) == 4 * 70000
-    # top-k lists: only rows longer than one 32768-key chunk need the banks
-    assert ds.topk_workspace_bytes(t) == 2 * 8 * 512 * (3 + 2)
-    assert ds.topk_workspace_bytes(itab((1000, 32768))) == 0
+    # top-k lists: rows longer than one chunk need the banks. The call's
+    # longest row (70000 <= 8 x 16384) sets chunks of 16384 scores: 5, 2 and 3
+    # chunks of 512 keys for the rows of 70000, 32768 and 32769 keys
+    assert ds.topk_workspace_bytes(t) == 2 * 8 * 512 * (5 + 2 + 3)
+    assert ds.topk_workspace_bytes(itab((1000, 32768))) == 2 * 8 * 512 * 2
+    assert ds.topk_workspace_bytes(itab((1000, 16384))) == 0      # one chunk per row
+    # beyond 8 x 16384 scores in a row, chunks of 32768: 200000 -> 7 chunks
+    assert ds.topk_workspace_bytes(itab((1000, 200000))) == 2 * 8 * 512 * 7
     # fused: 128 candidate keys and four u64 floors per 1024-key block (each
     # region 256-byte aligned), plus two list banks for rows whose candidates
     # exceed one 8192-key chunk (rows over 65536 keys): here the 70000-key

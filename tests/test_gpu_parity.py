@@ -294,3 +294,32 @@ def test_first_level_sizes_at_their_edges(longest, ternary):
     got1 = one.results()
     for r in range(inp.rows):
         check_row(got1[r], orc[r], f"edge {longest} row {r} one call", gathered=False)
+
+
+@pytest.mark.parametrize("kv_len", [(1000, 20000), (20000,) * 8, (1000, 70000, 32768, 32769), (3000, 131072),
+                                    (700, 200000)])
+def test_topk_banks_hold_every_first_level_chunk(kv_len):
+    # ds_rows_topk over scores split into chunks of 16384 (a longest row of at
+    # most 8 x 16384) or 32768: the list banks the workspace query sizes hold
+    # every chunk's list. The workspace is exactly that size, followed by a
+    # canary that must come back untouched; the indices are the oracle's.
+    rows = len(kv_len)
+    rng = np.random.default_rng(sum(kv_len))
+    sp = [4 * n - 1 for n in kv_len]
+    table = ds.indexer_rows(list(kv_len), sp, [0] * rows, list(range(rows)), [512 * r for r in range(rows)])
+    stride = max(kv_len)
+    scores = np.full((rows, stride), -np.inf, np.float32)
+    for r, n in enumerate(kv_len):
+        scores[r, :n] = rng.standard_normal(n).astype(np.float32)
+    need = ds.topk_workspace_bytes(table)
+    canary = 1 << 16
+    ws = torch.full((need + canary,), 0x5A, dtype=torch.uint8, device="cuda")
+    idx = torch.full((512 * rows,), -7, dtype=torch.int32, device="cuda")
+    say("top-k banks", kv_len, "workspace", need)
+    ds.topk(table, torch.from_numpy(scores.reshape(-1)).cuda(), ws[:max(need, 1)], idx)
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0x5A).all()), "the selection wrote past its workspace"
+    got = idx.cpu().numpy().reshape(rows, 512)
+    for r, n in enumerate(kv_len):
+        want = O.topk_select(scores[r], O.valid_count(n, sp[r]), 0)
+        np.testing.assert_array_equal(got[r], want, err_msg=f"row {r} ({n} keys)")
