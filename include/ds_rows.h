@@ -380,7 +380,7 @@ ds_status ds_rows_indexer_topk_attn(const ds_indexer_rows *irows, const ds_spars
  * The array must hold ds_rows_indexer_topk_workspace_bytes(irows), rounded up
  * to 256, plus ds_rows_attn_workspace_bytes(srows); a larger call fails with
  * DS_ERR_INVALID_ARGUMENT before anything is enqueued (8 rows of 512 slots
- * fit up to 911360 keys each; one row up to 13.7 million keys). The array
+ * fit up to 897024 keys each; one row up to 13.59 million keys). The array
  * needs no clearing: no kernel depends on its contents at entry.
  * Calls on one GPU share its array: calls that overlap in time (e.g. on two
  * streams) race and must be serialised by the caller. The first call on a
