@@ -187,6 +187,19 @@ def test_size_queries(lib):
     assert ds.scores_elems(itab((0,))) == 0            # invalid table -> 0
 
 
+
+def test_noalloc_capacity_matches_the_header(lib):
+    # ds_rows.h states what the no-alloc array (DS_NOALLOC_SCRATCH_BYTES =
+    # 16 MiB) holds: both workspaces (the indexer's rounded up to 256 bytes)
+    # for 8 rows of 897024 keys or one row of 13.59 million, at width 512.
+    cap = 16 << 20
+    def need(rows, n):
+        it = itab((n,) * rows)
+        st = stab((n,) * rows)
+        return -(-ds.indexer_topk_workspace_bytes(it) // 256) * 256 + ds.attn_workspace_bytes(st)
+    assert need(8, 897024) <= cap < need(8, 897024 + 1024)
+    assert need(1, 13591552) <= cap < need(1, 13591552 + 1024)
+
 # ------------------------------------------------------- indexer-row checks
 
 @pytest.mark.parametrize("rows", [0, 9])
