@@ -130,15 +130,27 @@ def fused_route(kv_len):
     return min(kv_len) >= FUSED_MIN_VISIBLE
 
 
+def fused_wave_cand(kv_len):
+    """Candidates per wave of the fused stage: 8 when every row has at least
+    262144 visible keys, else 32 (the library's rule; the workloads' rows see
+    all of their keys)."""
+    return 8 if min(kv_len) >= 262144 else 32
+
+
+def indexer_kernel_name(kv_len):
+    return "indexer_score_kernel<%d>" % (fused_wave_cand(kv_len) if fused_route(kv_len) else 0)
+
+
 def indexer_bytes_flops(kv_len, fused):
     """Algorithmic HBM bytes and MFMA flops of one indexer launch: per key
     256 B of keys read + 4 B of score written and 64*128*2 flops; per row
     16 KiB of query and 256 B of weights read; in the fused form also, per
-    1024-key block, 128 candidate keys of 8 B and four 8 B floors written."""
+    1024-key block, 4 C candidate keys of 8 B (C per wave) and four 8 B floors
+    written."""
     keys = sum(kv_len)
     b = keys * (256 + 4) + len(kv_len) * (64 * 128 * 2 + 64 * 4)
     if fused:
-        b += sum(-(-n // 1024) for n in kv_len) * (128 * 8 + 4 * 8)
+        b += sum(-(-n // 1024) for n in kv_len) * (4 * fused_wave_cand(kv_len) * 8 + 4 * 8)
     return b, keys * 64 * 128 * 2
 
 
@@ -606,8 +618,8 @@ def main():
             "ms_per_step": ms_four, "rows_per_s": inp.rows / (ms_four * 1e-3), "per_call_ms": per_call_four},
         "wall_s_timed_region": wall,
         "roofline": {
-            "kernel": ("indexer_score_kernel<true> (indexer with the fused top-k candidate stage)" if fused
-                       else "indexer_score_kernel<false>"),
+            "kernel": (indexer_kernel_name(kv_len) + (" (indexer with the fused top-k candidate stage)" if fused
+                                                       else " (score kernel)")),
             "kernel_ms": idx_in_mean,
             "kernel_ms_median": idx_in_median,
             "timing": "in step: mean over n = %d one-call steps on the rotating copies of the indexer's execution "
@@ -678,7 +690,7 @@ def main():
                 "step_us_p90": spread["p90"], "rows_per_s": cinp.rows / (cms * 1e-3),
                 "keys_per_s": sum(cinp.kv_len) / (cms * 1e-3),
                 "step_algorithmic_gb_per_s": step_bytes(cinp.kv_len) / (cms * 1e-3) / 1e9,
-                "dominant_kernel": "indexer_score_kernel<true>" if cfused else "indexer_score_kernel<false>",
+                "dominant_kernel": indexer_kernel_name(cinp.kv_len),
                 "dominant_kernel_in_step_us": c_in * 1e3,
                 "dominant_kernel_hbm_frac": cb / (c_in * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "copies": ncopies, "steps": steps}

@@ -70,13 +70,14 @@ static_assert((kIdxMaxKeysPerBlock / (kIdxThreads / 64) / kIdxTile + kIdxRing - 
 // kidx[e] their key indices. Key indices increase with (3 - e, lane): e = 3
 // holds the wave's first group of tiles, and within a group lane row g holds
 // tile g of the group.
-template <uint32_t kCand>
+template <int kCand>
 __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint32_t (&o)[4],
                                                 const uint32_t (&kidx)[4], uint32_t block, uint32_t wave,
                                                 uint32_t lane) {
   constexpr uint32_t kKeep = kCand * 3 / 4;
   static_assert(kCand <= 64 && kKeep >= 1, "one slot per lane");
-  const uint64_t slot0 = static_cast<uint64_t>(block) * (kIdxThreads / 64) * kCand + wave * kCand;
+  constexpr uint32_t kC = kCand;
+  const uint64_t slot0 = static_cast<uint64_t>(block) * (kIdxThreads / 64) * kC + wave * kC;
   const uint64_t floor_at = static_cast<uint64_t>(block) * kIdxFloors + wave;
   auto count_ge = [&](uint32_t t) -> uint32_t {   // keys of the wave with score bits >= t
     uint32_t c = 0;
@@ -87,15 +88,15 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
   const uint32_t nvalid = count_ge(1u);
   uint32_t thr = 1;   // keep every valid key
   uint32_t kept = nvalid;
-  if (nvalid > kCand) {
+  if (nvalid > kC) {
     // T is built from the top two bits at a time (three candidate values per
     // step, whose counts are independent and overlap in latency), each time
     // taking the largest value that still has at least kKeep keys at
     // or above it. It stops as soon as the accepted T keeps at most
-    // kCand keys; otherwise it ends at the kKeep-th best score
-    // bits. Any T that keeps at most kCand keys is a valid floor: the
+    // kC keys; otherwise it ends at the kKeep-th best score
+    // bits. Any T that keeps at most kC keys is a valid floor: the
     // final level's check compares the floors with its 512th key, so which
-    // one is taken changes no index. If none keeps at most kCand, T
+    // one is taken changes no index. If none keeps at most kC, T
     // ends as the kKeep-th best score bits (ties at T overflow).
     thr = 0;
     kept = 256;   // count_ge(0); replaced at the first accepted step (count_ge(1) = nvalid > kKeep)
@@ -105,7 +106,7 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
       if (n3 >= kKeep) { thr = t3; kept = n3; }
       else if (n2 >= kKeep) { thr = t2; kept = n2; }
       else if (n1 >= kKeep) { thr = t1; kept = n1; }
-      if (kept <= kCand) break;   // uniform
+      if (kept <= kC) break;   // uniform
     }
   }
   auto prefix = [](uint64_t mask) {   // set lanes of `mask` below this lane
@@ -117,12 +118,12 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
   // ties in key-index order (e = 3 .. 0, lanes ascending).
   bool take[4];
   uint64_t floor = static_cast<uint64_t>(thr) << 32;   // after a clean threshold
-  if (kept <= kCand) {
+  if (kept <= kC) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) take[e] = o[e] >= thr;
     if (kept == nvalid) floor = 0;
   } else {
-    uint32_t room = kCand - count_ge(thr + 1);   // slots left for ties at T (> 0)
+    uint32_t room = kC - count_ge(thr + 1);   // slots left for ties at T (> 0)
     uint32_t first_unkept = 0xFFFFFFFFu;                // index of the best unwritten tie
 #pragma unroll
     for (int e = 3; e >= 0; --e) {
@@ -136,7 +137,7 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
       const uint32_t n = static_cast<uint32_t>(__popcll(m));
       room = n >= room ? 0u : room - n;
     }
-    kept = kCand;
+    kept = kC;
     floor = (static_cast<uint64_t>(thr) << 32) | static_cast<uint32_t>(~first_unkept);
   }
   uint32_t base = 0;
@@ -147,13 +148,13 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
     if (take[e]) a.cand[slot0 + pos] = (static_cast<uint64_t>(o[e]) << 32) | static_cast<uint32_t>(~kidx[e]);
     base += static_cast<uint32_t>(__popcll(mask));
   }
-  if (lane >= kept && lane < kCand) a.cand[slot0 + lane] = 0;   // unused slots
+  if (lane >= kept && lane < kC) a.cand[slot0 + lane] = 0;   // unused slots
   if (lane == 0) a.floors[floor_at] = floor;
 }
 
 // kCand: 0 for the plain kernel (scores only), else the fused stage's
 // per-wave candidate budget.
-template <uint32_t kCand>
+template <int kCand>
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs a) {
   constexpr bool kFused = kCand != 0;
   __shared__ u32x4 q_lds[kHeads * kIdxDim / 8];   // 16 KiB
@@ -305,9 +306,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
 hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, uint32_t wave_cand, hipStream_t s) {
   const dim3 grid(max_row_blocks, a.rows);
   if (wave_cand == kIdxWaveCand)
-    hipLaunchKernelGGL(indexer_score_kernel<kIdxWaveCand>, grid, dim3(kIdxThreads), 0, s, a);
+    hipLaunchKernelGGL(indexer_score_kernel<static_cast<int>(kIdxWaveCand)>, grid, dim3(kIdxThreads), 0, s, a);
   else if (wave_cand == kIdxWaveCandLong)
-    hipLaunchKernelGGL(indexer_score_kernel<kIdxWaveCandLong>, grid, dim3(kIdxThreads), 0, s, a);
+    hipLaunchKernelGGL(indexer_score_kernel<static_cast<int>(kIdxWaveCandLong)>, grid, dim3(kIdxThreads), 0, s, a);
   else
     hipLaunchKernelGGL(indexer_score_kernel<0>, grid, dim3(kIdxThreads), 0, s, a);
   return hipGetLastError();
