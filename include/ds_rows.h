@@ -467,12 +467,13 @@ ds_status ds_rows_compressor(const ds_compressor_rows *rows,
  * constant wall clock (hipDeviceAttributeWallClockRate, kHz). The span from
  * the smallest start to the largest end is the kernel's execution time where
  * it ran; the launch is an ordinary one (a few extra stores per workgroup),
- * so the kernels around it run as they would. The grid has
- * ceil(max kv_len / B) x rows workgroups: B = 1024 keys with the fused top-k
- * stage; the plain kernel takes the largest power of two B from 1024 down to
- * 64 for which the call has at least 256 blocks (sum over rows of
- * ceil(kv_len / B)), so ceil(max kv_len / 64) x rows x DS_TIMER_STAMPS_PER_WG
- * entries always suffice. A launch whose grid needs more entries than
+ * so the kernels around it run as they would. The grid has ceil(max kv_len
+ * / B) x rows workgroups, B = 1024 keys with the fused top-k stage; the plain
+ * kernel takes the largest power of two B from 1024 down to 64 keys giving
+ * at least 256 blocks (sum over rows of ceil(kv_len / B)), and one workgroup
+ * per block instead when that grid would be more than twice the blocks;
+ * ceil(max kv_len / 64) x rows x DS_TIMER_STAMPS_PER_WG entries always
+ * suffice. A launch whose grid needs more entries than
  * `stamps_elems` fails with DS_ERR_INVALID_ARGUMENT (nothing enqueued). One arm serves one launch; a call that fails its argument
  * checks before the launch leaves the arm in place. `stamps` must be
  * non-null (DS_ERR_INVALID_ARGUMENT otherwise); this call enqueues nothing. */

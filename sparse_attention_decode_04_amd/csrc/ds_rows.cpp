@@ -332,33 +332,51 @@ ds_status launch_indexer(const ds_indexer_rows *rows, const IndexerPlan &p, cons
   a.rows = p.rows;
   a.cand = cand;
   a.floors = floors;
+  // Slot y of the grid takes row order[y]. The fused stage keeps the rows in
+  // order (its candidate and floor layout is per 1024-key block, row after
+  // row). The plain kernel takes the rows longest first: workgroups are
+  // dispatched in grid order, and with a long row last its workgroups waited
+  // behind every short row's (mostly empty) grid row; at workload 3 (rows of
+  // 1 .. 131072 keys) the long row's last workgroup started 9.4 us into the
+  // kernel.
+  uint32_t order[ds::kRowsMax];
+  for (uint32_t r = 0; r < p.rows; ++r) order[r] = r;
   if (cand != nullptr) {
-    // The fused stage's candidate and floor layout is per 1024-key block.
     a.keys_per_block = kIndexerKeysPerBlock;
     for (uint32_t r = 0; r <= ds::kRowsMax; ++r) a.blk_begin[r] = p.blk_begin[r];
   } else {
     a.keys_per_block = plain_keys_per_block(rows, p.rows);
-    for (uint32_t r = 0; r < ds::kRowsMax; ++r)
-      a.blk_begin[r + 1] = a.blk_begin[r] + (r < p.rows ? div_up(rows->kv_len[r], a.keys_per_block) : 0);
+    std::stable_sort(order, order + p.rows,
+                     [&](uint32_t x, uint32_t y) { return rows->kv_len[x] > rows->kv_len[y]; });
+    for (uint32_t y = 0; y < ds::kRowsMax; ++y)
+      a.blk_begin[y + 1] = a.blk_begin[y] + (y < p.rows ? div_up(rows->kv_len[order[y]], a.keys_per_block) : 0);
   }
-  for (uint32_t r = 0; r < p.rows; ++r) {
-    a.keys[r] = static_cast<const uint16_t *>(rows->keys[r]);
-    a.kv_len[r] = rows->kv_len[r];
-    a.visible[r] = p.visible[r];
-    a.q_row[r] = rows->q_row[r];
+  for (uint32_t y = 0; y < p.rows; ++y) {
+    const uint32_t r = order[y];
+    a.keys[y] = static_cast<const uint16_t *>(rows->keys[r]);
+    a.kv_len[y] = rows->kv_len[r];
+    a.visible[y] = p.visible[r];
+    a.q_row[y] = rows->q_row[r];
+    a.score_row[y] = r;
   }
   uint32_t max_row_blocks = 1;
   for (uint32_t r = 0; r < p.rows; ++r) max_row_blocks = std::max(max_row_blocks, a.blk_begin[r + 1] - a.blk_begin[r]);
+  // The plain kernel takes a compact grid (one workgroup per block) when the
+  // (blocks of the longest row) x rows grid would be more than twice its
+  // blocks, i.e. mostly empty workgroups.
+  const uint64_t blocks = a.blk_begin[ds::kRowsMax];
+  const bool compact = cand == nullptr && uint64_t(max_row_blocks) * p.rows > 2 * blocks;
   if (t_timer_stamps != nullptr) {
-    const uint64_t need_elems = uint64_t(max_row_blocks) * p.rows * ds::kTimerStamps;
+    const uint64_t wgs = compact ? blocks : uint64_t(max_row_blocks) * p.rows;
+    const uint64_t need_elems = wgs * ds::kTimerStamps;
     if (t_timer_elems < need_elems)
-      return fail("the indexer timing buffer holds %zu entries; this launch's %u x %u workgroups need %llu",
-                  t_timer_elems, max_row_blocks, p.rows, static_cast<unsigned long long>(need_elems));
+      return fail("the indexer timing buffer holds %zu entries; this launch's %llu workgroups need %llu",
+                  t_timer_elems, static_cast<unsigned long long>(wgs), static_cast<unsigned long long>(need_elems));
     a.stamps = t_timer_stamps;
     t_timer_stamps = nullptr;
     t_timer_elems = 0;
   }
-  const hipError_t e = ds::launch_indexer_score(a, max_row_blocks, cand != nullptr ? fused_wave_cand(p) : 0,
+  const hipError_t e = ds::launch_indexer_score(a, max_row_blocks, cand != nullptr ? fused_wave_cand(p) : 0, compact,
                                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DS_OK : hip_fail(e, "indexer score launch");
 }

@@ -50,12 +50,16 @@ constexpr uint32_t kIdxFloors = kIdxThreads / 64;                   // 4 per blo
 constexpr uint32_t kTimerStamps = DS_TIMER_STAMPS_PER_WG;           // timing stamps per workgroup
 static_assert(kTimerStamps >= 1 + kIdxThreads / 64, "a start and one end per wave");
 
+// Per-row arrays are indexed by the grid row ("slot"): the plain kernel
+// takes the rows longest first (see launch_indexer), so slot y holds row
+// score_row[y]'s keys, lengths and query, and writes that row's scores.
 struct IndexerArgs {
-  const uint16_t *keys[kRowsMax];   // bf16 [kv_len, 128] per row
+  const uint16_t *keys[kRowsMax];   // bf16 [kv_len, 128] per slot
   const uint16_t *q;                // bf16 [_, 64, 128]
   const float *w;                   // f32 [_, 64]
   float *scores;                    // f32 [rows, score_stride]
   uint64_t score_stride;
+  uint32_t score_row[kRowsMax];     // the row whose scores slot y writes
   uint32_t rows;
   uint32_t keys_per_block;          // 1024 with the fused stage; the plain kernel 64 .. 1024 (a power of 2)
   uint32_t kv_len[kRowsMax];
@@ -67,10 +71,12 @@ struct IndexerArgs {
   uint64_t *stamps;                 // timing (ds_rows_time_next_indexer) or nullptr: per workgroup of the
                                     // grid, its start and each wave's end (wall clock)
 };
-// Grid (max_row_blocks, a.rows): workgroup (x, r) is row r's x-th block.
-// wave_cand: 0 for the plain kernel, else the fused stage's C (kIdxWaveCand
-// or kIdxWaveCandLong).
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, uint32_t wave_cand, hipStream_t s);
+// Grid (max_row_blocks, a.rows): workgroup (x, y) is slot y's x-th block;
+// with compact (plain kernel only), one workgroup per block, b = 0 ..
+// blk_begin[kRowsMax). wave_cand: 0 for the plain kernel, else the fused
+// stage's C (kIdxWaveCand or kIdxWaveCandLong).
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, uint32_t wave_cand, bool compact,
+                                hipStream_t s);
 
 // ------------------------------------------------------------------ top-k
 // One selection level: every workgroup reduces a chunk of one row's

@@ -153,41 +153,95 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
 }
 
 // kCand: 0 for the plain kernel (scores only), else the fused stage's
-// per-wave candidate budget.
-template <int kCand>
+// per-wave candidate budget. kCompact (plain kernel only): a 1-D grid of one
+// workgroup per block instead of the (blocks of the longest slot, slots) one.
+template <int kCand, bool kCompact = false>
 __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs a) {
+  static_assert(!kCompact || kCand == 0, "the fused stage keeps the 2-D grid");
   constexpr bool kFused = kCand != 0;
   __shared__ u32x4 q_lds[kHeads * kIdxDim / 8];   // 16 KiB
 
-  // Grid: (workgroups of the longest row, rows). Row r is blockIdx.y, known
-  // at launch, so every argument of the row is read in one batch of scalar
-  // loads (a row found from the block index would first wait for the block
-  // table). Workgroups past the row's own count have no keys and end after
-  // the common set-up, before any store.
-  const uint32_t r = blockIdx.y;
-  uint32_t blk0 = a.blk_begin[r], blk1 = a.blk_begin[r + 1], n = a.kv_len[r], visible = a.visible[r];
-  uint32_t qr = a.q_row[r];
-  uint64_t kbits = reinterpret_cast<uint64_t>(a.keys[r]), qbits = reinterpret_cast<uint64_t>(a.q),
-           wbits = reinterpret_cast<uint64_t>(a.w), sbits = reinterpret_cast<uint64_t>(a.scores);
+  // 2-D grid: (workgroups of the longest slot, slots); slot r is blockIdx.y,
+  // known at launch, so every argument of the slot is read in one batch of
+  // scalar loads (a slot found from the block index would first wait for the
+  // block table), and workgroups past the slot's own count have no keys and
+  // end after the common set-up, before any store. Compact grid (the plain
+  // kernel, when the 2-D grid would be mostly empty): one workgroup per block
+  // of the slots' concatenated blocks, no empty ones (at workload 3, rows of
+  // 1 .. 131072 keys, the 2-D grid dispatched over 1600 empty workgroups,
+  // ahead of the short rows' real ones: 48.8 -> 43.5 us per step); the block
+  // table and every slot's fields are loaded together and the slot is picked
+  // from them with scalar compares (the compiler issues those loads in two
+  // batches: about 0.5 us more per launch where the 2-D grid has few empty
+  // workgroups).
+  uint32_t r, blk0, blk1, n, visible, qr, srow, xb;
+  uint64_t kbits;
+  uint64_t qbits = reinterpret_cast<uint64_t>(a.q), wbits = reinterpret_cast<uint64_t>(a.w),
+           sbits = reinterpret_cast<uint64_t>(a.scores);
   uint64_t sstride = a.score_stride;
   uint64_t tbits = reinterpret_cast<uint64_t>(a.stamps);
-  // One use of them all: the compiler issues these scalar loads together and
-  // waits once, rather than in dependent batches ahead of their first uses.
-  asm volatile("" : "+s"(blk0), "+s"(blk1), "+s"(n), "+s"(visible), "+s"(qr), "+s"(kbits), "+s"(qbits), "+s"(wbits),
-               "+s"(sbits), "+s"(sstride), "+s"(tbits));
+  if constexpr (!kCompact) {
+    r = blockIdx.y;
+    blk0 = a.blk_begin[r], blk1 = a.blk_begin[r + 1], n = a.kv_len[r], visible = a.visible[r];
+    qr = a.q_row[r];
+    kbits = reinterpret_cast<uint64_t>(a.keys[r]);
+    srow = a.score_row[r];
+    // One use of them all: the compiler issues these scalar loads together
+    // and waits once, rather than in dependent batches ahead of their first
+    // uses.
+    asm volatile("" : "+s"(blk0), "+s"(blk1), "+s"(n), "+s"(visible), "+s"(qr), "+s"(kbits), "+s"(qbits),
+                 "+s"(wbits), "+s"(sbits), "+s"(sstride), "+s"(tbits), "+s"(srow));
+    xb = blockIdx.x;
+  } else {
+    uint32_t bb[kRowsMax + 1], kv[kRowsMax], vis[kRowsMax], qrs[kRowsMax], srs[kRowsMax];
+    uint64_t kp[kRowsMax];
+#pragma unroll
+    for (int i = 0; i < kRowsMax; ++i) {
+      bb[i] = a.blk_begin[i];
+      kv[i] = a.kv_len[i];
+      vis[i] = a.visible[i];
+      qrs[i] = a.q_row[i];
+      srs[i] = a.score_row[i];
+      kp[i] = reinterpret_cast<uint64_t>(a.keys[i]);
+    }
+    bb[kRowsMax] = a.blk_begin[kRowsMax];
+    static_assert(kRowsMax == 8, "the slot fields are listed one by one below");
+    // (All in one statement: split, the compiler waited for the first
+    // statement's loads before issuing the rest.)
+    asm volatile("" : "+s"(bb[0]), "+s"(bb[1]), "+s"(bb[2]), "+s"(bb[3]), "+s"(bb[4]), "+s"(bb[5]), "+s"(bb[6]),
+                 "+s"(bb[7]), "+s"(bb[8]), "+s"(kv[0]), "+s"(kv[1]), "+s"(kv[2]), "+s"(kv[3]), "+s"(kv[4]),
+                 "+s"(kv[5]), "+s"(kv[6]), "+s"(kv[7]), "+s"(vis[0]), "+s"(vis[1]), "+s"(vis[2]), "+s"(vis[3]),
+                 "+s"(vis[4]), "+s"(vis[5]), "+s"(vis[6]), "+s"(vis[7]), "+s"(qrs[0]), "+s"(qrs[1]), "+s"(qrs[2]),
+                 "+s"(qrs[3]), "+s"(qrs[4]), "+s"(qrs[5]), "+s"(qrs[6]), "+s"(qrs[7]), "+s"(srs[0]), "+s"(srs[1]),
+                 "+s"(srs[2]), "+s"(srs[3]), "+s"(srs[4]), "+s"(srs[5]), "+s"(srs[6]), "+s"(srs[7]), "+s"(kp[0]),
+                 "+s"(kp[1]), "+s"(kp[2]), "+s"(kp[3]), "+s"(kp[4]), "+s"(kp[5]), "+s"(kp[6]), "+s"(kp[7]),
+                 "+s"(qbits), "+s"(wbits), "+s"(sbits), "+s"(sstride), "+s"(tbits));
+    const uint32_t b = blockIdx.x;
+    r = 0;
+#pragma unroll
+    for (int i = 1; i < kRowsMax; ++i) r += b >= bb[i] ? 1u : 0u;   // slots past `rows` start at the total
+    blk0 = bb[0], blk1 = bb[1], n = kv[0], visible = vis[0], qr = qrs[0], srow = srs[0], kbits = kp[0];
+#pragma unroll
+    for (int i = 1; i < kRowsMax; ++i) {
+      if (r == static_cast<uint32_t>(i)) {
+        blk0 = bb[i], blk1 = bb[i + 1], n = kv[i], visible = vis[i], qr = qrs[i], srow = srs[i], kbits = kp[i];
+      }
+    }
+    xb = b - blk0;
+  }
   // Timing stamps (ds_rows_time_next_indexer): this workgroup's start now,
   // each wave's end where it leaves.
   uint64_t *const stamps = tbits != 0 ? global_ptr<uint64_t>(tbits) +
                                             static_cast<uint64_t>(blockIdx.y * gridDim.x + blockIdx.x) * kTimerStamps
-                                      : nullptr;
+                                      : nullptr;   // (a compact grid is 1-D: blockIdx.y = 0)
   if (stamps != nullptr && threadIdx.x == 0) stamps[0] = wall_clock64();
   auto stamp_end = [&]() {
     if (stamps != nullptr && (threadIdx.x & 63) == 0) stamps[1 + (threadIdx.x >> 6)] = wall_clock64();
   };
   const uint16_t *const keys = global_ptr<const uint16_t>(kbits);
   const uint32_t nblk = blk1 - blk0;
-  const bool live = blockIdx.x < nblk;   // uniform
-  const uint32_t block = blk0 + blockIdx.x;   // workgroup index in the candidate layout
+  const bool live = xb < nblk;   // uniform (always, on a compact grid)
+  const uint32_t block = blk0 + xb;   // workgroup index in the candidate layout
   // Tiles of 16 keys are dealt round robin over the row's waves: wave w of
   // the row's workgroup b takes tiles t0 = 4b + w, t0 + S, t0 + 2S, ...
   // (S = 4 x the row's workgroups), so at any time the row's waves read
@@ -195,7 +249,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   const uint32_t tstride = kIdxWaves * nblk;
   const uint16_t *__restrict__ q = global_ptr<const uint16_t>(qbits) + static_cast<uint64_t>(qr) * kHeads * kIdxDim;
   const float *__restrict__ w = global_ptr<const float>(wbits) + static_cast<uint64_t>(qr) * kHeads;
-  float *__restrict__ scores = global_ptr<float>(sbits) + static_cast<uint64_t>(r) * sstride;
+  float *__restrict__ scores = global_ptr<float>(sbits) + static_cast<uint64_t>(srow) * sstride;
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -212,7 +266,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   const float wv = w[tid & (kHeads - 1)];
 
   const uint32_t tiles = (n + kIdxTile - 1) / kIdxTile;
-  const uint32_t t0 = kIdxWaves * blockIdx.x + wave;
+  const uint32_t t0 = kIdxWaves * xb + wave;
   const uint32_t mine = live && tiles > t0 ? (tiles - t0 + tstride - 1) / tstride : 0;
   auto key_of = [&](uint32_t i) { return (t0 + tstride * i) * kIdxTile + col; };
   auto load_tile = [&](uint32_t i, u32x4 (&kb)[4]) {
@@ -303,9 +357,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   stamp_end();
 }
 
-hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, uint32_t wave_cand, hipStream_t s) {
-  const dim3 grid(max_row_blocks, a.rows);
-  if (wave_cand == kIdxWaveCand)
+hipError_t launch_indexer_score(const IndexerArgs &a, uint32_t max_row_blocks, uint32_t wave_cand, bool compact,
+                                hipStream_t s) {
+  const dim3 grid = compact ? dim3(a.blk_begin[kRowsMax]) : dim3(max_row_blocks, a.rows);
+  if (compact)
+    hipLaunchKernelGGL((indexer_score_kernel<0, true>), grid, dim3(kIdxThreads), 0, s, a);
+  else if (wave_cand == kIdxWaveCand)
     hipLaunchKernelGGL(indexer_score_kernel<static_cast<int>(kIdxWaveCand)>, grid, dim3(kIdxThreads), 0, s, a);
   else if (wave_cand == kIdxWaveCandLong)
     hipLaunchKernelGGL(indexer_score_kernel<static_cast<int>(kIdxWaveCandLong)>, grid, dim3(kIdxThreads), 0, s, a);

@@ -276,7 +276,7 @@ def test_step_permuted_row_subsets_match_full_launch():
             assert np.array_equal(got4[i]["out"].view(np.uint32), ref4[r]["out"].view(np.uint32)), (sel, r)
 
 
-@pytest.mark.parametrize("cid", [1, 2])
+@pytest.mark.parametrize("cid", [0, 1, 2, 3])
 def test_timed_indexer_launch_changes_nothing(cid):
     """ds_rows_time_next_indexer: the armed step's indexer writes a start and
     four wave ends per workgroup (ends after starts, a span below a second),
@@ -291,15 +291,20 @@ def test_timed_indexer_launch_changes_nothing(cid):
     ref_out, ref_idx, ref_sc = run.out.clone(), run.indices.clone(), run.scores.clone()
     run.out.zero_()
     run.indices.fill_(-7)
-    # The grid the header states: 1024-key blocks with the fused stage (every
-    # row has 16384 visible keys or more), else the largest power of two from
-    # 1024 down to 64 that gives the call at least 256 blocks.
+    # The grid the header states: 1024-key blocks on a (blocks, rows) grid
+    # with the fused stage (every row has 16384 visible keys or more), else
+    # the largest power of two from 1024 down to 64 that gives the call at
+    # least 256 blocks, on that grid or, when it would be more than twice
+    # the blocks, one workgroup per block.
     visible = [min(n, (sp + 1) // 4) for n, sp in zip(inp.kv_len, inp.start_pos)]
     block = 1024
     if min(visible) < 16384:
         while block > 64 and sum(-(-n // block) for n in inp.kv_len) < 256:
             block //= 2
+    blocks = sum(-(-n // block) for n in inp.kv_len)
     wgs = -(-max(inp.kv_len) // block) * inp.rows
+    if min(visible) < 16384 and wgs > 2 * blocks:
+        wgs = blocks   # the plain kernel's compact grid: one workgroup per block
     stamps = torch.zeros(wgs * ds.TIMER_STAMPS_PER_WG, dtype=torch.int64, device="cuda")
     ds.time_next_indexer(stamps)
     run.step_one()
