@@ -164,6 +164,14 @@ def attention_bytes_flops(kv_len):
     return b, sum(2 * 2 * 64 * 512 * wi for wi in w)
 
 
+def gather_bytes(kv_len):
+    """Algorithmic bytes of ds_rows_gather: per selected slot the 4-byte index
+    and the 1 KiB KV row read, the 1 KiB gathered row and 2-byte mask entry
+    written; per row its 4-byte invalid flag."""
+    w = [min(n, 512) for n in kv_len]
+    return sum(wi * (4 + 1024 + 1024 + 2) + 4 for wi in w)
+
+
 def step_bytes(kv_len):
     """Algorithmic bytes of one step: the indexer (fused form when taken), the
     selection's reads (candidates or scores) and index writes, and the
@@ -171,7 +179,7 @@ def step_bytes(kv_len):
     fused = fused_route(kv_len)
     blocks = sum(-(-n // 1024) for n in kv_len)
     idx_b, _ = indexer_bytes_flops(kv_len, fused)
-    sel_b = (blocks * (128 * 8 + 4 * 8) if fused else 4 * sum(kv_len)) + len(kv_len) * 512 * 4
+    sel_b = (blocks * (4 * fused_wave_cand(kv_len) * 8 + 4 * 8) if fused else 4 * sum(kv_len)) + len(kv_len) * 512 * 4
     attn_b, _ = attention_bytes_flops(kv_len)
     return idx_b + sel_b + attn_b
 
@@ -661,6 +669,14 @@ def main():
             "traffic": (attn_traffic[0] + attn_traffic[1]) if attn_traffic else None,
             "traffic_fetch_write": list(attn_traffic) if attn_traffic else None,
             "traffic_over_algorithmic": ((attn_traffic[0] + attn_traffic[1]) / attn_b) if attn_traffic else None,
+        },
+        "gather": {
+            "call": "ds_rows_gather (the four-call pipeline's third call)",
+            "algorithmic_bytes": gather_bytes(kv_len),
+            "us": per_call_four["gather"] * 1e3,
+            "timing": "HIP events around the call inside the four-call steps (its flag-clearing kernel included)",
+            "achieved_gb_s": gather_bytes(kv_len) / (per_call_four["gather"] * 1e-3) / 1e9,
+            "hbm_frac": gather_bytes(kv_len) / (per_call_four["gather"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
     }
     del runs
