@@ -138,7 +138,17 @@ def fused_wave_cand(kv_len):
 
 
 def indexer_kernel_name(kv_len):
-    return "indexer_score_kernel<%d>" % (fused_wave_cand(kv_len) if fused_route(kv_len) else 0)
+    """The indexer kernel a one-call step on rows of these lengths launches
+    (the library's rules: fused stage and its budget; for the plain kernel,
+    its block size and whether its grid is the compact one)."""
+    if fused_route(kv_len):
+        return "indexer_score_kernel<%d, false>" % fused_wave_cand(kv_len)
+    block = 1024
+    while block > 64 and sum(-(-n // block) for n in kv_len) < 256:
+        block //= 2
+    blocks = sum(-(-n // block) for n in kv_len)
+    compact = -(-max(kv_len) // block) * len(kv_len) > 2 * blocks
+    return "indexer_score_kernel<0, %s>" % ("true" if compact else "false")
 
 
 def indexer_bytes_flops(kv_len, fused):
