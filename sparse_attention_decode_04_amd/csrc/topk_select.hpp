@@ -13,7 +13,18 @@ namespace ds {
 
 constexpr int kBins = 1024;
 constexpr uint32_t kFastBinMax = 256;   // largest bin the counting select ranks by comparisons
+// A sampled threshold keeps the keys at or above the kSampleMin-th best of
+// the 1024 samples (each thread's first key) at 32 keys per thread, about
+// 2048 of 32768; with fewer keys per thread the target rises in proportion
+// (sample_target), so that about 2048 are kept at any chunk size (at 8 per
+// thread a fixed 64 kept about 512, under the 512 needed half of the time,
+// and the selection then fell back to its slow path over every key).
 constexpr uint32_t kSampleMin = 64;
+template <int kPer>
+__device__ __forceinline__ uint32_t sample_target(uint32_t nsamp) {
+  static_assert(kPer >= 1 && kPer <= 32, "keys per thread");
+  return min(nsamp, kSampleMin * (32u / kPer));
+}
 constexpr int kWaves = kTopkThreads / 64;
 constexpr uint32_t kCompactPerWave = 512;                  // compaction capacity of one wave
 constexpr int kCompactPerLane = kCompactPerWave / 64;      // 8 compacted keys per thread
@@ -225,7 +236,7 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
     {
       uint32_t h, above, maxge, nsamp;
       scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, nsamp);
-      const uint32_t target = min(nsamp, kSampleMin);
+      const uint32_t target = sample_target<kPer>(nsamp);
       if (target > 0 && above < target && target <= above + h) sh.lo = kBins - 1 - tid;
     }
     __syncthreads();
@@ -685,7 +696,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
         __syncthreads();
         uint32_t h, above, maxge, nsamp;
         scan_bins(sh.hist, sh.wsum, sh.wmax, tid, h, above, maxge, nsamp);
-        const uint32_t target = min(nsamp, kSampleMin);
+        const uint32_t target = sample_target<kPer>(nsamp);
         if (target > 0 && above < target && target <= above + h) sh.lo = kBins - 1 - tid;
         if (nsamp == 0 && tid == 0) sh.lo = 0;
         __syncthreads();
