@@ -107,20 +107,21 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
 
   // m, the bad flag and Z over all chunks, with the sink (phase 1 stores the
   // head's sink with every statistic).
-  const HeadNorm hn = head_norm<kB>(x[0].w, nch, [&](uint32_t cc) { return x[cc]; }, stat_at);
+  float w[kB];
+  const HeadNorm hn = head_norm<kB>(x[0].w, nch, [&](uint32_t cc) { return x[cc]; }, stat_at, w);
 
-  // acc = sum_c exp(m_c - m) O_c in chunk order, over the row's chunks only.
+  // acc = sum_c exp(m_c - m) O_c in chunk order, over the row's chunks only
+  // (selects, not branches, for the first batch).
   f32x4 acc[kVec];
 #pragma unroll
   for (int h = 0; h < kVec; ++h) acc[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < kB; ++i) {
-    if (static_cast<uint32_t>(i) >= nch) break;
-    const float w = chunk_weight(x[i], hn.m);
+    const bool in = static_cast<uint32_t>(i) < nch;
 #pragma unroll
     for (int h = 0; h < kVec; ++h)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(w, pv[i][h][k], acc[h][k]);
+      for (int k = 0; k < 4; ++k) acc[h][k] = in ? fmaf(w[i], pv[i][h][k], acc[h][k]) : acc[h][k];
   }
   for (uint32_t cc = kB; cc < nch; ++cc) {
     const float w = chunk_weight(stat_at(cc), hn.m);

@@ -123,9 +123,12 @@ __device__ __forceinline__ float chunk_weight(const float4 &s, float m) { return
 // first_at(cc) gives the statistics of the first kUnrolled chunks (called
 // with compile-time cc, so statistics held in register arrays stay in
 // registers), later_at(cc) those of the rest; chunks are taken in order.
+// w_first[cc] receives the weight of each of the first kUnrolled chunks (0
+// past the row's chunks), so that the weighted sum need not recompute them.
+// The unrolled part selects rather than branches on cc < nch.
 template <int kUnrolled, class FirstAt, class LaterAt>
 __device__ __forceinline__ HeadNorm head_norm(float sink, uint32_t nch, const FirstAt &first_at,
-                                              const LaterAt &later_at) {
+                                              const LaterAt &later_at, float (&w_first)[kUnrolled]) {
   bool bad = !__builtin_isfinite(sink);
   float m = bad ? 0.0f : sink;
   auto take_max = [&](const float4 &s) {
@@ -133,16 +136,21 @@ __device__ __forceinline__ HeadNorm head_norm(float sink, uint32_t nch, const Fi
     if (s.y > 0.0f) m = fmaxf(m, s.x);
   };
 #pragma unroll
-  for (int cc = 0; cc < kUnrolled; ++cc)
-    if (static_cast<uint32_t>(cc) < nch) take_max(first_at(cc));
+  for (int cc = 0; cc < kUnrolled; ++cc) {
+    const float4 s = first_at(cc);
+    const bool in = static_cast<uint32_t>(cc) < nch;
+    bad |= in && s.z != 0.0f;
+    m = (in && s.y > 0.0f) ? fmaxf(m, s.x) : m;
+  }
   for (uint32_t cc = kUnrolled; cc < nch; ++cc) take_max(later_at(cc));
   float z = bad ? 0.0f : expf(sink - m);
 #pragma unroll
-  for (int cc = 0; cc < kUnrolled; ++cc)
-    if (static_cast<uint32_t>(cc) < nch) {
-      const float4 s = first_at(cc);
-      z = fmaf(s.y, chunk_weight(s, m), z);
-    }
+  for (int cc = 0; cc < kUnrolled; ++cc) {
+    const float4 s = first_at(cc);
+    const bool in = static_cast<uint32_t>(cc) < nch;
+    w_first[cc] = in ? chunk_weight(s, m) : 0.0f;
+    z = in ? fmaf(s.y, w_first[cc], z) : z;
+  }
   for (uint32_t cc = kUnrolled; cc < nch; ++cc) {
     const float4 s = later_at(cc);
     z = fmaf(s.y, chunk_weight(s, m), z);
