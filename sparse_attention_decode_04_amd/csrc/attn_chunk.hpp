@@ -222,9 +222,11 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
   #pragma unroll
       for (int s = 0; s < kSlots; ++s) asm volatile("" : "+v"(raw_index[s]));
     }
-    // The row's fields once, out of the loop below.
-    const uint32_t kv_len = a.kv_len;
-    const uint16_t *const kv_row0 = a.rows;
+    // The row's fields once, out of the loop below. An index i is live when
+    // 0 <= i < kv_len, i.e. when it is below min(kv_len, 2^31) as an
+    // unsigned number (one compare); past the width it reads as -1 (skip).
+    const uint32_t kv_lim = min(a.kv_len, 0x80000000u);
+    const uint16_t *const lane_row0 = a.rows + 8 * lane;   // this lane's 16 bytes of KV row 0
     uint32_t st[kSlots];
     bool use[kSlots];
     const uint16_t *src[kSlots];
@@ -233,18 +235,19 @@ __device__ __forceinline__ void attn_chunk_body(AttnChunkShared &sm, const AttnR
       const uint32_t slot = s0 + s;
       if (kDirect) {
         const int32_t i = slot < width ? raw_index[s] : -1;
-        const bool ok = i >= 0 && static_cast<uint32_t>(i) < kv_len;
-        st[s] = ok ? kLive : ((slot < width && i != -1) ? kBad : kSkip);
-        src[s] = kv_row0 + static_cast<uint64_t>(ok ? i : 0) * kDim;
+        const uint32_t iu = static_cast<uint32_t>(i);
+        const bool ok = iu < kv_lim;
+        st[s] = ok ? kLive : (i != -1 ? kBad : kSkip);
+        src[s] = lane_row0 + static_cast<uint64_t>(ok ? iu : 0u) * kDim;
       } else {
         st[s] = (slot < width && raw_mask[s] != kBf16NegInf) ? kLive : kSkip;
-        src[s] = kv_row0 + static_cast<uint64_t>(min(slot, width - 1)) * kDim;
+        src[s] = lane_row0 + static_cast<uint64_t>(min(slot, width - 1)) * kDim;
       }
       use[s] = kDirect ? st[s] == kLive : slot < width;
     }
     u32x4 gb[kSlots];
   #pragma unroll
-    for (int s = 0; s < kSlots; ++s) gb[s] = load16(src[s] + 8 * lane);
+    for (int s = 0; s < kSlots; ++s) gb[s] = load16(src[s]);
     const uint16_t *qbase = a.q + (kHg * hg + kQHeads * wave) * kDim + 8 * lane;
     u32x4 qv[kQHeads];
   #pragma unroll
