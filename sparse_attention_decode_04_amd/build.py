@@ -3,7 +3,8 @@
 Usage: python -m sparse_attention_decode_04_amd.build   (or build() from Python)
 
 Every source is compiled for gfx950 only. Device code is built with packed
-FP32 instructions disabled (-packed-fp32-ops), as required on this hardware.
+FP32 instructions disabled (-packed-fp32-ops), as required on this hardware,
+and with kernel-argument preloading into scalar registers.
 """
 from __future__ import annotations
 
@@ -23,7 +24,12 @@ SOURCES = ["indexer_score.hip", "indexer_mq.hip", "topk.hip", "gather.hip", "att
            "topk_attn.hip", "noalloc.hip", "ds_rows.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Kernel arguments: the first 8 dwords of a kernel's arguments arrive preloaded
+# in scalar registers (the attention combine passes its buffer pointers and row
+# stride there, so its first loads wait for no argument load). A kernel whose
+# first argument is a structure preloads nothing.
+DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=8"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -65,11 +65,16 @@ __global__ __launch_bounds__(kChunkThreads) void attn_chunk_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------- phase 2
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const float4 *stats_all, const float *opart_all,
+                                                                      float *out_all, uint32_t row_chunks,
+                                                                      AttnArgs a) {
   // Grid (dim chunk, row). Thread t: head t / 4, dims d0 .. d0 + 4 kVec of
-  // the workgroup's kAttnDimChunk.
+  // the workgroup's kAttnDimChunk. The leading arguments arrive in scalar
+  // registers (kernel-argument preloading); row r's statistics and partials
+  // start at r * row_chunks chunks, so the first loads are issued at once,
+  // while the row's chunk count and output row are still being read.
   constexpr int kVec = kAttnDimChunk / 4 / 4;   // f32x4 per thread
-  const uint32_t r = blockIdx.y;
+  const uint32_t r = blockIdx.y;   // < rows: one row of workgroups per table row
   // Workgroup x of a row runs on XCD x % 8 (the grid's rows are whole
   // multiples of 8 workgroups). XCD k takes the row's dim chunks 4k .. 4k + 3:
   // 64 consecutive dims, two whole 128-byte lines of every partial row, so
@@ -77,33 +82,40 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   // different XCDs every line was fetched twice, once per half).
   static_assert(kDim / kAttnDimChunk == 4 * kXcds, "four dim chunks per XCD");
   const uint32_t dc = 4 * (blockIdx.x % kXcds) + blockIdx.x / kXcds;
-  // The row's arguments in one batch of scalar loads (one wait).
-  uint32_t rows = a.rows, nch = a.chunks[r], q_row = a.q_row[r];
-  uint64_t sbits = reinterpret_cast<uint64_t>(a.stats), sbase = a.stat_base[r];
-  uint64_t pbits = reinterpret_cast<uint64_t>(a.opart), pbase = a.part_base[r];
-  uint64_t obits = reinterpret_cast<uint64_t>(a.out);
-  asm volatile("" : "+s"(rows), "+s"(nch), "+s"(q_row), "+s"(sbits), "+s"(sbase), "+s"(pbits), "+s"(pbase), "+s"(obits));
-  if (r >= rows) return;
+  const uint32_t nch = a.chunks[r], q_row = a.q_row[r];
   const uint32_t tid = threadIdx.x;
   const uint32_t head = tid >> 2;
   const uint32_t d0 = kAttnDimChunk * dc + 4 * kVec * (tid & 3);
-  const float4 *stats = global_ptr<const float4>(sbits) + sbase + head;
-  const float *op = global_ptr<const float>(pbits) + pbase + static_cast<uint64_t>(head) * kDim + d0;
+  const float4 *stats = stats_all + static_cast<uint64_t>(r) * row_chunks * kHeads + head;
+  const float *op = opart_all + (static_cast<uint64_t>(r) * row_chunks * kHeads + head) * kDim + d0;
   constexpr int kB = 8;   // chunks per batch of loads
+  // Chunk c of the row (c < nch). The first batch is clamped to the row's
+  // room instead, so that its loads need no argument; the chunks in
+  // [nch, room) it reads hold nothing of this call and are never used:
+  // every use of the first batch below is a select on c < nch.
   auto stat_at = [&](uint32_t cc) { return stats[static_cast<uint64_t>(min(cc, nch - 1)) * kHeads]; };
   auto part_at = [&](uint32_t cc, int h) {
     return *reinterpret_cast<const f32x4 *>(op + static_cast<uint64_t>(min(cc, nch - 1)) * kHeads * kDim + 4 * h);
   };
+  auto room_at = [&](int i) { return static_cast<uint64_t>(min(static_cast<uint32_t>(i), row_chunks - 1)); };
 
   // First batch of statistics and outputs, all loads in flight at once.
   float4 x[kB];
   f32x4 pv[kB][kVec];
 #pragma unroll
-  for (int i = 0; i < kB; ++i) x[i] = stat_at(i);
+  for (int i = 0; i < kB; ++i) x[i] = stats[room_at(i) * kHeads];
 #pragma unroll
   for (int i = 0; i < kB; ++i)
 #pragma unroll
-    for (int h = 0; h < kVec; ++h) pv[i][h] = part_at(i, h);
+    for (int h = 0; h < kVec; ++h)
+      pv[i][h] = *reinterpret_cast<const f32x4 *>(op + room_at(i) * kHeads * kDim + 4 * h);
+  // Every load is issued here, before any result is used: otherwise the
+  // compiler sinks the partials' loads to their first use, after the
+  // statistics' arithmetic, and the workgroup waits for two memory round
+  // trips one after the other. (The memory clobber keeps the loads above
+  // this point; the scheduling barrier keeps that arithmetic below it.)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 
   // m, the bad flag and Z over all chunks, with the sink (phase 1 stores the
   // head's sink with every statistic).
@@ -132,7 +144,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
       for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(w, q[k], acc[h][k]);
     }
   }
-  float *dst = global_ptr<float>(obits) + (static_cast<uint64_t>(q_row) * kHeads + head) * kDim + d0;
+  float *dst = out_all + (static_cast<uint64_t>(q_row) * kHeads + head) * kDim + d0;
 #pragma unroll
   for (int h = 0; h < kVec; ++h) {
     f32x4 v;
@@ -152,7 +164,8 @@ hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t max_chunk
 }
 
 hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(kDim / kAttnDimChunk, a.rows), dim3(kCombineThreads), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(kDim / kAttnDimChunk, a.rows), dim3(kCombineThreads), 0, s,
+                     static_cast<const float4 *>(a.stats), static_cast<const float *>(a.opart), a.out, a.row_chunks, a);
   return hipGetLastError();
 }
 

@@ -264,11 +264,16 @@ ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
     p->slots += t->width[r];
     p->chunks[r] = div_up(t->width[r], ds::kAttnChunk);
     p->max_chunks = std::max(p->max_chunks, p->chunks[r]);
-    p->stat_base[r] = p->stat_elems;
-    p->stat_elems += uint64_t(ds::kHeads) * p->chunks[r];
-    p->part_base[r] = p->part_elems;
-    p->part_elems += uint64_t(ds::kHeads) * ds::kDim * p->chunks[r];
   }
+  // Every row gets room for the call's largest chunk count, so that a row's
+  // statistics and partials start at r * max_chunks chunks: the combine finds
+  // them from its row index alone.
+  for (uint32_t r = 0; r < t->rows; ++r) {
+    p->stat_base[r] = uint64_t(r) * p->max_chunks * ds::kHeads;
+    p->part_base[r] = uint64_t(r) * p->max_chunks * ds::kHeads * ds::kDim;
+  }
+  p->stat_elems = uint64_t(t->rows) * p->max_chunks * ds::kHeads;
+  p->part_elems = uint64_t(t->rows) * p->max_chunks * ds::kHeads * ds::kDim;
   // Each row writes its own query row of the output: no two may share one.
   uint64_t qr[DS_ROWS_MAX];
   for (uint32_t r = 0; r < t->rows; ++r) qr[r] = t->q_row[r];
@@ -278,7 +283,8 @@ ds_status check_sparse(const ds_sparse_rows *t, SparsePlan *p) {
   return DS_OK;
 }
 
-// Attention workspace: f32x4 chunk statistics, then the f32 chunk outputs.
+// Attention workspace: f32x4 chunk statistics, then the f32 chunk outputs,
+// each with max_chunks chunks per row.
 uint64_t attn_stat_bytes(const SparsePlan &p) { return align256(p.stat_elems * 16); }
 uint64_t attn_workspace_bytes(const SparsePlan &p) {
   return attn_stat_bytes(p) + align256(p.part_elems * sizeof(float));
@@ -677,6 +683,7 @@ ds::AttnArgs attention_args(const ds_sparse_rows *rows, const SparsePlan &p, con
   a.out = out;
   a.scale = scale;
   a.rows = p.rows;
+  a.row_chunks = p.max_chunks;
   for (uint32_t r = 0; r < p.rows; ++r) {
     a.kv[r] = static_cast<const uint16_t *>(rows->kv[r]);
     a.kv_len[r] = rows->kv_len[r];

@@ -173,6 +173,7 @@ struct AttnArgs {
   float *out;                       // f32 [_, 64, 512]
   float scale;
   uint32_t rows;
+  uint32_t row_chunks;              // chunks of room per row: stat_base[r] = r * row_chunks * 64, etc.
   uint32_t width[kRowsMax];
   uint32_t chunks[kRowsMax];        // ceil(width / 64)
   uint32_t q_row[kRowsMax];
@@ -186,7 +187,8 @@ struct AttnArgs {
 // chunk 8 (x / 32) + x % 8 of row r with head group (x / 8) % 4. Workgroups go
 // to the 8 XCDs by linear id, so the four head groups of a chunk share one
 // XCD (and its L2, where they read the chunk's rows). Phase-2 grid
-// (512 / kAttnDimChunk, rows).
+// (512 / kAttnDimChunk, rows); its kernel takes stats, opart, out and
+// row_chunks as leading (preloaded) arguments.
 hipError_t launch_attn_chunks(const AttnArgs &a, bool direct, uint32_t max_chunks, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s);
 

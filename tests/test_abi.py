@@ -179,7 +179,7 @@ def test_size_queries(lib):
     s = stab((1000, 37, 1), width=(512, 37, 1))
     assert ds.gathered_elems(s) == (512 + 37 + 1) * 512
     assert ds.mask_elems(s) == 512 + 37 + 1
-    chunks = 8 + 1 + 1                          # 64-slot chunks of widths 512, 37, 1
+    chunks = 3 * 8                              # every row has room for the call's most chunks (512 slots: 8)
     stat_bytes = 64 * chunks * 16               # f32x4 statistics per (chunk, head)
     part_bytes = chunks * 64 * 512 * 4          # f32 output of each chunk
     up = lambda x: (x + 255) // 256 * 256

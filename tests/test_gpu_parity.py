@@ -245,13 +245,16 @@ def test_widths_other_than_512():
     gathered = torch.empty(ds.gathered_elems(t), dtype=torch.int16, device="cuda")
     mask = torch.empty(ds.mask_elems(t), dtype=torch.int16, device="cuda")
     invalid = torch.full((3,), 5, dtype=torch.int32, device="cuda")
-    ws = torch.empty(ds.attn_workspace_bytes(t), dtype=torch.uint8, device="cuda")
+    # The workspace starts as NaN bytes: the rows of 2 and 1 chunks have room
+    # for 11 like the widest, and nothing left in that room may reach an output.
+    ws = torch.full((ds.attn_workspace_bytes(t),), 0xFF, dtype=torch.uint8, device="cuda")
     out = torch.zeros(3 * 64 * 512, dtype=torch.float32, device="cuda")
     say("widths", width, "direct")
     ds.sparse_attn_direct(t, dev.attn_q, dev.sinks, d_idx, inp.scale, ws, out)
     torch.cuda.synchronize()
     o_direct = out.cpu().numpy().reshape(3, 64, 512).copy()
     out.zero_()
+    ws.fill_(0xFF)
     say("widths", width, "gather + attention")
     ds.gather(t, d_idx, gathered, mask, invalid)
     ds.sparse_attn(t, dev.attn_q, dev.sinks, gathered, mask, invalid, inp.scale, ws, out)
