@@ -37,12 +37,14 @@ namespace ds {
 // chunk, direct variant) read in one batch of scalar loads at entry, waited
 // for once; rows and chunks are read in the same batch.
 __device__ __forceinline__ void topk_attn_rows(const TopkLevelArgs &t, const AttnArgs &a, uint32_t r, uint32_t &rows,
-                                               uint32_t &chunks, LevelRow &lr, AttnRow &ar) {
+                                               uint32_t &chunks, LevelRow &lr, AttnRow &ar, int32_t *&out) {
   uint64_t in = reinterpret_cast<uint64_t>(t.in), in_base = t.in_base[r];
   uint64_t sc = reinterpret_cast<uint64_t>(t.scores), stride = t.score_stride;
   uint64_t fl = reinterpret_cast<uint64_t>(t.floors);
   uint32_t floor_begin = t.floor_begin[r], count = t.count[r], fc = t.floor_count[r], fb = t.fallback_count[r];
   uint32_t off = static_cast<uint32_t>(t.offset[r]), fmask = t.final_mask, cmask = t.check_mask;
+  uint64_t ibits = reinterpret_cast<uint64_t>(t.indices);
+  uint32_t out_off = t.out_offset[r];
   uint64_t kv = reinterpret_cast<uint64_t>(a.kv[r]), q = reinterpret_cast<uint64_t>(a.q);
   uint64_t sinks = reinterpret_cast<uint64_t>(a.sinks);
   uint64_t stats = reinterpret_cast<uint64_t>(a.stats), stat_base = a.stat_base[r];
@@ -53,7 +55,8 @@ __device__ __forceinline__ void topk_attn_rows(const TopkLevelArgs &t, const Att
   asm volatile("" : "+s"(in), "+s"(in_base), "+s"(sc), "+s"(stride), "+s"(fl), "+s"(floor_begin), "+s"(count),
                "+s"(fc), "+s"(fb), "+s"(off), "+s"(fmask), "+s"(cmask), "+s"(kv), "+s"(q), "+s"(sinks), "+s"(stats),
                "+s"(stat_base), "+s"(opart), "+s"(part_base), "+s"(q_row), "+s"(width), "+s"(kv_len), "+s"(scale),
-               "+s"(rows), "+s"(chunks));
+               "+s"(rows), "+s"(chunks), "+s"(ibits), "+s"(out_off));
+  out = global_ptr<int32_t>(ibits) + out_off;
   lr.in = global_ptr<const uint64_t>(in) + in_base;
   lr.scores = global_ptr<const float>(sc) + r * stride;
   lr.floors = global_ptr<const uint64_t>(fl) + floor_begin;
@@ -91,13 +94,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   uint32_t rows, chunks;
   LevelRow lr;
   AttnRow ar;
-  topk_attn_rows(t, a, r, rows, chunks, lr, ar);
+  int32_t *out;   // the row's index output
+  topk_attn_rows(t, a, r, rows, chunks, lr, ar, out);
   if (r >= rows || c >= chunks) return;   // uniform
   const uint32_t lo = c * kAttnChunk;
   // Head group 0 writes the index output: each chunk its own 64 slots, the
   // last chunk also every slot past the row's width.
   const uint32_t out_end = c + 1 == chunks ? static_cast<uint32_t>(kTopK) : lo + kAttnChunk;
-  int32_t *const out = t.indices + t.out_offset[r];
   if (lr.final_level) {   // uniform
     select_level<kFromScores, kPer>(u.sel, lr, 0, [&](uint32_t pos, int32_t index) {
       if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
