@@ -114,12 +114,16 @@ __device__ __forceinline__ uint32_t wave_prefix_max(uint32_t x) {
 // wave halves (v_permlane32_swap). Each step combines a lane with a partner
 // holding the same two operands in the other order, so every lane ends with
 // the same bits (also for floating point).
+// (Every lane has a source lane in these rotations and swaps, so the moves'
+// `old` operand is never used; passing 0 rather than x lets the compiler fold
+// each move into its operation, one DPP instruction per step instead of a
+// copy, a wait state, a move and the operation.)
 template <class Op>
 __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
-  x = op(x, dpp_u32<kDppRowRor8>(x, x));
-  x = op(x, dpp_u32<kDppRowRor4>(x, x));
-  x = op(x, dpp_u32<kDppQuadSwap2>(x, x));
-  x = op(x, dpp_u32<kDppQuadSwap1>(x, x));
+  x = op(x, dpp_u32<kDppRowRor8>(0u, x));
+  x = op(x, dpp_u32<kDppRowRor4>(0u, x));
+  x = op(x, dpp_u32<kDppQuadSwap2>(0u, x));
+  x = op(x, dpp_u32<kDppQuadSwap1>(0u, x));
   const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
   x = op(r[0], r[1]);
   const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
