@@ -338,12 +338,7 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
         uint32_t v[4], sum = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) { v[k] = sh.hist[255 - 4 * t - k]; sum += v[k]; }
-        uint32_t incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t up = __shfl_up(incl, o);
-          if (t >= static_cast<uint32_t>(o)) incl += up;
-        }
+        const uint32_t incl = wave_prefix_sum(sum);   // wave 0, every lane active
         uint32_t before = incl - sum;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -429,8 +424,7 @@ __device__ __forceinline__ void select_from_scores(TopkShared &sh, const float *
         hist_add(sh.hist, match ? static_cast<uint32_t>(kk[u] >> shift) & 255u : 256u, 256, lane);
       }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) nv += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nv), off));
+    nv = wave_sum(nv);
     if (lane == 0) atomicAdd(&sh.count, nv);
     __syncthreads();
     total = sh.count;
@@ -441,12 +435,7 @@ __device__ __forceinline__ void select_from_scores(TopkShared &sh, const float *
       uint32_t v[4], sum = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) { v[k] = sh.hist[255 - 4 * t - k]; sum += v[k]; }
-      uint32_t incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t up = __shfl_up(incl, o);
-        if (t >= static_cast<uint32_t>(o)) incl += up;
-      }
+      const uint32_t incl = wave_prefix_sum(sum);   // wave 0, every lane active
       uint32_t before = incl - sum;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
