@@ -74,7 +74,7 @@ struct TopkShared {
   uint64_t s_floor;                                          // candidate statistics of the level,
   uint32_t s_total, s_min1, s_max;                           // combined by LDS atomics
   uint64_t wkmin[kWaves], wkmax[kWaves];                     // radix fallback: key range per wave
-  uint32_t count, lo, digit, above, bin, kept, maxbin, hist_total, thr, viol;
+  uint32_t count, lo, digit, above, bin, kept, maxbin, hist_total, viol;
 };
 
 // Suffix scan of the 1024-bin histogram by the first four waves, four bins
@@ -559,7 +559,6 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
   sh.hist[tid] = 0;
   sh.cursor[tid] = 0;
   if (tid == 0) {
-    sh.thr = 0xFFFFFFFFu;
     sh.count = 0;
     sh.lo = 0;
     sh.viol = 0;
@@ -690,11 +689,17 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
         if (nsamp == 0 && tid == 0) sh.lo = 0;
         __syncthreads();
         const uint32_t lo = sh.lo;
-        uint32_t t = (b0 < kBins && b0 >= lo) ? o0 : 0xFFFFFFFFu;
-        t = wave_min(t);
-        if (lane == 0) atomicMin(&sh.thr, t);
-        __syncthreads();
-        thr = sh.thr;
+        // T: the score bits of the lower edge of bin lo - 1, one bin below
+        // the sampled bin, so that the keys binned at lo or above (about the
+        // sample's share) are kept with a few more; lo = 0 (also a zero
+        // range) keeps every valid key. Whatever T is, the keys at or above
+        // it are the best ones in score order: when they number at least
+        // `need`, the selection over them is exact, and otherwise the path
+        // below selects over every candidate.
+        if (lo > 0) {
+          const float edge = smin + static_cast<float>(lo - 1) / scale;
+          thr = max(1u, static_cast<uint32_t>(topk_key(edge, 0) >> 32));
+        }
       }
       if constexpr (!kFromScores) {
         if (!sampled) {
