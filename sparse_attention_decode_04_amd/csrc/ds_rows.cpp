@@ -192,12 +192,19 @@ ds_status check_indexer(const ds_indexer_rows *t, IndexerPlan *p) {
 uint64_t topk_workspace_bytes(const IndexerPlan &p) { return 2 * p.topk_bank * sizeof(uint64_t); }
 
 // Fused workspace: candidate lists (kIdxCand keys per indexer block), wave
-// floors (kIdxFloors per block), then two ping-pong banks of list keys.
+// floors (kIdxFloors per block), then two ping-pong banks of list keys. Every
+// row has room for the widest row's blocks (the fused indexer's grid width),
+// so row r's candidates and floors start at block r * room.
+uint32_t fused_room_blocks(const IndexerPlan &p) {
+  uint32_t room = 1;
+  for (uint32_t r = 0; r < p.rows; ++r) room = std::max(room, p.blk_begin[r + 1] - p.blk_begin[r]);
+  return room;
+}
 uint64_t fused_cand_bytes(const IndexerPlan &p) {
-  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxCand * sizeof(uint64_t));
+  return align256(uint64_t(p.rows) * fused_room_blocks(p) * ds::kIdxCand * sizeof(uint64_t));
 }
 uint64_t fused_floor_bytes(const IndexerPlan &p) {
-  return align256(uint64_t(p.blk_begin[ds::kRowsMax]) * ds::kIdxFloors * sizeof(uint64_t));
+  return align256(uint64_t(p.rows) * fused_room_blocks(p) * ds::kIdxFloors * sizeof(uint64_t));
 }
 uint64_t fused_workspace_bytes(const IndexerPlan &p) {
   return fused_cand_bytes(p) + fused_floor_bytes(p) + 2 * p.fused_bank * sizeof(uint64_t);
@@ -395,17 +402,23 @@ struct TopkInput {
   const uint64_t *floors = nullptr;
   uint32_t count[ds::kRowsMax] = {};
   uint64_t base[ds::kRowsMax] = {};
+  uint32_t room = 0;          // lists: entries of room per row (row r's at r * room)
+  uint32_t floor_room = 0;    // floors of room per row
 };
 
-// The fused indexer's candidates: 4 waves x C slots per 1024-key block.
+// The fused indexer's candidates: 4 waves x C slots per 1024-key block, row r
+// from block r * room (room = the widest row's blocks).
 TopkInput fused_input(const IndexerPlan &p, const uint64_t *cand, const uint64_t *floors) {
   TopkInput in{};
   in.lists = cand;
   in.floors = floors;
   const uint32_t per_block = ds::kIdxFloors * fused_wave_cand(p);
+  const uint32_t room = fused_room_blocks(p);
+  in.room = room * per_block;
+  in.floor_room = room * ds::kIdxFloors;
   for (uint32_t r = 0; r < p.rows; ++r) {
     in.count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * per_block;
-    in.base[r] = uint64_t(p.blk_begin[r]) * per_block;
+    in.base[r] = uint64_t(r) * in.room;
   }
   return in;
 }
@@ -438,6 +451,8 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
     a.rows = p.rows;
     a.from_scores = (level == 0 && !from_lists) ? 1 : 0;
     a.floors = in.floors;
+    a.list_room = level == 0 ? in.room : 0;   // later levels' lists sit one row after another
+    a.floor_room = in.floor_room;
     // Candidates per thread, and so the chunk size: the smallest of 4, 8 and
     // 16 that holds every row still selecting, which makes this the final
     // level; otherwise chunks of scores (see scores_per_thread) or of 8192
@@ -469,7 +484,7 @@ ds_status run_topk_levels(const ds_indexer_rows *rows, const IndexerPlan &p, con
         a.final_mask |= 1u << r;
         if (from_lists) {
           a.check_mask |= 1u << r;
-          a.floor_begin[r] = p.blk_begin[r] * ds::kIdxFloors;
+          a.floor_begin[r] = uint64_t(r) * in.floor_room;
           a.floor_count[r] = (p.blk_begin[r + 1] - p.blk_begin[r]) * ds::kIdxFloors;
           a.fallback_count[r] = p.visible[r];
         }

@@ -111,6 +111,9 @@ struct TopkLevelArgs {
   uint64_t out_base[kRowsMax];      // element offset of row r's lists in `out`
   int32_t offset[kRowsMax];
   uint32_t out_offset[kRowsMax];
+  // Final level inside the attention: the room per row of the input lists
+  // (0 when they are not laid out one row per room) and of the floors.
+  uint32_t list_room, floor_room;
   uint32_t blk_begin[kRowsMax + 1];
   // Candidates from the fused indexer: on the final level of a row with bit r
   // of check_mask, the result stands only if no block floor of the row says

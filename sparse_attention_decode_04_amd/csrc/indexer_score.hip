@@ -241,7 +241,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_score_kernel(IndexerArgs 
   const uint16_t *const keys = global_ptr<const uint16_t>(kbits);
   const uint32_t nblk = blk1 - blk0;
   const bool live = xb < nblk;   // uniform (always, on a compact grid)
-  const uint32_t block = blk0 + xb;   // workgroup index in the candidate layout
+  // Workgroup index in the fused candidate layout: every row has room for
+  // the grid's blocks per row (the widest row's), so row r's candidates and
+  // floors start at block r * gridDim.x and a reader finds them from the row
+  // alone (only the fused stage, which keeps the 2-D grid, uses it).
+  const uint32_t block = r * gridDim.x + xb;
   // Tiles of 16 keys are dealt round robin over the row's waves: wave w of
   // the row's workgroup b takes tiles t0 = 4b + w, t0 + S, t0 + 2S, ...
   // (S = 4 x the row's workgroups), so at any time the row's waves read

@@ -79,8 +79,15 @@ __device__ __forceinline__ void topk_attn_rows(const TopkLevelArgs &t, const Att
   ar.scale = __uint_as_float(scale);
 }
 
+// The leading arguments arrive in scalar registers (kernel-argument
+// preloading): the level's input lists and the fused indexer's floors, with
+// the room per row of each (row r's at r * room; a list room of 0: the lists
+// are not in that layout). With them the row's candidates and floors are
+// loaded first, before the other arguments are read.
 template <bool kFromScores, int kPer>
-__global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t, AttnArgs a) {
+__global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(const uint64_t *lists, const uint64_t *floors,
+                                                                 uint32_t list_room, uint32_t floor_room,
+                                                                 TopkLevelArgs t, AttnArgs a) {
   __shared__ union Shared {
     TopkShared sel;
     AttnChunkShared att;
@@ -89,6 +96,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
 
   // Grid (x, row), as the attention's phase 1.
   const uint32_t r = blockIdx.y;
+  const uint32_t tid = threadIdx.x;
+  const bool have_pre = !kFromScores && list_room != 0;   // uniform
+  const bool have_pre_floor = !kFromScores && floor_room != 0;
+  uint64_t pre_keys[kPer] = {};
+  uint64_t pre_floor = 0;
+  if constexpr (!kFromScores) {
+    // Unconditional loads (both pointers are valid for a level over lists;
+    // a room of 0 reads entry 0, unused), so that nothing waits for them
+    // before the selection does.
+    const uint64_t *row = lists + static_cast<uint64_t>(r) * list_room;
+    const uint32_t last = list_room > 0 ? list_room - 1 : 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) pre_keys[e] = row[min(tid + kTopkThreads * e, last)];
+    const uint32_t flast = floor_room > 0 ? floor_room - 1 : 0;
+    pre_floor = floors[static_cast<uint64_t>(r) * floor_room + min(tid, flast)];
+  }
   uint32_t c, hg;
   attn_block(blockIdx.x, c, hg);
   uint32_t rows, chunks;
@@ -102,10 +125,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
   // last chunk also every slot past the row's width.
   const uint32_t out_end = c + 1 == chunks ? static_cast<uint32_t>(kTopK) : lo + kAttnChunk;
   if (lr.final_level) {   // uniform
-    select_level<kFromScores, kPer>(u.sel, lr, 0, [&](uint32_t pos, int32_t index) {
-      if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
-      if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
-    });
+    select_level<kFromScores, kPer>(
+        u.sel, lr, 0,
+        [&](uint32_t pos, int32_t index) {
+          if (pos - lo < static_cast<uint32_t>(kAttnChunk)) slot_index[pos - lo] = index;   // pos in [lo, lo + 64)
+          if (hg == 0 && pos >= lo && pos < out_end) out[pos] = index;
+        },
+        have_pre, pre_keys, have_pre_floor, pre_floor);
   } else if (threadIdx.x < static_cast<uint32_t>(kAttnChunk)) {
     // The row finished its selection in an earlier pass: its indices are in
     // the output already.
@@ -118,20 +144,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_attn_kernel(TopkLevelArgs t
 
 hipError_t launch_topk_attn(const TopkLevelArgs &t, const AttnArgs &a, uint32_t max_chunks, hipStream_t s) {
   const dim3 blocks(kXcds * kAttnHeadGroups * ((max_chunks + kXcds - 1) / kXcds), a.rows);
+  // A level without floors passes its lists in their place (a valid address
+  // for the kernel's unconditional floor load) and a floor room of 0.
+  const uint64_t *fl = t.floors != nullptr ? t.floors : t.in;
+  const uint32_t froom = t.floors != nullptr ? t.floor_room : 0;
   if (t.from_scores) {
     // The scores of every row fit one chunk of 4, 8 or 16 per thread.
     if (t.per_thread == 4)
-      hipLaunchKernelGGL((topk_attn_kernel<true, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+      hipLaunchKernelGGL((topk_attn_kernel<true, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, t.in, fl, t.list_room, froom, t, a);
     else if (t.per_thread == 8)
-      hipLaunchKernelGGL((topk_attn_kernel<true, 8>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+      hipLaunchKernelGGL((topk_attn_kernel<true, 8>), dim3(blocks), dim3(kTopkThreads), 0, s, t.in, fl, t.list_room, froom, t, a);
     else
-      hipLaunchKernelGGL((topk_attn_kernel<true, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+      hipLaunchKernelGGL((topk_attn_kernel<true, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, t.in, fl, t.list_room, froom, t, a);
   } else if (t.per_thread == 4)
-    hipLaunchKernelGGL((topk_attn_kernel<false, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+    hipLaunchKernelGGL((topk_attn_kernel<false, 4>), dim3(blocks), dim3(kTopkThreads), 0, s, t.in, fl, t.list_room, froom, t, a);
   else if (t.per_thread == 16)
-    hipLaunchKernelGGL((topk_attn_kernel<false, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+    hipLaunchKernelGGL((topk_attn_kernel<false, 16>), dim3(blocks), dim3(kTopkThreads), 0, s, t.in, fl, t.list_room, froom, t, a);
   else
-    hipLaunchKernelGGL((topk_attn_kernel<false, kTopkPerThreadLater>), dim3(blocks), dim3(kTopkThreads), 0, s, t, a);
+    hipLaunchKernelGGL((topk_attn_kernel<false, kTopkPerThreadLater>), dim3(blocks), dim3(kTopkThreads), 0, s, t.in, fl, t.list_room, froom, t, a);
   return hipGetLastError();
 }
 

@@ -543,9 +543,16 @@ __device__ __forceinline__ LevelRow level_row(const TopkLevelArgs &a, uint32_t r
 // when every row of the level has at most 4096.
 // emit_final(pos, index): the final level's index of rank pos (index +
 // offset, or -1 for an empty slot).
+// A caller that has already loaded the level's candidates (kFromScores
+// false, chunk 0: candidate e of this thread at position tid + 1024 e, from
+// anywhere in the row's room) passes them as pre_keys with have_pre set, and
+// likewise the floor at position min(tid, room - 1) as pre_floor with
+// have_pre_floor set; positions past the row's own count are masked here.
 template <bool kFromScores, int kPer, class EmitFinal>
 __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr, uint32_t chunk,
-                                             const EmitFinal &emit_final) {
+                                             const EmitFinal &emit_final, bool have_pre,
+                                             const uint64_t (&pre_keys)[kPer], bool have_pre_floor,
+                                             uint64_t pre_floor) {
   static_assert(kPer <= kTopkPerThreadFirst, "the first level's LDS holds 32 score slots per thread");
   constexpr uint32_t kChunk = kTopkThreads * kPer;
 
@@ -588,10 +595,15 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
       ordv[e] = p < end ? static_cast<uint32_t>(topk_key(__uint_as_float(ordv[e]), p) >> 32) : 0u;
     }
   } else {
-    const char *in = reinterpret_cast<const char *>(lr.in);
+    if (have_pre) {   // uniform
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      keyv[e] = *reinterpret_cast<const uint64_t *>(in + 8u * min(begin + tid + kTopkThreads * e, lastp));
+      for (int e = 0; e < kPer; ++e) keyv[e] = pre_keys[e];
+    } else {
+      const char *in = reinterpret_cast<const char *>(lr.in);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        keyv[e] = *reinterpret_cast<const uint64_t *>(in + 8u * min(begin + tid + kTopkThreads * e, lastp));
+    }
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       if (begin + tid + kTopkThreads * e >= end) keyv[e] = 0;
@@ -602,7 +614,8 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
   uint64_t floor_hi = 0;
   if constexpr (!kFromScores) {
     if (check_row && lr.floor_count > 0) {
-      floor_hi = lr.floors[min(tid, lr.floor_count - 1)];
+      // (A prefetched floor past the row's own floors is not one of them: 0.)
+      floor_hi = have_pre_floor ? (tid < lr.floor_count ? pre_floor : 0ull) : lr.floors[min(tid, lr.floor_count - 1)];
       for (uint32_t b = tid + kTopkThreads; b < lr.floor_count; b += kTopkThreads) floor_hi = max(floor_hi, lr.floors[b]);
     }
   }
@@ -770,6 +783,13 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
   };
   if constexpr (kFromScores) run(OrdCand<kPer>{ordv, begin + tid});
   else run(KeyCand<kPer>{keyv});
+}
+// The same, loading the candidates and floors itself.
+template <bool kFromScores, int kPer, class EmitFinal>
+__device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr, uint32_t chunk,
+                                             const EmitFinal &emit_final) {
+  const uint64_t none[kPer] = {};
+  select_level<kFromScores, kPer>(sh, lr, chunk, emit_final, false, none, false, 0ull);
 }
 
 }  // namespace ds

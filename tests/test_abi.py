@@ -160,12 +160,14 @@ def test_size_queries(lib):
     assert ds.topk_workspace_bytes(itab((1000, 16384))) == 0      # one chunk per row
     # beyond 8 x 16384 scores in a row, chunks of 32768: 200000 -> 7 chunks
     assert ds.topk_workspace_bytes(itab((1000, 200000))) == 2 * 8 * 512 * 7
-    # fused: 128 candidate keys and four u64 floors per 1024-key block (each
-    # region 256-byte aligned), plus two list banks for rows whose candidates
-    # exceed one 8192-key chunk (rows over 65536 keys): here the 70000-key
-    # row, 69 blocks -> 8832 candidates -> 2 chunks of 512
-    blocks = 1 + 69 + 32 + 33
-    assert ds.indexer_topk_workspace_bytes(t) == blocks * 128 * 8 + 4352 + 2 * 2 * 512 * 8
+    # fused: 128 candidate keys and four u64 floors per 1024-key block, every
+    # row with room for the widest row's blocks (here the 70000-key row's 69;
+    # each region 256-byte aligned), plus two list banks for rows whose
+    # candidates exceed one 8192-key chunk (rows over 65536 keys): here the
+    # 70000-key row, 69 blocks -> 8832 candidates -> 2 chunks of 512
+    room = 69
+    floors = -(-4 * room * 4 * 8 // 256) * 256
+    assert ds.indexer_topk_workspace_bytes(t) == 4 * room * 128 * 8 + floors + 2 * 2 * 512 * 8
     big = itab((200000,))
     nb = 196
     cand = -(-nb * 128 * 8 // 256) * 256
