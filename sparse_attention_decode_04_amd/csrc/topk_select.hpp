@@ -560,7 +560,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
   const uint32_t end = min(lr.count, begin + kChunk);
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const uint32_t wave = tid >> 6;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, known to the compiler
   const bool final_level = lr.final_level;
 
   sh.hist[tid] = 0;
@@ -625,33 +625,41 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
   auto run = [&](const auto &c) {
     // Count and extreme score bits of the valid keys. A missing key has high
     // word 0 (every valid key's is nonzero), so it never raises the maximum
-    // and, as 0 - 1 in unsigned arithmetic, never lowers the minimum.
+    // and, as 0 - 1 in unsigned arithmetic, never lowers the minimum. The
+    // count comes from one ballot per candidate slot (scalar popcounts); the
+    // extremes from lane reductions. Sixteen waves share the CU's four SIMDs
+    // here, so every vector instruction of this phase is paid four times.
     uint32_t nvalid = 0, omin1 = 0xFFFFFFFFu, omax = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const uint32_t o = c.hi(e);
-      nvalid += o != 0 ? 1u : 0u;
+      nvalid += static_cast<uint32_t>(__popcll(__ballot(o != 0)));
       omin1 = min(omin1, o - 1u);
       omax = max(omax, o);
     }
     // Per-wave totals, combined across the waves by one LDS atomic per
     // statistic from each wave; every thread reads the four results after a
     // barrier (combining sixteen per-wave slots in every thread cost more
-    // than the rest of this phase).
-    nvalid = wave_sum(nvalid);
-    omin1 = wave_min(omin1);
-    omax = wave_max(omax);
+    // than the rest of this phase). The reduced values are made explicitly
+    // wave-uniform, so that each atomic is a single instruction rather than
+    // the compiler's loop over the active lanes.
+    omin1 = __builtin_amdgcn_readfirstlane(wave_min(omin1));
+    omax = __builtin_amdgcn_readfirstlane(wave_max(omax));
+    // Only the waves holding floors (threads below floor_count) reduce them;
+    // the others' floors are all 0, the maximum's starting value.
+    const bool wave_floors = check_row && wave * 64u < lr.floor_count;   // uniform
     uint64_t wfloor = 0;
-    if (check_row) {   // 64-bit wave maximum: the high words, then the low words of the lanes holding it
-      const uint32_t hi = wave_max(static_cast<uint32_t>(floor_hi >> 32));
-      const uint32_t lo = wave_max(static_cast<uint32_t>(floor_hi >> 32) == hi ? static_cast<uint32_t>(floor_hi) : 0u);
+    if (wave_floors) {   // 64-bit wave maximum: the high words, then the low words of the lanes holding it
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(wave_max(static_cast<uint32_t>(floor_hi >> 32)));
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(
+          wave_max(static_cast<uint32_t>(floor_hi >> 32) == hi ? static_cast<uint32_t>(floor_hi) : 0u));
       wfloor = (static_cast<uint64_t>(hi) << 32) | lo;
     }
     if (lane == 0) {
       atomicAdd(&sh.s_total, nvalid);
       atomicMin(&sh.s_min1, omin1);
       atomicMax(&sh.s_max, omax);
-      if (check_row) atomicMax(reinterpret_cast<unsigned long long *>(&sh.s_floor), static_cast<unsigned long long>(wfloor));
+      if (wave_floors) atomicMax(reinterpret_cast<unsigned long long *>(&sh.s_floor), static_cast<unsigned long long>(wfloor));
     }
     __syncthreads();
     const uint32_t total = sh.s_total, min1 = sh.s_min1, gmax = sh.s_max;
