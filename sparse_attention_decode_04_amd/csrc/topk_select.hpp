@@ -196,7 +196,12 @@ struct KeyCand {
 // kFresh: hist, cursor, count and lo still hold the zeros written at the
 // start of the kernel (published by a barrier since), and no earlier reader
 // of the shared arrays remains, so they are not cleared again.
-template <int kPer, bool kSample, bool kFresh = false, class Cand, class Emit>
+// kIntBins: bins of equal width in the score bits rather than in the score,
+// (o - omin) >> shift: half the instructions per key and no division. Any
+// binning that preserves the score order gives the same selection; this one
+// suits candidates that are a row's best keys (a narrow range of scores),
+// not raw scores around zero, whose bits span many binades.
+template <int kPer, bool kSample, bool kFresh = false, bool kIntBins = false, class Cand, class Emit>
 __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, uint32_t total, uint32_t need,
                                                 uint32_t omin, uint32_t omax, const Emit &emit) {
   const uint32_t tid = threadIdx.x;
@@ -209,18 +214,31 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
     __syncthreads();
   }
 
-  const float smin = ord_score(omin), smax = ord_score(omax);
-  const float range = smax - smin;
-  const float scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
+  static_assert(kBins == 1 << 10, "integer bins take the top 10 bits of the span");
+  float smin = 0.0f, scale = 0.0f;
+  uint32_t shift = 0;
+  if constexpr (kIntBins) {
+    // (omax - omin) >> shift < kBins; every valid key's bits lie in [omin, omax].
+    const uint32_t span = omax - omin;
+    shift = span < static_cast<uint32_t>(kBins) ? 0u : static_cast<uint32_t>(32 - __builtin_clz(span) - 10);
+  } else {
+    smin = ord_score(omin);
+    const float range = ord_score(omax) - smin;
+    scale = (range > 0.0f && __builtin_isfinite(range)) ? static_cast<float>(kBins) / range : 0.0f;
+  }
+  // Bin of a key's score bits o (nonzero: a valid key). A zero range gives
+  // every (finite) key bin 0.
+  auto bin_of = [&](uint32_t o) -> uint32_t {
+    if constexpr (kIntBins) return (o - omin) >> shift;
+    else return static_cast<uint32_t>(fminf((ord_score(o) - smin) * scale, static_cast<float>(kBins - 1)));
+  };
   // Bin of every candidate, once, two 16-bit bins per register; kBins = no
-  // key. A zero range gives scale 0 and every (finite) key bin 0.
+  // key.
   uint32_t binp[kPer / 2];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const uint32_t o = c.hi(e);
-    const float x = (ord_score(o) - smin) * scale;
-    const uint32_t b = o != 0 ? static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)))
-                              : static_cast<uint32_t>(kBins);
+    const uint32_t b = o != 0 ? bin_of(o) : static_cast<uint32_t>(kBins);
     if (e & 1) binp[e / 2] |= b << 16;
     else binp[e / 2] = b;
   }
@@ -274,8 +292,7 @@ __device__ __forceinline__ void counting_select(TopkShared &sh, const Cand &c, u
     __syncthreads();
     if (tid < kept) {
       const uint64_t kk = sh.cand[tid];
-      const float x = (ord_score(static_cast<uint32_t>(kk >> 32)) - smin) * scale;
-      const uint32_t b = static_cast<uint32_t>(fminf(x, static_cast<float>(kBins - 1)));
+      const uint32_t b = bin_of(static_cast<uint32_t>(kk >> 32));
       const uint32_t base = sh.sfx[b], n = sh.hist[b];
       uint32_t rank = 0;
       for (uint32_t q = 0; q < n; ++q) rank += sh.cand[base + q] > kk ? 1u : 0u;
@@ -726,7 +743,7 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
         if (!sampled) {
           // Every valid key stays: select over the candidates as loaded, on
           // the shared arrays as the kernel initialised them.
-          counting_select<kPer, false, true>(sh, c, total, need, gmin, gmax, emit);
+          counting_select<kPer, false, true, true>(sh, c, total, need, gmin, gmax, emit);
           return;
         }
       }
@@ -761,8 +778,8 @@ __device__ __forceinline__ void select_level(TopkShared &sh, const LevelRow &lr,
   #pragma unroll
         for (int j = 0; j < kCompactPerLane; ++j)
           kc[j] = lane + 64u * j < wcount ? region[lane + 64 * j] : 0ull;
-        counting_select<kCompactPerLane, false>(sh, KeyCand<kCompactPerLane>{kc}, kept, need, max(thr, gmin), gmax,
-                                                emit);
+        counting_select<kCompactPerLane, false, false, !kFromScores>(sh, KeyCand<kCompactPerLane>{kc}, kept, need,
+                                                                     max(thr, gmin), gmax, emit);
       } else if constexpr (kFromScores) {
         // Heavy ties: select over every candidate. The score bits move to LDS
         // (over the compaction regions), which frees their registers.
