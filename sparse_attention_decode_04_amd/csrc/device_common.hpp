@@ -149,14 +149,6 @@ __device__ __forceinline__ float half_sum(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float half_max(float v) {
-  v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
-  v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
-  v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
-  v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 // Whether any lane of this lane's 32-lane half has the flag set.
 __device__ __forceinline__ bool half_any(bool f) {
   const uint64_t m = __ballot(f);
@@ -170,11 +162,6 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   v = half_sum(v);
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(h[0]) + __uint_as_float(h[1]);
-}
-__device__ __forceinline__ float wave_max_f(float v) {
-  v = half_max(v);
-  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
 }
 
 // max(x, 0) with maxNum's treatment of a NaN input (the result is 0) in one
@@ -192,6 +179,32 @@ __device__ __forceinline__ float opaque_inf() {
   return inf;
 }
 __device__ __forceinline__ float relu_num(float x, float inf) { return __builtin_amdgcn_fmed3f(x, 0.0f, inf); }
+
+// Maxima of values that are never NaN (finite or infinite), over the 32
+// lanes of a wave half and over the whole wave, in every lane: the scheme of
+// half_sum / wave_sum_f with max(a, b) as the median of a, b and +inf, one
+// instruction per step (fmaxf adds a NaN-quieting instruction to each).
+// The maximum is exact, so every lane ends with the same bits. (A med3
+// cannot take a DPP operand, so the lane moves are plain DPP moves: every
+// lane has a source in these patterns.)
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float half_max(float v) {
+  const float inf = opaque_inf();
+  v = __builtin_amdgcn_fmed3f(v, dpp_mov_f32<kDppRowRor8>(v), inf);
+  v = __builtin_amdgcn_fmed3f(v, dpp_mov_f32<kDppRowRor4>(v), inf);
+  v = __builtin_amdgcn_fmed3f(v, dpp_mov_f32<kDppQuadSwap2>(v), inf);
+  v = __builtin_amdgcn_fmed3f(v, dpp_mov_f32<kDppQuadSwap1>(v), inf);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), inf);
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = half_max(v);
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_amdgcn_fmed3f(__uint_as_float(h[0]), __uint_as_float(h[1]), opaque_inf());
+}
 
 // A device pointer handed over as its integer bits (to pass it through an
 // empty asm statement), rebuilt as a global-memory pointer so that accesses
