@@ -89,23 +89,23 @@ __device__ __forceinline__ void wave_candidates(const IndexerArgs &a, const uint
   uint32_t thr = 1;   // keep every valid key
   uint32_t kept = nvalid;
   if (nvalid > kC) {
-    // T is built from the top two bits at a time (three candidate values per
-    // step, whose counts are independent and overlap in latency), each time
-    // taking the largest value that still has at least kKeep keys at
-    // or above it. It stops as soon as the accepted T keeps at most
-    // kC keys; otherwise it ends at the kKeep-th best score
-    // bits. Any T that keeps at most kC keys is a valid floor: the
-    // final level's check compares the floors with its 512th key, so which
-    // one is taken changes no index. If none keeps at most kC, T
-    // ends as the kKeep-th best score bits (ties at T overflow).
+    // T is built from the top bit down, one bit per step, each time taking
+    // the larger value that still has at least kKeep keys at or above it.
+    // It stops as soon as the accepted T keeps at most kC keys; otherwise
+    // it ends at the kKeep-th best score bits. Any T that keeps at most kC
+    // keys is a valid floor: the final level's check compares the floors
+    // with its 512th key, so which one is taken changes no index. If none
+    // keeps at most kC, T ends as the kKeep-th best score bits (ties at T
+    // overflow). The search runs on the compute unit's one scalar ALU (the
+    // ballots' popcounts and sums) for every wave of the CU at once, so its
+    // cost is its scalar instruction count: one count per bit takes fewer
+    // in all than three counts per two bits, though the steps double.
     thr = 0;
     kept = 256;   // count_ge(0); replaced at the first accepted step (count_ge(1) = nvalid > kKeep)
-    for (int b = 30; b >= 0; b -= 2) {
-      const uint32_t t1 = thr | (1u << b), t2 = thr | (2u << b), t3 = thr | (3u << b);
-      const uint32_t n1 = count_ge(t1), n2 = count_ge(t2), n3 = count_ge(t3);
-      if (n3 >= kKeep) { thr = t3; kept = n3; }
-      else if (n2 >= kKeep) { thr = t2; kept = n2; }
-      else if (n1 >= kKeep) { thr = t1; kept = n1; }
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t t1 = thr | (1u << b);
+      const uint32_t n1 = count_ge(t1);
+      if (n1 >= kKeep) { thr = t1; kept = n1; }
       if (kept <= kC) break;   // uniform
     }
   }
